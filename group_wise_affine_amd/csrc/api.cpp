@@ -1,0 +1,227 @@
+// libqmm C ABI: argument validation, routing and launch. Every check runs on
+// the host before any launch; on error nothing is queued and the thread-local
+// message is set. The checks mirror the argument errors of the mlx ops
+// ("Add the 3bit packed qmm_t", ops.cpp extract_quantized_matmul_dims and
+// quantized_matmul; "mlx 1.0.0 backend/cpu/quantized.cpp", the bits / group
+// size / dtype switches).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <limits>
+
+#include "../../include/libqmm.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qmm_status fail(qmm_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+qmm_status check_bits_gs(int bits, int gs) {
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 ||
+        bits == 8))
+    return fail(QMM_E_BITS, "bits must be 2, 3, 4, 5, 6 or 8 (got %d)", bits);
+  if (!(gs == 32 || gs == 64 || gs == 128))
+    return fail(QMM_E_GROUP, "group_size must be 32, 64 or 128 (got %d)", gs);
+  return QMM_OK;
+}
+
+qmm_status check_k(int64_t K, int gs) {
+  if (K < 1 || K % gs != 0)
+    return fail(QMM_E_SHAPE,
+                "K (%lld) must be a positive multiple of group_size (%d); "
+                "pad the weight rows with zeros",
+                (long long)K, gs);
+  return QMM_OK;
+}
+
+size_t elem_bytes(qmm_dtype dt) { return dt == QMM_F32 ? 4 : 2; }
+
+qmm_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(QMM_E_LAUNCH, "%s: launch failed: %s", what,
+                hipGetErrorString(e));
+  g_err[0] = 0;
+  return QMM_OK;
+}
+
+constexpr int64_t kI32 = std::numeric_limits<int32_t>::max();
+
+// Largest K the streaming GEMV stages in LDS (one row of x plus chunk sums
+// within 64 KiB; 8-bit bf16 stages fp32 activations).
+int64_t qmv_max_k(int bits, qmm_dtype dt) {
+  const int64_t words = (bits == 8 && dt == QMM_BF16) ? 33 : 17;
+  return (64 * 1024 / (words * 4)) * 32;
+}
+
+qmm_status check_matmul(const char* tag, const void* x, const uint32_t* wq,
+                        const void* s, const void* b, qmm_dtype dt, int64_t M,
+                        int64_t N, int64_t K, int gs, int bits, const void* y) {
+  if (!x || !wq || !s || !b || !y)
+    return fail(QMM_E_NULL, "%s: x, wq, scales, biases and y must be non-NULL",
+                tag);
+  qmm_status st = check_bits_gs(bits, gs);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE,
+                "%s: only float16 and bfloat16 are supported (got dtype %d)",
+                tag, (int)dt);
+  if (M < 1 || N < 1)
+    return fail(QMM_E_SHAPE, "%s: M (%lld) and N (%lld) must be >= 1", tag,
+                (long long)M, (long long)N);
+  st = check_k(K, gs);
+  if (st) return st;
+  if (M > kI32 || N > kI32 || K > kI32 || M * K > ((int64_t)1 << 40) ||
+      N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "%s: problem too large", tag);
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "%s: x, wq and y must be 16-byte aligned", tag);
+  if (!aligned(s, 2) || !aligned(b, 2))
+    return fail(QMM_E_ALIGN, "%s: scales and biases must be 2-byte aligned",
+                tag);
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmm_last_error(void) { return g_err; }
+
+int qmm_crossover_m(int bits, qmm_dtype dt) {
+  return qmm::crossover_m(bits, (int)dt);
+}
+
+qmm_status qmm_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
+                        int group_size, int bits, uint32_t* wq, void* scales,
+                        void* biases, void* stream) {
+  if (!w || !wq || !scales || !biases)
+    return fail(QMM_E_NULL, "qmm_quantize: w, wq, scales and biases must be non-NULL");
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16 && dt != QMM_F32)
+    return fail(QMM_E_DTYPE, "qmm_quantize: only floating point inputs are supported");
+  if (rows < 1) return fail(QMM_E_SHAPE, "qmm_quantize: rows must be >= 1");
+  st = check_k(K, group_size);
+  if (st) return st;
+  if (rows * K > ((int64_t)1 << 42))
+    return fail(QMM_E_SHAPE, "qmm_quantize: problem too large");
+  if (!aligned(w, 16) || !aligned(wq, 16))
+    return fail(QMM_E_ALIGN, "qmm_quantize: w and wq must be 16-byte aligned");
+  if (!aligned(scales, elem_bytes(dt)) || !aligned(biases, elem_bytes(dt)))
+    return fail(QMM_E_ALIGN, "qmm_quantize: scales/biases misaligned");
+  return launched(qmm::launch_quantize((int)dt, bits, group_size, w, rows, K, wq,
+                                       scales, biases, (hipStream_t)stream),
+                  "qmm_quantize");
+}
+
+qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
+                          const void* biases, qmm_dtype dt, int64_t rows,
+                          int64_t K, int group_size, int bits, void* w_out,
+                          void* stream) {
+  if (!wq || !scales || !biases || !w_out)
+    return fail(QMM_E_NULL, "qmm_dequantize: wq, scales, biases and w_out must be non-NULL");
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16 && dt != QMM_F32)
+    return fail(QMM_E_DTYPE, "qmm_dequantize: only floating point outputs are supported");
+  if (rows < 1) return fail(QMM_E_SHAPE, "qmm_dequantize: rows must be >= 1");
+  st = check_k(K, group_size);
+  if (st) return st;
+  if (rows * K > ((int64_t)1 << 42))
+    return fail(QMM_E_SHAPE, "qmm_dequantize: problem too large");
+  if (!aligned(wq, 16) || !aligned(w_out, 16))
+    return fail(QMM_E_ALIGN, "qmm_dequantize: wq and w_out must be 16-byte aligned");
+  if (!aligned(scales, elem_bytes(dt)) || !aligned(biases, elem_bytes(dt)))
+    return fail(QMM_E_ALIGN, "qmm_dequantize: scales/biases misaligned");
+  return launched(qmm::launch_dequantize((int)dt, bits, group_size, wq, scales,
+                                         biases, rows, K, w_out,
+                                         (hipStream_t)stream),
+                  "qmm_dequantize");
+}
+
+qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
+               const void* biases, qmm_dtype dt, int64_t M, int64_t N,
+               int64_t K, int group_size, int bits, void* y, void* stream) {
+  qmm_status st = check_matmul("qmv", x, wq, scales, biases, dt, M, N, K,
+                               group_size, bits, y);
+  if (st) return st;
+  if (K > qmv_max_k(bits, dt))
+    return fail(QMM_E_SHAPE, "qmv: K (%lld) exceeds the streaming kernel's limit %lld; use qmm_t",
+                (long long)K, (long long)qmv_max_k(bits, dt));
+  return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
+                                  biases, M, N, K, y, (hipStream_t)stream),
+                  "qmv");
+}
+
+qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
+                 const void* biases, qmm_dtype dt, int64_t M, int64_t N,
+                 int64_t K, int group_size, int bits, void* y, void* stream) {
+  qmm_status st = check_matmul("qmm_t", x, wq, scales, biases, dt, M, N, K,
+                               group_size, bits, y);
+  if (st) return st;
+  if (M < qmm::crossover_m(bits, (int)dt) && K <= qmv_max_k(bits, dt))
+    return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
+                                    biases, M, N, K, y, (hipStream_t)stream),
+                    "qmm_t");
+  return launched(qmm::launch_qmm_mfma((int)dt, bits, group_size, x, wq, scales,
+                                       biases, M, N, K, y, (hipStream_t)stream),
+                  "qmm_t");
+}
+
+qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
+                        int64_t C, const uint32_t* wq, const void* scales,
+                        const void* biases, int64_t O, int kh, int kw,
+                        int stride_h, int stride_w, int pad_h, int pad_w,
+                        int groups, qmm_dtype dt, int group_size, int bits,
+                        void* y, void* stream) {
+  if (!x || !wq || !scales || !biases || !y)
+    return fail(QMM_E_NULL, "qconv2d_nhwc: x, wq, scales, biases and y must be non-NULL");
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qconv2d_nhwc: only float16 and bfloat16 are supported");
+  if (B < 1 || H < 1 || W < 1 || C < 1 || O < 1 || kh < 1 || kw < 1 ||
+      stride_h < 1 || stride_w < 1 || pad_h < 0 || pad_w < 0 || groups < 1)
+    return fail(QMM_E_SHAPE, "qconv2d_nhwc: sizes, kernel and strides must be >= 1, padding >= 0");
+  if (C % groups || O % groups)
+    return fail(QMM_E_SHAPE, "qconv2d_nhwc: C (%lld) and O (%lld) must be divisible by groups (%d)",
+                (long long)C, (long long)O, groups);
+  qmm::ConvGeom g{};
+  g.B = B; g.H = H; g.W = W; g.C = C; g.O = O;
+  g.kh = kh; g.kw = kw; g.sh = stride_h; g.sw = stride_w; g.ph = pad_h; g.pw = pad_w;
+  g.groups = groups;
+  g.OH = (H + 2 * (int64_t)pad_h - kh) / stride_h + 1;
+  g.OW = (W + 2 * (int64_t)pad_w - kw) / stride_w + 1;
+  if (H + 2 * (int64_t)pad_h < kh || W + 2 * (int64_t)pad_w < kw || g.OH < 1 || g.OW < 1)
+    return fail(QMM_E_SHAPE, "qconv2d_nhwc: the kernel does not fit the padded input");
+  g.Cg = C / groups;
+  g.Og = O / groups;
+  g.K_true = (int64_t)kh * kw * g.Cg;
+  g.K_pad = (g.K_true + group_size - 1) / group_size * group_size;
+  const int64_t npix = B * g.OH * g.OW;
+  if (npix > kI32 || g.K_pad > kI32 || B * H * W * C > ((int64_t)1 << 40) ||
+      npix * O > ((int64_t)1 << 40) || groups > 65535)
+    return fail(QMM_E_SHAPE, "qconv2d_nhwc: problem too large");
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qconv2d_nhwc: x, wq and y must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(biases, 2))
+    return fail(QMM_E_ALIGN, "qconv2d_nhwc: scales and biases must be 2-byte aligned");
+  return launched(qmm::launch_qconv_mfma((int)dt, bits, group_size, x, g, wq,
+                                         scales, biases, y, (hipStream_t)stream),
+                  "qconv2d_nhwc");
+}
+
+}  // extern "C"

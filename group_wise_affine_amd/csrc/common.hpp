@@ -1,0 +1,169 @@
+// Device helpers shared by the libqmm kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+// ----------------------------------------------------------------- types
+// Element types are carried as raw storage words (uint16_t for f16/bf16,
+// float for f32) so that every conversion is explicit.
+
+struct F16 {
+  using word = uint16_t;
+  static constexpr uint32_t kMagic = 0x64006400u;  // half2(1024, 1024)
+  static constexpr float kMagicF = 1024.0f;
+};
+struct BF16 {
+  using word = uint16_t;
+  static constexpr uint32_t kMagic = 0x43004300u;  // bf16x2(128, 128)
+  static constexpr float kMagicF = 128.0f;
+};
+struct F32 {
+  using word = float;
+};
+
+__device__ __forceinline__ float to_f32(F16, uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float to_f32(BF16, uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+__device__ __forceinline__ float to_f32(F32, float f) { return f; }
+
+// fp32 -> f16 with the hardware conversion (round to nearest even under the
+// default rounding mode).
+__device__ __forceinline__ uint16_t from_f32(F16, float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t from_f32(BF16, float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float from_f32(F32, float f) { return f; }
+
+// ----------------------------------------------------------------- packing
+// A row of K codes is a little-endian bit stream, code k at bit k*bits.
+// Codes are handled in chunks of 32 consecutive codes (4*bits bytes), which
+// always lie inside one quantization group (group sizes are multiples of 32).
+
+template <int BITS>
+struct Pack {
+  static constexpr bool kPow2 = (BITS & (BITS - 1)) == 0;
+  // codes per pack and bytes per pack: a 32-bit word for power-of-two
+  // widths; 8 codes in 3 bytes (3-bit), 8 in 5 bytes (5-bit), 4 in 3 bytes
+  // (6-bit)
+  static constexpr int kVals = kPow2 ? 32 / BITS : (BITS == 6 ? 4 : 8);
+  static constexpr int kBytes = kPow2 ? 4 : (BITS == 5 ? 5 : 3);
+  static constexpr int kChunkBytes = 4 * BITS;  // 32 codes
+  static constexpr int kChunkWords = BITS;
+  static constexpr uint32_t kMask = (1u << BITS) - 1u;
+};
+
+// Two bytes of a chunk starting at compile-time byte offset o, in the low 16
+// bits of the result (upper bits unspecified).
+template <int O>
+__device__ __forceinline__ uint32_t bytes2_at(const uint32_t* w) {
+  constexpr int i = O / 4, s = O % 4;
+  if constexpr (s <= 2) {
+    return w[i] >> (8 * s);
+  } else {
+    return __builtin_amdgcn_alignbit(w[i + 1], w[i], 24);
+  }
+}
+
+// Code j of a chunk held in 32-bit words (reference unpack, any width).
+template <int BITS, int J>
+__device__ __forceinline__ uint32_t code_at(const uint32_t* w) {
+  constexpr int bit = J * BITS, i = bit / 32, off = bit % 32;
+  if constexpr (off + BITS <= 32) {
+    return (w[i] >> off) & Pack<BITS>::kMask;
+  } else {
+    return __builtin_amdgcn_alignbit(w[i + 1], w[i], off) & Pack<BITS>::kMask;
+  }
+}
+
+// ------------------------------------------------------------ pair layout
+// The streaming kernels turn codes into 16-bit float pairs with the
+// "magic number" trick: a code q (< 1024 for f16, < 128 for bf16) OR-ed into
+// the mantissa of 1024.0 (f16) or 128.0 (bf16) is exactly the float
+// MAGIC + q. Two codes go into one 32-bit register as (low half, high half),
+// which a v_dot2 instruction multiplies with a pair of activations. The order
+// in which codes land in pairs depends on the width; the activations are
+// staged in the same order:
+//  * power-of-two widths: inside each 32-bit word, field f of the low half
+//    pairs with field f of the high half, i.e. code (word*V + f) with code
+//    (word*V + f + V/2), V = codes per word; one shift + one and-or per pair.
+//  * 3/5/6 bits: code j of pack 2r pairs with code j of pack 2r+1, both read
+//    from two-byte windows at the same offset inside their packs.
+// pair_slot(k) gives, for code k of a chunk (0..31), its pair index (0..15)
+// and half (0 low, 1 high).
+
+template <int BITS>
+__host__ __device__ constexpr int pair_index(int k) {
+  if constexpr (Pack<BITS>::kPow2) {
+    constexpr int V = Pack<BITS>::kVals, H = V / 2;
+    return (k / V) * H + (k % V) % H;
+  } else {
+    constexpr int V = Pack<BITS>::kVals;
+    return ((k / V) / 2) * V + k % V;
+  }
+}
+template <int BITS>
+__host__ __device__ constexpr int pair_half(int k) {
+  if constexpr (Pack<BITS>::kPow2) {
+    constexpr int V = Pack<BITS>::kVals, H = V / 2;
+    return (k % V) / H;
+  } else {
+    constexpr int V = Pack<BITS>::kVals;
+    return (k / V) % 2;
+  }
+}
+
+// Pair P (0..15) of a chunk as two magic floats, for widths <= 7 with bf16 or
+// <= 8 with f16. MAGIC is the 32-bit magic pattern.
+template <int BITS, int P, uint32_t MAGIC>
+__device__ __forceinline__ uint32_t magic_pair(const uint32_t* w) {
+  constexpr uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
+  if constexpr (Pack<BITS>::kPow2) {
+    constexpr int H = Pack<BITS>::kVals / 2;
+    constexpr int word = P / H, f = P % H;
+    return ((w[word] >> (f * BITS)) & m2) | MAGIC;
+  } else {
+    constexpr int V = Pack<BITS>::kVals, NB = Pack<BITS>::kBytes;
+    constexpr int r = P / V, j = P % V;
+    constexpr int bit = j * BITS;
+    constexpr int ws = (bit / 8) < (NB - 2) ? (bit / 8) : (NB - 2);
+    constexpr int off = bit - 8 * ws;
+    static_assert(off + BITS <= 16, "field must fit a two-byte window");
+    const uint32_t lo = bytes2_at<(2 * r) * NB + ws>(w);
+    const uint32_t hi = bytes2_at<(2 * r + 1) * NB + ws>(w);
+    const uint32_t pr = (lo & 0xffffu) | (hi << 16);
+    return ((pr >> off) & m2) | MAGIC;
+  }
+}
+
+// -------------------------------------------------------- dot products
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(F16, uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                __builtin_bit_cast(half2_t, b), c, false);
+}
+__device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                         __builtin_bit_cast(bf162_t, b), c,
+                                         false);
+}
+
+// ------------------------------------------------------------ misc
+__host__ __device__ constexpr int ilog2(int v) {
+  return v <= 1 ? 0 : 1 + ilog2(v / 2);
+}
+
+}  // namespace qmm

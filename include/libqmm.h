@@ -1,0 +1,146 @@
+/*
+ * libqmm -- affine group-wise quantized matrix multiply for MI355X (gfx950).
+ *
+ * y = x . dequant(Wq)^T, where each row of W is split into groups of
+ * group_size consecutive elements along K and every group carries one scale
+ * and one bias: w ~ scale * q + bias with an unsigned code q of `bits` bits.
+ * The quantizer, the packing and the operation follow:
+ *  - "Improvements in the quantizer and dequantization kernel" (mlx PR 1061),
+ *    item 1 a-c: the bias is the group extreme of larger magnitude, the scale
+ *    runs from it to the other extreme and is adjusted so 0 is on the grid;
+ *  - "mlx 1.0.0 backend/cpu/quantized.cpp", functions quantize,
+ *    get_pack_factor, get_bytes_per_pack, extract_bits and _qmm_t: the
+ *    per-group steps, the packed layout and y[m,n] = sum_k x[m,k] *
+ *    (scale[n,k/gs] * q[n,k] + bias[n,k/gs]);
+ *  - "Add the 3bit packed qmm_t" (mlx compare sdpa-test...packed-quants),
+ *    ops.cpp extract_quantized_matmul_dims / quantized_matmul: the argument
+ *    checks, one element type for x, scales, biases and y, and the
+ *    small-M / large-M split between a GEMV and a tiled GEMM;
+ *  - "[Feature] Quantized Convolution 2D - Possible PR?" (mlx issue 2714):
+ *    the conv weight reshape with K zero-padded to a multiple of group_size,
+ *    and the im2col patch order (dy, dx, c) over NHWC input.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers, allocated and owned by the
+ *    caller; the library never allocates, frees or keeps them.
+ *  - Arrays are row-major and contiguous. x, wq, w_out and y must be 16-byte
+ *    aligned; scales and biases 2-byte aligned (4-byte for QMM_F32).
+ *  - Packed weights wq hold K*bits/8 bytes per row (K*bits/32 uint32 words):
+ *    code k of a row sits at bit k*bits of the row's little-endian byte
+ *    stream. For bits 2, 4, 8 that is 32/bits codes per uint32 word, low
+ *    bits first; for bits 3 and 6 it is 8 (resp. 4) codes per 3 bytes and
+ *    for bits 5 eight codes per 5 bytes.
+ *  - scales and biases are [rows, K/group_size] of the element type.
+ *  - Each call validates its arguments synchronously, before any launch, and
+ *    returns a status; on error nothing is launched or written and
+ *    qmm_last_error() describes the problem. On success the work is queued
+ *    asynchronously on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream). No call synchronizes the host. Device faults surface at
+ *    the caller's next synchronization.
+ *  - Supported: bits in {2,3,4,5,6,8}; group_size in {32,64,128};
+ *    K a positive multiple of group_size.
+ */
+#ifndef LIBQMM_H
+#define LIBQMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMM_F16 = 0,  /* IEEE binary16 */
+  QMM_BF16 = 1, /* bfloat16 */
+  QMM_F32 = 2   /* binary32: accepted by qmm_quantize / qmm_dequantize only */
+} qmm_dtype;
+
+typedef enum {
+  QMM_OK = 0,
+  QMM_E_NULL = 1,   /* a required pointer is NULL */
+  QMM_E_BITS = 2,   /* bits not in {2,3,4,5,6,8} */
+  QMM_E_GROUP = 3,  /* group_size not in {32,64,128} */
+  QMM_E_SHAPE = 4,  /* a size < 1, K % group_size != 0, or bad conv geometry */
+  QMM_E_DTYPE = 5,  /* element type not supported by this call */
+  QMM_E_ALIGN = 6,  /* a pointer violates the alignment rules above */
+  QMM_E_LAUNCH = 7  /* the kernel launch itself failed (hipGetLastError) */
+} qmm_status;
+
+/*
+ * Quantize w[rows, K] (element type dt: f16, bf16 or f32) group by group.
+ * Per group: min/max in fp32; the bias candidate is the extreme of larger
+ * magnitude (max on a tie); scale = +-max((max-min)/(2^bits-1), 1e-7) pointing
+ * from that extreme to the other; q0 = rint(edge/scale); if q0 != 0 then
+ * scale = edge/q0 and bias = edge, else bias = 0; code = clamp(rint((w -
+ * bias)/scale), 0, 2^bits-1). All in IEEE fp32 with correctly rounded
+ * division and ties-to-even rounding; scale and bias are stored rounded to
+ * nearest even in dt. (Source: mlx PR 1061 item 1; mlx 1.0.0 CPU backend,
+ * function quantize.)
+ * Outputs: wq [rows, K*bits/32] uint32, scales [rows, K/gs], biases [rows,
+ * K/gs] in dt.
+ */
+qmm_status qmm_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
+                        int group_size, int bits, uint32_t* wq, void* scales,
+                        void* biases, void* stream);
+
+/*
+ * Dequantize: w_out[n,k] = dt(fl32(fl32(scale*q) + bias)) with the stored
+ * scale and bias widened to fp32 (scale*q is exact for f16/bf16 scales).
+ * (Source: mlx 1.0.0 CPU backend, functions extract_bits and _qmm_t_simd.)
+ */
+qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
+                          const void* biases, qmm_dtype dt, int64_t rows,
+                          int64_t K, int group_size, int bits, void* w_out,
+                          void* stream);
+
+/*
+ * y[M,N] = x[M,K] . dequant(wq, scales, biases)[N,K]^T, fp32 accumulation,
+ * y rounded to nearest even in dt (f16 or bf16). Routes small M to the
+ * streaming GEMV (qmv) and larger M to the MFMA tile kernel; the crossover
+ * is returned by qmm_crossover_m. (Source: mlx 1.0.0 CPU backend, _qmm_t;
+ * the packed-quants compare, the qmv/qmm_t split in the Metal dispatch.)
+ */
+qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
+                 const void* biases, qmm_dtype dt, int64_t M, int64_t N,
+                 int64_t K, int group_size, int bits, void* y, void* stream);
+
+/*
+ * Same operation and arguments as qmm_t, always on the streaming GEMV, which
+ * reads every packed weight from HBM once per 8 rows of x. Meant for M <= 16
+ * (decode); correct for any M.
+ */
+qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
+               const void* biases, qmm_dtype dt, int64_t M, int64_t N,
+               int64_t K, int group_size, int bits, void* y, void* stream);
+
+/*
+ * Quantized 2-D convolution, NHWC, dilation 1, no bias:
+ *   x [B,H,W,C] (dt), y [B,OH,OW,O] (dt), OH = (H + 2*pad_h - kh)/stride_h + 1,
+ *   OW likewise. The weight [O, kh, kw, C/groups] is reshaped to
+ *   [O, K_true = kh*kw*C/groups] in (dy, dx, c) order, zero-padded on the
+ *   right to K_pad = ceil(K_true/group_size)*group_size and quantized with
+ *   qmm_quantize: wq [O, K_pad*bits/32], scales/biases [O, K_pad/gs].
+ *   Output channel o belongs to conv group o / (O/groups), which reads input
+ *   channels [g*C/groups, (g+1)*C/groups). Computed as an implicit-im2col
+ *   GEMM (rows = output pixels, columns = output channels), with patch
+ *   elements outside the image and k >= K_true contributing zero.
+ *   (Source: mlx issue 2714, quantize_weights / img2col / forward.)
+ */
+qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
+                        int64_t C, const uint32_t* wq, const void* scales,
+                        const void* biases, int64_t O, int kh, int kw,
+                        int stride_h, int stride_w, int pad_h, int pad_w,
+                        int groups, qmm_dtype dt, int group_size, int bits,
+                        void* y, void* stream);
+
+/* Smallest M for which qmm_t uses the MFMA tile kernel instead of qmv. */
+int qmm_crossover_m(int bits, qmm_dtype dt);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* qmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,157 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/libqmm.h declares, and rejects each kind of bad argument with the
+documented status before anything is launched (no valid call is made here,
+so no GPU is needed). The rejected cases follow the argument errors of the
+mlx ops on the pages (bits / group size / dtype switches, K a multiple of
+the group size, conv geometry)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from group_wise_affine_amd import qmm as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libqmm.h")
+
+# aligned, non-NULL placeholders: validation never dereferences pointers
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x10002)  # 2-byte but not 16-byte aligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(Q.LIB_PATH):
+        from group_wise_affine_amd import build
+        build.build()
+    return Q.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(Q.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", Q.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def _st(L, fn, *args):
+    return getattr(L, fn)(*args)
+
+
+BAD_BITS = [1, 7, 9, 16, 0, -4]
+BAD_GS = [16, 48, 256, 0, -64]
+
+
+@pytest.mark.parametrize("bits", BAD_BITS)
+def test_bad_bits(L, bits):
+    assert _st(L, "qmm_quantize", P, 0, 4, 64, 64, bits, P, P, P, None) == Q.QMM_E_BITS
+    assert _st(L, "qmm_dequantize", P, P, P, 0, 4, 64, 64, bits, P, None) == Q.QMM_E_BITS
+    for fn in ("qmm_t", "qmv"):
+        assert _st(L, fn, P, P, P, P, 0, 1, 8, 64, 64, bits, P, None) == Q.QMM_E_BITS
+    assert _st(L, "qconv2d_nhwc", P, 1, 8, 8, 8, P, P, P, 8, 3, 3, 1, 1, 1, 1, 1,
+               0, 64, bits, P, None) == Q.QMM_E_BITS
+    assert b"bits" in L.qmm_last_error()
+
+
+@pytest.mark.parametrize("gs", BAD_GS)
+def test_bad_group_size(L, gs):
+    assert _st(L, "qmm_quantize", P, 0, 4, 256, gs, 4, P, P, P, None) == Q.QMM_E_GROUP
+    assert _st(L, "qmm_dequantize", P, P, P, 1, 4, 256, gs, 4, P, None) == Q.QMM_E_GROUP
+    for fn in ("qmm_t", "qmv"):
+        assert _st(L, fn, P, P, P, P, 0, 1, 8, 256, gs, 4, P, None) == Q.QMM_E_GROUP
+    assert b"group_size" in L.qmm_last_error()
+
+
+def test_null_pointers(L):
+    for i in range(4):
+        args = [P, P, P, P]
+        args[i] = None
+        st = _st(L, "qmm_quantize", args[0], 0, 4, 64, 64, 4, args[1], args[2], args[3], None)
+        assert st == Q.QMM_E_NULL
+    for fn in ("qmm_t", "qmv"):
+        for i in range(5):
+            a = [P, P, P, P, P]
+            a[i] = None
+            assert _st(L, fn, a[0], a[1], a[2], a[3], 0, 1, 8, 64, 64, 4, a[4], None) == Q.QMM_E_NULL
+    assert _st(L, "qmm_dequantize", None, P, P, 0, 4, 64, 64, 4, P, None) == Q.QMM_E_NULL
+    assert _st(L, "qconv2d_nhwc", None, 1, 8, 8, 8, P, P, P, 8, 3, 3, 1, 1, 1, 1, 1,
+               0, 64, 4, P, None) == Q.QMM_E_NULL
+
+
+@pytest.mark.parametrize("K", [0, -64, 96, 100, 65])
+def test_k_not_multiple_of_group(L, K):
+    assert _st(L, "qmm_quantize", P, 0, 4, K, 64, 4, P, P, P, None) == Q.QMM_E_SHAPE
+    assert _st(L, "qmm_dequantize", P, P, P, 0, 4, K, 64, 4, P, None) == Q.QMM_E_SHAPE
+    for fn in ("qmm_t", "qmv"):
+        assert _st(L, fn, P, P, P, P, 0, 2, 8, K, 64, 4, P, None) == Q.QMM_E_SHAPE
+
+
+def test_bad_sizes(L):
+    for fn in ("qmm_t", "qmv"):
+        assert _st(L, fn, P, P, P, P, 0, 0, 8, 64, 64, 4, P, None) == Q.QMM_E_SHAPE
+        assert _st(L, fn, P, P, P, P, 0, 4, 0, 64, 64, 4, P, None) == Q.QMM_E_SHAPE
+        assert _st(L, fn, P, P, P, P, 0, -1, 8, 64, 64, 4, P, None) == Q.QMM_E_SHAPE
+    assert _st(L, "qmm_quantize", P, 0, 0, 64, 64, 4, P, P, P, None) == Q.QMM_E_SHAPE
+    # the streaming kernel's K limit is reported, qmm_t is not limited by it
+    assert _st(L, "qmv", P, P, P, P, 0, 1, 8, 1 << 20, 64, 4, P, None) == Q.QMM_E_SHAPE
+    assert b"K" in L.qmm_last_error()
+
+
+def test_bad_dtype(L):
+    for fn in ("qmm_t", "qmv"):
+        assert _st(L, fn, P, P, P, P, 2, 1, 8, 64, 64, 4, P, None) == Q.QMM_E_DTYPE
+        assert _st(L, fn, P, P, P, P, 7, 1, 8, 64, 64, 4, P, None) == Q.QMM_E_DTYPE
+    assert _st(L, "qmm_quantize", P, 3, 4, 64, 64, 4, P, P, P, None) == Q.QMM_E_DTYPE
+    assert _st(L, "qmm_dequantize", P, P, P, -1, 4, 64, 64, 4, P, None) == Q.QMM_E_DTYPE
+    assert _st(L, "qconv2d_nhwc", P, 1, 8, 8, 8, P, P, P, 8, 3, 3, 1, 1, 1, 1, 1,
+               2, 64, 4, P, None) == Q.QMM_E_DTYPE
+
+
+def test_alignment(L):
+    for fn in ("qmm_t", "qmv"):
+        assert _st(L, fn, P2, P, P, P, 0, 1, 8, 64, 64, 4, P, None) == Q.QMM_E_ALIGN
+        assert _st(L, fn, P, P2, P, P, 0, 1, 8, 64, 64, 4, P, None) == Q.QMM_E_ALIGN
+        assert _st(L, fn, P, P, P, P, 0, 1, 8, 64, 64, 4, P2, None) == Q.QMM_E_ALIGN
+        odd = ctypes.c_void_p(0x10001)
+        assert _st(L, fn, P, P, odd, P, 0, 1, 8, 64, 64, 4, P, None) == Q.QMM_E_ALIGN
+    assert _st(L, "qmm_quantize", P2, 0, 4, 64, 64, 4, P, P, P, None) == Q.QMM_E_ALIGN
+    assert _st(L, "qmm_quantize", P, 2, 4, 64, 64, 4, P, P2, P, None) == Q.QMM_E_ALIGN
+
+
+def test_conv_geometry(L):
+    def conv(B=1, H=8, W=8, C=8, O=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, g=1):
+        return _st(L, "qconv2d_nhwc", P, B, H, W, C, P, P, P, O, kh, kw, sh, sw, ph, pw,
+                   g, 0, 64, 4, P, None)
+    assert conv(C=9, g=2) == Q.QMM_E_SHAPE
+    assert conv(O=9, g=2) == Q.QMM_E_SHAPE
+    assert conv(kh=11, ph=1) == Q.QMM_E_SHAPE  # kernel larger than padded input
+    assert conv(sh=0) == Q.QMM_E_SHAPE
+    assert conv(ph=-1) == Q.QMM_E_SHAPE
+    assert conv(g=0) == Q.QMM_E_SHAPE
+    assert conv(B=0) == Q.QMM_E_SHAPE
+
+
+def test_crossover_is_positive(L):
+    for bits in (2, 3, 4, 5, 6, 8):
+        for dt in (0, 1):
+            assert L.qmm_crossover_m(bits, dt) >= 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(Q, "_lib", None)
+    monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        Q.lib()

@@ -1,0 +1,259 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Gates: quantize / pack / dequantize bit-exact; qmv, qmm_t and qconv2d against
+the oracle's fp32 result y32 within relative Frobenius error 1e-3 (beyond the
+oracle's own rounding of y32 to the element type) and max error
+1e-2 * max|y32| (tests/helpers.py). Sizes span several tiles with ragged tails in M, N and K; the
+full-size workloads are checked whole where the oracle is fast enough and on
+sampled rows otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+from group_wise_affine_amd import qmm as Q
+from group_wise_affine_amd import synth
+from tests.helpers import (assert_parity, bytes_to_words_dev, from_dev, orc_code,
+                           to_dev, words_dev_to_bytes)
+
+pytestmark = pytest.mark.gpu
+
+BITS = [2, 3, 4, 5, 6, 8]
+GS = [32, 64, 128]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    Q.lib()
+
+
+def _quantized(orc, dt, N, K, gs, bits, seed=2, sigma=1.0, structured=False):
+    code = orc_code(orc, dt)
+    w = synth.normal((N, K), seed=seed, sigma=sigma, dt=dt)
+    if structured:
+        w[: min(N, 9)] = synth.structured_rows(min(N, 9), K, gs, seed=seed + 1, dt=dt)
+    wq, s, b = orc.quantize(w, code, gs, bits)
+    return w, wq, s, b
+
+
+# ------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("gs", GS)
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_quantize_bit_exact(orc, dt, gs, bits):
+    rows, K = 37, gs * 5
+    w = synth.normal((rows, K), seed=10 + bits, sigma=2.0, dt=dt)
+    w[:18] = synth.structured_rows(18, K, gs, seed=4, dt=dt)
+    wq_o, s_o, b_o = orc.quantize(w, orc_code(orc, dt), gs, bits)
+    wq, s, b = Q.qmm_quantize(to_dev(w, dt), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_dev_to_bytes(wq), wq_o)
+    assert np.array_equal(from_dev(s), s_o)
+    assert np.array_equal(from_dev(b), b_o)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_dequantize_bit_exact(orc, dt, bits):
+    gs, rows, K = 64, 29, 448
+    w, wq, s, b = _quantized(orc, dt, rows, K, gs, bits, structured=True)
+    _, w_o = orc.dequantize(wq, s, b, orc_code(orc, dt), K, gs, bits)
+    out = Q.qmm_dequantize(bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), w_o)
+
+
+def test_quantize_large_rows(orc):
+    """configs-scale weight (4096 x 4096, 4-bit g64 f16), bit-exact."""
+    w = synth.normal((4096, 4096), seed=1)
+    wq_o, s_o, b_o = orc.quantize(w, orc.F16, 64, 4)
+    wq, s, b = Q.qmm_quantize(to_dev(w, "f16"), 64, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_dev_to_bytes(wq), wq_o)
+    assert np.array_equal(from_dev(s), s_o) and np.array_equal(from_dev(b), b_o)
+
+
+# ------------------------------------------------------------ qmv
+
+def _run_mm(fn, orc, dt, M, N, K, gs, bits, seed=0, sigma_w=1.0, rows=None):
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=seed, dt=dt)
+    w, wq, s, b = _quantized(orc, dt, N, K, gs, bits, seed=seed + 1, sigma=sigma_w)
+    y = fn(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    torch.cuda.synchronize()
+    yg = from_dev(y)
+    if rows is not None:
+        yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8, rows=rows)
+        yg = yg[rows[0]:rows[1]]
+    else:
+        yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
+    return assert_parity(yg, yo, dt, f"{fn.__name__} {dt} M{M} N{N} K{K} g{gs} b{bits}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("gs", GS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qmv_parity(orc, dt, gs, bits):
+    # K = 640: 20 chunks of 32 codes (ragged against the lanes per row);
+    # N = 70: ragged against the rows per workgroup
+    for M in (1, 3, 8):
+        _run_mm(Q.qmv, orc, dt, M, 70, 640, gs, bits, seed=M)
+
+
+@pytest.mark.parametrize("M", [2, 5, 11, 16, 20])
+def test_qmv_multi_m_blocks(orc, M):
+    _run_mm(Q.qmv, orc, "f16", M, 130, 1024, 64, 4, seed=M)
+    _run_mm(Q.qmv, orc, "bf16", M, 33, 2048, 128, 3, seed=M)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 64), (257, 96), (64, 8192), (3, 15872)])
+def test_qmv_edge_shapes(orc, N, K):
+    gs = 32
+    _run_mm(Q.qmv, orc, "f16", 1, N, K, gs, 4, seed=N)
+    _run_mm(Q.qmv, orc, "bf16", 2, N, K, gs, 8, seed=N)
+
+
+def test_qmv_max_k(orc):
+    """The largest K the streaming kernel accepts (f16 4-bit, g32)."""
+    _run_mm(Q.qmv, orc, "f16", 1, 3, 30720, 32, 4, seed=3)
+
+
+# ------------------------------------------------------------ qmm_t (MFMA)
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("gs", GS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qmm_t_mfma_parity(orc, dt, gs, bits):
+    # M >= crossover routes to the MFMA kernel; ragged M, N and a K with a
+    # half K-step tail (K % 64 == 32 when gs == 32)
+    K = 384 if gs != 32 else 352
+    _run_mm(Q.qmm_t, orc, dt, 100, 72, K, gs, bits, seed=bits)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 64), (129, 200, 640), (300, 520, 256),
+                                   (1, 128, 128), (513, 33, 1024)])
+def test_qmm_t_shapes(orc, M, N, K):
+    _run_mm(Q.qmm_t, orc, "f16", M, N, K, 64, 4, seed=M)
+    _run_mm(Q.qmm_t, orc, "bf16", M, N, K, 64, 6, seed=M)
+
+
+def test_qmm_t_routes_consistently(orc):
+    """Around the crossover both kernels agree with the oracle."""
+    mx = Q.crossover_m(4)
+    for M in (mx - 1, mx, mx + 1):
+        if M >= 1:
+            _run_mm(Q.qmm_t, orc, "f16", M, 96, 512, 64, 4, seed=M)
+
+
+# ------------------------------------------------------------ qconv2d
+
+CONV = [
+    # B, H, W, C, O, kh, kw, stride, pad, groups, gs, bits
+    (1, 9, 7, 16, 24, 3, 3, (1, 1), (1, 1), 1, 32, 4),
+    (2, 8, 8, 16, 8, 3, 3, (2, 1), (1, 0), 2, 32, 4),
+    (1, 10, 6, 8, 6, 5, 3, (1, 2), (2, 1), 1, 64, 3),
+    (1, 6, 6, 32, 16, 1, 1, (1, 1), (0, 0), 1, 32, 8),
+    (1, 7, 5, 20, 10, 3, 2, (1, 1), (0, 1), 5, 32, 6),   # Cg = 4: scalar im2col
+    (1, 5, 5, 24, 12, 3, 3, (1, 1), (1, 1), 3, 128, 5),
+    (2, 17, 19, 64, 96, 3, 3, (1, 1), (1, 1), 1, 64, 2),
+    (1, 12, 12, 48, 40, 3, 3, (2, 2), (0, 0), 2, 64, 4),
+]
+
+
+@pytest.mark.parametrize("case", CONV)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qconv2d_parity(orc, dt, case):
+    B, H, W, C, O, kh, kw, stride, pad, groups, gs, bits = case
+    code = orc_code(orc, dt)
+    x = synth.normal((B, H, W, C), seed=12, dt=dt)
+    wconv = synth.normal((O, kh, kw, C // groups), seed=13, sigma=0.5, dt=dt)
+    wm = orc.conv_weight_matrix(wconv, groups, gs)
+    wq, s, b = orc.quantize(wm, code, gs, bits)
+    yo, _ = orc.qconv2d_nhwc(x, wq, s, b, code, O, kh, kw, stride, pad, groups, gs, bits,
+                             nthreads=8)
+    y = Q.qconv2d_nhwc(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                       O, kh, kw, stride, pad, groups, gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"conv {case} {dt}")
+
+
+def test_conv_weight_prep_matches_oracle(orc):
+    """The binding's reshape + zero pad + GPU quantize equals the oracle's."""
+    wconv = synth.normal((20, 3, 3, 30), seed=3)
+    wm_o = orc.conv_weight_matrix(wconv, 1, 64)
+    wq_o, s_o, b_o = orc.quantize(wm_o, orc.F16, 64, 4)
+    wq, s, b = Q.quantize_conv_weight(to_dev(wconv, "f16"), 64, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_dev_to_bytes(wq), wq_o)
+    assert np.array_equal(from_dev(s), s_o) and np.array_equal(from_dev(b), b_o)
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def test_tiny_qmm_t_config(orc):
+    """x f16 [8,512], W [512,512] 4-bit g64, seed 0."""
+    _run_mm(Q.qmm_t, orc, "f16", 8, 512, 512, 64, 4, seed=0)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_qmv_config(orc, bits, M):
+    """x f16 [M,4096], W [4096,4096] g64, full output against the oracle."""
+    _run_mm(Q.qmv, orc, "f16", M, 4096, 4096, 64, bits, seed=0)
+    _run_mm(Q.qmm_t, orc, "f16", M, 4096, 4096, 64, bits, seed=0)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_chained_qmm_config(orc, bits):
+    """First loop of x = qmm(qmm(x, W1), W2), x [1024,1024], W1 [4096,1024],
+    W2 [1024,4096], g64 f16: checked on sampled rows (the oracle recomputes
+    rows 0..15 and 1000..1023 of each product)."""
+    gs = 64
+    x = synth.normal((1024, 1024), seed=0)
+    _, wq1, s1, b1 = _quantized(orc, "f16", 4096, 1024, gs, bits, seed=1)
+    _, wq2, s2, b2 = _quantized(orc, "f16", 1024, 4096, gs, bits, seed=2)
+    xd = to_dev(x, "f16")
+    h = Q.qmm_t(xd, bytes_to_words_dev(wq1), to_dev(s1, "f16"), to_dev(b1, "f16"), gs, bits)
+    y = Q.qmm_t(h, bytes_to_words_dev(wq2), to_dev(s2, "f16"), to_dev(b2, "f16"), gs, bits)
+    torch.cuda.synchronize()
+    hg, yg = from_dev(h), from_dev(y)
+    for rows in [(0, 16), (1000, 1024)]:
+        ho, _ = orc.qmm_t(x, wq1, s1, b1, orc.F16, gs, bits, nthreads=8, rows=rows)
+        assert_parity(hg[rows[0]:rows[1]], ho, "f16", f"chained h bits{bits}")
+        # second product on the GPU's own h rows (isolates the second kernel)
+        yo, _ = orc.qmm_t(hg, wq2, s2, b2, orc.F16, gs, bits, nthreads=8, rows=rows)
+        assert_parity(yg[rows[0]:rows[1]], yo, "f16", f"chained y bits{bits}")
+
+
+SWEEP_NK = [(2048, 2048), (512, 2048), (8192, 2048), (2048, 8192)]
+
+
+@pytest.mark.parametrize("N,K", SWEEP_NK)
+@pytest.mark.parametrize("bits", [4, 3, 6])
+def test_small_m_sweep_config(orc, N, K, bits):
+    """bf16 Llama-3.2-1B-shaped layers, W ~ N(0, 0.02), g64; every M of the
+    sweep, sampled rows for the large M."""
+    for M in (1, 2, 4, 8, 16, 32, 64, 512):
+        rows = (0, M) if M <= 64 else (M - 24, M)
+        _run_mm(Q.qmm_t, orc, "bf16", M, N, K, 64, bits, seed=M, sigma_w=0.02, rows=rows)
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+def test_conv_config(orc, groups):
+    """x f16 [1,64,64,320], W [320,3,3,320/groups] ~ N(0, 0.05), 4-bit g64,
+    stride 1, pad 1: full output against the oracle."""
+    dt, gs, bits = "f16", 64, 4
+    x = synth.normal((1, 64, 64, 320), seed=0)
+    wconv = synth.normal((320, 3, 3, 320 // groups), seed=1, sigma=0.05)
+    wm = orc.conv_weight_matrix(wconv, groups, gs)
+    wq, s, b = orc.quantize(wm, orc.F16, gs, bits)
+    yo, _ = orc.qconv2d_nhwc(x, wq, s, b, orc.F16, 320, 3, 3, (1, 1), (1, 1), groups, gs,
+                             bits, nthreads=16)
+    y = Q.qconv2d_nhwc(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                       320, 3, 3, (1, 1), (1, 1), groups, gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"conv config groups={groups}")
