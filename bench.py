@@ -1,0 +1,326 @@
+"""Benchmark of the libqmm hot path on one MI355X.
+
+Headline (one step = one decode GEMV through the C ABI):
+  qmv, x f16 [1, 4096], W [4096, 4096] quantized affine 4-bit, group 64, fp16
+  scales/biases. Every step reads a different copy of W from a pool of at
+  least 1 GiB, so no step is served from the 256 MB MALL (a decode step
+  walks a layer stack). value = algorithmic bytes / time in GB/s, where the
+  algorithmic bytes are packed W + scales + biases + x + y.
+
+The other rows of the hot path are measured in the same run and reported
+under "rows": quantize, dequantize, qmv at bits 2/8 and M <= 16, the chained
+qmm_t bench (10 loops of x = qmm(qmm(x, W1), W2), M=1024), the quantized
+conv2d (x [1,64,64,320], 3x3, groups 1 and 2) and the bf16 small-M sweep.
+
+Timing: the K timed launches are captured in one HIP graph and replayed
+between two HIP events on the launch stream, after a synchronize; a warmup
+graph of W launches runs first. Inputs are seeded and synthetic and already
+resident in HBM.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA
+POOL_BYTES = 1 << 30
+METRIC = ("qmm GB/s (M≤16) & TFLOP/s (M≥1024) vs HBM/MFMA peak, "
+          "4-bit g64 fp16")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(M, N, K, bits, gs, esize=2):
+    return N * K * bits // 8 + N * (K // gs) * 2 * esize + M * K * esize + M * N * esize
+
+
+class Timer:
+    """Capture `launch(i)` for i in range(n) into a graph; time replays."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.Stream()
+
+    def graph(self, launch, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(n):
+                launch(i)
+        return g
+
+    def run(self, launch, steps, warmup):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for i in range(min(2, steps)):  # eager first calls
+                launch(i)
+        torch.cuda.synchronize()
+        gw = self.graph(launch, max(warmup, 1))
+        gt = self.graph(launch, steps)
+        with torch.cuda.stream(self.stream):
+            gw.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            gt.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        del gw, gt
+        return ms / steps  # ms per launch
+
+
+def make_layer(torch, Q, synth, dt, N, K, gs, bits, seed, sigma=1.0):
+    from tests.helpers import to_dev
+    w = to_dev(synth.normal((N, K), seed=seed, sigma=sigma, dt=dt), dt)
+    return Q.qmm_quantize(w, gs, bits)
+
+
+def pooled(torch, layer, min_bytes=POOL_BYTES):
+    """Distinct device copies of (wq, s, b) totalling >= min_bytes."""
+    wq, s, b = layer
+    per = wq.numel() * 4 + s.numel() * s.element_size() * 2
+    P = max(2, -(-min_bytes // per))
+    wqs = wq.unsqueeze(0).expand(P, *wq.shape).contiguous()
+    ss = s.unsqueeze(0).expand(P, *s.shape).contiguous()
+    bs = b.unsqueeze(0).expand(P, *b.shape).contiguous()
+    return wqs, ss, bs, P
+
+
+def bench_qmv(torch, Q, synth, timer, dt, M, N, K, bits, gs, steps, warmup, fn=None,
+              seed=0, sigma=1.0):
+    from tests.helpers import to_dev
+    fn = fn or Q.qmv
+    layer = make_layer(torch, Q, synth, dt, N, K, gs, bits, seed + 1, sigma)
+    wqs, ss, bs, P = pooled(torch, layer)
+    x = to_dev(synth.normal((M, K), seed=seed, dt=dt), dt)
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+
+    def launch(i):
+        j = i % P
+        fn(x, wqs[j], ss[j], bs[j], gs, bits, out=y)
+
+    ms = timer.run(launch, steps, warmup)
+    nbytes = alg_bytes(M, N, K, bits, gs)
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "pool_copies": P}
+
+
+def bench_quantize(torch, Q, synth, timer, steps, warmup):
+    from tests.helpers import to_dev
+    N = K = 4096
+    w = to_dev(synth.normal((N, K), seed=1), "f16")
+    wq, s, b = Q.qmm_quantize(w, 64, 4)
+    out = (wq, s, b)
+    ms = timer.run(lambda i: Q.qmm_quantize(w, 64, 4, out=out), steps, warmup)
+    nbytes = N * K * 2 + N * K // 2 + N * (K // 64) * 4
+    res = {"quantize": {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                        "workload": "W f16 [4096,4096] -> 4-bit g64"}}
+    wo = torch.empty_like(w)
+    ms = timer.run(lambda i: Q.qmm_dequantize(wq, s, b, 64, 4, out=wo), steps, warmup)
+    res["dequantize"] = {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                         "workload": "4-bit g64 [4096,4096] -> f16"}
+    return res
+
+
+def bench_chained(torch, Q, synth, timer, bits, steps, warmup):
+    """10 loops of x = qmm(qmm(x, W1), W2): x [1024,1024], W1 [4096,1024],
+    W2 [1024,4096], g64 f16. One step = the 20 launches of the 10 loops."""
+    from tests.helpers import to_dev
+    gs = 64
+    x = to_dev(synth.normal((1024, 1024), seed=0), "f16")
+    l1 = make_layer(torch, Q, synth, "f16", 4096, 1024, gs, bits, 1)
+    l2 = make_layer(torch, Q, synth, "f16", 1024, 4096, gs, bits, 2)
+    h = torch.empty((1024, 4096), dtype=torch.float16, device="cuda")
+    xs = [x.clone(), torch.empty_like(x)]
+
+    def launch(i):
+        for loop in range(10):
+            Q.qmm_t(xs[loop % 2], *l1, gs, bits, out=h)
+            Q.qmm_t(h, *l2, gs, bits, out=xs[(loop + 1) % 2])
+
+    ms = timer.run(launch, steps, warmup)
+    flops = 10 * 2 * (2 * 1024 * 4096 * 1024)
+    return {"us_per_10_loops": ms * 1e3, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+
+
+def bench_conv(torch, Q, synth, timer, groups, steps, warmup):
+    from tests.helpers import to_dev
+    gs, bits = 64, 4
+    x = to_dev(synth.normal((1, 64, 64, 320), seed=0), "f16")
+    wc = to_dev(synth.normal((320, 3, 3, 320 // groups), seed=1, sigma=0.05), "f16")
+    wq, s, b = Q.quantize_conv_weight(wc, gs, bits)
+    y = torch.empty((1, 64, 64, 320), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.qconv2d_nhwc(x, wq, s, b, 320, 3, 3, (1, 1), (1, 1),
+                                            groups, gs, bits, out=y), steps, warmup)
+    flops = 2 * 64 * 64 * 320 * (9 * 320 // groups)
+    return {"us": ms * 1e3, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+
+
+def cpu_baseline(seconds=10.0):
+    """The oracle on the host cores, headline workload, bounded sample."""
+    import numpy as np
+    import oracle as orc
+    from group_wise_affine_amd import synth
+    M, N, K, gs, bits = 1, 4096, 4096, 64, 4
+    x = synth.normal((M, K), seed=0)
+    w = synth.normal((N, K), seed=1)
+    wq, s, b = orc.quantize(w, orc.F16, gs, bits)
+    orc.qmm_t(x, wq, s, b, orc.F16, gs, bits)  # warm
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.qmm_t(x, wq, s, b, orc.F16, gs, bits, nthreads=1)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    nbytes = alg_bytes(M, N, K, bits, gs)
+    del np
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} oracle calls of the headline decode qmv (M=1, 4096x4096, "
+                      f"4-bit g64 f16) in {el:.1f} s, {per * 1e3:.1f} ms per call; the "
+                      f"oracle parallelises over rows of x, so M=1 runs on one thread"}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("common.hpp", "qmv.hip"):
+        with open(os.path.join(ROOT, "group_wise_affine_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed rocprofv3
+    PMC summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "qmv_decode_4bit_g64_f16_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline decode GEMV (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the path is measured on a single "
+              "MI355X (multi-GPU sharding is described in DESIGN.md, not run).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from group_wise_affine_amd import qmm as Q
+    from group_wise_affine_amd import synth
+    torch.cuda.set_device(0)
+    Q.lib()
+    timer = Timer(torch)
+    K_, W_ = args.steps, args.warmup
+
+    log("headline: qmv 4-bit g64 f16 M=1 4096x4096")
+    torch.cuda.synchronize()
+    head = bench_qmv(torch, Q, synth, timer, "f16", 1, 4096, 4096, 4, 64, K_, W_)
+    log(f"  {head['us']:.3f} us  {head['GB/s']:.1f} GB/s")
+
+    rows = {}
+    if not args.headline_only:
+        n_small = max(50, min(K_, 500))
+        rows.update(bench_quantize(torch, Q, synth, timer, 20, 5))
+        log("quantize/dequantize done")
+        dec = {}
+        for bits in (2, 4, 8):
+            for M in (1, 2, 4, 8, 16):
+                if bits != 4 and M != 1:
+                    continue
+                r = bench_qmv(torch, Q, synth, timer, "f16", M, 4096, 4096, bits, 64,
+                              n_small, 20)
+                dec[f"bits{bits}_M{M}"] = {k: round(v, 4) if isinstance(v, float) else v
+                                           for k, v in r.items()}
+        rows["qmv_decode_4096x4096_f16_g64"] = dec
+        log("decode rows done")
+        ch = {}
+        for bits in (2, 4, 8):
+            ch[f"bits{bits}"] = {k: round(v, 4) for k, v in
+                                 bench_chained(torch, Q, synth, timer, bits, 10, 2).items()}
+        rows["qmm_t_chained_M1024_f16_g64"] = ch
+        log("chained done")
+        rows["qconv2d_64x64x320_3x3_f16_4bit_g64"] = {
+            f"groups{g}": {k: round(v, 4) for k, v in
+                           bench_conv(torch, Q, synth, timer, g, 50, 5).items()}
+            for g in (1, 2)}
+        log("conv done")
+        sweep = {}
+        for (N, K) in [(2048, 2048), (512, 2048), (8192, 2048), (2048, 8192)]:
+            for bits in (4, 3, 6):
+                key = f"N{N}_K{K}_bits{bits}"
+                sweep[key] = {}
+                for M in (1, 2, 4, 8, 16, 32, 64, 512):
+                    r = bench_qmv(torch, Q, synth, timer, "bf16", M, N, K, bits, 64,
+                                  200, 20, fn=Q.qmm_t, sigma=0.02)
+                    sweep[key][f"M{M}"] = {"us": round(r["us"], 3),
+                                           "GB/s": round(r["GB/s"], 1),
+                                           "TFLOP/s": round(2 * M * N * K / (r["us"] * 1e-6) / 1e12, 3)}
+        rows["small_m_sweep_bf16_g64"] = sweep
+        log("sweep done")
+
+    achieved = head["GB/s"]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic()}
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+    out = {
+        "metric": METRIC,
+        "value": round(head["GB/s"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": W_,
+        "ms_per_step": round(head["us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode qmv: x f16 [1,4096] ~N(0,1), W [4096,4096] ~N(0,1) "
+                               "quantized affine 4-bit g64 with f16 scales/biases; each step "
+                               f"reads a different copy of W from a {head['pool_copies']}-copy "
+                               "(>=1 GiB) pool",
+                   "M": 1, "N": 4096, "K": 4096, "bits": 4, "group_size": 64,
+                   "algorithmic_bytes_per_step": head["bytes"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -59,10 +59,11 @@ qmm_status launched(hipError_t e, const char* what) {
 
 constexpr int64_t kI32 = std::numeric_limits<int32_t>::max();
 
-// Largest K the streaming GEMV stages in LDS (one row of x plus chunk sums
-// within 64 KiB; 8-bit bf16 stages fp32 activations).
+// Largest K the streaming GEMV stages in LDS (one row of x plus two fp32
+// constants per 32-element chunk within 64 KiB; 8-bit bf16 stages fp32
+// activations).
 int64_t qmv_max_k(int bits, qmm_dtype dt) {
-  const int64_t words = (bits == 8 && dt == QMM_BF16) ? 33 : 17;
+  const int64_t words = (bits == 8 && dt == QMM_BF16) ? 34 : 18;
   return (64 * 1024 / (words * 4)) * 32;
 }
 

@@ -89,19 +89,41 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w) {
 
 // ------------------------------------------------------------ pair layout
 // The streaming kernels turn codes into 16-bit float pairs with the
-// "magic number" trick: a code q (< 1024 for f16, < 128 for bf16) OR-ed into
-// the mantissa of 1024.0 (f16) or 128.0 (bf16) is exactly the float
-// MAGIC + q. Two codes go into one 32-bit register as (low half, high half),
-// which a v_dot2 instruction multiplies with a pair of activations. The order
-// in which codes land in pairs depends on the width; the activations are
-// staged in the same order:
+// "magic number" trick: a code field q*2^o (q < 2^BITS) OR-ed into the
+// mantissa of MAGIC = 1024.0 (f16) or 128.0 (bf16) is exactly the float
+// MAGIC + q*2^o, provided q*2^o fits the mantissa (10 bits for f16, 7 for
+// bf16). Two codes go into one 32-bit register as (low half, high half),
+// and a v_dot2 instruction multiplies them with a pair of activations that
+// were pre-scaled by 2^-o, so each product is x*q plus an offset x*MAGIC*2^-o
+// that depends on x only (removed through a per-chunk constant).
+// A field at in-half offset o <= kMaxOff needs no shift; for f16 the offset
+// is capped at 4 so that pre-scaled activations rarely reach subnormals.
+// The order in which codes land in pairs depends on the width:
 //  * power-of-two widths: inside each 32-bit word, field f of the low half
 //    pairs with field f of the high half, i.e. code (word*V + f) with code
-//    (word*V + f + V/2), V = codes per word; one shift + one and-or per pair.
+//    (word*V + f + V/2), V = codes per word;
 //  * 3/5/6 bits: code j of pack 2r pairs with code j of pack 2r+1, both read
 //    from two-byte windows at the same offset inside their packs.
-// pair_slot(k) gives, for code k of a chunk (0..31), its pair index (0..15)
-// and half (0 low, 1 high).
+// pair_index(k) / pair_half(k) / pair_off(k) give, for code k of a chunk
+// (0..31), its pair (0..15), its half (0 low, 1 high) and its offset o.
+
+template <class T> struct Mant;
+template <> struct Mant<F16> { static constexpr int bits = 10, cap = 4; };
+template <> struct Mant<BF16> { static constexpr int bits = 7, cap = 7; };
+
+template <class T, int BITS>
+__host__ __device__ constexpr int max_off() {
+  const int m = Mant<T>::bits - BITS;
+  return m < Mant<T>::cap ? m : Mant<T>::cap;
+}
+
+// power-of-two widths: right shift applied to the word for field f, and the
+// field's remaining offset
+template <class T, int BITS>
+__host__ __device__ constexpr int pow2_shift(int f) {
+  const int step = (max_off<T, BITS>() / BITS + 1) * BITS;
+  return (BITS * f / step) * step;
+}
 
 template <int BITS>
 __host__ __device__ constexpr int pair_index(int k) {
@@ -124,26 +146,55 @@ __host__ __device__ constexpr int pair_half(int k) {
   }
 }
 
-// Pair P (0..15) of a chunk as two magic floats, for widths <= 7 with bf16 or
-// <= 8 with f16. MAGIC is the 32-bit magic pattern.
-template <int BITS, int P, uint32_t MAGIC>
-__device__ __forceinline__ uint32_t magic_pair(const uint32_t* w) {
-  constexpr uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
+// window geometry of code j of a non-power-of-two pack
+template <int BITS>
+__host__ __device__ constexpr int win_start(int j) {
+  constexpr int NB = Pack<BITS>::kBytes;
+  return (j * BITS / 8) < (NB - 2) ? (j * BITS / 8) : (NB - 2);
+}
+template <int BITS>
+__host__ __device__ constexpr int win_off(int j) {
+  return j * BITS - 8 * win_start<BITS>(j);
+}
+
+// offset o of code k's field when it meets the magic number
+template <class T, int BITS>
+__host__ __device__ constexpr int pair_off(int k) {
+  if constexpr (Pack<BITS>::kPow2) {
+    constexpr int H = Pack<BITS>::kVals / 2;
+    const int f = (k % Pack<BITS>::kVals) % H;
+    return BITS * f - pow2_shift<T, BITS>(f);
+  } else {
+    const int off = win_off<BITS>(k % Pack<BITS>::kVals);
+    return off <= max_off<T, BITS>() ? off : 0;
+  }
+}
+
+// Pair P (0..15) of a chunk as two magic floats (see above). m2 must hold
+// kMask | kMask << 16 and magic the 32-bit magic pattern; both are passed in
+// registers so that mask + or fuse into one v_and_or_b32.
+template <class T, int BITS, int P>
+__device__ __forceinline__ uint32_t magic_pair(const uint32_t* w, uint32_t m2,
+                                               uint32_t magic) {
   if constexpr (Pack<BITS>::kPow2) {
     constexpr int H = Pack<BITS>::kVals / 2;
     constexpr int word = P / H, f = P % H;
-    return ((w[word] >> (f * BITS)) & m2) | MAGIC;
+    constexpr int sh = pow2_shift<T, BITS>(f);
+    constexpr int o = BITS * f - sh;
+    const uint32_t v = sh ? (w[word] >> sh) : w[word];
+    return (v & (m2 << o)) | magic;
   } else {
     constexpr int V = Pack<BITS>::kVals, NB = Pack<BITS>::kBytes;
     constexpr int r = P / V, j = P % V;
-    constexpr int bit = j * BITS;
-    constexpr int ws = (bit / 8) < (NB - 2) ? (bit / 8) : (NB - 2);
-    constexpr int off = bit - 8 * ws;
+    constexpr int ws = win_start<BITS>(j), off = win_off<BITS>(j);
     static_assert(off + BITS <= 16, "field must fit a two-byte window");
     const uint32_t lo = bytes2_at<(2 * r) * NB + ws>(w);
     const uint32_t hi = bytes2_at<(2 * r + 1) * NB + ws>(w);
     const uint32_t pr = (lo & 0xffffu) | (hi << 16);
-    return ((pr >> off) & m2) | MAGIC;
+    constexpr int o = pair_off<T, BITS>(j);
+    constexpr int sh = off - o;
+    const uint32_t v = sh ? (pr >> sh) : pr;
+    return (v & (m2 << o)) | magic;
   }
 }
 

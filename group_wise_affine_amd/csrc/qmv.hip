@@ -57,160 +57,247 @@ __device__ __forceinline__ void load_chunk(const uint8_t* p, uint32_t w[BITS]) {
   }
 }
 
-// sum over the chunk of x_pair . (MAGIC + q)_pair
-template <class T, int BITS, int P = 0>
+// sum over the chunk of x'_pair . (MAGIC + q*2^o)_pair
+template <class T, int P = 0>
 __device__ __forceinline__ float chunk_dot_pairs(const uint32_t* pairs,
                                                  const uint32_t* xp, float d) {
   if constexpr (P == 16) {
     return d;
   } else {
     d = dot2(T{}, pairs[P], xp[P], d);
-    return chunk_dot_pairs<T, BITS, P + 1>(pairs, xp, d);
+    return chunk_dot_pairs<T, P + 1>(pairs, xp, d);
   }
 }
 
 template <class T, int BITS, int P = 0>
-__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* pr) {
+__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t m2,
+                                             uint32_t magic, uint32_t* pr) {
   if constexpr (P < 16) {
-    pr[P] = magic_pair<BITS, P, T::kMagic>(w);
-    unpack_pairs<T, BITS, P + 1>(w, pr);
+    pr[P] = magic_pair<T, BITS, P>(w, m2, magic);
+    unpack_pairs<T, BITS, P + 1>(w, m2, magic, pr);
   }
 }
 
-template <class T, int BITS, int MB>
-__global__ __launch_bounds__(256) void qmv_kernel(
+constexpr int kWWaves = 4;                        // wavefronts streaming W
+constexpr int kXWaves = 2;                        // wavefronts staging x
+constexpr int kThreads = (kWWaves + kXWaves) * 64;
+
+// One workgroup = 4 W wavefronts + 2 x wavefronts.
+//  x wavefronts: issue the x loads of their first staging task, barrier 1,
+//    then permute / pre-scale / sum into LDS, barrier 2.
+//  W wavefronts: barrier 1 (so that the x loads are ahead of them in the
+//    CU's memory queue), issue every weight load of the lane, barrier 2
+//    (which does not wait for those loads), then multiply chunk by chunk as
+//    the weight data arrives.
+// Lane work: R rows x CPL chunks; lane t of a row group handles chunks
+// c = t + TPR*i (i < CPL) of each of its R rows, so an x chunk read from LDS
+// serves R rows.
+template <class T, int BITS, int MB, int CPL, int R>
+__global__ __launch_bounds__(kThreads) void qmv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    uint16_t* __restrict__ y, int M, int N, int K, int gs_log2,
-    int tpr_log2) {
+    uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, int tpr_log2,
+    uint32_t m2, uint32_t magic) {
   using Cfg = QmvCfg<T, BITS>;
   constexpr int XW = Cfg::kXWords;
   extern __shared__ uint32_t smem[];
   const int nch = K >> 5;
-  uint32_t* xs = smem;                                          // [MB][nch][XW]
-  float* xsum = reinterpret_cast<float*>(smem + MB * nch * XW);  // [MB][nch]
+  const int ntask = MB * nch;
+  uint32_t* xs = smem;                                            // [MB*nch][XW]
+  float* xsum = reinterpret_cast<float*>(smem + ntask * XW);       // [MB*nch]
+  float* xd0 = xsum + ntask;                                       // [MB*nch]
   const int m0 = blockIdx.y * MB;
 
-  // ---- stage x (permuted into pair order) and per-chunk sums
-  for (int i = threadIdx.x; i < MB * nch; i += blockDim.x) {
-    const int m = i / nch, c = i - m * nch;
-    uint32_t px[XW];
-    float sum = 0.0f;
-    if (m0 + m < M) {
-      const uint4* src =
-          reinterpret_cast<const uint4*>(x + (int64_t)(m0 + m) * K + c * 32);
-      uint32_t raw[16];
+  const int tpr = 1 << tpr_log2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool w_wave = wave < kWWaves;
+  const int slot = lane >> tpr_log2, t = lane & (tpr - 1);
+  const int slots = 64 >> tpr_log2;  // row groups per wavefront
+  const int row0 = ((blockIdx.x * kWWaves + wave) * slots + slot) * R;
+
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  const int G = K >> gs_log2;
+  const int batch = tpr * CPL;  // chunks of a row covered by one batch
+  uint32_t wv[R][CPL][BITS];
+  uint16_t sw[R][CPL], bw[R][CPL];  // raw scale / bias words
+  bool ok[R][CPL];
+  // Branch-free: out-of-range chunks read a clamped valid address and are
+  // zeroed through their scale and bias, so all loads issue back to back.
+  auto load_batch = [&](int cb) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const uint4 u = src[q];
-        raw[4 * q] = u.x; raw[4 * q + 1] = u.y;
-        raw[4 * q + 2] = u.z; raw[4 * q + 3] = u.w;
+    for (int r = 0; r < R; r++) {
+      const int row = row0 + r;
+      const int rowc = row < N ? row : N - 1;
+#pragma unroll
+      for (int i = 0; i < CPL; i++) {
+        const int c = cb + t + i * tpr;
+        const int cc = c < nch ? c : nch - 1;
+        ok[r][i] = (row < N) && (c < nch);
+        load_chunk<BITS>(wq + (int64_t)rowc * row_bytes + (int64_t)cc * (4 * BITS), wv[r][i]);
+        const int g = (cc << 5) >> gs_log2;
+        sw[r][i] = scales[(int64_t)rowc * G + g];
+        bw[r][i] = biases[(int64_t)rowc * G + g];
       }
-      if constexpr (Cfg::kF32) {
+    }
+  };
+
+  // x staging: task = (row of x, chunk); activations permuted into pair
+  // order and pre-scaled by 2^-o, plus the chunk's sum and magic offset
+  auto x_load = [&](int task, uint4* raw4) {
+    const int tk = task < ntask ? task : ntask - 1;
+    const int m = tk / nch, c = tk - m * nch;
+    const int mr = m0 + m < M ? m0 + m : M - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)mr * K + c * 32);
 #pragma unroll
-        for (int k = 0; k < 32; k++) {
-          const float f = to_f32(T{}, (uint16_t)(raw[k / 2] >> (16 * (k % 2))));
-          px[k] = __builtin_bit_cast(uint32_t, f);
-          sum += f;
-        }
-      } else {
+    for (int q = 0; q < 4; q++) raw4[q] = src[q];
+  };
+  auto stage = [&](int task, const uint4* raw4) {
+    const int m = task / nch;
+    uint32_t raw[16];
 #pragma unroll
-        for (int p = 0; p < 16; p++) px[p] = 0;
+    for (int q = 0; q < 4; q++) {
+      raw[4 * q] = raw4[q].x; raw[4 * q + 1] = raw4[q].y;
+      raw[4 * q + 2] = raw4[q].z; raw[4 * q + 3] = raw4[q].w;
+    }
+    const bool live = m0 + m < M;
+    uint32_t px[XW];
+    float sum = 0.0f, d0 = 0.0f;
+    if constexpr (Cfg::kF32) {
 #pragma unroll
-        for (int k = 0; k < 32; k++) {
-          const uint32_t h = (raw[k / 2] >> (16 * (k % 2))) & 0xffffu;
-          px[pair_index<BITS>(k)] |= h << (16 * pair_half<BITS>(k));
-          sum += to_f32(T{}, (uint16_t)h);
-        }
+      for (int k = 0; k < 32; k++) {
+        const float f = live ? to_f32(T{}, (uint16_t)(raw[k / 2] >> (16 * (k % 2)))) : 0.0f;
+        px[k] = __builtin_bit_cast(uint32_t, f);
+        sum += f;
       }
     } else {
 #pragma unroll
-      for (int p = 0; p < XW; p++) px[p] = 0;
+      for (int p = 0; p < 16; p++) px[p] = 0;
+#pragma unroll
+      for (int k = 0; k < 32; k++) {
+        const float f = live ? to_f32(T{}, (uint16_t)(raw[k / 2] >> (16 * (k % 2)))) : 0.0f;
+        constexpr float kScale[8] = {1.f, 0.5f, 0.25f, 0.125f, 0.0625f, 0.03125f,
+                                     0.015625f, 0.0078125f};
+        const uint16_t h = from_f32(T{}, f * kScale[pair_off<T, BITS>(k)]);
+        px[pair_index<BITS>(k)] |= (uint32_t)h << (16 * pair_half<BITS>(k));
+        sum += f;
+        d0 += to_f32(T{}, h);
+      }
+      d0 *= T::kMagicF;
     }
-    uint4* dst = reinterpret_cast<uint4*>(xs + (int64_t)i * XW);
+    uint4* dst = reinterpret_cast<uint4*>(xs + (int64_t)task * XW);
 #pragma unroll
     for (int q = 0; q < XW / 4; q++)
       dst[q] = make_uint4(px[4 * q], px[4 * q + 1], px[4 * q + 2], px[4 * q + 3]);
-    xsum[i] = sum;
+    xsum[task] = sum;
+    xd0[task] = d0;
+  };
+
+  if (w_wave) {
+    __syncthreads();  // 1: the x loads of this workgroup are queued first
+    load_batch(0);
+    __syncthreads();  // 2: x staged (does not wait for the weight loads)
+  } else {
+    const int xl = (wave - kWWaves) * 64 + lane;
+    uint4 raw4[4];
+    x_load(xl, raw4);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // 1
+    if (xl < ntask) stage(xl, raw4);
+    for (int task = xl + kXWaves * 64; task < ntask; task += kXWaves * 64) {
+      x_load(task, raw4);
+      stage(task, raw4);
+    }
+    __syncthreads();  // 2
+    return;
   }
-  __syncthreads();
 
-  // ---- stream W
-  const int tpr = 1 << tpr_log2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane >> tpr_log2, t = lane & (tpr - 1);
-  const int row = (blockIdx.x * (blockDim.x >> 6) + wave) * (64 >> tpr_log2) + slot;
-  const bool active = row < N;
-  float acc[MB];
+  // ---- multiply
+  // The magic pattern lives in a VGPR and the mask in an SGPR, so that
+  // mask-and-or is one v_and_or_b32 (a VOP3 reads one SGPR at most and no
+  // literal on gfx9).
+  uint32_t magic_v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(magic));
+  float acc[R][MB];
 #pragma unroll
-  for (int m = 0; m < MB; m++) acc[m] = 0.0f;
+  for (int r = 0; r < R; r++)
+#pragma unroll
+    for (int m = 0; m < MB; m++) acc[r][m] = 0.0f;
 
-  if (active) {
-    const int64_t row_bytes = (int64_t)K * BITS / 8;
-    const uint8_t* wrow = wq + (int64_t)row * row_bytes;
-    const uint16_t* srow = scales + (int64_t)row * (K >> gs_log2);
-    const uint16_t* brow = biases + (int64_t)row * (K >> gs_log2);
-    constexpr int U = 4;  // chunks in flight per lane
-    for (int c0 = t; c0 < nch; c0 += U * tpr) {
-      uint32_t wv[U][BITS];
-      float sv[U], bv[U];
+  for (int cb = 0;;) {
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int c = c0 + u * tpr;
-        if (c < nch) {
-          load_chunk<BITS>(wrow + (int64_t)c * (4 * BITS), wv[u]);
-          const int g = (c << 5) >> gs_log2;
-          sv[u] = to_f32(T{}, srow[g]);
-          bv[u] = to_f32(T{}, brow[g]);
+    for (int i = 0; i < CPL; i++) {
+      const int c = cb + t + i * tpr;
+      if (c < nch) {
+        float sf[R], bf[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+          sf[r] = ok[r][i] ? to_f32(T{}, sw[r][i]) : 0.0f;
+          bf[r] = ok[r][i] ? to_f32(T{}, bw[r][i]) : 0.0f;
         }
-      }
+        if constexpr (Cfg::kF32) {
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int c = c0 + u * tpr;
-        if (c < nch) {
-          const float s = sv[u];
-          if constexpr (Cfg::kF32) {
-            float fq[32];
+          for (int m = 0; m < MB; m++) {
+            const float* xp = reinterpret_cast<const float*>(xs + (int64_t)(m * nch + c) * XW);
+            float xv[32];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-              fq[4 * i + 0] = (float)((wv[u][i] >> 0) & 0xffu);
-              fq[4 * i + 1] = (float)((wv[u][i] >> 8) & 0xffu);
-              fq[4 * i + 2] = (float)((wv[u][i] >> 16) & 0xffu);
-              fq[4 * i + 3] = (float)((wv[u][i] >> 24) & 0xffu);
-            }
+            for (int k = 0; k < 32; k++) xv[k] = xp[k];
+            const float xsm = xsum[m * nch + c];
 #pragma unroll
-            for (int m = 0; m < MB; m++) {
-              const float* xp = reinterpret_cast<const float*>(xs + (int64_t)(m * nch + c) * XW);
+            for (int r = 0; r < R; r++) {
               float d = 0.0f;
 #pragma unroll
-              for (int k = 0; k < 32; k++) d = fmaf(xp[k], fq[k], d);
-              acc[m] = fmaf(s, d, fmaf(bv[u], xsum[m * nch + c], acc[m]));
-            }
-          } else {
-            const float boff = fmaf(-T::kMagicF, s, bv[u]);
-            uint32_t pr[16];
-            unpack_pairs<T, BITS>(wv[u], pr);
+              for (int w = 0; w < 8; w++)
 #pragma unroll
-            for (int m = 0; m < MB; m++) {
-              const uint32_t* xp = xs + (int64_t)(m * nch + c) * XW;
-              const float d = chunk_dot_pairs<T, BITS>(pr, xp, 0.0f);
-              acc[m] = fmaf(s, d, fmaf(boff, xsum[m * nch + c], acc[m]));
+                for (int bb = 0; bb < 4; bb++)
+                  d = fmaf(xv[4 * w + bb], (float)((wv[r][i][w] >> (8 * bb)) & 0xffu), d);
+              acc[r][m] = fmaf(sf[r], d, fmaf(bf[r], xsm, acc[r][m]));
+            }
+          }
+        } else {
+          uint32_t pr[R][16];
+#pragma unroll
+          for (int r = 0; r < R; r++) unpack_pairs<T, BITS>(wv[r][i], m2, magic_v, pr[r]);
+#pragma unroll
+          for (int m = 0; m < MB; m++) {
+            const uint4* xp4 = reinterpret_cast<const uint4*>(xs + (int64_t)(m * nch + c) * XW);
+            uint32_t xp[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const uint4 u = xp4[q];
+              xp[4 * q] = u.x; xp[4 * q + 1] = u.y; xp[4 * q + 2] = u.z; xp[4 * q + 3] = u.w;
+            }
+            const float xsm = xsum[m * nch + c];
+            const float d0 = xd0[m * nch + c];
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+              const float d = chunk_dot_pairs<T>(pr[r], xp, 0.0f) - d0;
+              acc[r][m] = fmaf(sf[r], d, fmaf(bf[r], xsm, acc[r][m]));
             }
           }
         }
       }
     }
+    cb += batch;
+    if (cb >= nch) break;
+    load_batch(cb);  // rows longer than one batch (very large K)
   }
 
   // ---- reduce the TPR partial sums of each row
   for (int o = tpr >> 1; o >= 1; o >>= 1) {
 #pragma unroll
-    for (int m = 0; m < MB; m++) acc[m] += __shfl_xor(acc[m], o);
-  }
-  if (active && t == 0) {
+    for (int r = 0; r < R; r++)
 #pragma unroll
-    for (int m = 0; m < MB; m++)
-      if (m0 + m < M) y[(int64_t)(m0 + m) * N + row] = from_f32(T{}, acc[m]);
+      for (int m = 0; m < MB; m++) acc[r][m] += __shfl_xor(acc[r][m], o);
+  }
+  if (t == 0) {
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int row = row0 + r;
+#pragma unroll
+      for (int m = 0; m < MB; m++)
+        if (row < N && m0 + m < M)
+          y[(int64_t)(m0 + m) * N + row] = from_f32(T{}, acc[r][m]);
+    }
   }
 }
 
@@ -218,27 +305,70 @@ __global__ __launch_bounds__(256) void qmv_kernel(
 
 static constexpr int kMaxLds = 64 * 1024;
 
-template <class T, int BITS, int MB>
-static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
-                            const void* b, int M, int N, int K, int gs,
-                            void* y, hipStream_t st) {
+// Lane work shapes (chunks per lane, rows per lane) compiled in.
+struct Shape {
+  int cpl, r;
+};
+static constexpr Shape kShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}};
+
+// Threads per row for a lane shape: enough lanes that CPL chunks each cover
+// the row (a power of two, at most 64).
+static int tpr_for(int nch, int cpl) {
+  int tpr = 1;
+  while (tpr < 64 && tpr * cpl < nch) tpr *= 2;
+  return tpr;
+}
+
+template <class T, int BITS, int MB, int CPL, int R>
+static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
+                               const void* b, int M, int N, int K, int gs,
+                               int tpr, void* y, hipStream_t st) {
   using Cfg = QmvCfg<T, BITS>;
   const int nch = K / 32;
-  // threads per row: enough workgroups to fill 256 CUs, at least one chunk
-  // per lane
-  int tpr = 16;
-  while (tpr < 64 && (int64_t)N * tpr / 256 < 256 && nch >= 2 * tpr) tpr *= 2;
-  while (tpr > 1 && tpr > nch) tpr /= 2;
-  const int rows_per_block = 4 * (64 / tpr);
+  const int rows_per_block = kWWaves * (64 / tpr) * R;
   const dim3 grid((N + rows_per_block - 1) / rows_per_block, (M + MB - 1) / MB);
-  const size_t lds = (size_t)MB * nch * (Cfg::kXWords + 1) * 4;
-  hipLaunchKernelGGL((qmv_kernel<T, BITS, MB>), grid, dim3(256), lds, st,
+  const size_t lds = (size_t)MB * nch * (Cfg::kXWords + 2) * 4;
+  const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
+  uint32_t magic = 0;
+  if constexpr (!Cfg::kF32) magic = T::kMagic;
+  hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R>), grid, dim3(kThreads), lds, st,
                      static_cast<const uint16_t*>(x),
                      reinterpret_cast<const uint8_t*>(wq),
                      static_cast<const uint16_t*>(s),
                      static_cast<const uint16_t*>(b),
-                     static_cast<uint16_t*>(y), M, N, K, ilog2(gs), ilog2(tpr));
+                     static_cast<uint16_t*>(y), M, N, K, ilog2(gs), ilog2(tpr), m2, magic);
   return hipGetLastError();
+}
+
+template <class T, int BITS, int MB>
+static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
+                            const void* b, int M, int N, int K, int gs,
+                            void* y, hipStream_t st) {
+  const int nch = K / 32;
+  // Pick the lane shape: the chunks of a row must fit in 64 lanes x CPL; prefer
+  // at least 256 workgroups (one per CU), then the most work per lane.
+  int best = -1;
+  int64_t best_key = -1;
+  for (int i = 0; i < 4; i++) {
+    const Shape sh = kShapes[i];
+    const int tpr = tpr_for(nch, sh.cpl);
+    const int rows_per_block = kWWaves * (64 / tpr) * sh.r;
+    const int64_t blocks = (int64_t)((N + rows_per_block - 1) / rows_per_block) *
+                           ((M + MB - 1) / MB);
+    // a shape whose batch covers the row beats one that needs several
+    const int work = (tpr * sh.cpl >= nch ? 64 : 0) + sh.cpl * sh.r;
+    const int64_t key = (blocks >= 256 ? (1 << 20) : blocks * 64) + work;
+    if (key > best_key) { best_key = key; best = i; }
+  }
+  if (best < 0) best = 3;
+  const Shape sh = kShapes[best];
+  const int tpr = tpr_for(nch, sh.cpl);
+  switch (best) {
+    case 0: return launch_shape<T, BITS, MB, 2, 1>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    case 1: return launch_shape<T, BITS, MB, 4, 1>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    case 2: return launch_shape<T, BITS, MB, 4, 2>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    default: return launch_shape<T, BITS, MB, 8, 1>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+  }
 }
 
 template <class T, int BITS>
@@ -246,13 +376,12 @@ static hipError_t launch_t(const void* x, const uint32_t* wq, const void* s,
                            const void* b, int M, int N, int K, int gs, void* y,
                            hipStream_t st) {
   using Cfg = QmvCfg<T, BITS>;
-  const int64_t per_row = (int64_t)(K / 32) * (Cfg::kXWords + 1) * 4;
+  const int64_t per_row = (int64_t)(K / 32) * (Cfg::kXWords + 2) * 4;
   int mb_max = (int)(kMaxLds / per_row);
-  int want = 1;  // smallest of 1, 2, 4, 8 covering M (8 at most)
-  while (want < M && want < 8) want *= 2;
+  int want = 1;  // smallest of 1, 2, 4 covering M (4 at most)
+  while (want < M && want < 4) want *= 2;
   while (want > 1 && want > mb_max) want /= 2;
   switch (want) {
-    case 8: return launch_mb<T, BITS, 8>(x, wq, s, b, M, N, K, gs, y, st);
     case 4: return launch_mb<T, BITS, 4>(x, wq, s, b, M, N, K, gs, y, st);
     case 2: return launch_mb<T, BITS, 2>(x, wq, s, b, M, N, K, gs, y, st);
     default: return launch_mb<T, BITS, 1>(x, wq, s, b, M, N, K, gs, y, st);

@@ -110,7 +110,7 @@ def test_qmv_multi_m_blocks(orc, M):
     _run_mm(Q.qmv, orc, "bf16", M, 33, 2048, 128, 3, seed=M)
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (5, 64), (257, 96), (64, 8192), (3, 15872)])
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 64), (257, 96), (64, 8192), (3, 15360)])
 def test_qmv_edge_shapes(orc, N, K):
     gs = 32
     _run_mm(Q.qmv, orc, "f16", 1, N, K, gs, 4, seed=N)
@@ -119,7 +119,7 @@ def test_qmv_edge_shapes(orc, N, K):
 
 def test_qmv_max_k(orc):
     """The largest K the streaming kernel accepts (f16 4-bit, g32)."""
-    _run_mm(Q.qmv, orc, "f16", 1, 3, 30720, 32, 4, seed=3)
+    _run_mm(Q.qmv, orc, "f16", 1, 3, 29120, 32, 4, seed=3)
 
 
 # ------------------------------------------------------------ qmm_t (MFMA)
