@@ -22,6 +22,8 @@
 //    tile loader: GEMM row m = output pixel (b, oy, ox), column k =
 //    (dy, dx, c) of conv group g = blockIdx.z, zero for taps outside the
 //    image and for the zero-padded tail k >= K_true.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,6 +34,7 @@ typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
+  uint32_t magic;    // magic-number pattern of the element type (f16 path)
   const uint16_t* x;
   const uint8_t* wq;
   const uint16_t* s;
@@ -80,40 +83,95 @@ __device__ __forceinline__ void load_wchunk(const uint8_t* p, uint32_t w[BITS]) 
   }
 }
 
-// Dequantize the 32 codes of a chunk: out[j] = fl32(s*q_j + b) (s*q exact).
-template <int BITS, int J = 0>
-__device__ __forceinline__ void dequant_chunk(const uint32_t* w, float s,
-                                              float b, float* out) {
-  if constexpr (J < 32) {
-    out[J] = fmaf(s, (float)code_at<BITS, J>(w), b);
-    dequant_chunk<BITS, J + 1>(w, s, b, out);
+// f16 dequantization of a 32-code chunk into 16 natural-order f16 pairs.
+// Codes are first turned into magic f16 values 1024 + q*2^o (one v_and_or_b32
+// per pair, see common.hpp); each is then mapped through one fp32 FMA with
+// s*2^-o and b - 1024*s*2^-o and rounded once to f16 (v_fma_mix), giving
+// f16(s*q + b) up to a 2^-14 |s| perturbation of the constant.
+template <int BITS>
+__device__ __forceinline__ void dequant_chunk_f16(const uint32_t* w, float s,
+                                                  float b, uint32_t m2,
+                                                  uint32_t magic, uint32_t* out) {
+  uint32_t pr[16];
+#pragma unroll
+  for (int p = 0; p < 16; p++) pr[p] = 0;
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    ((pr[P] = magic_pair<F16, BITS, P>(w, m2, magic)), ...);
+  }(std::make_integer_sequence<int, 16>{});
+  float so[8], co[8];
+#pragma unroll
+  for (int o = 0; o < 8; o++) {
+    so[o] = s * __builtin_bit_cast(float, (uint32_t)(127 - o) << 23);
+    co[o] = fmaf(-1024.0f, so[o], b);
+  }
+#pragma unroll
+  for (int k = 0; k < 32; k += 2) {
+    uint32_t v[2];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const int kk = k + e;
+      const int p = pair_index<BITS>(kk), h = pair_half<BITS>(kk);
+      const int o = pair_off<F16, BITS>(kk);
+      const uint16_t hb = (uint16_t)(pr[p] >> (16 * h));
+      const float q = (float)__builtin_bit_cast(_Float16, hb);
+      v[e] = from_f32(F16{}, fmaf(q, so[o], co[o]));
+    }
+    out[k / 2] = v[0] | (v[1] << 16);
   }
 }
 
-__device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
-  return (uint32_t)from_f32(F16{}, a) | ((uint32_t)from_f32(F16{}, b) << 16);
-}
-__device__ __forceinline__ uint32_t pack2(BF16, float a, float b) {
-  return (uint32_t)from_f32(BF16{}, a) | ((uint32_t)from_f32(BF16{}, b) << 16);
+// bf16 dequantization of a chunk, split as hi = bf16(w), lo = bf16(w - hi).
+template <int BITS>
+__device__ __forceinline__ void dequant_chunk_bf16(const uint32_t* w, float s,
+                                                   float b, uint32_t* hi,
+                                                   uint32_t* lo) {
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    float f[32] = {fmaf(s, (float)code_at<BITS, J>(w), b)...};
+#pragma unroll
+    for (int k = 0; k < 32; k += 2) {
+      const uint16_t h0 = from_f32(BF16{}, f[k]), h1 = from_f32(BF16{}, f[k + 1]);
+      hi[k / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      const uint16_t l0 = from_f32(BF16{}, f[k] - to_f32(BF16{}, h0));
+      const uint16_t l1 = from_f32(BF16{}, f[k + 1] - to_f32(BF16{}, h1));
+      lo[k / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+  }(std::make_integer_sequence<int, 32>{});
 }
 
 constexpr int kBK = 64;       // K step
 constexpr int kPad = 8;       // LDS row padding in 16-bit elements
 constexpr int kLdsRow = kBK + kPad;
 
+template <int BM, int BN, int BITS>
+struct TileRegs {
+  static constexpr int A_VECS = BM * kBK / 8 / 256;
+  static constexpr int W_PER_T = (BN * 2 + 255) / 256;
+  uint4 a[A_VECS];
+  bool al[A_VECS];
+  uint32_t w[W_PER_T][BITS];
+  uint16_t s[W_PER_T], b[W_PER_T];
+  bool wl[W_PER_T];
+};
+
+// Workgroup tile BM x BN of y, 256 threads = 2x2 wavefronts, K in steps of
+// 64. LDS holds two stages (x tile + dequantized W tile each); the global
+// loads of step k+2 are in flight in registers while step k multiplies and
+// step k+1 is dequantized into the other LDS stage: one barrier per step.
 template <class T, int BITS, int BM, int BN, bool CONV, bool CONV_VEC>
 __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
   constexpr bool kSplit = __is_same(T, BF16);
   constexpr int WTM = BM / 2, WTN = BN / 2;  // wavefront tile
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_VECS = BM * kBK / 8 / 256;  // 16-byte x vectors per thread
+  using Regs = TileRegs<BM, BN, BITS>;
+  constexpr int A_VECS = Regs::A_VECS;
   constexpr int W_CHUNKS = BN * 2;            // 32-code chunks per K step
-  constexpr int W_PER_T = (W_CHUNKS + 255) / 256;
+  constexpr int W_PER_T = Regs::W_PER_T;
+  constexpr int A_STAGE = BM * kLdsRow, W_STAGE = BN * kLdsRow;
   static_assert(A_VECS >= 1, "BM too small");
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[BN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Wl[kSplit ? BN * kLdsRow : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2 * W_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Wl[kSplit ? 2 * W_STAGE : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -131,6 +189,8 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
     sp += (int64_t)g * a.Og * n_groups_row;
     bp += (int64_t)g * a.Og * n_groups_row;
   }
+  uint32_t magic_v, m2_s = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(a.magic));
 
   // ---- per-thread x rows (fixed across K steps)
   int a_row[A_VECS], a_kv[A_VECS];
@@ -152,30 +212,29 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
     }
   }
 
-  uint4 a_reg[A_VECS];
-  uint32_t w_reg[W_PER_T][BITS];
-  float s_reg[W_PER_T], b_reg[W_PER_T];
-
-  auto load_tile = [&](int kt) {
+  // Global loads of one K step into registers. Branch-free: out-of-range
+  // elements read a clamped valid address and are zeroed when stored, so the
+  // loads of a step issue back to back and stay in flight.
+  auto load_tile = [&](int kt, Regs& r) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int v = 0; v < A_VECS; v++) {
       const int k = k0 + a_kv[v] * 8;
-      uint4 val = make_uint4(0, 0, 0, 0);
       if constexpr (!CONV) {
-        if (a_ok[v] && k < a.K)
-          val = *reinterpret_cast<const uint4*>(
-              a.x + (int64_t)(m_blk + a_row[v]) * a.K + k);
+        const int kc = k < a.K ? k : a.K - 8;
+        const int m = a_ok[v] ? m_blk + a_row[v] : a.M - 1;
+        r.al[v] = a_ok[v] && k < a.K;
+        r.a[v] = *reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.K + kc);
       } else if constexpr (CONV_VEC) {
-        if (a_ok[v] && k < a.K_true) {
-          const int tap = k / a.Cg, c = k - tap * a.Cg;
-          const int dy = tap / a.kw, dx = tap - dy * a.kw;
-          const int iy = pix_y[v] + dy, ix = pix_x[v] + dx;
-          if (iy >= 0 && iy < a.H && ix >= 0 && ix < a.W)
-            val = *reinterpret_cast<const uint4*>(
-                a.x + (((int64_t)pix_b[v] * a.H + iy) * a.W + ix) * a.C +
-                g * a.Cg + c);
-        }
+        const int kk = k < a.K_true ? k : 0;
+        const int tap = kk / a.Cg, c = kk - tap * a.Cg;
+        const int dy = tap / a.kw, dx = tap - dy * a.kw;
+        const int iy = pix_y[v] + dy, ix = pix_x[v] + dx;
+        const bool in = a_ok[v] && k < a.K_true && iy >= 0 && iy < a.H && ix >= 0 && ix < a.W;
+        r.al[v] = in;
+        const int iyc = in ? iy : 0, ixc = in ? ix : 0;
+        r.a[v] = *reinterpret_cast<const uint4*>(
+            a.x + (((int64_t)pix_b[v] * a.H + iyc) * a.W + ixc) * a.C + g * a.Cg + c);
       } else {
         uint16_t e[8];
 #pragma unroll
@@ -187,65 +246,58 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
             const int dy = tap / a.kw, dx = tap - dy * a.kw;
             const int iy = pix_y[v] + dy, ix = pix_x[v] + dx;
             if (iy >= 0 && iy < a.H && ix >= 0 && ix < a.W)
-              e[i] = a.x[(((int64_t)pix_b[v] * a.H + iy) * a.W + ix) * a.C +
-                         g * a.Cg + c];
+              e[i] = a.x[(((int64_t)pix_b[v] * a.H + iy) * a.W + ix) * a.C + g * a.Cg + c];
           }
         }
-        val = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
-                         e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+        r.al[v] = true;
+        r.a[v] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                            e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
       }
-      a_reg[v] = val;
     }
 #pragma unroll
     for (int u = 0; u < W_PER_T; u++) {
       const int ci = tid + 256 * u;
       const int n = n_blk + ci / 2;
       const int kc = k0 + (ci % 2) * 32;
-#pragma unroll
-      for (int i = 0; i < BITS; i++) w_reg[u][i] = 0;
-      s_reg[u] = 0.0f;
-      b_reg[u] = 0.0f;
-      if (ci < W_CHUNKS && n < a.N && kc < a.K) {
-        load_wchunk<BITS>(wq + (int64_t)n * w_row_bytes + (int64_t)kc * BITS / 8,
-                          w_reg[u]);
-        const int gi = kc >> a.gs_log2;
-        s_reg[u] = to_f32(T{}, sp[(int64_t)n * n_groups_row + gi]);
-        b_reg[u] = to_f32(T{}, bp[(int64_t)n * n_groups_row + gi]);
-      }
+      r.wl[u] = ci < W_CHUNKS && n < a.N && kc < a.K;
+      const int nc = n < a.N ? n : a.N - 1;
+      const int kcc = kc < a.K ? kc : a.K - 32;
+      load_wchunk<BITS>(wq + (int64_t)nc * w_row_bytes + (int64_t)kcc * BITS / 8, r.w[u]);
+      const int gi = kcc >> a.gs_log2;
+      r.s[u] = sp[(int64_t)nc * n_groups_row + gi];
+      r.b[u] = bp[(int64_t)nc * n_groups_row + gi];
     }
   };
 
-  auto store_tile = [&]() {
+  // Registers of one K step -> LDS stage (x as is, W dequantized).
+  auto store_tile = [&](const Regs& r, int stage) {
+    uint16_t* as = As + stage * A_STAGE;
 #pragma unroll
     for (int v = 0; v < A_VECS; v++)
-      *reinterpret_cast<uint4*>(&As[a_row[v] * kLdsRow + a_kv[v] * 8]) = a_reg[v];
+      *reinterpret_cast<uint4*>(&as[a_row[v] * kLdsRow + a_kv[v] * 8]) =
+          r.al[v] ? r.a[v] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < W_PER_T; u++) {
       const int ci = tid + 256 * u;
       if (ci < W_CHUNKS) {
-        const int r = ci / 2, h = ci % 2;
-        float f[32];
-        dequant_chunk<BITS>(w_reg[u], s_reg[u], b_reg[u], f);
+        const int row = ci / 2, h = ci % 2;
+        const float sc = r.wl[u] ? to_f32(T{}, r.s[u]) : 0.0f;
+        const float bi = r.wl[u] ? to_f32(T{}, r.b[u]) : 0.0f;
         uint32_t hi[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) hi[i] = pack2(T{}, f[2 * i], f[2 * i + 1]);
-        uint4* dst = reinterpret_cast<uint4*>(&Ws[r * kLdsRow + h * 32]);
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          dst[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
+        uint4* dst = reinterpret_cast<uint4*>(&Ws[stage * W_STAGE + row * kLdsRow + h * 32]);
         if constexpr (kSplit) {
           uint32_t lo[16];
-#pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const float h0 = to_f32(BF16{}, (uint16_t)(hi[i] & 0xffffu));
-            const float h1 = to_f32(BF16{}, (uint16_t)(hi[i] >> 16));
-            lo[i] = pack2(BF16{}, f[2 * i] - h0, f[2 * i + 1] - h1);
-          }
-          uint4* dl = reinterpret_cast<uint4*>(&Wl[r * kLdsRow + h * 32]);
+          dequant_chunk_bf16<BITS>(r.w[u], sc, bi, hi, lo);
+          uint4* dl = reinterpret_cast<uint4*>(&Wl[stage * W_STAGE + row * kLdsRow + h * 32]);
 #pragma unroll
           for (int q = 0; q < 4; q++)
             dl[q] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
+        } else {
+          dequant_chunk_f16<BITS>(r.w[u], sc, bi, m2_s, magic_v, hi);
         }
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          dst[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
       }
     }
   };
@@ -256,12 +308,10 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  const int nkt = (a.K + kBK - 1) / kBK;
-  load_tile(0);
-  for (int kt = 0; kt < nkt; kt++) {
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < nkt) load_tile(kt + 1);
+  auto mma_stage = [&](int stage) {
+    const uint16_t* as = As + stage * A_STAGE;
+    const uint16_t* ws = Ws + stage * W_STAGE;
+    const uint16_t* wl = Wl + (kSplit ? stage * W_STAGE : 0);
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; kk++) {
       const int kof = kk * 32 + 8 * (lane >> 4);
@@ -269,14 +319,14 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < FM; i++)
         af[i] = *reinterpret_cast<const uint4*>(
-            &As[(wm * WTM + 16 * i + (lane & 15)) * kLdsRow + kof]);
+            &as[(wm * WTM + 16 * i + (lane & 15)) * kLdsRow + kof]);
 #pragma unroll
       for (int j = 0; j < FN; j++) {
         bf[j] = *reinterpret_cast<const uint4*>(
-            &Ws[(wn * WTN + 16 * j + (lane & 15)) * kLdsRow + kof]);
+            &ws[(wn * WTN + 16 * j + (lane & 15)) * kLdsRow + kof]);
         if constexpr (kSplit)
           bl[j] = *reinterpret_cast<const uint4*>(
-              &Wl[(wn * WTN + 16 * j + (lane & 15)) * kLdsRow + kof]);
+              &wl[(wn * WTN + 16 * j + (lane & 15)) * kLdsRow + kof]);
       }
 #pragma unroll
       for (int i = 0; i < FM; i++)
@@ -286,22 +336,69 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
           if constexpr (kSplit) acc[i][j] = mfma16(T{}, af[i], bl[j], acc[i][j]);
         }
     }
+  };
+
+  // ---- pipeline: regs r0/r1 alternate; LDS stages alternate
+  const int nkt = (a.K + kBK - 1) / kBK;
+  Regs r0, r1;
+  load_tile(0, r0);
+  if (nkt > 1) load_tile(1, r1);
+  store_tile(r0, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    // stage 0 holds step kt, r1 holds step kt+1
+    if (kt + 2 < nkt) load_tile(kt + 2, r0);
+    mma_stage(0);
+    store_tile(r1, 1);
+    __syncthreads();
+    // stage 1 holds step kt+1, r0 holds step kt+2
+    if (kt + 3 < nkt) load_tile(kt + 3, r1);
+    mma_stage(1);
+    if (kt + 2 < nkt) store_tile(r0, 0);
+    __syncthreads();
+  }
+  if (kt < nkt) {  // odd number of steps: the last one sits in stage 0
+    mma_stage(0);
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each tile
-  uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : 0);
+  // ---- epilogue: accumulators -> T -> LDS tile -> 16-byte coalesced stores.
+  // Lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile.
+  constexpr int CROW = BN + 8;
+  static_assert(BM * CROW <= 2 * A_STAGE, "epilogue tile must fit the x stages");
+  uint16_t* cs = As;
 #pragma unroll
   for (int i = 0; i < FM; i++)
 #pragma unroll
     for (int j = 0; j < FN; j++) {
-      const int n = n_blk + wn * WTN + 16 * j + (lane & 15);
+      const int col = wn * WTN + 16 * j + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int m = m_blk + wm * WTM + 16 * i + 4 * (lane >> 4) + r;
-        if (m < a.M && n < a.N) yb[(int64_t)m * a.ldy + n] = from_f32(T{}, acc[i][j][r]);
+        const int row = wm * WTM + 16 * i + 4 * (lane >> 4) + r;
+        cs[row * CROW + col] = from_f32(T{}, acc[i][j][r]);
       }
     }
+  __syncthreads();
+  uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : 0);
+  constexpr int VPR = BN / 8;  // 16-byte vectors per tile row
+  const bool vec_ok = (a.N % 8 == 0) && (a.ldy % 8 == 0);
+#pragma unroll
+  for (int it = 0; it < BM * VPR / 256; it++) {
+    const int idx = tid + 256 * it;
+    const int row = idx / VPR, cv = idx % VPR;
+    const int m = m_blk + row, n = n_blk + cv * 8;
+    if (m < a.M) {
+      const uint16_t* src = &cs[row * CROW + cv * 8];
+      if (vec_ok && n + 8 <= a.N) {
+        *reinterpret_cast<uint4*>(yb + (int64_t)m * a.ldy + n) =
+            *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int e = 0; e < 8; e++)
+          if (n + e < a.N) yb[(int64_t)m * a.ldy + n + e] = src[e];
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------------------- launch
@@ -348,6 +445,7 @@ hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.gs_log2 = ilog2(gs);
   a.ldy = N;
+  a.magic = F16::kMagic;
   if (dt == 0) return launch_bits<F16, false, false>(bits, a, 1, st);
   return launch_bits<BF16, false, false>(bits, a, 1, st);
 }
@@ -367,6 +465,7 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
   a.K = (int)cg.K_pad;
   a.gs_log2 = ilog2(gs);
   a.ldy = cg.O;
+  a.magic = F16::kMagic;
   a.H = (int)cg.H; a.W = (int)cg.W; a.C = (int)cg.C;
   a.OH = (int)cg.OH; a.OW = (int)cg.OW;
   a.kh = cg.kh; a.kw = cg.kw; a.sh = cg.sh; a.sw = cg.sw;

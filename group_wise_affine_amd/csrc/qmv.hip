@@ -32,28 +32,29 @@ struct QmvCfg {
   static constexpr int kXWords = kF32 ? 32 : 16;  // LDS words per x chunk
 };
 
+// Weight chunks are read exactly once per call: nontemporal loads stream
+// them past the caches, which keeps x, scales and biases resident in L2.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const uint8_t* p, uint32_t w[BITS]) {
-  if constexpr (BITS == 4) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-  } else if constexpr (BITS == 8) {
-    const uint4 u = reinterpret_cast<const uint4*>(p)[0];
-    const uint4 v = reinterpret_cast<const uint4*>(p)[1];
-    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-    w[4] = v.x; w[5] = v.y; w[6] = v.z; w[7] = v.w;
-  } else if constexpr (BITS == 2) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    w[0] = u.x; w[1] = u.y;
-  } else if constexpr (BITS == 6) {
+  if constexpr (BITS == 4 || BITS == 8) {
 #pragma unroll
-    for (int i = 0; i < 3; i++) {
-      const uint2 u = reinterpret_cast<const uint2*>(p)[i];
-      w[2 * i] = u.x; w[2 * i + 1] = u.y;
+    for (int h = 0; h < BITS / 4; h++) {
+      const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + h);
+      w[4 * h] = u.x; w[4 * h + 1] = u.y; w[4 * h + 2] = u.z; w[4 * h + 3] = u.w;
+    }
+  } else if constexpr (BITS == 2 || BITS == 6) {
+#pragma unroll
+    for (int h = 0; h < BITS / 2; h++) {
+      const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + h);
+      w[2 * h] = u.x; w[2 * h + 1] = u.y;
     }
   } else {  // 3 and 5 bits: 4-byte aligned chunks
 #pragma unroll
-    for (int i = 0; i < BITS; i++) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
+    for (int i = 0; i < BITS; i++)
+      w[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + i);
   }
 }
 
