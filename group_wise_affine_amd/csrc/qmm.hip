@@ -32,6 +32,7 @@ namespace qmm {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
   uint32_t magic;    // magic-number pattern of the element type (f16 path)
@@ -46,6 +47,21 @@ struct GemmArgs {
   // implicit im2col (conv only)
   int H, W, C, OH, OW, kh, kw, sh, sw, ph, pw, Cg, Og, K_true;
 };
+
+// v_mfma_f32_32x32x16: A[i][k] from lane i%32 + 32*(k/8) (element k%8), B[k][j]
+// from lane j + 32*(k/8), D[i][j] in lane j + 32*((i/4)%2), element
+// 4*(i/8) + i%4. One wavefront sustains close to the matrix-core peak with
+// four independent 32x32 accumulators (measured), unlike the 16x16x32 form.
+__device__ __forceinline__ float16_t mfma32(F16, const uint4& a, const uint4& b,
+                                            float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+      __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float16_t mfma32(BF16, const uint4& a, const uint4& b,
+                                            float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
+}
 
 __device__ __forceinline__ float4_t mfma16(F16, const uint4& a, const uint4& b,
                                            float4_t c) {
@@ -138,46 +154,81 @@ __device__ __forceinline__ void dequant_chunk_bf16(const uint32_t* w, float s,
   }(std::make_integer_sequence<int, 32>{});
 }
 
+// Instruction interleave for one half step (one basic block): after the
+// first LDS fragment reads, each MFMA is followed by one LDS read (next
+// fragments), one global load while any remain and a few VALU instructions
+// of the dequantization, so the VALU and memory work runs in the shadow of
+// the matrix core; the rest of the VALU work and the LDS writes follow.
+template <int NM, int NDR, int NVM, int NV>
+__device__ __forceinline__ void interleave_half_step() {
+  constexpr int first = NDR / (NM > 0 ? NM : 1) > 0 ? NDR - (NM - 1) : NDR;
+  __builtin_amdgcn_sched_group_barrier(0x100, first > 0 ? first : 0, 0);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
+      __builtin_amdgcn_sched_group_barrier(0x100, (I < NDR - first) ? 1 : 0, 0),
+      __builtin_amdgcn_sched_group_barrier(0x020, (I < NVM) ? 1 : 0, 0),
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0)),
+     ...);
+  }(std::make_integer_sequence<int, NM>{});
+}
+
 constexpr int kBK = 64;       // K step
 constexpr int kPad = 8;       // LDS row padding in 16-bit elements
 constexpr int kLdsRow = kBK + kPad;
 
+// Per-thread register state of one K step.
+//  x part: A_VECS 16-byte vectors of the x tile (written to LDS).
+//  W part: for each of the wavefront's FN 32-row blocks, the lane's raw
+//  32-code chunk of its weight row plus that chunk's scale and bias words.
 template <int BM, int BN, int BITS>
 struct TileRegs {
   static constexpr int A_VECS = BM * kBK / 8 / 256;
-  static constexpr int W_PER_T = (BN * 2 + 255) / 256;
+  static constexpr int FN = BN / 64;
   uint4 a[A_VECS];
   bool al[A_VECS];
-  uint32_t w[W_PER_T][BITS];
-  uint16_t s[W_PER_T], b[W_PER_T];
-  bool wl[W_PER_T];
+  uint32_t w[FN][BITS];
+  uint16_t s[FN], b[FN];
+  bool wl[FN];
 };
 
-// Workgroup tile BM x BN of y, 256 threads = 2x2 wavefronts, K in steps of
-// 64. LDS holds two stages (x tile + dequantized W tile each); the global
-// loads of step k+2 are in flight in registers while step k multiplies and
-// step k+1 is dequantized into the other LDS stage: one barrier per step.
+// Workgroup tile BM x BN of y, 256 threads = 2x2 wavefronts, wavefront tile
+// (BM/2) x (BN/2) of 32x32 MFMA tiles, K in steps of 64.
+//
+// K order inside a step: MFMA kk (0..3) takes, in lane group g = lane/32,
+// the 8 elements k = 32g + 8kk .. +7 (the same permutation for x and W, so the
+// product is unchanged). A lane's weight operand for a whole step is then one
+// contiguous 32-code chunk of its W row, loaded straight from global memory
+// and dequantized in registers by the wavefront that uses it: no LDS for W.
+// x goes through two LDS stages (shared by the two wavefronts of a row).
+// Registers hold the global loads of step k+2 and the dequantized weights of
+// step k+1 while step k multiplies; one barrier per step.
 template <class T, int BITS, int BM, int BN, bool CONV, bool CONV_VEC>
 __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
   constexpr bool kSplit = __is_same(T, BF16);
-  constexpr int WTM = BM / 2, WTN = BN / 2;  // wavefront tile
-  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int WTM = BM / 2, WTN = BN / 2;      // wavefront tile
+  constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 accumulator tiles
   using Regs = TileRegs<BM, BN, BITS>;
   constexpr int A_VECS = Regs::A_VECS;
-  constexpr int W_CHUNKS = BN * 2;            // 32-code chunks per K step
-  constexpr int W_PER_T = Regs::W_PER_T;
-  constexpr int A_STAGE = BM * kLdsRow, W_STAGE = BN * kLdsRow;
-  static_assert(A_VECS >= 1, "BM too small");
+  constexpr int A_STAGE = BM * kLdsRow;
+  constexpr int NB = kSplit ? 2 : 1;             // weight operands per MFMA
+  static_assert(A_VECS >= 1 && FN == Regs::FN, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2 * A_STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2 * W_STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t Wl[kSplit ? 2 * W_STAGE : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m_blk = blockIdx.y * BM, n_blk = blockIdx.x * BN;
   const int g = CONV ? blockIdx.z : 0;
+  // Tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous
+  // band of tiles (row-major over N fastest) so that its concurrent
+  // workgroups share x rows and weight rows in its L2.
+  int tile = blockIdx.x;
+  {
+    const int nt = gridDim.x;
+    if ((nt & 7) == 0) tile = (tile & 7) * (nt >> 3) + (tile >> 3);
+  }
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int m_blk = (tile / tiles_n) * BM, n_blk = (tile % tiles_n) * BN;
 
   const uint8_t* wq = a.wq;
   const uint16_t* sp = a.s;
@@ -211,11 +262,23 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
       pix_x[v] = (r % a.OW) * a.sw - a.pw;
     }
   }
+  // weight rows of this lane (one per 32-row block of the wavefront tile)
+  int w_n[FN];
+  bool w_ok[FN];
+#pragma unroll
+  for (int j = 0; j < FN; j++) {
+    const int n = n_blk + wn * WTN + 32 * j + (lane & 31);
+    w_ok[j] = n < a.N;
+    w_n[j] = w_ok[j] ? n : a.N - 1;
+  }
+  const int w_koff = 32 * (lane >> 5);  // this lane's 32 codes of a step
 
-  // Global loads of one K step into registers. Branch-free: out-of-range
-  // elements read a clamped valid address and are zeroed when stored, so the
-  // loads of a step issue back to back and stay in flight.
-  auto load_tile = [&](int kt, Regs& r) {
+  const int nkt = (a.K + kBK - 1) / kBK;
+  // Steps past the end (the phantom half of an odd step count) re-read the
+  // last tile and are marked dead, so they contribute zeros.
+  auto load_tile = [&](int kt_in, Regs& r) {
+    const bool step_ok = kt_in < nkt;
+    const int kt = step_ok ? kt_in : nkt - 1;
     const int k0 = kt * kBK;
 #pragma unroll
     for (int v = 0; v < A_VECS; v++) {
@@ -223,14 +286,15 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
       if constexpr (!CONV) {
         const int kc = k < a.K ? k : a.K - 8;
         const int m = a_ok[v] ? m_blk + a_row[v] : a.M - 1;
-        r.al[v] = a_ok[v] && k < a.K;
+        r.al[v] = step_ok && a_ok[v] && k < a.K;
         r.a[v] = *reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.K + kc);
       } else if constexpr (CONV_VEC) {
         const int kk = k < a.K_true ? k : 0;
         const int tap = kk / a.Cg, c = kk - tap * a.Cg;
         const int dy = tap / a.kw, dx = tap - dy * a.kw;
         const int iy = pix_y[v] + dy, ix = pix_x[v] + dx;
-        const bool in = a_ok[v] && k < a.K_true && iy >= 0 && iy < a.H && ix >= 0 && ix < a.W;
+        const bool in = step_ok && a_ok[v] && k < a.K_true && iy >= 0 && iy < a.H &&
+                        ix >= 0 && ix < a.W;
         r.al[v] = in;
         const int iyc = in ? iy : 0, ixc = in ? ix : 0;
         r.a[v] = *reinterpret_cast<const uint4*>(
@@ -249,122 +313,116 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
               e[i] = a.x[(((int64_t)pix_b[v] * a.H + iy) * a.W + ix) * a.C + g * a.Cg + c];
           }
         }
-        r.al[v] = true;
+        r.al[v] = step_ok;
         r.a[v] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
                             e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
       }
     }
+    const int kc = k0 + w_koff;
+    const bool kc_ok = kc < a.K;
+    const int kcc = kc_ok ? kc : a.K - 32;
+    const int gi = kcc >> a.gs_log2;
 #pragma unroll
-    for (int u = 0; u < W_PER_T; u++) {
-      const int ci = tid + 256 * u;
-      const int n = n_blk + ci / 2;
-      const int kc = k0 + (ci % 2) * 32;
-      r.wl[u] = ci < W_CHUNKS && n < a.N && kc < a.K;
-      const int nc = n < a.N ? n : a.N - 1;
-      const int kcc = kc < a.K ? kc : a.K - 32;
-      load_wchunk<BITS>(wq + (int64_t)nc * w_row_bytes + (int64_t)kcc * BITS / 8, r.w[u]);
-      const int gi = kcc >> a.gs_log2;
-      r.s[u] = sp[(int64_t)nc * n_groups_row + gi];
-      r.b[u] = bp[(int64_t)nc * n_groups_row + gi];
+    for (int j = 0; j < FN; j++) {
+      r.wl[j] = step_ok && w_ok[j] && kc_ok;
+      load_wchunk<BITS>(wq + (int64_t)w_n[j] * w_row_bytes + (int64_t)kcc * BITS / 8, r.w[j]);
+      r.s[j] = sp[(int64_t)w_n[j] * n_groups_row + gi];
+      r.b[j] = bp[(int64_t)w_n[j] * n_groups_row + gi];
     }
   };
 
-  // Registers of one K step -> LDS stage (x as is, W dequantized).
-  auto store_tile = [&](const Regs& r, int stage) {
+  // x registers of one step -> LDS stage (masking, not branches)
+  auto store_x = [&](const Regs& r, int stage) {
     uint16_t* as = As + stage * A_STAGE;
 #pragma unroll
-    for (int v = 0; v < A_VECS; v++)
+    for (int v = 0; v < A_VECS; v++) {
+      const uint32_t keep = r.al[v] ? 0xffffffffu : 0u;
       *reinterpret_cast<uint4*>(&as[a_row[v] * kLdsRow + a_kv[v] * 8]) =
-          r.al[v] ? r.a[v] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < W_PER_T; u++) {
-      const int ci = tid + 256 * u;
-      if (ci < W_CHUNKS) {
-        const int row = ci / 2, h = ci % 2;
-        const float sc = r.wl[u] ? to_f32(T{}, r.s[u]) : 0.0f;
-        const float bi = r.wl[u] ? to_f32(T{}, r.b[u]) : 0.0f;
-        uint32_t hi[16];
-        uint4* dst = reinterpret_cast<uint4*>(&Ws[stage * W_STAGE + row * kLdsRow + h * 32]);
-        if constexpr (kSplit) {
-          uint32_t lo[16];
-          dequant_chunk_bf16<BITS>(r.w[u], sc, bi, hi, lo);
-          uint4* dl = reinterpret_cast<uint4*>(&Wl[stage * W_STAGE + row * kLdsRow + h * 32]);
-#pragma unroll
-          for (int q = 0; q < 4; q++)
-            dl[q] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
-        } else {
-          dequant_chunk_f16<BITS>(r.w[u], sc, bi, m2_s, magic_v, hi);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          dst[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
-      }
+          make_uint4(r.a[v].x & keep, r.a[v].y & keep, r.a[v].z & keep, r.a[v].w & keep);
     }
   };
 
-  float4_t acc[FM][FN];
+  // weight registers of one step -> MFMA B operands: bfr[j][h][kk] holds the
+  // 8 values of k = 32*(lane/32) + 8*kk of row block j (h: bf16 hi / lo)
+  auto dequant_w = [&](const Regs& r, uint4 (&bfr)[FN][NB][4]) {
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+      const float sc = r.wl[j] ? to_f32(T{}, r.s[j]) : 0.0f;
+      const float bi = r.wl[j] ? to_f32(T{}, r.b[j]) : 0.0f;
+      uint32_t hi[16];
+      if constexpr (kSplit) {
+        uint32_t lo[16];
+        dequant_chunk_bf16<BITS>(r.w[j], sc, bi, hi, lo);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+          bfr[j][1][kk] = make_uint4(lo[4 * kk], lo[4 * kk + 1], lo[4 * kk + 2], lo[4 * kk + 3]);
+      } else {
+        dequant_chunk_f16<BITS>(r.w[j], sc, bi, m2_s, magic_v, hi);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++)
+        bfr[j][0][kk] = make_uint4(hi[4 * kk], hi[4 * kk + 1], hi[4 * kk + 2], hi[4 * kk + 3]);
+    }
+  };
+
+  float16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; i++)
 #pragma unroll
-    for (int j = 0; j < FN; j++) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  auto mma_stage = [&](int stage) {
-    const uint16_t* as = As + stage * A_STAGE;
-    const uint16_t* ws = Ws + stage * W_STAGE;
-    const uint16_t* wl = Wl + (kSplit ? stage * W_STAGE : 0);
+    for (int j = 0; j < FN; j++)
 #pragma unroll
-    for (int kk = 0; kk < kBK / 32; kk++) {
-      const int kof = kk * 32 + 8 * (lane >> 4);
-      uint4 af[FM], bf[FN], bl[FN];
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  auto mma_step = [&](int stage, const uint4 (&bfr)[FN][NB][4]) {
+    const uint16_t* as = As + stage * A_STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      const int kof = 32 * (lane >> 5) + 8 * kk;
+      uint4 af[FM];
 #pragma unroll
       for (int i = 0; i < FM; i++)
         af[i] = *reinterpret_cast<const uint4*>(
-            &as[(wm * WTM + 16 * i + (lane & 15)) * kLdsRow + kof]);
-#pragma unroll
-      for (int j = 0; j < FN; j++) {
-        bf[j] = *reinterpret_cast<const uint4*>(
-            &ws[(wn * WTN + 16 * j + (lane & 15)) * kLdsRow + kof]);
-        if constexpr (kSplit)
-          bl[j] = *reinterpret_cast<const uint4*>(
-              &wl[(wn * WTN + 16 * j + (lane & 15)) * kLdsRow + kof]);
-      }
+            &as[(wm * WTM + 32 * i + (lane & 31)) * kLdsRow + kof]);
 #pragma unroll
       for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-          acc[i][j] = mfma16(T{}, af[i], bf[j], acc[i][j]);
-          if constexpr (kSplit) acc[i][j] = mfma16(T{}, af[i], bl[j], acc[i][j]);
-        }
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+          for (int h = 0; h < NB; h++) acc[i][j] = mfma32(T{}, af[i], bfr[j][h][kk], acc[i][j]);
     }
   };
 
-  // ---- pipeline: regs r0/r1 alternate; LDS stages alternate
-  const int nkt = (a.K + kBK - 1) / kBK;
+  // ---- pipeline (unrolled by two so that register sets are static)
   Regs r0, r1;
+  uint4 b0[FN][NB][4], b1[FN][NB][4];
   load_tile(0, r0);
-  if (nkt > 1) load_tile(1, r1);
-  store_tile(r0, 0);
+  load_tile(1, r1);
+  store_x(r0, 0);
+  dequant_w(r0, b0);
   __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < nkt; kt += 2) {
-    // stage 0 holds step kt, r1 holds step kt+1
-    if (kt + 2 < nkt) load_tile(kt + 2, r0);
-    mma_stage(0);
-    store_tile(r1, 1);
+  constexpr int kMfma = 4 * FM * FN * NB;
+  constexpr int kDsRead = 4 * FM;
+  constexpr int kVmem = A_VECS + FN * 3;
+  for (int kt = 0; kt < nkt; kt += 2) {
+    // step kt: LDS stage 0 + b0; r1 holds step kt+1
+    load_tile(kt + 2, r0);
+    mma_step(0, b0);
+    store_x(r1, 1);
+    dequant_w(r1, b1);
+    if constexpr (!CONV || CONV_VEC) interleave_half_step<kMfma, kDsRead, kVmem, 6>();
     __syncthreads();
-    // stage 1 holds step kt+1, r0 holds step kt+2
-    if (kt + 3 < nkt) load_tile(kt + 3, r1);
-    mma_stage(1);
-    if (kt + 2 < nkt) store_tile(r0, 0);
-    __syncthreads();
-  }
-  if (kt < nkt) {  // odd number of steps: the last one sits in stage 0
-    mma_stage(0);
+    // step kt+1 (zeros past the end): LDS stage 1 + b1; r0 holds step kt+2
+    load_tile(kt + 3, r1);
+    mma_step(1, b1);
+    store_x(r0, 0);
+    dequant_w(r0, b0);
+    if constexpr (!CONV || CONV_VEC) interleave_half_step<kMfma, kDsRead, kVmem, 6>();
     __syncthreads();
   }
 
   // ---- epilogue: accumulators -> T -> LDS tile -> 16-byte coalesced stores.
-  // Lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile.
+  // Lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4 of each
+  // 32x32 tile.
   constexpr int CROW = BN + 8;
   static_assert(BM * CROW <= 2 * A_STAGE, "epilogue tile must fit the x stages");
   uint16_t* cs = As;
@@ -372,10 +430,10 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
   for (int i = 0; i < FM; i++)
 #pragma unroll
     for (int j = 0; j < FN; j++) {
-      const int col = wn * WTN + 16 * j + (lane & 15);
+      const int col = wn * WTN + 32 * j + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int row = wm * WTM + 16 * i + 4 * (lane >> 4) + r;
+      for (int r = 0; r < 16; r++) {
+        const int row = wm * WTM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         cs[row * CROW + col] = from_f32(T{}, acc[i][j][r]);
       }
     }
@@ -405,7 +463,8 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
 
 template <class T, int BITS, int BM, int BN, bool CONV, bool CONV_VEC>
 static hipError_t launch_tile(const GemmArgs& a, int groups, hipStream_t st) {
-  const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, groups);
+  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
+  const dim3 grid(tiles, 1, groups);
   hipLaunchKernelGGL((qmm_mfma_kernel<T, BITS, BM, BN, CONV, CONV_VEC>), grid,
                      dim3(256), 0, st, a);
   return hipGetLastError();
