@@ -177,6 +177,9 @@ qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
     return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                     biases, M, N, K, y, (hipStream_t)stream),
                     "qmm_t");
+  if (K >= qmm::kTileMaxK)
+    return fail(QMM_E_SHAPE, "qmm_t: K (%lld) must be below %lld for M >= %d",
+                (long long)K, (long long)qmm::kTileMaxK, qmm::crossover_m(bits, (int)dt));
   return launched(qmm::launch_qmm_mfma((int)dt, bits, group_size, x, wq, scales,
                                        biases, M, N, K, y, (hipStream_t)stream),
                   "qmm_t");

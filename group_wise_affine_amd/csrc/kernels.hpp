@@ -20,7 +20,10 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
                       int64_t M, int64_t N, int64_t K, void* y,
                       hipStream_t st);
 
-// MFMA tile GEMM: y[M,N] = x[M,K] . dequant(W)[N,K]^T.
+// MFMA tile GEMM: y[M,N] = x[M,K] . dequant(W)[N,K]^T. K must be below
+// kTileMaxK (byte offsets inside a tile stay below 2^30, in range of the
+// buffer resources the tile kernel reads through).
+constexpr int64_t kTileMaxK = (int64_t)1 << 22;
 hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,
                            int64_t M, int64_t N, int64_t K, void* y,

@@ -3,25 +3,27 @@
 //
 // Operation: "mlx 1.0.0 backend/cpu/quantized.cpp", _qmm_t (y[m,n] =
 // sum_k x[m,k] * (s*q + b)); tile structure in the spirit of the Metal
-// qmm_t of "Add the 3bit packed qmm_t" (affine_packed_qmm_t_impl: per K
-// step, load an x tile, dequantize a W tile into on-chip memory, multiply),
-// rebuilt for gfx950:
-//  * 256 threads = 4 wavefronts in a 2x2 grid; a workgroup owns a BM x BN
-//    tile of y and walks K in steps of 64 (one f16/bf16 x tile and one
-//    dequantized W tile in LDS, single-buffered, with the next step's global
-//    loads in flight in registers while the MFMAs of the current one run).
-//  * v_mfma_f32_16x16x32_{f16,bf16}: each wavefront holds
-//    (BM/32) x (BN/32) accumulator tiles of 16x16 in fp32.
-//  * W is dequantized once per workgroup and K step, w = fl32(s*q + b)
-//    rounded to the element type. For bf16 a single rounding to 8
-//    significand bits would cost ~1e-3 relative error, so W is split as
-//    hi = bf16(w), lo = bf16(w - hi) and both halves go through the MFMA
-//    (error ~2^-17 relative).
-//  * The conv variant ("[Feature] Quantized Convolution 2D" issue, img2col
-//    + quantized_matmul) computes the im2col patch addresses inside the x
-//    tile loader: GEMM row m = output pixel (b, oy, ox), column k =
-//    (dy, dx, c) of conv group g = blockIdx.z, zero for taps outside the
-//    image and for the zero-padded tail k >= K_true.
+// qmm_t of "Add the 3bit packed qmm_t" (per K step: an x tile, a W tile
+// dequantized on chip, a multiply), rebuilt for gfx950.
+//
+// Two kernels:
+//  * qmm_dma_kernel (plain GEMM, and convolutions whose per-group channel
+//    count is a multiple of 8): x and packed W tiles are copied global ->
+//    LDS by buffer loads that write LDS directly, three K steps ahead, into a
+//    four-slot ring; each wavefront dequantizes its W operands of the next
+//    step from LDS in small pieces placed between the MFMAs of the current
+//    step (v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulators).
+//  * qmm_mfma_kernel (the remaining convolutions): register-staged x
+//    gathers, one K step of prefetch.
+// W values are fl32(s*q + b) rounded to the element type. For bf16 a single
+// rounding to 8 significand bits would cost ~1e-3 relative error, so W is
+// split as hi = bf16(w), lo = bf16(w - hi) and both halves go through the
+// MFMA (error ~2^-17 relative).
+// The conv variants ("[Feature] Quantized Convolution 2D" issue, img2col +
+// quantized_matmul) compute the im2col addresses inside the x loader: GEMM
+// row m = output pixel (b, oy, ox), column k = (dy, dx, c) of conv group g =
+// blockIdx.z, zero for taps outside the image and for the padded tail
+// k >= K_true.
 #include <utility>
 
 #include "common.hpp"
@@ -33,6 +35,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   uint32_t magic;    // magic-number pattern of the element type (f16 path)
@@ -122,17 +125,19 @@ __device__ __forceinline__ void dequant_chunk_f16(const uint32_t* w, float s,
   }
 #pragma unroll
   for (int k = 0; k < 32; k += 2) {
-    uint32_t v[2];
+    float v[2];
 #pragma unroll
     for (int e = 0; e < 2; e++) {
       const int kk = k + e;
       const int p = pair_index<BITS>(kk), h = pair_half<BITS>(kk);
       const int o = pair_off<F16, BITS>(kk);
-      const uint16_t hb = (uint16_t)(pr[p] >> (16 * h));
-      const float q = (float)__builtin_bit_cast(_Float16, hb);
-      v[e] = from_f32(F16{}, fmaf(q, so[o], co[o]));
+      const float q = (float)__builtin_bit_cast(half2_t, pr[p])[h];
+      v[e] = fmaf(q, so[o], co[o]);
     }
-    out[k / 2] = v[0] | (v[1] << 16);
+    // building the pair as a vector lets the two roundings land in the low
+    // and high halves directly (v_fma_mixlo_f16 / v_fma_mixhi_f16)
+    const half2_t hv = {(_Float16)v[0], (_Float16)v[1]};
+    out[k / 2] = __builtin_bit_cast(uint32_t, hv);
   }
 }
 
@@ -459,35 +464,690 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
   }
 }
 
-// ----------------------------------------------------------------- launch
+// ------------------------------------------------------- LDS-DMA tile GEMM
+//
+// Main MFMA path (plain GEMM and convolutions whose per-group channel count
+// is a multiple of 8). Per K step of 64 codes a workgroup needs a BM x 64 x
+// tile and a BN x 64-code W tile; both are copied global -> LDS by the
+// load-to-LDS form of the vector loads (no registers, no LDS store
+// instructions), three steps ahead, into a ring of four LDS slots. The
+// slots are separate LDS arrays: the compiler tracks pending LDS-DMA writes
+// per array, so reading one slot does not wait for the copies into another.
+// Every copy instruction moves 64 x 16 bytes (or 64 x 4) into consecutive
+// LDS; which global piece each lane fetches implements the LDS layout:
+//  * x slot: BM rows of 128 bytes (eight 16-byte units); unit c of row r sits
+//    at position c ^ ((r >> 1) & 7), so the 32 rows read by one MFMA operand
+//    load spread over all banks.
+//  * W slot: BN rows of 8*BITS bytes (the row's 64 codes of the step); for
+//    16-byte units the unit index is XOR-ed with a row-derived value for the
+//    same reason.
+// Scales and biases come in stages of 8 steps (512 codes): cooperative
+// 2-byte loads (consecutive lanes on consecutive groups of a row), stored to
+// LDS as (scale | bias << 16) words, double-buffered.
+// While the MFMAs of step t run, each wavefront dequantizes its W operands of
+// step t+1 from LDS into registers (same K permutation as above: lane group g
+// takes codes 32g..32g+31 of the step). One wait + barrier per step.
 
-template <class T, int BITS, int BM, int BN, bool CONV, bool CONV_VEC>
-static hipError_t launch_tile(const GemmArgs& a, int groups, hipStream_t st) {
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Buffer resource over [base, base + bytes): raw (stride 0) 32-bit words;
+// loads at offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Offset that is out of range for every resource here (their sizes stay
+// below 2^31): the load returns zeros.
+constexpr uint32_t kOob = 0x80000000u;
+
+// U bytes per lane from rsrc at (voff + soff) into LDS at lds + 16*lane
+// (lds must be the same in every lane of the wavefront).
+template <int U>
+__device__ __forceinline__ void dma_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                        uint32_t soff) {
+  static_assert(U == 4 || U == 16, "DMA unit");
+  if constexpr (U == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt low bits 3:0, high bits 15:14;
+// expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. No memory fence: a fence
+// would also wait for every LDS-DMA copy in flight (they count as pending LDS
+// writes), which is exactly what the ring is meant to keep going. The empty
+// asm statements keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0), then s_barrier (see wait_vmcnt_barrier)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// empty asm that "uses" a value: keeps its computation in the current block
+// (the compiler would otherwise sink the next step's dequantization past the
+// copy-issue branches of that step, out of the MFMA shadow)
+__device__ __forceinline__ void keep(const uint4& v) {
+  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
+constexpr int kStageSteps = 8;      // K steps per scale stage (512 codes)
+constexpr int kKtabMax = 4096;      // conv k-unit table entries (K_pad <= 32768)
+
+template <int BM, int BN, int BITS>
+struct DmaGeo {
+  // wavefront grid: 1 x 4 for 128-wide tiles (each W chunk is dequantized by
+  // exactly one wavefront), 2 x 2 for 64 x 64 tiles
+  static constexpr int WAVES_N = BN >= 128 ? 4 : 2, WAVES_M = 4 / WAVES_N;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_ELEMS = BM * 64;          // x tile of one step
+  static constexpr int A_BLOCKS = BM / 8;          // 8 rows per DMA instruction
+  static constexpr int A_PER_WAVE = A_BLOCKS / 4;
+  static constexpr int WU = (BITS == 8 || (BITS == 4 && BN == 128)) ? 16 : 4;
+  static constexpr int W_ROW = 8 * BITS;           // bytes per W row and step
+  static constexpr int W_BYTES = BN * W_ROW;
+  static constexpr int UPR = W_ROW / WU;           // DMA units per W row
+  static constexpr int W_BLOCKS = W_BYTES / WU / 64;
+  static constexpr int W_HI = (W_BLOCKS + 3) / 4;  // W instructions of wave 0
+  static constexpr int W_LO = W_BLOCKS / 4;        // ... of wave 3
+  static constexpr int SWZ = WU == 16 ? ilog2(16 / UPR) : 0;
+  static_assert(A_BLOCKS % 4 == 0 && W_BYTES % (64 * WU) == 0, "DMA blocks");
+};
+
+// ------------------------------------------------------------ dequant pieces
+// A piece is a run of consecutive codes of a 32-code chunk whose magic pairs
+// (see common.hpp) all lie inside the run: 8 codes for 4/6/8 bits, 16 for
+// 2/3/5 bits. Pieces let the tile kernel spread the dequantization of the
+// next K step between the MFMAs of the current one.
+template <int BITS>
+constexpr int piece_codes() {
+  return (BITS == 2 || BITS == 3 || BITS == 5) ? 16 : 8;
+}
+
+template <int BITS, int C0, int PC>
+constexpr bool piece_has_pair(int P) {
+  for (int k = C0; k < C0 + PC; k++)
+    if (pair_index<BITS>(k) == P) return true;
+  return false;
+}
+
+// f16 constants of a chunk for every field offset o: s*2^-o and b - 1024*s*2^-o
+struct F16Consts {
+  float so[8], co[8];
+};
+__device__ __forceinline__ void f16_consts(float s, float b, F16Consts& c) {
+#pragma unroll
+  for (int o = 0; o < 8; o++) {
+    c.so[o] = s * __builtin_bit_cast(float, (uint32_t)(127 - o) << 23);
+    c.co[o] = fmaf(-1024.0f, c.so[o], b);
+  }
+}
+
+// codes [C0, C0+PC) of a chunk -> f16 pairs out[C0/2 .. (C0+PC)/2)
+template <int BITS, int C0, int PC>
+__device__ __forceinline__ void dequant_piece_f16(const uint32_t* w, const F16Consts& c,
+                                                  uint32_t m2, uint32_t magic,
+                                                  uint32_t* out) {
+  uint32_t pr[16];
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    ([&] {
+       if constexpr (piece_has_pair<BITS, C0, PC>(P))
+         pr[P] = magic_pair<F16, BITS, P>(w, m2, magic);
+       else
+         pr[P] = 0;
+     }(),
+     ...);
+  }(std::make_integer_sequence<int, 16>{});
+#pragma unroll
+  for (int k = C0; k < C0 + PC; k += 2) {
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const int kk = k + e;
+      const int p = pair_index<BITS>(kk), hf = pair_half<BITS>(kk);
+      const int o = pair_off<F16, BITS>(kk);
+      const float q = (float)__builtin_bit_cast(half2_t, pr[p])[hf];
+      v[e] = fmaf(q, c.so[o], c.co[o]);
+    }
+    const half2_t hv = {(_Float16)v[0], (_Float16)v[1]};
+    out[k / 2] = __builtin_bit_cast(uint32_t, hv);
+  }
+}
+
+// codes [C0, C0+8) of a chunk -> bf16 hi/lo pairs (see dequant_chunk_bf16)
+template <int BITS, int C0>
+__device__ __forceinline__ void dequant_piece_bf16(const uint32_t* w, float s, float b,
+                                                   uint32_t* hi, uint32_t* lo) {
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    float f[8] = {fmaf(s, (float)code_at<BITS, C0 + J>(w), b)...};
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const uint16_t h0 = from_f32(BF16{}, f[k]), h1 = from_f32(BF16{}, f[k + 1]);
+      hi[(C0 + k) / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      const uint16_t l0 = from_f32(BF16{}, f[k] - to_f32(BF16{}, h0));
+      const uint16_t l1 = from_f32(BF16{}, f[k + 1] - to_f32(BF16{}, h1));
+      lo[(C0 + k) / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+  }(std::make_integer_sequence<int, 8>{});
+}
+
+// slot (MFMA index) after which filler f of nf is emitted: the first kLead
+// MFMAs cover the latency of the LDS reads, the fillers are spread evenly
+// over the rest
+constexpr int filler_slot(int f, int nf, int nm, int lead) {
+  return lead + (f * (nm - lead)) / nf;
+}
+
+template <class T, int BITS, int BM, int BN, bool CONV>
+__global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
+  using G = DmaGeo<BM, BN, BITS>;
+  constexpr bool kSplit = __is_same(T, BF16);
+  constexpr int NB = kSplit ? 2 : 1;
+  constexpr int FM = G::FM, FN = G::FN, WTM = G::WTM, WTN = G::WTN;
+  constexpr int WU = G::WU, UPR = G::UPR;
+  constexpr int NDMA_LO = G::A_PER_WAVE + G::W_LO, NDMA_HI = G::A_PER_WAVE + G::W_HI;
+  constexpr int PC = kSplit ? 8 : piece_codes<BITS>();
+  constexpr int NP = 32 / PC;                    // pieces per chunk
+  constexpr int kM = 4 * FM * FN * NB;           // MFMAs per step
+  constexpr int kNF = FN + FN * NP + (FM >= 2 ? 0 : 4 * FM);  // fillers per step
+  constexpr int kLead = kM >= 16 ? 4 : 1;
+
+  // one LDS array per ring slot (x tile, then W tile): the compiler tracks
+  // pending LDS-DMA writes per array for a handful of arrays only
+  constexpr int kSlotBytes = G::A_ELEMS * 2 + G::W_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t sl0[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sl1[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sl3[kSlotBytes];
+  __shared__ uint32_t sct[2 * BN * 17];
+  __shared__ uint32_t ktab[CONV ? kKtabMax : 1];
+  // target of the filler W copies of wavefronts with one block fewer
+  __shared__ __attribute__((aligned(16))) uint8_t wjunk[G::W_BLOCKS % 4 ? 64 * WU : 16];
+
+  auto slot = [&]<int S>() -> uint8_t* {
+    if constexpr (S == 0) return sl0;
+    else if constexpr (S == 1) return sl1;
+    else if constexpr (S == 2) return sl2;
+    else return sl3;
+  };
+  auto xslot = [&]<int S>() -> uint16_t* {
+    return reinterpret_cast<uint16_t*>(slot.template operator()<S>());
+  };
+  auto wslot = [&]<int S>() -> uint8_t* {
+    return slot.template operator()<S>() + G::A_ELEMS * 2;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, h = lane >> 5, rr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+  const int g = CONV ? blockIdx.z : 0;
+  int tile = blockIdx.x;
+  {
+    // workgroup i runs on XCD i % 8: give each XCD a contiguous band of tiles
+    const int nt = gridDim.x;
+    if ((nt & 7) == 0) tile = (tile & 7) * (nt >> 3) + (tile >> 3);
+  }
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int m_blk = (tile / tiles_n) * BM, n_blk = (tile % tiles_n) * BN;
+
+  const int K = a.K;                       // W row length in codes
+  const int nk = (K + 63) >> 6;            // K steps
+  const int row_bytes = K / 8 * BITS;
+  const int n_groups = K >> a.gs_log2;
+  const uint8_t* wq = a.wq;
+  const uint16_t* sp = a.s;
+  const uint16_t* bp = a.b;
+  if constexpr (CONV) {
+    wq += (int64_t)g * a.Og * row_bytes;
+    sp += (int64_t)g * a.Og * n_groups;
+    bp += (int64_t)g * a.Og * n_groups;
+  }
+
+  uint32_t magic_v;
+  const uint32_t m2_s = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(a.magic));
+
+  // ---- conv: k-unit table (dy, dx, channel) of every 8-channel unit
+  if constexpr (CONV) {
+    for (int ku = tid; ku < nk * 8; ku += 256) {
+      const int k = ku * 8;
+      uint32_t e = 0xffffffffu;
+      if (k < a.K_true) {
+        const int tap = k / a.Cg, c0 = k - tap * a.Cg;
+        const int dy = tap / a.kw, dx = tap - dy * a.kw;
+        e = ((uint32_t)dy << 24) | ((uint32_t)dx << 16) | (uint32_t)c0;
+      }
+      ktab[ku] = e;
+    }
+    __syncthreads();
+  }
+
+  // ---- x pieces: instruction i of this wavefront fills rows 8*blk..+7 of a
+  // slot, lane -> (row, position); the unit fetched is position ^ swizzle.
+  // Plain GEMM: byte offset from the tile's first row (rows past M re-read
+  // row M-1; their results are not stored). Conv: offsets from channel g*Cg
+  // of the image, computed per step from the k table.
+  const char* xbase = reinterpret_cast<const char*>(a.x) +
+                      (CONV ? (int64_t)g * a.Cg * 2 : (int64_t)m_blk * a.K * 2);
+  const int64_t x_bytes =
+      CONV ? (int64_t)(a.M / (a.OH * a.OW)) * a.H * a.W * a.C * 2 - (int64_t)g * a.Cg * 2
+           : (int64_t)(a.M - m_blk) * a.K * 2;
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(xbase, (uint32_t)(x_bytes < 0x7fffffff ? x_bytes : 0x7fffffff));
+  uint32_t xoff[G::A_PER_WAVE];
+  int xcol[G::A_PER_WAVE];
+  int pix_b[CONV ? G::A_PER_WAVE : 1], pix_y[CONV ? G::A_PER_WAVE : 1],
+      pix_x[CONV ? G::A_PER_WAVE : 1];
+#pragma unroll
+  for (int i = 0; i < G::A_PER_WAVE; i++) {
+    const int blk = 4 * i + wave;
+    const int r = 8 * blk + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    xcol[i] = 8 * c;
+    const int m = m_blk + r;
+    if constexpr (!CONV) {
+      const int rc = m < a.M ? r : a.M - 1 - m_blk;
+      xoff[i] = (uint32_t)(((int64_t)rc * a.K + 8 * c) * 2);
+    } else {
+      const int mm = m < a.M ? m : 0;
+      const int b = mm / (a.OH * a.OW), rem = mm - b * a.OH * a.OW;
+      const int oy = rem / a.OW, ox = rem - oy * a.OW;
+      pix_b[i] = b * a.H;
+      // rows past M get an impossible y so that every tap reads zeros
+      pix_y[i] = m < a.M ? oy * a.sh - a.ph : -(1 << 28);
+      pix_x[i] = ox * a.sw - a.pw;
+      xoff[i] = 0;
+    }
+  }
+
+  // ---- W pieces: lane -> (row, unit) of a W slot; byte offset from the
+  // tile's first row (rows past N re-read row N-1)
+  const char* wbase = reinterpret_cast<const char*>(wq) + (int64_t)n_blk * row_bytes;
+  const int64_t w_bytes = (int64_t)(a.N - n_blk) * row_bytes;
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(wbase, (uint32_t)(w_bytes < 0x7fffffff ? w_bytes : 0x7fffffff));
+  uint32_t woff[G::W_HI];
+  int wuo[G::W_HI];
+#pragma unroll
+  for (int i = 0; i < G::W_HI; i++) {
+    const int blk = 4 * i + wave;
+    const int ui = 64 * (blk < G::W_BLOCKS ? blk : 0) + lane;
+    const int r = ui / UPR, p = ui % UPR;
+    const int u = WU == 16 ? (p ^ ((r >> G::SWZ) & (UPR - 1))) : p;
+    const int rc = n_blk + r < a.N ? r : a.N - 1 - n_blk;
+    wuo[i] = WU * u;
+    woff[i] = (uint32_t)rc * (uint32_t)row_bytes + (uint32_t)(WU * u);
+  }
+
+  // ---- issue the copies of step tt into slot S. Pieces past the end of a
+  // row (and whole steps past the end of K) get an out-of-range offset and
+  // land as zeros; every wavefront issues the same number of copies every
+  // step (those without a W block of their own copy zeros into wjunk), so one
+  // vmcnt value fits all. No branches: a stage of steps stays one block.
+  auto issue = [&]<int S>(int tt) {
+    uint16_t* xd = xslot.template operator()<S>();
+    uint8_t* wd = wslot.template operator()<S>();
+    if constexpr (CONV) {
+#pragma unroll
+      for (int i = 0; i < G::A_PER_WAVE; i++) {
+        const int blk = 4 * i + wave;
+        const int ku = 8 * tt + (xcol[i] >> 3);
+        const uint32_t e = ku < nk * 8 ? ktab[ku] : 0xffffffffu;
+        const int dy = (int)(e >> 24), dx = (int)((e >> 16) & 0xff);
+        const int iy = pix_y[i] + dy, ix = pix_x[i] + dx;
+        const bool in = e != 0xffffffffu && (unsigned)iy < (unsigned)a.H &&
+                        (unsigned)ix < (unsigned)a.W;
+        const uint32_t off =
+            (uint32_t)((((pix_b[i] + iy) * a.W + ix) * a.C + (int)(e & 0xffff)) * 2);
+        dma_lds<16>(xr, xd + blk * 512, in ? off : kOob, 0);
+      }
+    } else {
+      const uint32_t soff = 128u * tt;
+#pragma unroll
+      for (int i = 0; i < G::A_PER_WAVE; i++) {
+        const bool ok = 64 * tt + xcol[i] < K;
+        dma_lds<16>(xr, xd + (4 * i + wave) * 512, ok ? xoff[i] : kOob, soff);
+      }
+    }
+    const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;
+#pragma unroll
+    for (int i = 0; i < G::W_HI; i++) {
+      const int blk = 4 * i + wave;
+      const bool real = G::W_BLOCKS % 4 == 0 || blk < G::W_BLOCKS;
+      const bool ok = real && (int)wsoff + wuo[i] < row_bytes;
+      dma_lds<WU>(wr, real ? (void*)(wd + blk * 64 * WU) : (void*)wjunk, ok ? woff[i] : kOob,
+                  wsoff);
+    }
+  };
+  // end of a step: wait until only the youngest step of copies is in flight,
+  // then barrier
+  auto step_sync = [&]() {
+    wait_vmcnt<G::A_PER_WAVE + G::W_HI>();
+    lds_barrier();
+  };
+
+  // ---- scales and biases, in stages of 8 steps
+  const int sg_log2 = 9 - a.gs_log2;          // groups per stage: 4, 8 or 16
+  const int SG = 1 << sg_log2, SGP = SG + 1;
+  // 2-byte loads per thread: (2 * BN * SG) / 256 of them are distinct; the
+  // loop always runs the maximum (16 for 128 rows) over indices taken modulo
+  // the element count, so that it has no branches (repeats rewrite the same
+  // value)
+  const int n_el_mask = 2 * BN * SG - 1;
+  constexpr int kSLoads = 2 * BN * 16 / 256;
+  uint32_t sreg[kSLoads];
+  auto scale_load = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < kSLoads; i++) {
+      const int e = (tid + 256 * i) & n_el_mask;
+      const int grp = e & (SG - 1), row = (e >> sg_log2) & (BN - 1);
+      const int which = e >> (sg_log2 + ilog2(BN));
+      const int gi = j * SG + grp < n_groups ? j * SG + grp : n_groups - 1;
+      const int n = n_blk + row < a.N ? n_blk + row : a.N - 1;
+      sreg[i] = (which ? bp : sp)[(int64_t)n * n_groups + gi];
+    }
+  };
+  auto scale_store = [&](int j) {
+    uint16_t* base = reinterpret_cast<uint16_t*>(sct + (j & 1) * BN * SGP);
+#pragma unroll
+    for (int i = 0; i < kSLoads; i++) {
+      const int e = (tid + 256 * i) & n_el_mask;
+      const int grp = e & (SG - 1), row = (e >> sg_log2) & (BN - 1);
+      const int which = e >> (sg_log2 + ilog2(BN));
+      base[2 * (row * SGP + grp) + which] = (uint16_t)sreg[i];
+    }
+  };
+
+  // ---- per-step register state. x fragments: with several row blocks per
+  // wavefront (kJit) slice kk+1 is read while the MFMAs of slice kk run and
+  // slice 0 of the next step during slice 3 (one buffer); with one row block
+  // the next step's four slices are read during the current step (two
+  // buffers).
+  constexpr bool kJit = FM >= 2;
+  uint4 af[kJit ? 1 : 2][4][FM];
+  uint4 bq[2][FN][NB][4];        // W operands (row block, hi/lo, K slice)
+  uint32_t wc[FN][BITS];         // raw W chunks of the next step
+  uint32_t sbw[FN];              // (scale | bias << 16) of the next step
+  F16Consts cst[FN];
+  float sf[FN], bf[FN];
+
+  // W chunks and scale words of step tt from slot S
+  auto read_w = [&]<int S>(int tt) {
+    const uint8_t* wsl = wslot.template operator()<S>();
+    const uint32_t* scs = sct + ((tt >> 3) & 1) * BN * SGP;
+    const int gl = (((tt & 7) << 6) + 32 * h) >> a.gs_log2;
+#pragma unroll
+    for (int j = 0; j < FN; j++) sbw[j] = scs[(wn * WTN + 32 * j + rr) * SGP + gl];
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+      const int r = wn * WTN + 32 * j + rr;
+      // (vector-typed 16-byte loads: a load split into words and merged again
+      // loses the information that it reads this slot only, and the compiler
+      // then waits for every LDS copy in flight)
+      if constexpr (WU == 16 && BITS == 4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+            wsl + r * 32 + 16 * (h ^ ((r >> G::SWZ) & 1)));
+#pragma unroll
+        for (int q = 0; q < 4; q++) wc[j][q] = v[q];
+      } else if constexpr (WU == 16 && BITS == 8) {
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+          const int u = (2 * h + e) ^ ((r >> G::SWZ) & 3);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wsl + r * 64 + 16 * u);
+#pragma unroll
+          for (int q = 0; q < 4; q++) wc[j][4 * e + q] = v[q];
+        }
+      } else {
+        const uint32_t* pw =
+            reinterpret_cast<const uint32_t*>(wsl + r * (8 * BITS) + 4 * BITS * h);
+#pragma unroll
+        for (int q = 0; q < BITS; q++) wc[j][q] = pw[q];
+      }
+    }
+  };
+  // x fragment (K slice KK, row block I) of slot S
+  auto read_x = [&]<int S, int KK, int I>(uint4 (&afr)[4][FM]) {
+    const uint16_t* xsl = xslot.template operator()<S>();
+    const int ra = wm * WTM + 32 * I + rr;
+    const int c = (4 * h + KK) ^ ((ra >> 1) & 7);
+    afr[KK][I] = *reinterpret_cast<const uint4*>(xsl + ra * 64 + 8 * c);
+  };
+  auto prep = [&]<int J>() {
+    sf[J] = to_f32(T{}, (uint16_t)sbw[J]);
+    bf[J] = to_f32(T{}, (uint16_t)(sbw[J] >> 16));
+    if constexpr (!kSplit) f16_consts(sf[J], bf[J], cst[J]);
+  };
+  auto piece = [&]<int J, int P>(uint4 (&bqn)[FN][NB][4]) {
+    uint32_t hi[16], lo[16];
+    if constexpr (kSplit) {
+      dequant_piece_bf16<BITS, P * 8>(wc[J], sf[J], bf[J], hi, lo);
+      bqn[J][1][P] = make_uint4(lo[4 * P], lo[4 * P + 1], lo[4 * P + 2], lo[4 * P + 3]);
+      bqn[J][0][P] = make_uint4(hi[4 * P], hi[4 * P + 1], hi[4 * P + 2], hi[4 * P + 3]);
+    } else {
+      dequant_piece_f16<BITS, P * PC, PC>(wc[J], cst[J], m2_s, magic_v, hi);
+#pragma unroll
+      for (int kk = P * PC / 8; kk < (P + 1) * PC / 8; kk++)
+        bqn[J][0][kk] = make_uint4(hi[4 * kk], hi[4 * kk + 1], hi[4 * kk + 2], hi[4 * kk + 3]);
+    }
+  };
+  // filler F of a step: scale prep, a dequant piece, or (without kJit) an x
+  // fragment read of the next step (slot SN)
+  auto filler = [&]<int F, int SN>(uint4 (&afn)[4][FM], uint4 (&bqn)[FN][NB][4]) {
+    if constexpr (F < FN) {
+      prep.template operator()<F>();
+    } else if constexpr (F < FN + FN * NP) {
+      constexpr int idx = F - FN;
+      piece.template operator()<idx % FN, idx / FN>(bqn);
+    } else {
+      constexpr int idx = F - FN - FN * NP;
+      read_x.template operator()<SN, idx / FM, idx % FM>(afn);
+    }
+  };
+
+  float16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  // fillers of MFMA slot MM (next step's state goes to bq[1-C] and, without
+  // kJit, af[1-C], from slot SN)
+  auto slot_fill = [&]<int MM, int C, int SN>() {
+    [&]<int... F>(std::integer_sequence<int, F...>) {
+      ([&] {
+         if constexpr (filler_slot(F, kNF, kM, kLead) == MM) {
+           filler.template operator()<F, SN>(af[kJit ? 0 : 1 - C], bq[1 - C]);
+           __builtin_amdgcn_sched_barrier(0);
+         }
+       }(),
+       ...);
+    }(std::make_integer_sequence<int, kNF>{});
+  };
+  constexpr int kSlice = FM * FN * NB;       // MFMAs per K slice
+  auto read_slice = [&]<int S, int KK>() {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (read_x.template operator()<S, KK, I>(af[0]), ...);
+    }(std::make_integer_sequence<int, FM>{});
+  };
+  auto mfma_at = [&]<int MM, int C, int SC, int SN>() {
+    constexpr int kk = MM / kSlice;
+    constexpr int i = (MM / (FN * NB)) % FM;
+    constexpr int j = (MM / NB) % FN;
+    constexpr int e = MM % NB;
+    acc[i][j] = mfma32(T{}, af[kJit ? 0 : C][kk][i], bq[C][j][e][kk], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kJit && MM % kSlice == 0) {
+      // x fragments of the next slice (slice 0 of the next step after slice 3)
+      if constexpr (kk < 3) read_slice.template operator()<SC, kk + 1>();
+      else read_slice.template operator()<SN, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // one step body: MFMAs from af/bq[C] (x slot SC); the next step's state
+  // (slot SN) is built between them, in a fixed order
+  auto body = [&]<int C, int SC, int SN>(int tt) {
+    read_w.template operator()<SN>(tt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    [&]<int... M>(std::integer_sequence<int, M...>) {
+      ((mfma_at.template operator()<M, C, SC, SN>(),
+        slot_fill.template operator()<M, C, SN>()),
+       ...);
+    }(std::make_integer_sequence<int, kM>{});
+  };
+
+  // ---- prologue: scales of stage 0, copies of steps 0..2, state of step 0
+  scale_load(0);
+  issue.template operator()<0>(0);
+  issue.template operator()<1>(1);
+  issue.template operator()<2>(2);
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+  scale_store(0);
+  wait_vmcnt_barrier<0>();
+  read_w.template operator()<0>(0);
+  [&]<int... F>(std::integer_sequence<int, F...>) {
+    (filler.template operator()<F, 0>(af[0], bq[0]), ...);
+  }(std::make_integer_sequence<int, kNF>{});
+  if constexpr (kJit) read_slice.template operator()<0, 0>();
+
+  // every LDS read of the prologue has landed before the loop (so that the
+  // compiler does not carry them into the loop body)
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4));
+
+  // ---- main loop: stages of 8 steps. Step tt multiplies from bq[tt % 2]
+  // (built from slot tt % 4 during step tt-1) and builds bq[(tt+1) % 2] from
+  // slot (tt+1) % 4; the copies of step tt+3 go to slot (tt+3) % 4, whose
+  // last reads were made during step tt-2. Full stages run unguarded; only a
+  // last partial stage checks each step against nk.
+  auto stage = [&]<bool kFull>(int js) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      (([&] {
+         const int tt = kStageSteps * js + U;
+         if (kFull || tt < nk) {
+           if constexpr (U == 1) scale_load(js + 1);
+           issue.template operator()<(U + 3) % 4>(tt + 3);
+           if constexpr (U == 2) scale_store(js + 1);
+           body.template operator()<U % 2, U % 4, (U + 1) % 4>(tt);
+#pragma unroll
+           for (int j = 0; j < FN; j++)
+#pragma unroll
+             for (int e = 0; e < NB; e++)
+#pragma unroll
+               for (int kk = 0; kk < 4; kk++) keep(bq[(U + 1) % 2][j][e][kk]);
+           step_sync();
+         }
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, kStageSteps>{});
+  };
+  const int n_full = nk / kStageSteps;
+  for (int js = 0; js < n_full; js++) stage.template operator()<true>(js);
+  if (nk % kStageSteps) stage.template operator()<false>(n_full);
+
+  // ---- epilogue: each wavefront stages its WTM x WTN tile in "its" x slot
+  // (all copies have landed and all slot reads are done), then writes rows
+  // of 16-byte vectors.
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint16_t* cs = reinterpret_cast<uint16_t*>(wave == 0 ? sl0 : wave == 1 ? sl1 : wave == 2 ? sl2 : sl3);
+  constexpr int CROW = WTN + 8;
+  static_assert(WTM * CROW <= G::A_ELEMS, "epilogue tile must fit an x slot");
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+      const int col = 32 * j + rr;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        cs[row * CROW + col] = from_f32(T{}, acc[i][j][r]);
+      }
+    }
+  __syncthreads();
+  uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : 0);
+  constexpr int VPR = WTN / 8;
+  const bool vec_ok = (a.N % 8 == 0) && (a.ldy % 8 == 0);
+#pragma unroll
+  for (int it = 0; it < WTM * VPR / 64; it++) {
+    const int idx = lane + 64 * it;
+    const int row = idx / VPR, cv = idx % VPR;
+    const int m = m_blk + wm * WTM + row, n = n_blk + wn * WTN + cv * 8;
+    if (m < a.M) {
+      const uint16_t* src = &cs[row * CROW + cv * 8];
+      if (vec_ok && n + 8 <= a.N) {
+        *reinterpret_cast<uint4*>(yb + (int64_t)m * a.ldy + n) =
+            *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int e = 0; e < 8; e++)
+          if (n + e < a.N) yb[(int64_t)m * a.ldy + n + e] = src[e];
+      }
+    }
+  }
+}
+
+// gather kernel: convolutions whose per-group channel count is not a
+// multiple of 8 (x pieces are not 16-byte units) or whose k table would not
+// fit in LDS
+template <class T, int BITS, int BM, int BN>
+static hipError_t launch_gather(const GemmArgs& a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   const dim3 grid(tiles, 1, groups);
-  hipLaunchKernelGGL((qmm_mfma_kernel<T, BITS, BM, BN, CONV, CONV_VEC>), grid,
-                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL((qmm_mfma_kernel<T, BITS, BM, BN, true, false>), grid, dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 
-template <class T, int BITS, bool CONV, bool CONV_VEC>
-static hipError_t launch_shape(const GemmArgs& a, int groups, hipStream_t st) {
-  const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
-  if (tiles128 >= 256)
-    return launch_tile<T, BITS, 128, 128, CONV, CONV_VEC>(a, groups, st);
-  return launch_tile<T, BITS, 64, 64, CONV, CONV_VEC>(a, groups, st);
+template <class T, int BITS, int BM, int BN, bool CONV>
+static hipError_t launch_dma(const GemmArgs& a, int groups, hipStream_t st) {
+  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
+  const dim3 grid(tiles, 1, groups);
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
-template <class T, bool CONV, bool CONV_VEC>
+template <class T, int BITS, bool CONV, bool DMA>
+static hipError_t launch_shape(const GemmArgs& a, int groups, hipStream_t st) {
+  const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
+  if constexpr (DMA) {
+    if (tiles128 >= 256) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
+    return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
+  } else {
+    if (tiles128 >= 256) return launch_gather<T, BITS, 128, 128>(a, groups, st);
+    return launch_gather<T, BITS, 64, 64>(a, groups, st);
+  }
+}
+
+template <class T, bool CONV, bool DMA>
 static hipError_t launch_bits(int bits, const GemmArgs& a, int groups,
                               hipStream_t st) {
   switch (bits) {
-    case 2: return launch_shape<T, 2, CONV, CONV_VEC>(a, groups, st);
-    case 3: return launch_shape<T, 3, CONV, CONV_VEC>(a, groups, st);
-    case 4: return launch_shape<T, 4, CONV, CONV_VEC>(a, groups, st);
-    case 5: return launch_shape<T, 5, CONV, CONV_VEC>(a, groups, st);
-    case 6: return launch_shape<T, 6, CONV, CONV_VEC>(a, groups, st);
-    default: return launch_shape<T, 8, CONV, CONV_VEC>(a, groups, st);
+    case 2: return launch_shape<T, 2, CONV, DMA>(a, groups, st);
+    case 3: return launch_shape<T, 3, CONV, DMA>(a, groups, st);
+    case 4: return launch_shape<T, 4, CONV, DMA>(a, groups, st);
+    case 5: return launch_shape<T, 5, CONV, DMA>(a, groups, st);
+    case 6: return launch_shape<T, 6, CONV, DMA>(a, groups, st);
+    default: return launch_shape<T, 8, CONV, DMA>(a, groups, st);
   }
 }
 
@@ -505,8 +1165,8 @@ hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
   a.gs_log2 = ilog2(gs);
   a.ldy = N;
   a.magic = F16::kMagic;
-  if (dt == 0) return launch_bits<F16, false, false>(bits, a, 1, st);
-  return launch_bits<BF16, false, false>(bits, a, 1, st);
+  if (dt == 0) return launch_bits<F16, false, true>(bits, a, 1, st);
+  return launch_bits<BF16, false, true>(bits, a, 1, st);
 }
 
 hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
@@ -530,12 +1190,17 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
   a.kh = cg.kh; a.kw = cg.kw; a.sh = cg.sh; a.sw = cg.sw;
   a.ph = cg.ph; a.pw = cg.pw;
   a.Cg = (int)cg.Cg; a.Og = (int)cg.Og; a.K_true = (int)cg.K_true;
-  const bool vec = (cg.Cg % 8) == 0;
+  // the DMA path needs 16-byte x pieces (8 channels of one tap) and a k
+  // table (one entry per 8 channels, dy and dx below 256) that fits in LDS
+  const int64_t nk = (cg.K_pad + 63) / 64;
+  // (and x below 2^30 bytes, in range of one buffer resource)
+  const bool dma = (cg.Cg % 8) == 0 && nk * 8 <= kKtabMax && cg.kh < 256 && cg.kw < 256 &&
+                   cg.B * cg.H * cg.W * cg.C < ((int64_t)1 << 29);
   if (dt == 0) {
-    return vec ? launch_bits<F16, true, true>(bits, a, cg.groups, st)
+    return dma ? launch_bits<F16, true, true>(bits, a, cg.groups, st)
                : launch_bits<F16, true, false>(bits, a, cg.groups, st);
   }
-  return vec ? launch_bits<BF16, true, true>(bits, a, cg.groups, st)
+  return dma ? launch_bits<BF16, true, true>(bits, a, cg.groups, st)
              : launch_bits<BF16, true, false>(bits, a, cg.groups, st);
 }
 

@@ -108,6 +108,9 @@ def test_bad_sizes(L):
     # the streaming kernel's K limit is reported, qmm_t is not limited by it
     assert _st(L, "qmv", P, P, P, P, 0, 1, 8, 1 << 20, 64, 4, P, None) == Q.QMM_E_SHAPE
     assert b"K" in L.qmm_last_error()
+    # the tile kernel keeps lane offsets inside a tile in 32 bits: K < 2^24
+    assert _st(L, "qmm_t", P, P, P, P, 0, 64, 8, 1 << 24, 64, 4, P, None) == Q.QMM_E_SHAPE
+    assert b"K" in L.qmm_last_error()
 
 
 def test_bad_dtype(L):
