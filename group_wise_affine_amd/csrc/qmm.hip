@@ -31,6 +31,10 @@
 
 namespace qmm {
 
+// the kernels are written with many small lambdas; all of them must be
+// inlined (an outlined step would move the accumulators to scratch memory)
+#define QMM_INLINE __attribute__((always_inline))
+
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -490,6 +494,7 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(GemmArgs a) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+
 // Buffer resource over [base, base + bytes): raw (stride 0) 32-bit words;
 // loads at offsets past `bytes` return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -607,8 +612,8 @@ __device__ __forceinline__ void dequant_piece_f16(const uint32_t* w, const F16Co
                                                   uint32_t m2, uint32_t magic,
                                                   uint32_t* out) {
   uint32_t pr[16];
-  [&]<int... P>(std::integer_sequence<int, P...>) {
-    ([&] {
+  [&]<int... P>(std::integer_sequence<int, P...>) QMM_INLINE {
+    ([&]() QMM_INLINE {
        if constexpr (piece_has_pair<BITS, C0, PC>(P))
          pr[P] = magic_pair<F16, BITS, P>(w, m2, magic);
        else
@@ -632,11 +637,65 @@ __device__ __forceinline__ void dequant_piece_f16(const uint32_t* w, const F16Co
   }
 }
 
+// field offset o of magic pair P (both codes of a pair share it)
+template <int BITS>
+constexpr int pair_o(int P) {
+  for (int k = 0; k < 32; k++)
+    if (pair_index<BITS>(k) == P) return pair_off<F16, BITS>(k);
+  return 0;
+}
+// byte selector of v_perm_b32(hi_src, lo_src, sel) that takes 16-bit half hl
+// of lo_src into the low half and half hh of hi_src into the high half
+constexpr uint32_t half_sel(int hl, int hh) {
+  return (uint32_t)(2 * hl) | ((uint32_t)(2 * hl + 1) << 8) | ((uint32_t)(4 + 2 * hh) << 16) |
+         ((uint32_t)(4 + 2 * hh + 1) << 24);
+}
+
+// codes [C0, C0+PC) of a chunk -> f16 pairs out[C0/2 .. (C0+PC)/2) with
+// packed f16 arithmetic (cheap next to the MFMAs): magic pair (1024 + q*2^o)
+// -> q exactly (times 2^-o, minus 1024*2^-o: both exact), then w = s*q + b
+// rounded once (v_pk_fma_f16), then v_perm into natural code order. s2 and b2
+// hold the scale and the bias in both halves.
+template <int BITS, int C0, int PC>
+__device__ __forceinline__ void dequant_piece_f16_pk(const uint32_t* w, uint32_t s2, uint32_t b2,
+                                                     uint32_t m2, uint32_t magic,
+                                                     uint32_t* out) {
+  uint32_t pr[16];
+  [&]<int... P>(std::integer_sequence<int, P...>) QMM_INLINE {
+    ([&]() QMM_INLINE {
+       if constexpr (piece_has_pair<BITS, C0, PC>(P)) {
+         constexpr int o = pair_o<BITS>(P);
+         constexpr uint16_t e = (uint16_t)((15 - o) << 10);              // 2^-o
+         constexpr uint16_t f = (uint16_t)(0x8000 | ((25 - o) << 10));  // -1024 * 2^-o
+         const half2_t mp = __builtin_bit_cast(half2_t, magic_pair<F16, BITS, P>(w, m2, magic));
+         const half2_t q = __builtin_elementwise_fma(
+             mp, __builtin_bit_cast(half2_t, (uint32_t)e * 0x10001u),
+             __builtin_bit_cast(half2_t, (uint32_t)f * 0x10001u));
+         pr[P] = __builtin_bit_cast(
+             uint32_t, __builtin_elementwise_fma(q, __builtin_bit_cast(half2_t, s2),
+                                                 __builtin_bit_cast(half2_t, b2)));
+       } else {
+         pr[P] = 0;
+       }
+     }(),
+     ...);
+  }(std::make_integer_sequence<int, 16>{});
+  [&]<int... J>(std::integer_sequence<int, J...>) QMM_INLINE {
+    ([&]() QMM_INLINE {
+       constexpr int k = C0 + 2 * J;
+       constexpr int pl = pair_index<BITS>(k), hl = pair_half<BITS>(k);
+       constexpr int ph = pair_index<BITS>(k + 1), hh = pair_half<BITS>(k + 1);
+       out[k / 2] = __builtin_amdgcn_perm(pr[ph], pr[pl], half_sel(hl, hh));
+     }(),
+     ...);
+  }(std::make_integer_sequence<int, PC / 2>{});
+}
+
 // codes [C0, C0+8) of a chunk -> bf16 hi/lo pairs (see dequant_chunk_bf16)
 template <int BITS, int C0>
 __device__ __forceinline__ void dequant_piece_bf16(const uint32_t* w, float s, float b,
                                                    uint32_t* hi, uint32_t* lo) {
-  [&]<int... J>(std::integer_sequence<int, J...>) {
+  [&]<int... J>(std::integer_sequence<int, J...>) QMM_INLINE {
     float f[8] = {fmaf(s, (float)code_at<BITS, C0 + J>(w), b)...};
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
@@ -682,16 +741,16 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // target of the filler W copies of wavefronts with one block fewer
   __shared__ __attribute__((aligned(16))) uint8_t wjunk[G::W_BLOCKS % 4 ? 64 * WU : 16];
 
-  auto slot = [&]<int S>() -> uint8_t* {
+  auto slot = [&]<int S>() -> uint8_t* QMM_INLINE {
     if constexpr (S == 0) return sl0;
     else if constexpr (S == 1) return sl1;
     else if constexpr (S == 2) return sl2;
     else return sl3;
   };
-  auto xslot = [&]<int S>() -> uint16_t* {
+  auto xslot = [&]<int S>() -> uint16_t* QMM_INLINE {
     return reinterpret_cast<uint16_t*>(slot.template operator()<S>());
   };
-  auto wslot = [&]<int S>() -> uint8_t* {
+  auto wslot = [&]<int S>() -> uint8_t* QMM_INLINE {
     return slot.template operator()<S>() + G::A_ELEMS * 2;
   };
 
@@ -803,13 +862,13 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // land as zeros; every wavefront issues the same number of copies every
   // step (those without a W block of their own copy zeros into wjunk), so one
   // vmcnt value fits all. No branches: a stage of steps stays one block.
-  auto issue = [&]<int S>(int tt) {
-    uint16_t* xd = xslot.template operator()<S>();
-    uint8_t* wd = wslot.template operator()<S>();
-    if constexpr (CONV) {
-#pragma unroll
-      for (int i = 0; i < G::A_PER_WAVE; i++) {
-        const int blk = 4 * i + wave;
+  constexpr int kDma = G::A_PER_WAVE + G::W_HI;   // copies per step and wavefront
+  auto issue_one = [&]<int S, int D>(int tt) QMM_INLINE {
+    if constexpr (D < G::A_PER_WAVE) {
+      constexpr int i = D;
+      const int blk = 4 * i + wave;
+      uint16_t* xd = xslot.template operator()<S>() + blk * 512;
+      if constexpr (CONV) {
         const int ku = 8 * tt + (xcol[i] >> 3);
         const uint32_t e = ku < nk * 8 ? ktab[ku] : 0xffffffffu;
         const int dy = (int)(e >> 24), dx = (int)((e >> 16) & 0xff);
@@ -818,19 +877,15 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
                         (unsigned)ix < (unsigned)a.W;
         const uint32_t off =
             (uint32_t)((((pix_b[i] + iy) * a.W + ix) * a.C + (int)(e & 0xffff)) * 2);
-        dma_lds<16>(xr, xd + blk * 512, in ? off : kOob, 0);
+        dma_lds<16>(xr, xd, in ? off : kOob, 0);
+      } else {
+        const bool ok = 64 * tt + xcol[i] < K;
+        dma_lds<16>(xr, xd, ok ? xoff[i] : kOob, 128u * tt);
       }
     } else {
-      const uint32_t soff = 128u * tt;
-#pragma unroll
-      for (int i = 0; i < G::A_PER_WAVE; i++) {
-        const bool ok = 64 * tt + xcol[i] < K;
-        dma_lds<16>(xr, xd + (4 * i + wave) * 512, ok ? xoff[i] : kOob, soff);
-      }
-    }
-    const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;
-#pragma unroll
-    for (int i = 0; i < G::W_HI; i++) {
+      constexpr int i = D - G::A_PER_WAVE;
+      uint8_t* wd = wslot.template operator()<S>();
+      const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;
       const int blk = 4 * i + wave;
       const bool real = G::W_BLOCKS % 4 == 0 || blk < G::W_BLOCKS;
       const bool ok = real && (int)wsoff + wuo[i] < row_bytes;
@@ -838,60 +893,84 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
                   wsoff);
     }
   };
+  auto issue = [&]<int S>(int tt) QMM_INLINE {
+    [&]<int... D>(std::integer_sequence<int, D...>) QMM_INLINE {
+      (issue_one.template operator()<S, D>(tt), ...);
+    }(std::make_integer_sequence<int, kDma>{});
+  };
   // end of a step: wait until only the youngest step of copies is in flight,
   // then barrier
-  auto step_sync = [&]() {
-    wait_vmcnt<G::A_PER_WAVE + G::W_HI>();
+  // (in steps 1 and 2 of a stage the scale loads issued after step 1's copies
+  // may stay in flight too; they must land by the end of step 3)
+  auto step_sync = [&]<int U>() QMM_INLINE {
+    constexpr int kSLoads = 2 * (BN * 16 / 256);
+    wait_vmcnt<G::A_PER_WAVE + G::W_HI + ((U == 1 || U == 2) ? kSLoads : 0)>();
     lds_barrier();
   };
 
   // ---- scales and biases, in stages of 8 steps
   const int sg_log2 = 9 - a.gs_log2;          // groups per stage: 4, 8 or 16
   const int SG = 1 << sg_log2, SGP = SG + 1;
-  // 2-byte loads per thread: (2 * BN * SG) / 256 of them are distinct; the
-  // loop always runs the maximum (16 for 128 rows) over indices taken modulo
-  // the element count, so that it has no branches (repeats rewrite the same
-  // value)
-  const int n_el_mask = 2 * BN * SG - 1;
-  constexpr int kSLoads = 2 * BN * 16 / 256;
-  uint32_t sreg[kSLoads];
-  auto scale_load = [&](int j) {
+  // Each thread loads kSL scales and kSL biases per stage (element e =
+  // thread + 256 i modulo BN*SG: group e % SG of tile row e / SG; repeats
+  // rewrite the same value) through buffer resources over the tile's rows, at
+  // loop-invariant lane offsets plus a per-stage scalar offset. Groups past
+  // the end of a row read the next row (or zeros): they only meet zero x.
+  constexpr int kSL = BN * 16 / 256;
+  const char* sbase = reinterpret_cast<const char*>(sp + (int64_t)n_blk * n_groups);
+  const char* bbase = reinterpret_cast<const char*>(bp + (int64_t)n_blk * n_groups);
+  const int64_t s_bytes = (int64_t)(a.N - n_blk) * n_groups * 2;
+  const uint32_t s_rb = (uint32_t)(s_bytes < 0x7fffffff ? s_bytes : 0x7fffffff);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(sbase, s_rb), br = make_rsrc(bbase, s_rb);
+  uint32_t soffv[kSL];
+  int sdst[kSL];
 #pragma unroll
-    for (int i = 0; i < kSLoads; i++) {
-      const int e = (tid + 256 * i) & n_el_mask;
-      const int grp = e & (SG - 1), row = (e >> sg_log2) & (BN - 1);
-      const int which = e >> (sg_log2 + ilog2(BN));
-      const int gi = j * SG + grp < n_groups ? j * SG + grp : n_groups - 1;
-      const int n = n_blk + row < a.N ? n_blk + row : a.N - 1;
-      sreg[i] = (which ? bp : sp)[(int64_t)n * n_groups + gi];
+  for (int i = 0; i < kSL; i++) {
+    const int e = (tid + 256 * i) & (BN * SG - 1);
+    const int grp = e & (SG - 1), row = e >> sg_log2;
+    const int rc = n_blk + row < a.N ? row : a.N - 1 - n_blk;
+    soffv[i] = (uint32_t)((rc * n_groups + grp) * 2);
+    sdst[i] = row * SGP + grp;
+  }
+  uint32_t sreg[kSL], breg[kSL];
+  constexpr int kSGrp = kSL >= 4 ? 4 : kSL;          // loads of a group (each array)
+  auto scale_load_grp = [&]<int GR>(int j) QMM_INLINE {
+    const uint32_t so = (uint32_t)(j * SG * 2);
+#pragma unroll
+    for (int i = GR * kSGrp; i < (GR + 1) * kSGrp; i++) {
+      sreg[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soffv[i], so, 0);
+      breg[i] = __builtin_amdgcn_raw_buffer_load_b16(br, soffv[i], so, 0);
     }
   };
-  auto scale_store = [&](int j) {
+  auto scale_load = [&](int j) QMM_INLINE {
+    [&]<int... GR>(std::integer_sequence<int, GR...>) QMM_INLINE {
+      (scale_load_grp.template operator()<GR>(j), ...);
+    }(std::make_integer_sequence<int, kSL / kSGrp>{});
+  };
+  auto scale_store = [&](int j) QMM_INLINE {
     uint16_t* base = reinterpret_cast<uint16_t*>(sct + (j & 1) * BN * SGP);
 #pragma unroll
-    for (int i = 0; i < kSLoads; i++) {
-      const int e = (tid + 256 * i) & n_el_mask;
-      const int grp = e & (SG - 1), row = (e >> sg_log2) & (BN - 1);
-      const int which = e >> (sg_log2 + ilog2(BN));
-      base[2 * (row * SGP + grp) + which] = (uint16_t)sreg[i];
+    for (int i = 0; i < kSL; i++) {
+      base[2 * sdst[i]] = (uint16_t)sreg[i];
+      base[2 * sdst[i] + 1] = (uint16_t)breg[i];
     }
   };
 
   // ---- per-step register state. x fragments: with several row blocks per
-  // wavefront (kJit) slice kk+1 is read while the MFMAs of slice kk run and
-  // slice 0 of the next step during slice 3 (one buffer); with one row block
-  // the next step's four slices are read during the current step (two
-  // buffers).
+  // wavefront (kJit) slice kk+2 is read while the MFMAs of slice kk run
+  // (slices 0 and 1 of the next step during slices 2 and 3; one buffer);
+  // with one row block the next step's four slices are read during the
+  // current step (two buffers).
   constexpr bool kJit = FM >= 2;
   uint4 af[kJit ? 1 : 2][4][FM];
   uint4 bq[2][FN][NB][4];        // W operands (row block, hi/lo, K slice)
   uint32_t wc[FN][BITS];         // raw W chunks of the next step
   uint32_t sbw[FN];              // (scale | bias << 16) of the next step
-  F16Consts cst[FN];
-  float sf[FN], bf[FN];
+  uint32_t s2v[FN], b2v[FN];      // f16 scale / bias in both halves
+  float sf[FN], bf[FN];           // bf16 path: scale / bias in fp32
 
   // W chunks and scale words of step tt from slot S
-  auto read_w = [&]<int S>(int tt) {
+  auto read_w = [&]<int S>(int tt) QMM_INLINE {
     const uint8_t* wsl = wslot.template operator()<S>();
     const uint32_t* scs = sct + ((tt >> 3) & 1) * BN * SGP;
     const int gl = (((tt & 7) << 6) + 32 * h) >> a.gs_log2;
@@ -925,25 +1004,29 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     }
   };
   // x fragment (K slice KK, row block I) of slot S
-  auto read_x = [&]<int S, int KK, int I>(uint4 (&afr)[4][FM]) {
+  auto read_x = [&]<int S, int KK, int I>(uint4 (&afr)[4][FM]) QMM_INLINE {
     const uint16_t* xsl = xslot.template operator()<S>();
     const int ra = wm * WTM + 32 * I + rr;
     const int c = (4 * h + KK) ^ ((ra >> 1) & 7);
     afr[KK][I] = *reinterpret_cast<const uint4*>(xsl + ra * 64 + 8 * c);
   };
-  auto prep = [&]<int J>() {
-    sf[J] = to_f32(T{}, (uint16_t)sbw[J]);
-    bf[J] = to_f32(T{}, (uint16_t)(sbw[J] >> 16));
-    if constexpr (!kSplit) f16_consts(sf[J], bf[J], cst[J]);
+  auto prep = [&]<int J>() QMM_INLINE {
+    if constexpr (kSplit) {
+      sf[J] = to_f32(T{}, (uint16_t)sbw[J]);
+      bf[J] = to_f32(T{}, (uint16_t)(sbw[J] >> 16));
+    } else {
+      s2v[J] = __builtin_amdgcn_perm(sbw[J], sbw[J], 0x01000100u);
+      b2v[J] = __builtin_amdgcn_perm(sbw[J], sbw[J], 0x03020302u);
+    }
   };
-  auto piece = [&]<int J, int P>(uint4 (&bqn)[FN][NB][4]) {
+  auto piece = [&]<int J, int P>(uint4 (&bqn)[FN][NB][4]) QMM_INLINE {
     uint32_t hi[16], lo[16];
     if constexpr (kSplit) {
       dequant_piece_bf16<BITS, P * 8>(wc[J], sf[J], bf[J], hi, lo);
       bqn[J][1][P] = make_uint4(lo[4 * P], lo[4 * P + 1], lo[4 * P + 2], lo[4 * P + 3]);
       bqn[J][0][P] = make_uint4(hi[4 * P], hi[4 * P + 1], hi[4 * P + 2], hi[4 * P + 3]);
     } else {
-      dequant_piece_f16<BITS, P * PC, PC>(wc[J], cst[J], m2_s, magic_v, hi);
+      dequant_piece_f16_pk<BITS, P * PC, PC>(wc[J], s2v[J], b2v[J], m2_s, magic_v, hi);
 #pragma unroll
       for (int kk = P * PC / 8; kk < (P + 1) * PC / 8; kk++)
         bqn[J][0][kk] = make_uint4(hi[4 * kk], hi[4 * kk + 1], hi[4 * kk + 2], hi[4 * kk + 3]);
@@ -951,7 +1034,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   };
   // filler F of a step: scale prep, a dequant piece, or (without kJit) an x
   // fragment read of the next step (slot SN)
-  auto filler = [&]<int F, int SN>(uint4 (&afn)[4][FM], uint4 (&bqn)[FN][NB][4]) {
+  auto filler = [&]<int F, int SN>(uint4 (&afn)[4][FM], uint4 (&bqn)[FN][NB][4]) QMM_INLINE {
     if constexpr (F < FN) {
       prep.template operator()<F>();
     } else if constexpr (F < FN + FN * NP) {
@@ -973,9 +1056,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
 
   // fillers of MFMA slot MM (next step's state goes to bq[1-C] and, without
   // kJit, af[1-C], from slot SN)
-  auto slot_fill = [&]<int MM, int C, int SN>() {
-    [&]<int... F>(std::integer_sequence<int, F...>) {
-      ([&] {
+  auto slot_fill = [&]<int MM, int C, int SN>() QMM_INLINE {
+    [&]<int... F>(std::integer_sequence<int, F...>) QMM_INLINE {
+      ([&]() QMM_INLINE {
          if constexpr (filler_slot(F, kNF, kM, kLead) == MM) {
            filler.template operator()<F, SN>(af[kJit ? 0 : 1 - C], bq[1 - C]);
            __builtin_amdgcn_sched_barrier(0);
@@ -985,12 +1068,12 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     }(std::make_integer_sequence<int, kNF>{});
   };
   constexpr int kSlice = FM * FN * NB;       // MFMAs per K slice
-  auto read_slice = [&]<int S, int KK>() {
-    [&]<int... I>(std::integer_sequence<int, I...>) {
+  auto read_slice = [&]<int S, int KK>() QMM_INLINE {
+    [&]<int... I>(std::integer_sequence<int, I...>) QMM_INLINE {
       (read_x.template operator()<S, KK, I>(af[0]), ...);
     }(std::make_integer_sequence<int, FM>{});
   };
-  auto mfma_at = [&]<int MM, int C, int SC, int SN>() {
+  auto mfma_at = [&]<int MM, int C, int SC, int SN>() QMM_INLINE {
     constexpr int kk = MM / kSlice;
     constexpr int i = (MM / (FN * NB)) % FM;
     constexpr int j = (MM / NB) % FN;
@@ -998,20 +1081,55 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     acc[i][j] = mfma32(T{}, af[kJit ? 0 : C][kk][i], bq[C][j][e][kk], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kJit && MM % kSlice == 0) {
-      // x fragments of the next slice (slice 0 of the next step after slice 3)
-      if constexpr (kk < 3) read_slice.template operator()<SC, kk + 1>();
-      else read_slice.template operator()<SN, 0>();
+      // x fragments two slices ahead (slices 0 and 1 of the next step during
+      // slices 2 and 3): ax[kk+2] was last used in slice kk+2 of the previous
+      // step
+      if constexpr (kk < 2) read_slice.template operator()<SC, kk + 2>();
+      else read_slice.template operator()<SN, kk - 2>();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // copies of step tt+3 (slot SD) and, in step 1 of a stage, the scale loads
+  // of the next stage, spread over the MFMA slots (a burst of copies would
+  // stall on the address unit): copy d after MFMA 2d, the scale groups after
+  // the last copy (the end-of-step vmcnt values count on that order)
+  constexpr int kNGrp = kSL / kSGrp;
+  auto extras = [&]<int MM, int SD, bool kScales>(int tt, int js) QMM_INLINE {
+    [&]<int... D>(std::integer_sequence<int, D...>) QMM_INLINE {
+      ([&]() QMM_INLINE {
+         constexpr int slot = 2 * D < kM ? 2 * D : kM - 1;
+         if constexpr (slot == MM) {
+           issue_one.template operator()<SD, D>(tt + 3);
+           __builtin_amdgcn_sched_barrier(0);
+         }
+       }(),
+       ...);
+    }(std::make_integer_sequence<int, kDma>{});
+    if constexpr (kScales) {
+      [&]<int... GR>(std::integer_sequence<int, GR...>) QMM_INLINE {
+        ([&]() QMM_INLINE {
+           constexpr int last = 2 * (kDma - 1) < kM ? 2 * (kDma - 1) : kM - 1;
+           constexpr int slot = last + 1 + GR < kM ? last + 1 + GR : kM - 1;
+           if constexpr (slot == MM) {
+             scale_load_grp.template operator()<GR>(js + 1);
+             __builtin_amdgcn_sched_barrier(0);
+           }
+         }(),
+         ...);
+      }(std::make_integer_sequence<int, kNGrp>{});
+    }
+  };
+
   // one step body: MFMAs from af/bq[C] (x slot SC); the next step's state
-  // (slot SN) is built between them, in a fixed order
-  auto body = [&]<int C, int SC, int SN>(int tt) {
+  // (slot SN) is built between them, in a fixed order, with the copies of
+  // step tt+3 (slot SD)
+  auto body = [&]<int C, int SC, int SN, int SD, bool kScales>(int tt, int js) QMM_INLINE {
     read_w.template operator()<SN>(tt + 1);
     __builtin_amdgcn_sched_barrier(0);
-    [&]<int... M>(std::integer_sequence<int, M...>) {
+    [&]<int... M>(std::integer_sequence<int, M...>) QMM_INLINE {
       ((mfma_at.template operator()<M, C, SC, SN>(),
+        extras.template operator()<M, SD, kScales>(tt, js),
         slot_fill.template operator()<M, C, SN>()),
        ...);
     }(std::make_integer_sequence<int, kM>{});
@@ -1026,10 +1144,13 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   scale_store(0);
   wait_vmcnt_barrier<0>();
   read_w.template operator()<0>(0);
-  [&]<int... F>(std::integer_sequence<int, F...>) {
+  [&]<int... F>(std::integer_sequence<int, F...>) QMM_INLINE {
     (filler.template operator()<F, 0>(af[0], bq[0]), ...);
   }(std::make_integer_sequence<int, kNF>{});
-  if constexpr (kJit) read_slice.template operator()<0, 0>();
+  if constexpr (kJit) {
+    read_slice.template operator()<0, 0>();
+    read_slice.template operator()<0, 1>();
+  }
 
   // every LDS read of the prologue has landed before the loop (so that the
   // compiler does not carry them into the loop body)
@@ -1040,22 +1161,20 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // slot (tt+1) % 4; the copies of step tt+3 go to slot (tt+3) % 4, whose
   // last reads were made during step tt-2. Full stages run unguarded; only a
   // last partial stage checks each step against nk.
-  auto stage = [&]<bool kFull>(int js) {
-    [&]<int... U>(std::integer_sequence<int, U...>) {
-      (([&] {
+  auto stage = [&]<bool kFull>(int js) QMM_INLINE {
+    [&]<int... U>(std::integer_sequence<int, U...>) QMM_INLINE {
+      (([&]() QMM_INLINE {
          const int tt = kStageSteps * js + U;
          if (kFull || tt < nk) {
-           if constexpr (U == 1) scale_load(js + 1);
-           issue.template operator()<(U + 3) % 4>(tt + 3);
-           if constexpr (U == 2) scale_store(js + 1);
-           body.template operator()<U % 2, U % 4, (U + 1) % 4>(tt);
+           if constexpr (U == 4) scale_store(js + 1);
+           body.template operator()<U % 2, U % 4, (U + 1) % 4, (U + 3) % 4, U == 1>(tt, js);
 #pragma unroll
            for (int j = 0; j < FN; j++)
 #pragma unroll
              for (int e = 0; e < NB; e++)
 #pragma unroll
                for (int kk = 0; kk < 4; kk++) keep(bq[(U + 1) % 2][j][e][kk]);
-           step_sync();
+           step_sync.template operator()<U>();
          }
        }()),
        ...);
