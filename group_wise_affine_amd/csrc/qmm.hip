@@ -53,7 +53,15 @@ struct GemmArgs {
   int64_t ldy;       // row stride of y in elements
   // implicit im2col (conv only)
   int H, W, C, OH, OW, kh, kw, sh, sw, ph, pw, Cg, Og, K_true;
+  // split K (tile kernel only): blockIdx.y takes K steps [y*ksteps,
+  // (y+1)*ksteps) and, with ksplit > 1, writes fp32 partial sums to the
+  // split-K workspace instead of y
+  int ksplit, ksteps;
 };
+
+// Split-K workspace: [split][M][ldy] fp32 partial sums, library-owned.
+constexpr int64_t kSplitWsFloats = (int64_t)16 << 20;   // 64 MiB
+__device__ float g_splitk_ws[kSplitWsFloats];
 
 // v_mfma_f32_32x32x16: A[i][k] from lane i%32 + 32*(k/8) (element k%8), B[k][j]
 // from lane j + 32*(k/8), D[i][j] in lane j + 32*((i/4)%2), element
@@ -770,6 +778,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
 
   const int K = a.K;                       // W row length in codes
   const int nk = (K + 63) >> 6;            // K steps
+  const int sk = blockIdx.y;               // K split
+  const int t0 = sk * a.ksteps;            // first step (a multiple of 8)
+  const int t1 = t0 + a.ksteps < nk ? t0 + a.ksteps : nk;
   const int row_bytes = K / 8 * BITS;
   const int n_groups = K >> a.gs_log2;
   const uint8_t* wq = a.wq;
@@ -1136,14 +1147,15 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   };
 
   // ---- prologue: scales of stage 0, copies of steps 0..2, state of step 0
-  scale_load(0);
-  issue.template operator()<0>(0);
-  issue.template operator()<1>(1);
-  issue.template operator()<2>(2);
+  const int js0 = t0 / kStageSteps;
+  scale_load(js0);
+  issue.template operator()<0>(t0);
+  issue.template operator()<1>(t0 + 1);
+  issue.template operator()<2>(t0 + 2);
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
-  scale_store(0);
+  scale_store(js0);
   wait_vmcnt_barrier<0>();
-  read_w.template operator()<0>(0);
+  read_w.template operator()<0>(t0);
   [&]<int... F>(std::integer_sequence<int, F...>) QMM_INLINE {
     (filler.template operator()<F, 0>(af[0], bq[0]), ...);
   }(std::make_integer_sequence<int, kNF>{});
@@ -1165,7 +1177,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     [&]<int... U>(std::integer_sequence<int, U...>) QMM_INLINE {
       (([&]() QMM_INLINE {
          const int tt = kStageSteps * js + U;
-         if (kFull || tt < nk) {
+         if (kFull || tt < t1) {
            if constexpr (U == 4) scale_store(js + 1);
            body.template operator()<U % 2, U % 4, (U + 1) % 4, (U + 3) % 4, U == 1>(tt, js);
 #pragma unroll
@@ -1180,9 +1192,29 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
        ...);
     }(std::make_integer_sequence<int, kStageSteps>{});
   };
-  const int n_full = nk / kStageSteps;
-  for (int js = 0; js < n_full; js++) stage.template operator()<true>(js);
-  if (nk % kStageSteps) stage.template operator()<false>(n_full);
+  const int n_full = (t1 - t0) / kStageSteps;
+  for (int js = js0; js < js0 + n_full; js++) stage.template operator()<true>(js);
+  if ((t1 - t0) % kStageSteps) stage.template operator()<false>(js0 + n_full);
+
+  // ---- split K: fp32 partial sums straight from the accumulators (lane:
+  // column 32j + lane%32, rows 8(r/4) + 4(lane/32) + r%4 of each 32x32 tile;
+  // each store instruction covers two 128-byte row pieces)
+  if (a.ksplit > 1) {
+    wait_vmcnt<0>();   // no copy may still be landing in LDS when the wave ends
+    float* ws = g_splitk_ws + (int64_t)sk * a.M * a.ldy + (CONV ? (int64_t)g * a.Og : 0);
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) {
+        const int n = n_blk + wn * WTN + 32 * j + rr;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = m_blk + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < a.M && n < a.N) ws[(int64_t)m * a.ldy + n] = acc[i][j][r];
+        }
+      }
+    return;
+  }
 
   // ---- epilogue: each wavefront stages its WTM x WTN tile in "its" x slot
   // (all copies have landed and all slot reads are done), then writes rows
@@ -1238,18 +1270,79 @@ static hipError_t launch_gather(const GemmArgs& a, int groups, hipStream_t st) {
 }
 
 template <class T, int BITS, int BM, int BN, bool CONV>
-static hipError_t launch_dma(const GemmArgs& a, int groups, hipStream_t st) {
+static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   const dim3 grid(tiles, 1, groups);
+  a.ksplit = 1;
+  a.ksteps = ((a.K + 63) / 64 + kStageSteps - 1) / kStageSteps * kStageSteps;
   hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
+// y[m][c] = T(sum over splits of the fp32 partial sums), c < ncols, four
+// columns per thread
+template <class T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* y, int M, int ncols,
+                                                            int64_t ldy, int splits) {
+  const int64_t quads = (int64_t)M * (ncols / 4);
+  const int64_t plane = (int64_t)M * ldy;
+  for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < quads; q += (int64_t)gridDim.x * 256) {
+    const int m = (int)(q / (ncols / 4));
+    const int c = (int)(q - (int64_t)m * (ncols / 4)) * 4;
+    const float* p = g_splitk_ws + (int64_t)m * ldy + c;
+    float4 v = *reinterpret_cast<const float4*>(p);
+    for (int sp = 1; sp < splits; sp++) {
+      const float4 u = *reinterpret_cast<const float4*>(p + sp * plane);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    uint2 o;
+    o.x = (uint32_t)from_f32(T{}, v.x) | ((uint32_t)from_f32(T{}, v.y) << 16);
+    o.y = (uint32_t)from_f32(T{}, v.z) | ((uint32_t)from_f32(T{}, v.w) << 16);
+    *reinterpret_cast<uint2*>(y + (int64_t)m * ldy + c) = o;
+  }
+}
+
+// Split-K plan for the 128 x 128 tile kernel: as many splits as keep the
+// workgroups within one wave over the 256 CUs (a second, partial wave costs
+// more than it saves), each split a whole number of 8-step stages, and the
+// partial sums within the workspace. Returns 1 when K is not split.
+static int splitk_plan(const GemmArgs& a, int groups, int* ksteps) {
+  const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
+  const int nk = (a.K + 63) / 64;
+  *ksteps = ((nk + kStageSteps - 1) / kStageSteps) * kStageSteps;
+  if (tiles128 >= 192 || a.ldy % 4 != 0) return 1;
+  int s = (int)(256 / tiles128);
+  if (s > 8) s = 8;
+  if (s > nk / kStageSteps) s = nk / kStageSteps;
+  while (s > 1 && (int64_t)s * a.M * a.ldy > kSplitWsFloats) s--;
+  if (s < 2) return 1;
+  int per = (nk + s - 1) / s;
+  per = ((per + kStageSteps - 1) / kStageSteps) * kStageSteps;
+  *ksteps = per;
+  return (nk + per - 1) / per;
+}
+
 template <class T, int BITS, bool CONV, bool DMA>
-static hipError_t launch_shape(const GemmArgs& a, int groups, hipStream_t st) {
+static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
   const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
   if constexpr (DMA) {
-    if (tiles128 >= 256) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
+    int ksteps = 0;
+    a.ksplit = splitk_plan(a, groups, &ksteps);
+    a.ksteps = ksteps;
+    if (a.ksplit > 1) {
+      const int tiles = ((a.N + 127) / 128) * ((a.M + 127) / 128);
+      hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, 128, 128, CONV>), dim3(tiles, a.ksplit, groups),
+                         dim3(256), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int ncols = (int)a.ldy;    // every column of y (all conv groups)
+      const int64_t quads = (int64_t)a.M * (ncols / 4);
+      const int blocks = (int)((quads + 255) / 256 < 2048 ? (quads + 255) / 256 : 2048);
+      hipLaunchKernelGGL((splitk_reduce_kernel<T>), dim3(blocks), dim3(256), 0, st, a.y, a.M,
+                         ncols, a.ldy, a.ksplit);
+      return hipGetLastError();
+    }
+    if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
     return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
   } else {
     if (tiles128 >= 256) return launch_gather<T, BITS, 128, 128>(a, groups, st);

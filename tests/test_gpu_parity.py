@@ -141,6 +141,40 @@ def test_qmm_t_shapes(orc, M, N, K):
     _run_mm(Q.qmm_t, orc, "bf16", M, N, K, 64, 6, seed=M)
 
 
+@pytest.mark.parametrize("M,N,K,gs,bits", [
+    (130, 200, 1536, 64, 4),    # 24 steps: three whole stages over two splits
+    (64, 64, 2080, 32, 4),      # 33 steps: last split a single step, K % 64 == 32
+    (257, 130, 4160, 64, 8),    # ragged M and N, K not a multiple of a stage
+    (40, 300, 4096, 128, 2),
+    (100, 96, 2560, 32, 3),
+    (72, 136, 3072, 64, 5),
+    (33, 64, 2048, 128, 6),
+])
+def test_qmm_t_split_k(orc, M, N, K, gs, bits):
+    """Few output tiles: K is split over workgroups (fp32 partial sums in the
+    library's workspace, then a reduction)."""
+    _run_mm(Q.qmm_t, orc, "f16", M, N, K, gs, bits, seed=K)
+    _run_mm(Q.qmm_t, orc, "bf16", M, N, K, gs, bits, seed=K + 1)
+
+
+def test_qmm_t_split_k_back_to_back(orc):
+    """Two split-K calls in a row on one stream reuse the workspace: the second
+    (smaller) result must not see the first one's partial sums."""
+    code = orc_code(orc, "f16")
+    outs = []
+    for (M, N, K, seed) in [(96, 256, 4096, 5), (40, 128, 1024, 6)]:
+        x = synth.normal((M, K), seed=seed, dt="f16")
+        w = synth.normal((N, K), seed=seed + 1, dt="f16")
+        wq, s, b = orc.quantize(w, code, 64, 4)
+        yo, _ = orc.qmm_t(x, wq, s, b, code, 64, 4, nthreads=8)
+        y = Q.qmm_t(to_dev(x, "f16"), bytes_to_words_dev(wq), to_dev(s, "f16"),
+                    to_dev(b, "f16"), 64, 4)
+        outs.append((y, yo, (M, N, K)))
+    torch.cuda.synchronize()
+    for y, yo, shape in outs:
+        assert_parity(from_dev(y), yo, "f16", f"split-K back to back {shape}")
+
+
 def test_qmm_t_routes_consistently(orc):
     """Around the crossover both kernels agree with the oracle."""
     mx = Q.crossover_m(4)
@@ -161,6 +195,8 @@ CONV = [
     (1, 5, 5, 24, 12, 3, 3, (1, 1), (1, 1), 3, 128, 5),
     (2, 17, 19, 64, 96, 3, 3, (1, 1), (1, 1), 1, 64, 2),
     (1, 12, 12, 48, 40, 3, 3, (2, 2), (0, 0), 2, 64, 4),
+    (1, 16, 16, 128, 64, 3, 3, (1, 1), (1, 1), 1, 64, 4),  # 18 K steps: split K
+    (1, 14, 14, 256, 32, 3, 3, (1, 1), (1, 1), 2, 128, 4),  # split K per group
 ]
 
 
