@@ -59,14 +59,6 @@ qmm_status launched(hipError_t e, const char* what) {
 
 constexpr int64_t kI32 = std::numeric_limits<int32_t>::max();
 
-// Largest K the streaming GEMV stages in LDS (one row of x plus two fp32
-// constants per 32-element chunk within 64 KiB; 8-bit bf16 stages fp32
-// activations).
-int64_t qmv_max_k(int bits, qmm_dtype dt) {
-  const int64_t words = (bits == 8 && dt == QMM_BF16) ? 34 : 18;
-  return (64 * 1024 / (words * 4)) * 32;
-}
-
 qmm_status check_matmul(const char* tag, const void* x, const uint32_t* wq,
                         const void* s, const void* b, qmm_dtype dt, int64_t M,
                         int64_t N, int64_t K, int gs, int bits, const void* y) {
@@ -159,9 +151,11 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
   qmm_status st = check_matmul("qmv", x, wq, scales, biases, dt, M, N, K,
                                group_size, bits, y);
   if (st) return st;
-  if (K > qmv_max_k(bits, dt))
-    return fail(QMM_E_SHAPE, "qmv: K (%lld) exceeds the streaming kernel's limit %lld; use qmm_t",
-                (long long)K, (long long)qmv_max_k(bits, dt));
+  if (qmm::route((int)dt, bits, group_size, M, N, K, false) == qmm::kRouteNone)
+    return fail(QMM_E_SHAPE, "qmv: K (%lld) exceeds the GEMV kernels' limits (%lld for this "
+                "bits/dtype; M <= %d rows of x within %zu bytes of LDS for f16); use qmm_t",
+                (long long)K, (long long)qmm::qmv_max_k(bits, (int)dt), qmm::kQmvMfmaMaxM,
+                qmm::kQmvMfmaMaxLds);
   return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                   biases, M, N, K, y, (hipStream_t)stream),
                   "qmv");
@@ -173,13 +167,14 @@ qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
   qmm_status st = check_matmul("qmm_t", x, wq, scales, biases, dt, M, N, K,
                                group_size, bits, y);
   if (st) return st;
-  if (M < qmm::crossover_m(bits, (int)dt) && K <= qmv_max_k(bits, dt))
+  const qmm::Route r = qmm::route((int)dt, bits, group_size, M, N, K, true);
+  if (r == qmm::kRouteQmv || r == qmm::kRouteQmvMfma)
     return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                     biases, M, N, K, y, (hipStream_t)stream),
                     "qmm_t");
   if (K >= qmm::kTileMaxK)
-    return fail(QMM_E_SHAPE, "qmm_t: K (%lld) must be below %lld for M >= %d",
-                (long long)K, (long long)qmm::kTileMaxK, qmm::crossover_m(bits, (int)dt));
+    return fail(QMM_E_SHAPE, "qmm_t: K (%lld) must be below %lld for the MFMA tile kernel",
+                (long long)K, (long long)qmm::kTileMaxK);
   return launched(qmm::launch_qmm_mfma((int)dt, bits, group_size, x, wq, scales,
                                        biases, M, N, K, y, (hipStream_t)stream),
                   "qmm_t");

@@ -20,6 +20,24 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
                       int64_t M, int64_t N, int64_t K, void* y,
                       hipStream_t st);
 
+// GEMV on the matrix cores, f16, 1 <= M <= kQmvMfmaMaxM, K < kQmvMfmaMaxK
+// (byte offsets of its buffer loads stay below 2^31), x[0:M] small enough
+// for LDS (qmv_mfma_fits).
+constexpr int kQmvMfmaMaxM = 16;
+constexpr int64_t kQmvMfmaMaxK = (int64_t)1 << 25;
+constexpr size_t kQmvMfmaMaxLds = 128 * 1024;
+size_t qmv_mfma_lds(int64_t M, int64_t K, int gs);
+inline bool qmv_mfma_fits(int64_t M, int64_t K, int gs) {
+  // the workgroup's 1024 threads copy x with at most 8 16-byte loads each,
+  // the scales and biases with at most 2
+  return M >= 1 && M <= kQmvMfmaMaxM && K < kQmvMfmaMaxK &&
+         qmv_mfma_lds(M, K, gs) <= kQmvMfmaMaxLds && M * (K / 8) <= 8 * 1024 &&
+         (15 + 32 * (K / gs) + 15) / 16 <= 2 * 1024;
+}
+hipError_t launch_qmv_mfma(int bits, int gs, const void* x, const uint32_t* wq,
+                           const void* s, const void* b, int64_t M, int64_t N,
+                           int64_t K, void* y, hipStream_t st);
+
 // MFMA tile GEMM: y[M,N] = x[M,K] . dequant(W)[N,K]^T. K must be below
 // kTileMaxK (byte offsets inside a tile stay below 2^30, in range of the
 // buffer resources the tile kernel reads through).
@@ -40,7 +58,19 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
                              const void* s, const void* b, void* y,
                              hipStream_t st);
 
-// Smallest M routed to the MFMA kernel by qmm_t.
+// Kernel choice for y = x . dequant(W)^T (measured on MI355X, 4096-wide
+// layers): the MFMA GEMV for f16 from M = 3 up to 16 rows when x fits in
+// LDS, and for M <= 2 when K > 8192 on N >= 4096 (long rows make the
+// streaming GEMV's per-row passes slow); the streaming dot2 GEMV for a few
+// rows otherwise; the MFMA tile kernel for the rest. qmv never takes the
+// tile kernel (kRouteNone when neither GEMV accepts the shape).
+enum Route { kRouteNone = 0, kRouteQmv = 1, kRouteQmvMfma = 2, kRouteTile = 3 };
+Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allow_tile);
+
+// Largest K the streaming dot2 GEMV stages in LDS.
+int64_t qmv_max_k(int bits, int dt);
+
+// Smallest M routed to the MFMA tile kernel by qmm_t for K <= 4096.
 int crossover_m(int bits, int dt);
 
 }  // namespace qmm

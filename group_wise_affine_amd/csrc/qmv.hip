@@ -407,6 +407,8 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
                       const uint32_t* wq, const void* s, const void* b,
                       int64_t M, int64_t N, int64_t K, void* y,
                       hipStream_t st) {
+  if (route(dt, bits, gs, M, N, K, false) == kRouteQmvMfma)
+    return launch_qmv_mfma(bits, gs, x, wq, s, b, M, N, K, y, st);
   if (dt == 0)
     return launch_bits<F16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
   return launch_bits<BF16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);

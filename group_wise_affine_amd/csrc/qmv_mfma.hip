@@ -1,0 +1,328 @@
+// Quantized GEMV on the matrix cores for a few rows of x (M <= 16), f16:
+//   y[m, n] = sum_k x[m, k] * (s[n, g(k)] * q[n, k] + b[n, g(k)]),
+// the product the quantized matmul computes (mlx affine_qmv / qmm_t, "Add the
+// 3bit packed qmm_t"), with fp32 accumulation as the Metal qmv does (mlx PR
+// 1061 item 2).
+//
+// MI355X design (wave64, gfx950):
+//  * One workgroup = 16 wavefronts = 16 rows of W over the whole of K. A K
+//    step is 4 consecutive 32-code chunks of each of the 16 rows; wavefront w
+//    takes steps w, w+16, w+32, ... so that the 16 wavefronts stream one
+//    contiguous run of every row at a time.
+//  * Lane (n, g) = (lane % 16, lane / 16) loads chunk g of the step of row n
+//    and dequantizes it (magic pairs, packed f16 FMAs, one rounding of s*q+b)
+//    into four 8-code B fragments of v_mfma_f32_16x16x32_f16: MFMA i takes
+//    codes 8i..8i+7 of the four chunks, so A lane (m, g) holds the matching
+//    8 elements of row m of x in natural order (rows m >= M stay zero).
+//  * The workgroup copies x[0:M] and the scales and biases of its 16 rows
+//    into LDS once, with coalesced loads issued ahead of the weight loads; A
+//    fragments, scales and biases are read from there. The number of vector
+//    memory instructions per CU (and the cache lines each one touches) is
+//    what limits a kernel this short, so none of these is loaded per
+//    wavefront and step.
+//  * Every weight load of a wavefront (W chunk, scale, bias) is issued before
+//    any arithmetic: for K <= 8192 all of them are in flight at once (one
+//    round, no filler loads); longer rows run as a ring of 3 steps. Loads go
+//    through buffer resources, so that out-of-range elements (ragged N,
+//    chunks past the row end) read zero without a branch or a memory access.
+//    Byte offsets stay below 2^31 for K < kQmvMfmaMaxK; x[0:M] must fit in
+//    LDS (qmv_mfma_fits).
+//  * The 16 partial 16x16 tiles are summed through LDS and written as f16.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_common.hpp"
+
+namespace qmm {
+
+namespace {
+
+constexpr int kMvWaves = 16;                  // wavefronts per workgroup
+constexpr int kMvThreads = kMvWaves * 64;
+constexpr int kMvMaxXu = 8;                   // 16-byte x units per thread
+constexpr int kMvMaxSb = 2;                   // 16-byte scale (and bias) units per thread
+
+// Compiler fence between groups of loads: memory operations are not moved
+// across it, so the groups issue in program order and a wait for one group
+// leaves the later ones in flight.
+__device__ __forceinline__ void load_fence() { asm volatile("; load fence" ::: "memory"); }
+
+// W chunk of one lane (4*BITS bytes) from the buffer at byte offset off
+template <int BITS>
+__device__ __forceinline__ void load_wchunk_buf(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                uint32_t w[BITS]) {
+  if constexpr (BITS == 4 || BITS == 8) {
+#pragma unroll
+    for (int h = 0; h < BITS / 4; h++) {
+      const u32x4_t u = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0));
+      w[4 * h] = u.x; w[4 * h + 1] = u.y; w[4 * h + 2] = u.z; w[4 * h + 3] = u.w;
+    }
+  } else if constexpr (BITS == 2 || BITS == 6) {
+#pragma unroll
+    for (int h = 0; h < BITS / 2; h++) {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t u = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + 8 * h, 0, 0));
+      w[2 * h] = u.x; w[2 * h + 1] = u.y;
+    }
+  } else {  // 3 and 5 bits: 4-byte aligned chunks
+#pragma unroll
+    for (int i = 0; i < BITS; i++) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+  }
+}
+
+// Round structure: DEPTH steps of a wavefront are in flight at once. With
+// RING = false the kernel runs one round (every wavefront has at most DEPTH
+// steps); with RING = true slot d is refilled with the step one round later
+// right after it is consumed.
+template <int BITS, int DEPTH, bool RING>
+__global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, uint32_t m2, int xu, int sbu) {
+  // x rows [M][K + 8] f16 (8 halfs of padding per row spread the rows over
+  // the LDS banks), then scales [16][G] and biases [16][G]; afterwards the
+  // cross-wavefront reduction buffer
+  extern __shared__ uint4 smem4[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem4);
+  float* red = reinterpret_cast<float*>(smem4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int rows = N - n0 < 16 ? N - n0 : 16;
+  const int nch = K >> 5;
+  const int nsteps = (nch + 3) >> 2;
+  const int nsw = wave < nsteps ? (nsteps - wave + kMvWaves - 1) / kMvWaves : 0;
+  const int G = K >> gs_log2;
+  const int ldx = K + 8;
+  const uint32_t row_bytes = (uint32_t)K * BITS / 8;
+
+  // Buffers over this workgroup's rows of W / scales / biases and over x:
+  // offsets past their ends read zeros without a branch, which covers rows
+  // n >= N of the last row block and chunks past the row end (weight 0 from
+  // zero codes, scale and bias).
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (int64_t)n0 * row_bytes, rows * row_bytes);
+  // scales and biases of the 16 rows: 16*G contiguous halfs each, read as
+  // aligned 16-byte units that cover them (the range is widened to 16-byte
+  // boundaries at both ends; the extra bytes lie in the aligned blocks of
+  // the first and the last scale, so in mapped pages, and only feed rows or
+  // groups that are never used). The LDS copy keeps the offset sd / bd of
+  // the first scale / bias within its unit.
+  const uintptr_t sp = reinterpret_cast<uintptr_t>(scales + (int64_t)n0 * G);
+  const uintptr_t bp = reinterpret_cast<uintptr_t>(biases + (int64_t)n0 * G);
+  const uint32_t sd = sp & 15, bd = bp & 15;
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(reinterpret_cast<const void*>(sp - sd),
+                                              (sd + rows * G * 2 + 15) & ~15u);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(reinterpret_cast<const void*>(bp - bd),
+                                              (bd + rows * G * 2 + 15) & ~15u);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+  const uint32_t wbase = n * row_bytes;
+  const int sbun = (15 + 32 * G + 15) >> 4;   // 16-byte units per array
+  uint4* ss4 = smem4 + (((size_t)M * ldx + 7) >> 3);
+  uint4* bs4 = ss4 + sbun;
+  const uint8_t* ssb = reinterpret_cast<const uint8_t*>(ss4) + sd;
+  const uint8_t* bsb = reinterpret_cast<const uint8_t*>(bs4) + bd;
+
+  // ---- x loads first (the weight loads queue behind them): 16-byte units
+  // u = tid + 1024 i for i < xu
+  const int xrow_units = K >> 3, xunits = M * xrow_units;
+  uint4 xl[kMvMaxXu];
+  uint32_t xoff[kMvMaxXu];
+#pragma unroll
+  for (int i = 0; i < kMvMaxXu; i++) {
+    const int u = tid + kMvThreads * i;
+    xoff[i] = u < xunits ? (uint32_t)u * 16 : kOob;
+  }
+#pragma unroll
+  for (int i = 0; i < kMvMaxXu; i++) {
+    if (i < xu) {
+      const u32x4_t v =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], 0, 0));
+      xl[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  }
+  // scale and bias units (rows past N read zero), sbu per thread
+  uint4 sl[kMvMaxSb], bl[kMvMaxSb];
+  uint32_t soff[kMvMaxSb];
+#pragma unroll
+  for (int i = 0; i < kMvMaxSb; i++) {
+    const int u = tid + kMvThreads * i;
+    soff[i] = u < sbun ? (uint32_t)u * 16 : kOob;
+  }
+#pragma unroll
+  for (int i = 0; i < kMvMaxSb; i++) {
+    if (i < sbu) {
+      const u32x4_t v =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, soff[i], 0, 0));
+      const u32x4_t w =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(br, soff[i], 0, 0));
+      sl[i] = make_uint4(v.x, v.y, v.z, v.w);
+      bl[i] = make_uint4(w.x, w.y, w.z, w.w);
+    }
+  }
+  load_fence();
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint32_t wv[DEPTH][BITS];
+
+  auto issue = [&](int j, int d) QMM_INLINE {
+    const int c = 4 * (wave + kMvWaves * j) + g;
+    // kOob when c >= nch, else 0 (a mask, not a select: the compiler would
+    // turn a select of two offsets into a branch around two loads)
+    const uint32_t oob = (uint32_t)((nch - 1 - c) >> 31) & kOob;
+    load_wchunk_buf<BITS>(wr, (wbase + c * (4 * BITS)) | oob, wv[d]);
+  };
+
+#pragma unroll
+  for (int d = 0; d < DEPTH; d++) {
+    issue(d, d);
+    load_fence();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- x, scales and biases into LDS (waits for those loads only: they
+  // were issued first)
+#pragma unroll
+  for (int i = 0; i < kMvMaxXu; i++) {
+    const int u = tid + kMvThreads * i;
+    if (i < xu && u < xunits) {
+      const int m = u / xrow_units, kk = (u - m * xrow_units) * 8;
+      *reinterpret_cast<uint4*>(xs + m * ldx + kk) = xl[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMvMaxSb; i++) {
+    const int u = tid + kMvThreads * i;
+    if (i < sbu && u < sbun) {
+      ss4[u] = sl[i];
+      bs4[u] = bl[i];
+    }
+  }
+  __syncthreads();
+
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int j, int d) QMM_INLINE {
+    // A fragments: lane (m, g) = (n, g) takes 8 elements of row m of x
+    // (rows m >= M stay zero); the chunk is clamped into the row (a chunk
+    // past the end has zero weights)
+    // (scale and bias are zeroed too: the chunk's codes read zero, and
+    // s*0 + b must be 0 as well)
+    const int c = 4 * (wave + kMvWaves * j) + g;
+    const int cx = c < nch ? c : nch - 1;
+    const uint32_t keep = ~(uint32_t)((nch - 1 - c) >> 31);   // 0 past the row end
+    const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
+    const uint32_t s2 = (*reinterpret_cast<const uint16_t*>(ssb + gi) * 0x10001u) & keep;
+    const uint32_t b2 = (*reinterpret_cast<const uint16_t*>(bsb + gi) * 0x10001u) & keep;
+    uint4 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) a[i] = make_uint4(0, 0, 0, 0);
+    if (n < M) {
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + n * ldx + cx * 32);
+#pragma unroll
+      for (int i = 0; i < 4; i++) a[i] = xp[i];
+    }
+    uint32_t bf[16];
+    [&]<int... C>(std::integer_sequence<int, C...>) QMM_INLINE {
+      (dequant_piece_f16_pk<BITS, C * piece_codes<BITS>(), piece_codes<BITS>()>(
+           wv[d], s2, b2, m2, F16::kMagic, bf),
+       ...);
+    }(std::make_integer_sequence<int, 32 / piece_codes<BITS>()>{});
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      acc = mfma16(F16{}, a[i], make_uint4(bf[4 * i], bf[4 * i + 1], bf[4 * i + 2], bf[4 * i + 3]),
+                   acc);
+  };
+
+  if constexpr (!RING) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) {
+      compute(d, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // at least one round runs (a wavefront without steps multiplies zeros),
+    // so that no branch precedes the loop
+    const int nr = nsw > DEPTH ? (nsw + DEPTH - 1) / DEPTH : 1;
+    int r = 0;
+    do {
+#pragma unroll
+      for (int d = 0; d < DEPTH; d++) {
+        compute(r * DEPTH + d, d);
+        __builtin_amdgcn_sched_barrier(0);
+        issue((r + 1) * DEPTH + d, d);
+        load_fence();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } while (++r < nr);
+  }
+
+  // ---- sum the 16 wavefront tiles (the buffer overlays x: barrier first);
+  // D[m][n] with m = 4*(lane/16) + e
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; e++) red[(wave * 64 + lane) * 4 + e] = acc[e];
+  __syncthreads();
+  if (tid < 256) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMvWaves; w++) v += red[w * 256 + tid];
+    const int ln = tid >> 2, e = tid & 3;
+    const int m = 4 * (ln >> 4) + e, col = n0 + (ln & 15);
+    if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(F16{}, v);
+  }
+}
+
+template <int BITS, int DEPTH, bool RING>
+hipError_t launch_depth(const void* x, const uint32_t* wq, const void* s, const void* b, int M,
+                        int N, int K, int gs, void* y, hipStream_t st) {
+  const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
+  const int xu = (M * (K / 8) + kMvThreads - 1) / kMvThreads;
+  const int sbu = ((15 + 32 * (K / gs) + 15) / 16 + kMvThreads - 1) / kMvThreads;
+  hipLaunchKernelGGL((qmv_mfma_kernel<BITS, DEPTH, RING>), dim3((N + 15) / 16), dim3(kMvThreads),
+                     qmv_mfma_lds(M, K, gs), st, static_cast<const uint16_t*>(x),
+                     reinterpret_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(s),
+                     static_cast<const uint16_t*>(b), static_cast<uint16_t*>(y), M, N, K,
+                     ilog2(gs), m2, xu, sbu);
+  return hipGetLastError();
+}
+
+// one round when every wavefront has at most 4 steps (K <= 8192), else a
+// ring of 3 steps
+template <int BITS>
+hipError_t launch_bits(const void* x, const uint32_t* wq, const void* s, const void* b, int M,
+                       int N, int K, int gs, void* y, hipStream_t st) {
+  const int nsteps = (K / 32 + 3) / 4;
+  const int nsw = (nsteps + kMvWaves - 1) / kMvWaves;
+  if (nsw <= 1) return launch_depth<BITS, 1, false>(x, wq, s, b, M, N, K, gs, y, st);
+  if (nsw <= 2) return launch_depth<BITS, 2, false>(x, wq, s, b, M, N, K, gs, y, st);
+  if (nsw <= 4) return launch_depth<BITS, 4, false>(x, wq, s, b, M, N, K, gs, y, st);
+  return launch_depth<BITS, 3, true>(x, wq, s, b, M, N, K, gs, y, st);
+}
+
+}  // namespace
+
+// LDS of the GEMV kernel: x rows plus padding and the 16 rows of scales and
+// biases, or the reduction buffer if larger
+size_t qmv_mfma_lds(int64_t M, int64_t K, int gs) {
+  const size_t xb = (((size_t)M * (K + 8) + 7) & ~(size_t)7) * 2;
+  const size_t sb = (size_t)2 * 16 * ((15 + 32 * (K / gs) + 15) / 16);
+  const size_t rb = (size_t)kMvThreads * 4 * 4;
+  return xb + sb > rb ? xb + sb : rb;
+}
+
+hipError_t launch_qmv_mfma(int bits, int gs, const void* x, const uint32_t* wq, const void* s,
+                           const void* b, int64_t M, int64_t N, int64_t K, void* y,
+                           hipStream_t st) {
+  switch (bits) {
+    case 2: return launch_bits<2>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 3: return launch_bits<3>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 4: return launch_bits<4>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 5: return launch_bits<5>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 6: return launch_bits<6>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    default: return launch_bits<8>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+  }
+}
+
+}  // namespace qmm

@@ -1,0 +1,43 @@
+// Arguments of the MFMA tile kernels, shared by the host dispatch (qmm.hip)
+// and the translation units that instantiate the kernels (tile_*.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+struct GemmArgs {
+  uint32_t magic;    // magic-number pattern of the element type (f16 path)
+  const uint16_t* x;
+  const uint8_t* wq;
+  const uint16_t* s;
+  const uint16_t* b;
+  uint16_t* y;
+  int M, N, K;       // K: packed row length in codes (K_pad for conv)
+  int gs_log2;
+  int64_t ldy;       // row stride of y in elements
+  // implicit im2col (conv only)
+  int H, W, C, OH, OW, kh, kw, sh, sw, ph, pw, Cg, Og, K_true;
+  // split K (tile kernel only): blockIdx.y takes K steps [y*ksteps,
+  // (y+1)*ksteps) and, with ksplit > 1, writes fp32 partial sums to the
+  // split-K workspace ws ([split][M][ldy], kSplitWsFloats floats) instead of y
+  int ksplit, ksteps;
+  float* ws;
+};
+
+// Split-K workspace size: [split][M][ldy] fp32 partial sums, library-owned
+// (a static device array of the host dispatch, passed to the kernels as ws).
+constexpr int64_t kSplitWsFloats = (int64_t)16 << 20;   // 64 MiB
+constexpr int kKtabMax = 4096;      // conv k-unit table entries (K_pad <= 32768)
+
+// Tile kernel launchers, one translation unit each (they compile in
+// parallel): plain GEMM and convolution, f16 and bf16. dma selects the
+// buffer-load kernel for convolutions (else the gather kernel).
+hipError_t launch_tile_gemm_f16(int bits, const GemmArgs& a, hipStream_t st);
+hipError_t launch_tile_gemm_bf16(int bits, const GemmArgs& a, hipStream_t st);
+hipError_t launch_tile_conv_f16(int bits, const GemmArgs& a, int groups, bool dma,
+                                hipStream_t st);
+hipError_t launch_tile_conv_bf16(int bits, const GemmArgs& a, int groups, bool dma,
+                                 hipStream_t st);
+
+}  // namespace qmm

@@ -117,6 +117,43 @@ def test_qmv_edge_shapes(orc, N, K):
     _run_mm(Q.qmv, orc, "bf16", 2, N, K, gs, 8, seed=N)
 
 
+@pytest.mark.parametrize("M,N,K,gs,bits", [
+    (3, 17, 352, 32, 4),        # one ragged row block, K % 128 == 96: partial steps
+    (16, 200, 4160, 64, 4),     # 33 steps: one round of 4 with empty slots
+    (5, 300, 2080, 32, 3),      # one round of 2
+    (12, 64, 6144, 64, 5),
+    (9, 96, 2048, 128, 6),      # one step per wavefront
+    (7, 40, 4096, 32, 8),
+    (4, 130, 11008, 128, 2),    # ring of 3 steps, uneven steps per wavefront
+    (1, 4096, 8704, 64, 4),     # M = 1 on the MFMA GEMV: long rows, wide layer
+    (2, 4100, 12288, 64, 4),    # ring with whole rounds, ragged N
+])
+def test_qmv_mfma(orc, M, N, K, gs, bits):
+    """The MFMA GEMV (f16, up to 16 rows of x), through qmv and qmm_t."""
+    _run_mm(Q.qmv, orc, "f16", M, N, K, gs, bits, seed=K + M)
+    _run_mm(Q.qmm_t, orc, "f16", M, N, K, gs, bits, seed=K + M + 1)
+
+
+def test_qmv_mfma_unaligned_scales(orc):
+    """Scales and biases only 2-byte aligned (views at an odd element offset):
+    the MFMA GEMV reads them as aligned 16-byte units around the block."""
+    code = orc_code(orc, "f16")
+    M, N, K, gs, bits = 5, 70, 1024, 32, 4
+    x = synth.normal((M, K), seed=3, dt="f16")
+    w = synth.normal((N, K), seed=4, dt="f16")
+    wq, s, b = orc.quantize(w, code, gs, bits)
+    yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
+    sd, bd = to_dev(s, "f16"), to_dev(b, "f16")
+    s_big = torch.zeros(sd.numel() + 1, dtype=sd.dtype, device=sd.device)
+    b_big = torch.zeros(bd.numel() + 3, dtype=bd.dtype, device=bd.device)
+    s_big[1:].copy_(sd.reshape(-1))
+    b_big[3:].copy_(bd.reshape(-1))
+    y = Q.qmv(to_dev(x, "f16"), bytes_to_words_dev(wq), s_big[1:].view(sd.shape),
+              b_big[3:].view(bd.shape), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, "f16", "qmv unaligned scales")
+
+
 def test_qmv_max_k(orc):
     """The largest K the streaming kernel accepts (f16 4-bit, g32)."""
     _run_mm(Q.qmv, orc, "f16", 1, 3, 29120, 32, 4, seed=3)
@@ -155,6 +192,24 @@ def test_qmm_t_split_k(orc, M, N, K, gs, bits):
     library's workspace, then a reduction)."""
     _run_mm(Q.qmm_t, orc, "f16", M, N, K, gs, bits, seed=K)
     _run_mm(Q.qmm_t, orc, "bf16", M, N, K, gs, bits, seed=K + 1)
+
+
+@pytest.mark.parametrize("M,N,K,gs,bits", [
+    (2, 200, 384, 64, 4),       # one split, ragged N
+    (9, 130, 1088, 32, 4),      # K % 64 == 0, 17 steps over splits
+    (17, 300, 2080, 32, 2),     # K % 64 == 32
+    (32, 256, 4096, 64, 8),
+    (24, 96, 1536, 128, 3),
+    (31, 136, 3072, 64, 5),
+    (20, 64, 2048, 128, 6),
+])
+def test_qmm_t_skinny(orc, M, N, K, gs, bits):
+    """At most 32 rows above the crossover: 32-row tiles, K split over
+    workgroups when the output has few tiles."""
+    M = max(M, Q.crossover_m(bits, torch.float16))
+    _run_mm(Q.qmm_t, orc, "f16", M, N, K, gs, bits, seed=K + M)
+    M = max(M, Q.crossover_m(bits, torch.bfloat16))
+    _run_mm(Q.qmm_t, orc, "bf16", M, N, K, gs, bits, seed=K + M + 1)
 
 
 def test_qmm_t_split_k_back_to_back(orc):
