@@ -206,17 +206,52 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "qmv_decode_4096x4096_4bit_g64_f16_traffic.md")
+
+
 def measured_traffic():
     """HBM bytes per launch of the headline kernel from the committed rocprofv3
-    PMC summary, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", "qmv_decode_4bit_g64_f16_traffic.json")
-    if not os.path.exists(p):
+    PMC summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
+    size), if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
         return None
-    with open(p) as fh:
-        d = json.load(fh)
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    vals = {}
+    with open(TRAFFIC_SUMMARY) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe(torch, Q, synth, launches=20):
+    """For rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs: plain device copies
+    of 256 MiB between distinct buffers (2 GiB in all, so no copy reads data
+    a cache still holds: the counter calibration, 256 MiB read and 256 MiB
+    written per dispatch), then `launches` headline GEMV calls, each on its
+    own copy of W."""
+    bufs = [torch.full((64 << 20,), float(i), dtype=torch.float32, device="cuda")
+            for i in range(8)]
+    torch.cuda.synchronize()
+    for i in range(4):
+        bufs[4 + i].copy_(bufs[i])
+    torch.cuda.synchronize()
+    del bufs
+    layer = make_layer(torch, Q, synth, "f16", 4096, 4096, 64, 4, 1)
+    wqs, ss, bs, P = pooled(torch, layer)
+    from tests.helpers import to_dev
+    x = to_dev(synth.normal((1, 4096), seed=0), "f16")
+    y = torch.empty((1, 4096), dtype=x.dtype, device=x.device)
+    for i in range(launches):
+        j = i % P
+        Q.qmv(x, wqs[j], ss[j], bs[j], 64, 4, out=y)
+    torch.cuda.synchronize()
+    log(f"traffic probe: copy 4 x 256 MiB, qmv x {launches}")
 
 
 def main():
@@ -227,6 +262,10 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline decode GEMV (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run the PMC calibration copy and headline launches, print nothing else")
+    ap.add_argument("--mfma-only", action="store_true",
+                    help="time only the MFMA tile rows (chained 4-bit layers, conv), for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the path is measured on a single "
@@ -239,8 +278,17 @@ def main():
     from group_wise_affine_amd import synth
     torch.cuda.set_device(0)
     Q.lib()
+    if args.traffic_probe:
+        traffic_probe(torch, Q, synth)
+        return
     timer = Timer(torch)
     K_, W_ = args.steps, args.warmup
+    if args.mfma_only:
+        r = {"chained_bits4": bench_chained(torch, Q, synth, timer, 4, 10, 2),
+             "conv_groups1": bench_conv(torch, Q, synth, timer, 1, 50, 5),
+             "conv_groups2": bench_conv(torch, Q, synth, timer, 2, 50, 5)}
+        print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r.items()}))
+        return
 
     log("headline: qmv 4-bit g64 f16 M=1 4096x4096")
     torch.cuda.synchronize()

@@ -20,12 +20,12 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
                       int64_t M, int64_t N, int64_t K, void* y,
                       hipStream_t st);
 
-// GEMV on the matrix cores, f16, 1 <= M <= kQmvMfmaMaxM, K < kQmvMfmaMaxK
+// GEMV on the matrix cores, f16 / bf16, 1 <= M <= kQmvMfmaMaxM, K < kQmvMfmaMaxK
 // (byte offsets of its buffer loads stay below 2^31), x[0:M] small enough
 // for LDS (qmv_mfma_fits).
 constexpr int kQmvMfmaMaxM = 16;
 constexpr int64_t kQmvMfmaMaxK = (int64_t)1 << 25;
-constexpr size_t kQmvMfmaMaxLds = 128 * 1024;
+constexpr size_t kQmvMfmaMaxLds = 160 * 1024;
 size_t qmv_mfma_lds(int64_t M, int64_t K, int gs);
 inline bool qmv_mfma_fits(int64_t M, int64_t K, int gs) {
   // the workgroup's 1024 threads copy x with at most 8 16-byte loads each,
@@ -34,7 +34,7 @@ inline bool qmv_mfma_fits(int64_t M, int64_t K, int gs) {
          qmv_mfma_lds(M, K, gs) <= kQmvMfmaMaxLds && M * (K / 8) <= 8 * 1024 &&
          (15 + 32 * (K / gs) + 15) / 16 <= 2 * 1024;
 }
-hipError_t launch_qmv_mfma(int bits, int gs, const void* x, const uint32_t* wq,
+hipError_t launch_qmv_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                            const void* s, const void* b, int64_t M, int64_t N,
                            int64_t K, void* y, hipStream_t st);
 
@@ -59,11 +59,13 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
                              hipStream_t st);
 
 // Kernel choice for y = x . dequant(W)^T (measured on MI355X, 4096-wide
-// layers): the MFMA GEMV for f16 from M = 3 up to 16 rows when x fits in
-// LDS, and for M <= 2 when K > 8192 on N >= 4096 (long rows make the
-// streaming GEMV's per-row passes slow); the streaming dot2 GEMV for a few
-// rows otherwise; the MFMA tile kernel for the rest. qmv never takes the
-// tile kernel (kRouteNone when neither GEMV accepts the shape).
+// layers): the MFMA GEMV up to 16 rows when x fits in LDS, for f16 from
+// M = 3 (and M <= 2 when K > 8192 on N >= 4096: long rows make the
+// streaming GEMV's passes slow), for bf16 from M = 8 (4 when K > 4096; any
+// M for 8-bit codes); the
+// streaming dot2 GEMV for a few rows otherwise; the MFMA tile kernel for the
+// rest. qmv never takes the tile kernel (kRouteNone when neither GEMV
+// accepts the shape).
 enum Route { kRouteNone = 0, kRouteQmv = 1, kRouteQmvMfma = 2, kRouteTile = 3 };
 Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allow_tile);
 

@@ -87,12 +87,12 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
                  : launch_tile_conv_bf16(bits, a, cg.groups, dma, st);
 }
 
-// The GEMV kernels' share of small M (see route()): f16 up to 16 rows on
-// the MFMA GEMV; bf16 on the streaming GEMV, whose cost grows with M (one
-// pass over W per 4 rows at K = 4096, fp32 arithmetic for 8-bit codes).
+// The GEMV kernels' share of small M (see route()): up to 16 rows on the
+// MFMA GEMV when x fits in LDS (K <= 4096 at 16 rows).
 int crossover_m(int bits, int dt) {
-  if (dt == 0) return kQmvMfmaMaxM + 1;
-  return bits == 8 ? 2 : 16;
+  (void)bits;
+  (void)dt;
+  return kQmvMfmaMaxM + 1;
 }
 
 int64_t qmv_max_k(int bits, int dt) {
@@ -102,13 +102,18 @@ int64_t qmv_max_k(int bits, int dt) {
 
 Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allow_tile) {
   const bool dot2_ok = K <= qmv_max_k(bits, dt);
-  const bool mfma_ok = dt == 0 && qmv_mfma_fits(M, K, gs);
-  if (mfma_ok && (M >= 3 || (K > 8192 && N >= 4096) || !dot2_ok)) return kRouteQmvMfma;
+  const bool mfma_ok = qmv_mfma_fits(M, K, gs);
+  if (dt == 0 && mfma_ok && (M >= 3 || (K > 8192 && N >= 4096) || !dot2_ok)) return kRouteQmvMfma;
+  // bf16 dequantizes in fp32 and multiplies hi and lo halves: worth it from
+  // 8 rows (4 on rows longer than 4096, where the streaming GEMV makes more
+  // passes), and always for 8-bit codes, which the streaming GEMV handles in
+  // fp32
+  if (dt == 1 && mfma_ok && (M >= 8 || (M >= 4 && K > 4096) || bits == 8 || !dot2_ok))
+    return kRouteQmvMfma;
   if (!allow_tile) return dot2_ok ? kRouteQmv : kRouteNone;
-  int mx = crossover_m(bits, dt);
-  if (dt == 0) mx = 3;                  // past this the MFMA GEMV or the tile kernel
-  else if (K > 4096 && bits != 8) mx = 4;
-  if (M < mx && dot2_ok) return kRouteQmv;
+  // the MFMA GEMV does not take the shape: a few rows on the streaming GEMV
+  // (one pass over W per 4 rows at K = 4096), the rest on the tile kernel
+  if (M < (dt == 0 ? 4 : 8) && dot2_ok) return kRouteQmv;
   return kRouteTile;
 }
 

@@ -346,20 +346,22 @@ static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
                             const void* b, int M, int N, int K, int gs,
                             void* y, hipStream_t st) {
   const int nch = K / 32;
-  // Pick the lane shape: the chunks of a row must fit in 64 lanes x CPL; prefer
-  // at least 256 workgroups (one per CU), then the most work per lane.
+  // Pick the lane shape: 4 chunks x 2 rows per lane while that gives at
+  // least 256 workgroups (one per CU; measured best at M = 1 for 4096- and
+  // 11008-wide layers, also when a row needs several batches), else the
+  // shape with the most workgroups.
+  static constexpr int kOrder[] = {2, 1, 3, 0};
   int best = -1;
-  int64_t best_key = -1;
-  for (int i = 0; i < 4; i++) {
+  int64_t best_blocks = -1;
+  for (int oi = 0; oi < 4; oi++) {
+    const int i = kOrder[oi];
     const Shape sh = kShapes[i];
     const int tpr = tpr_for(nch, sh.cpl);
     const int rows_per_block = kWWaves * (64 / tpr) * sh.r;
     const int64_t blocks = (int64_t)((N + rows_per_block - 1) / rows_per_block) *
                            ((M + MB - 1) / MB);
-    // a shape whose batch covers the row beats one that needs several
-    const int work = (tpr * sh.cpl >= nch ? 64 : 0) + sh.cpl * sh.r;
-    const int64_t key = (blocks >= 256 ? (1 << 20) : blocks * 64) + work;
-    if (key > best_key) { best_key = key; best = i; }
+    if (blocks >= 256) { best = i; break; }
+    if (blocks > best_blocks) { best_blocks = blocks; best = i; }
   }
   if (best < 0) best = 3;
   const Shape sh = kShapes[best];
@@ -408,7 +410,7 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
                       int64_t M, int64_t N, int64_t K, void* y,
                       hipStream_t st) {
   if (route(dt, bits, gs, M, N, K, false) == kRouteQmvMfma)
-    return launch_qmv_mfma(bits, gs, x, wq, s, b, M, N, K, y, st);
+    return launch_qmv_mfma(dt, bits, gs, x, wq, s, b, M, N, K, y, st);
   if (dt == 0)
     return launch_bits<F16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
   return launch_bits<BF16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);

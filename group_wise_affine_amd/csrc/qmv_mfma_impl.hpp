@@ -1,4 +1,5 @@
-// Quantized GEMV on the matrix cores for a few rows of x (M <= 16), f16:
+// Quantized GEMV on the matrix cores for a few rows of x (M <= 16), f16 and
+// bf16 (kernel template; instantiated by qmv_mfma_f16.hip, qmv_mfma_bf16.hip):
 //   y[m, n] = sum_k x[m, k] * (s[n, g(k)] * q[n, k] + b[n, g(k)]),
 // the product the quantized matmul computes (mlx affine_qmv / qmm_t, "Add the
 // 3bit packed qmm_t"), with fp32 accumulation as the Metal qmv does (mlx PR
@@ -10,10 +11,13 @@
 //    takes steps w, w+16, w+32, ... so that the 16 wavefronts stream one
 //    contiguous run of every row at a time.
 //  * Lane (n, g) = (lane % 16, lane / 16) loads chunk g of the step of row n
-//    and dequantizes it (magic pairs, packed f16 FMAs, one rounding of s*q+b)
-//    into four 8-code B fragments of v_mfma_f32_16x16x32_f16: MFMA i takes
-//    codes 8i..8i+7 of the four chunks, so A lane (m, g) holds the matching
-//    8 elements of row m of x in natural order (rows m >= M stay zero).
+//    and dequantizes it into four 8-code B fragments of
+//    v_mfma_f32_16x16x32_{f16,bf16}: MFMA i takes codes 8i..8i+7 of the four
+//    chunks, so A lane (m, g) holds the matching 8 elements of row m of x in
+//    natural order (rows m >= M stay zero). f16: magic pairs and packed f16
+//    FMAs, one rounding of s*q+b. bf16: s*q+b in fp32 split into
+//    hi = bf16(w) and lo = bf16(w - hi), both multiplied (a single bf16
+//    rounding of the weights would cost ~1e-3 relative error).
 //  * The workgroup copies x[0:M] and the scales and biases of its 16 rows
 //    into LDS once, with coalesced loads issued ahead of the weight loads; A
 //    fragments, scales and biases are read from there. The number of vector
@@ -28,6 +32,7 @@
 //    Byte offsets stay below 2^31 for K < kQmvMfmaMaxK; x[0:M] must fit in
 //    LDS (qmv_mfma_fits).
 //  * The 16 partial 16x16 tiles are summed through LDS and written as f16.
+#pragma once
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_common.hpp"
@@ -75,7 +80,7 @@ __device__ __forceinline__ void load_wchunk_buf(__amdgpu_buffer_rsrc_t r, uint32
 // RING = false the kernel runs one round (every wavefront has at most DEPTH
 // steps); with RING = true slot d is refilled with the step one round later
 // right after it is consumed.
-template <int BITS, int DEPTH, bool RING>
+template <class T, int BITS, int DEPTH, bool RING>
 __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -213,8 +218,8 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const int cx = c < nch ? c : nch - 1;
     const uint32_t keep = ~(uint32_t)((nch - 1 - c) >> 31);   // 0 past the row end
     const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
-    const uint32_t s2 = (*reinterpret_cast<const uint16_t*>(ssb + gi) * 0x10001u) & keep;
-    const uint32_t b2 = (*reinterpret_cast<const uint16_t*>(bsb + gi) * 0x10001u) & keep;
+    const uint32_t sh = *reinterpret_cast<const uint16_t*>(ssb + gi) & keep;
+    const uint32_t bh = *reinterpret_cast<const uint16_t*>(bsb + gi) & keep;
     uint4 a[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) a[i] = make_uint4(0, 0, 0, 0);
@@ -223,16 +228,32 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; i++) a[i] = xp[i];
     }
-    uint32_t bf[16];
-    [&]<int... C>(std::integer_sequence<int, C...>) QMM_INLINE {
-      (dequant_piece_f16_pk<BITS, C * piece_codes<BITS>(), piece_codes<BITS>()>(
-           wv[d], s2, b2, m2, F16::kMagic, bf),
-       ...);
-    }(std::make_integer_sequence<int, 32 / piece_codes<BITS>()>{});
+    if constexpr (__is_same(T, F16)) {
+      uint32_t bf[16];
+      [&]<int... C>(std::integer_sequence<int, C...>) QMM_INLINE {
+        (dequant_piece_f16_pk<BITS, C * piece_codes<BITS>(), piece_codes<BITS>()>(
+             wv[d], sh * 0x10001u, bh * 0x10001u, m2, F16::kMagic, bf),
+         ...);
+      }(std::make_integer_sequence<int, 32 / piece_codes<BITS>()>{});
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      acc = mfma16(F16{}, a[i], make_uint4(bf[4 * i], bf[4 * i + 1], bf[4 * i + 2], bf[4 * i + 3]),
-                   acc);
+      for (int i = 0; i < 4; i++)
+        acc = mfma16(F16{}, a[i],
+                     make_uint4(bf[4 * i], bf[4 * i + 1], bf[4 * i + 2], bf[4 * i + 3]), acc);
+    } else {
+      const float sf = to_f32(BF16{}, (uint16_t)sh), bfl = to_f32(BF16{}, (uint16_t)bh);
+      uint32_t hi[16], lo[16];
+      dequant_piece_bf16<BITS, 0>(wv[d], sf, bfl, hi, lo);
+      dequant_piece_bf16<BITS, 8>(wv[d], sf, bfl, hi, lo);
+      dequant_piece_bf16<BITS, 16>(wv[d], sf, bfl, hi, lo);
+      dequant_piece_bf16<BITS, 24>(wv[d], sf, bfl, hi, lo);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        acc = mfma16(BF16{}, a[i],
+                     make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]), acc);
+        acc = mfma16(BF16{}, a[i],
+                     make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]), acc);
+      }
+    }
   };
 
   if constexpr (!RING) {
@@ -270,17 +291,17 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     for (int w = 0; w < kMvWaves; w++) v += red[w * 256 + tid];
     const int ln = tid >> 2, e = tid & 3;
     const int m = 4 * (ln >> 4) + e, col = n0 + (ln & 15);
-    if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(F16{}, v);
+    if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, v);
   }
 }
 
-template <int BITS, int DEPTH, bool RING>
+template <class T, int BITS, int DEPTH, bool RING>
 hipError_t launch_depth(const void* x, const uint32_t* wq, const void* s, const void* b, int M,
                         int N, int K, int gs, void* y, hipStream_t st) {
   const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
   const int xu = (M * (K / 8) + kMvThreads - 1) / kMvThreads;
   const int sbu = ((15 + 32 * (K / gs) + 15) / 16 + kMvThreads - 1) / kMvThreads;
-  hipLaunchKernelGGL((qmv_mfma_kernel<BITS, DEPTH, RING>), dim3((N + 15) / 16), dim3(kMvThreads),
+  hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING>), dim3((N + 15) / 16), dim3(kMvThreads),
                      qmv_mfma_lds(M, K, gs), st, static_cast<const uint16_t*>(x),
                      reinterpret_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(s),
                      static_cast<const uint16_t*>(b), static_cast<uint16_t*>(y), M, N, K,
@@ -290,39 +311,31 @@ hipError_t launch_depth(const void* x, const uint32_t* wq, const void* s, const 
 
 // one round when every wavefront has at most 4 steps (K <= 8192), else a
 // ring of 3 steps
-template <int BITS>
+template <class T, int BITS>
 hipError_t launch_bits(const void* x, const uint32_t* wq, const void* s, const void* b, int M,
                        int N, int K, int gs, void* y, hipStream_t st) {
   const int nsteps = (K / 32 + 3) / 4;
   const int nsw = (nsteps + kMvWaves - 1) / kMvWaves;
-  if (nsw <= 1) return launch_depth<BITS, 1, false>(x, wq, s, b, M, N, K, gs, y, st);
-  if (nsw <= 2) return launch_depth<BITS, 2, false>(x, wq, s, b, M, N, K, gs, y, st);
-  if (nsw <= 4) return launch_depth<BITS, 4, false>(x, wq, s, b, M, N, K, gs, y, st);
-  return launch_depth<BITS, 3, true>(x, wq, s, b, M, N, K, gs, y, st);
+  if (nsw <= 1) return launch_depth<T, BITS, 1, false>(x, wq, s, b, M, N, K, gs, y, st);
+  if (nsw <= 2) return launch_depth<T, BITS, 2, false>(x, wq, s, b, M, N, K, gs, y, st);
+  if (nsw <= 4) return launch_depth<T, BITS, 4, false>(x, wq, s, b, M, N, K, gs, y, st);
+  return launch_depth<T, BITS, 3, true>(x, wq, s, b, M, N, K, gs, y, st);
 }
 
-}  // namespace
-
-// LDS of the GEMV kernel: x rows plus padding and the 16 rows of scales and
-// biases, or the reduction buffer if larger
-size_t qmv_mfma_lds(int64_t M, int64_t K, int gs) {
-  const size_t xb = (((size_t)M * (K + 8) + 7) & ~(size_t)7) * 2;
-  const size_t sb = (size_t)2 * 16 * ((15 + 32 * (K / gs) + 15) / 16);
-  const size_t rb = (size_t)kMvThreads * 4 * 4;
-  return xb + sb > rb ? xb + sb : rb;
-}
-
-hipError_t launch_qmv_mfma(int bits, int gs, const void* x, const uint32_t* wq, const void* s,
-                           const void* b, int64_t M, int64_t N, int64_t K, void* y,
-                           hipStream_t st) {
+// all widths, one element type
+template <class T>
+hipError_t launch_qmv_mfma_t(int bits, int gs, const void* x, const uint32_t* wq, const void* s,
+                             const void* b, int64_t M, int64_t N, int64_t K, void* y,
+                             hipStream_t st) {
   switch (bits) {
-    case 2: return launch_bits<2>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 3: return launch_bits<3>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 4: return launch_bits<4>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 5: return launch_bits<5>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 6: return launch_bits<6>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    default: return launch_bits<8>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 2: return launch_bits<T, 2>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 3: return launch_bits<T, 3>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 4: return launch_bits<T, 4>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 5: return launch_bits<T, 5>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 6: return launch_bits<T, 6>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    default: return launch_bits<T, 8>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
   }
 }
 
+}  // namespace
 }  // namespace qmm

@@ -39,6 +39,12 @@
  *    the caller's next synchronization.
  *  - Supported: bits in {2,3,4,5,6,8}; group_size in {32,64,128};
  *    K a positive multiple of group_size.
+ *  - qmm_t and qconv2d_nhwc may split K over workgroups and keep fp32
+ *    partial sums in a library-owned workspace: one static 64 MiB device
+ *    array per GPU (nothing is allocated per call). Calls that run
+ *    concurrently on one GPU (different streams, or different host threads
+ *    without ordering) share it and must not overlap; calls queued on one
+ *    stream are ordered and safe.
  */
 #ifndef LIBQMM_H
 #define LIBQMM_H
@@ -95,9 +101,10 @@ qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
 
 /*
  * y[M,N] = x[M,K] . dequant(wq, scales, biases)[N,K]^T, fp32 accumulation,
- * y rounded to nearest even in dt (f16 or bf16). Routes small M to the
- * streaming GEMV (qmv) and larger M to the MFMA tile kernel; the crossover
- * is returned by qmm_crossover_m. (Source: mlx 1.0.0 CPU backend, _qmm_t;
+ * y rounded to nearest even in dt (f16 or bf16). Routes small M to the GEMV
+ * kernels of qmv (the MFMA GEMV up to 16 rows, the streaming GEMV for a
+ * few rows) and larger M to the MFMA tile kernel; the crossover is returned
+ * by qmm_crossover_m. (Source: mlx 1.0.0 CPU backend, _qmm_t;
  * the packed-quants compare, the qmv/qmm_t split in the Metal dispatch.)
  */
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
@@ -105,9 +112,11 @@ qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
                  int64_t K, int group_size, int bits, void* y, void* stream);
 
 /*
- * Same operation and arguments as qmm_t, always on the streaming GEMV, which
- * reads every packed weight from HBM once per 8 rows of x. Meant for M <= 16
- * (decode); correct for any M.
+ * Same operation and arguments as qmm_t, always on the GEMV kernels: the
+ * MFMA GEMV (up to 16 rows of x that fit in LDS; every packed weight read
+ * once) or the streaming GEMV (one pass over W per up to 4 rows of x).
+ * Meant for M <= 16 (decode); correct for any M. QMM_E_SHAPE when K exceeds
+ * both kernels' limits.
  */
 qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                const void* biases, qmm_dtype dt, int64_t M, int64_t N,
@@ -133,7 +142,11 @@ qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
                         int groups, qmm_dtype dt, int group_size, int bits,
                         void* y, void* stream);
 
-/* Smallest M for which qmm_t uses the MFMA tile kernel instead of qmv. */
+/*
+ * Smallest M for which qmm_t uses the MFMA tile kernel instead of the GEMV
+ * kernels, for layers whose rows of x fit the MFMA GEMV's LDS (K <= 4096 at
+ * 16 rows); longer rows leave the GEMV kernels earlier.
+ */
 int qmm_crossover_m(int bits, qmm_dtype dt);
 
 /* Message for the last non-OK status returned on the calling thread. */

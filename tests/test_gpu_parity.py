@@ -127,11 +127,14 @@ def test_qmv_edge_shapes(orc, N, K):
     (4, 130, 11008, 128, 2),    # ring of 3 steps, uneven steps per wavefront
     (1, 4096, 8704, 64, 4),     # M = 1 on the MFMA GEMV: long rows, wide layer
     (2, 4100, 12288, 64, 4),    # ring with whole rounds, ragged N
+    (6, 72, 9216, 32, 5),       # ring, 5-bit
+    (8, 40, 8704, 64, 8),       # ring, 8-bit
 ])
-def test_qmv_mfma(orc, M, N, K, gs, bits):
-    """The MFMA GEMV (f16, up to 16 rows of x), through qmv and qmm_t."""
-    _run_mm(Q.qmv, orc, "f16", M, N, K, gs, bits, seed=K + M)
-    _run_mm(Q.qmm_t, orc, "f16", M, N, K, gs, bits, seed=K + M + 1)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qmv_mfma(orc, dt, M, N, K, gs, bits):
+    """The MFMA GEMV (up to 16 rows of x), through qmv and qmm_t."""
+    _run_mm(Q.qmv, orc, dt, M, N, K, gs, bits, seed=K + M)
+    _run_mm(Q.qmm_t, orc, dt, M, N, K, gs, bits, seed=K + M + 1)
 
 
 def test_qmv_mfma_unaligned_scales(orc):
