@@ -726,7 +726,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // step (those without a W block of their own copy zeros into wjunk), so one
   // vmcnt value fits all. No branches: a stage of steps stays one block.
   constexpr int kDma = G::A_PER_WAVE + G::W_HI;   // copies per step and wavefront
-  auto issue_one = [&]<int S, int D>(int tt) QMM_INLINE {
+  // CHK = false: the caller guarantees that step tt lies inside K (whole
+  // 64-code steps), so the copies skip the range checks (plain GEMM)
+  auto issue_one = [&]<int S, int D, bool CHK>(int tt) QMM_INLINE {
     if constexpr (D < G::A_PER_WAVE) {
       constexpr int i = D;
       const int blk = 4 * i + wave;
@@ -741,9 +743,11 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
         const uint32_t off =
             (uint32_t)((((pix_b[i] + iy) * a.W + ix) * a.C + (int)(e & 0xffff)) * 2);
         dma_lds<16>(xr, xd, in ? off : kOob, 0);
-      } else {
+      } else if constexpr (CHK) {
         const bool ok = 64 * tt + xcol[i] < K;
         dma_lds<16>(xr, xd, ok ? xoff[i] : kOob, 128u * tt);
+      } else {
+        dma_lds<16>(xr, xd, xoff[i], 128u * tt);
       }
     } else {
       constexpr int i = D - G::A_PER_WAVE;
@@ -751,14 +755,15 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;
       const int blk = 4 * i + wave;
       const bool real = G::W_BLOCKS % 4 == 0 || blk < G::W_BLOCKS;
-      const bool ok = real && (int)wsoff + wuo[i] < row_bytes;
+      bool ok = real;
+      if constexpr (CHK) ok = ok && (int)wsoff + wuo[i] < row_bytes;
       dma_lds<WU>(wr, real ? (void*)(wd + blk * 64 * WU) : (void*)wjunk, ok ? woff[i] : kOob,
                   wsoff);
     }
   };
   auto issue = [&]<int S>(int tt) QMM_INLINE {
     [&]<int... D>(std::integer_sequence<int, D...>) QMM_INLINE {
-      (issue_one.template operator()<S, D>(tt), ...);
+      (issue_one.template operator()<S, D, true>(tt), ...);
     }(std::make_integer_sequence<int, kDma>{});
   };
   // end of a step: wait until only the youngest step of copies is in flight,
@@ -958,12 +963,12 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // stall on the address unit): copy d after MFMA 2d, the scale groups after
   // the last copy (the end-of-step vmcnt values count on that order)
   constexpr int kNGrp = kSL / kSGrp;
-  auto extras = [&]<int MM, int SD, bool kScales>(int tt, int js) QMM_INLINE {
+  auto extras = [&]<int MM, int SD, bool kScales, bool CHK>(int tt, int js) QMM_INLINE {
     [&]<int... D>(std::integer_sequence<int, D...>) QMM_INLINE {
       ([&]() QMM_INLINE {
          constexpr int slot = 2 * D < kM ? 2 * D : kM - 1;
          if constexpr (slot == MM) {
-           issue_one.template operator()<SD, D>(tt + 3);
+           issue_one.template operator()<SD, D, CHK>(tt + 3);
            __builtin_amdgcn_sched_barrier(0);
          }
        }(),
@@ -987,12 +992,13 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // one step body: MFMAs from af/bq[C] (x slot SC); the next step's state
   // (slot SN) is built between them, in a fixed order, with the copies of
   // step tt+3 (slot SD)
-  auto body = [&]<int C, int SC, int SN, int SD, bool kScales>(int tt, int js) QMM_INLINE {
+  auto body = [&]<int C, int SC, int SN, int SD, bool kScales, bool CHK>(int tt,
+                                                                         int js) QMM_INLINE {
     read_w.template operator()<SN>(tt + 1);
     __builtin_amdgcn_sched_barrier(0);
     [&]<int... M>(std::integer_sequence<int, M...>) QMM_INLINE {
       ((mfma_at.template operator()<M, C, SC, SN>(),
-        extras.template operator()<M, SD, kScales>(tt, js),
+        extras.template operator()<M, SD, kScales, CHK>(tt, js),
         slot_fill.template operator()<M, C, SN>()),
        ...);
     }(std::make_integer_sequence<int, kM>{});
@@ -1024,14 +1030,15 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // (built from slot tt % 4 during step tt-1) and builds bq[(tt+1) % 2] from
   // slot (tt+1) % 4; the copies of step tt+3 go to slot (tt+3) % 4, whose
   // last reads were made during step tt-2. Full stages run unguarded; only a
-  // last partial stage checks each step against nk.
-  auto stage = [&]<bool kFull>(int js) QMM_INLINE {
+  // last partial stage checks each step against nk. Stages whose copies
+  // (steps up to 8 js + 10) all lie inside K skip the copies' range checks.
+  auto stage = [&]<bool kFull, bool CHK>(int js) QMM_INLINE {
     [&]<int... U>(std::integer_sequence<int, U...>) QMM_INLINE {
       (([&]() QMM_INLINE {
          const int tt = kStageSteps * js + U;
          if (kFull || tt < t1) {
            if constexpr (U == 4) scale_store(js + 1);
-           body.template operator()<U % 2, U % 4, (U + 1) % 4, (U + 3) % 4, U == 1>(tt, js);
+           body.template operator()<U % 2, U % 4, (U + 1) % 4, (U + 3) % 4, U == 1, CHK>(tt, js);
 #pragma unroll
            for (int j = 0; j < FN; j++)
 #pragma unroll
@@ -1045,8 +1052,15 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     }(std::make_integer_sequence<int, kStageSteps>{});
   };
   const int n_full = (t1 - t0) / kStageSteps;
-  for (int js = js0; js < js0 + n_full; js++) stage.template operator()<true>(js);
-  if ((t1 - t0) % kStageSteps) stage.template operator()<false>(js0 + n_full);
+  int js = js0;
+  if constexpr (!CONV) {
+    const int kwhole = K >> 6;                 // whole 64-code steps
+    const int js_safe = kwhole > 10 ? (kwhole - 10 + kStageSteps - 1) / kStageSteps : 0;
+    const int js_u = js0 + n_full < js_safe ? js0 + n_full : js_safe;
+    for (; js < js_u; js++) stage.template operator()<true, false>(js);
+  }
+  for (; js < js0 + n_full; js++) stage.template operator()<true, true>(js);
+  if ((t1 - t0) % kStageSteps) stage.template operator()<false, true>(js0 + n_full);
 
   // ---- split K: fp32 partial sums straight from the accumulators (lane:
   // column 32j + lane%32, rows 8(r/4) + 4(lane/32) + r%4 of each 32x32 tile;
