@@ -1146,26 +1146,46 @@ static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
 }
 
 // y[m][c] = T(sum over splits of the fp32 partial sums), c < ncols, four
-// columns per thread
-template <class T>
+// columns per thread; SPLITS partial loads per thread are issued together
+template <class T, int SPLITS>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, uint16_t* y, int M,
-                                                            int ncols, int64_t ldy, int splits) {
+                                                            int ncols, int64_t ldy) {
   const int64_t quads = (int64_t)M * (ncols / 4);
   const int64_t plane = (int64_t)M * ldy;
   for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < quads; q += (int64_t)gridDim.x * 256) {
     const int m = (int)(q / (ncols / 4));
     const int c = (int)(q - (int64_t)m * (ncols / 4)) * 4;
     const float* p = ws + (int64_t)m * ldy + c;
-    float4 v = *reinterpret_cast<const float4*>(p);
-    for (int sp = 1; sp < splits; sp++) {
-      const float4 u = *reinterpret_cast<const float4*>(p + sp * plane);
-      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    float4 u[SPLITS];
+#pragma unroll
+    for (int sp = 0; sp < SPLITS; sp++) u[sp] = *reinterpret_cast<const float4*>(p + sp * plane);
+    float4 v = u[0];
+#pragma unroll
+    for (int sp = 1; sp < SPLITS; sp++) {
+      v.x += u[sp].x; v.y += u[sp].y; v.z += u[sp].z; v.w += u[sp].w;
     }
     uint2 o;
     o.x = (uint32_t)from_f32(T{}, v.x) | ((uint32_t)from_f32(T{}, v.y) << 16);
     o.y = (uint32_t)from_f32(T{}, v.z) | ((uint32_t)from_f32(T{}, v.w) << 16);
     *reinterpret_cast<uint2*>(y + (int64_t)m * ldy + c) = o;
   }
+}
+
+template <class T>
+hipError_t launch_splitk_reduce(const GemmArgs& a, int ncols, hipStream_t st) {
+  const int64_t quads = (int64_t)a.M * (ncols / 4);
+  const int blocks = (int)((quads + 255) / 256 < 2048 ? (quads + 255) / 256 : 2048);
+  const dim3 g(blocks), b(256);
+  switch (a.ksplit) {
+    case 2: hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+    case 3: hipLaunchKernelGGL((splitk_reduce_kernel<T, 3>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+    case 4: hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+    case 5: hipLaunchKernelGGL((splitk_reduce_kernel<T, 5>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+    case 6: hipLaunchKernelGGL((splitk_reduce_kernel<T, 6>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+    case 7: hipLaunchKernelGGL((splitk_reduce_kernel<T, 7>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+    default: hipLaunchKernelGGL((splitk_reduce_kernel<T, 8>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
+  }
+  return hipGetLastError();
 }
 
 // Split-K plan for the 128 x 128 tile kernel: as many splits as keep the
@@ -1199,12 +1219,7 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
                      dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
-  const int ncols = (int)a.ldy;    // every column of y (all conv groups)
-  const int64_t quads = (int64_t)a.M * (ncols / 4);
-  const int blocks = (int)((quads + 255) / 256 < 2048 ? (quads + 255) / 256 : 2048);
-  hipLaunchKernelGGL((splitk_reduce_kernel<T>), dim3(blocks), dim3(256), 0, st, a.ws, a.y, a.M,
-                     ncols, a.ldy, a.ksplit);
-  return hipGetLastError();
+  return launch_splitk_reduce<T>(a, (int)a.ldy, st);   // every column of y (all conv groups)
 }
 
 template <class T, int BITS, bool CONV, bool DMA>
@@ -1215,6 +1230,9 @@ static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
     if constexpr (!CONV) {
       if (a.M <= 32) return launch_dma_split<T, BITS, 32, 128, CONV>(a, groups, st);
     }
+    // 128-wide tiles that would leave more than half a tile of columns idle
+    // (e.g. 160-channel conv groups): 64 x 64 tiles
+    if (a.N % 128 != 0 && a.N % 128 < 64) return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
     if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
     int ks;
     if (splitk_plan(a, tiles128, &ks) > 1)
