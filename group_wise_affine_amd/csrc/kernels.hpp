@@ -25,13 +25,35 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
 // for LDS (qmv_mfma_fits).
 constexpr int kQmvMfmaMaxM = 16;
 constexpr int64_t kQmvMfmaMaxK = (int64_t)1 << 25;
-constexpr size_t kQmvMfmaMaxLds = 160 * 1024;
-size_t qmv_mfma_lds(int64_t M, int64_t K, int gs);
-inline bool qmv_mfma_fits(int64_t M, int64_t K, int gs) {
+constexpr size_t kQmvMfmaMaxLds = 160 * 1024 - 256;   // LDS per CU, less static LDS
+// K split of the MFMA GEMV: layers with fewer than 256 blocks of 16 rows
+// split K into ks ranges of sps steps (128 codes each) so that the launch
+// fills the CUs, as long as each range keeps all 16 wavefronts busy;
+// klen = codes of the longest range.
+struct QmvMfmaPlan {
+  int ks, sps, klen;
+};
+inline QmvMfmaPlan qmv_mfma_plan(int64_t N, int64_t K) {
+  const int64_t nsteps = (K / 32 + 3) / 4, rb = (N + 15) / 16;
+  int64_t ks = 1;
+  if (rb < 256) {
+    ks = 256 / rb;
+    if (ks > 8) ks = 8;
+    if (ks > nsteps / 16) ks = nsteps / 16;   // every wavefront keeps a step
+    if (ks < 1) ks = 1;
+  }
+  const int64_t sps = (nsteps + ks - 1) / ks;
+  ks = (nsteps + sps - 1) / sps;          // no empty range
+  const int64_t klen = sps * 128 < K ? sps * 128 : K;
+  return {(int)ks, (int)sps, (int)klen};
+}
+size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs);
+inline bool qmv_mfma_fits(int64_t M, int64_t N, int64_t K, int gs) {
+  if (M < 1 || M > kQmvMfmaMaxM || K >= kQmvMfmaMaxK) return false;
+  const QmvMfmaPlan p = qmv_mfma_plan(N, K);
   // the workgroup's 1024 threads copy x with at most 8 16-byte loads each,
   // the scales and biases with at most 2
-  return M >= 1 && M <= kQmvMfmaMaxM && K < kQmvMfmaMaxK &&
-         qmv_mfma_lds(M, K, gs) <= kQmvMfmaMaxLds && M * (K / 8) <= 8 * 1024 &&
+  return qmv_mfma_lds(M, p.klen, K, gs) <= kQmvMfmaMaxLds && M * (p.klen / 8) <= 8 * 1024 &&
          (15 + 32 * (K / gs) + 15) / 16 <= 2 * 1024;
 }
 hipError_t launch_qmv_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,

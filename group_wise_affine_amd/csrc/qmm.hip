@@ -102,7 +102,7 @@ int64_t qmv_max_k(int bits, int dt) {
 
 Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allow_tile) {
   const bool dot2_ok = K <= qmv_max_k(bits, dt);
-  const bool mfma_ok = qmv_mfma_fits(M, K, gs);
+  const bool mfma_ok = qmv_mfma_fits(M, N, K, gs);
   if (dt == 0 && mfma_ok && (M >= 3 || (K > 8192 && N >= 4096) || !dot2_ok)) return kRouteQmvMfma;
   // bf16 dequantizes in fp32 and multiplies hi and lo halves: worth it from
   // 8 rows (4 on rows longer than 4096, where the streaming GEMV makes more

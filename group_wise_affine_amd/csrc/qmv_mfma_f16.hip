@@ -1,16 +1,51 @@
 // MFMA GEMV, f16 instantiations, and the entry points of the MFMA GEMV.
+#include <mutex>
+
 #include "qmv_mfma_impl.hpp"
 
 namespace qmm {
 
-hipError_t launch_qmv_mfma_bf16(int bits, int gs, const void* x, const uint32_t* wq, const void* s,
-                                const void* b, int64_t M, int64_t N, int64_t K, void* y,
-                                hipStream_t st);
+// Split-K workspace of the MFMA GEMV: 16 x 16 fp32 partial tiles of at most
+// 256 row blocks x 8 splits, and one arrival counter per row block (zero at
+// load; the last workgroup of a row block resets its counter). Calls that
+// overlap on one device share them.
+constexpr int kMvWsFloats = 256 * 8 * 256;
+__device__ float g_mv_ws[kMvWsFloats];
+__device__ unsigned g_mv_cnt[256];
 
-// LDS of the GEMV kernel: x rows plus padding and the 16 rows of scales and
-// biases, or the reduction buffer if larger
-size_t qmv_mfma_lds(int64_t M, int64_t K, int gs) {
-  const size_t xb = (((size_t)M * (K + 8) + 7) & ~(size_t)7) * 2;
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// addresses of the current device's workspace and counters
+bool mv_workspace(float** ws, unsigned** cnt) {
+  static std::mutex mu;
+  static float* wsa[kMaxDevices] = {};
+  static unsigned* cnta[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!wsa[dev]) {
+    void *p = nullptr, *q = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_mv_ws)) != hipSuccess ||
+        hipGetSymbolAddress(&q, HIP_SYMBOL(g_mv_cnt)) != hipSuccess)
+      return false;
+    wsa[dev] = static_cast<float*>(p);
+    cnta[dev] = static_cast<unsigned*>(q);
+  }
+  *ws = wsa[dev];
+  *cnt = cnta[dev];
+  return true;
+}
+
+}  // namespace
+
+hipError_t launch_qmv_mfma_bf16(int bits, const MvLaunch& L, hipStream_t st);
+
+// LDS of the GEMV kernel: rows of x over a K range of klen plus padding and
+// the 16 rows of scales and biases, or the reduction buffer if larger
+size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs) {
+  const size_t xb = (((size_t)M * (klen + 8) + 7) & ~(size_t)7) * 2;
   const size_t sb = (size_t)2 * 16 * ((15 + 32 * (K / gs) + 15) / 16);
   const size_t rb = (size_t)kMvThreads * 4 * 4;
   return xb + sb > rb ? xb + sb : rb;
@@ -19,8 +54,10 @@ size_t qmv_mfma_lds(int64_t M, int64_t K, int gs) {
 hipError_t launch_qmv_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                            const void* s, const void* b, int64_t M, int64_t N, int64_t K,
                            void* y, hipStream_t st) {
-  if (dt == 0) return launch_qmv_mfma_t<F16>(bits, gs, x, wq, s, b, M, N, K, y, st);
-  return launch_qmv_mfma_bf16(bits, gs, x, wq, s, b, M, N, K, y, st);
+  MvLaunch L{x, s, b, wq, y, (int)M, (int)N, (int)K, gs, nullptr, nullptr};
+  if (!mv_workspace(&L.ws, &L.cnt)) return hipErrorInvalidSymbol;
+  if (dt == 0) return launch_qmv_mfma_t<F16>(bits, L, st);
+  return launch_qmv_mfma_bf16(bits, L, st);
 }
 
 }  // namespace qmm

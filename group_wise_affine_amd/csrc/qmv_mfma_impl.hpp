@@ -31,13 +31,26 @@
 //    chunks past the row end) read zero without a branch or a memory access.
 //    Byte offsets stay below 2^31 for K < kQmvMfmaMaxK; x[0:M] must fit in
 //    LDS (qmv_mfma_fits).
-//  * The 16 partial 16x16 tiles are summed through LDS and written as f16.
+//  * The 16 partial 16x16 tiles are summed through LDS and written as T.
+//  * Layers with fewer than 256 row blocks split K over up to 8 workgroups
+//    per row block (contiguous K ranges, so each copies only its part of x);
+//    the last workgroup of a row block to finish adds the partial tiles.
 #pragma once
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_common.hpp"
 
 namespace qmm {
+
+// arguments of one MFMA GEMV call (shared by the f16 and bf16 units)
+struct MvLaunch {
+  const void *x, *s, *b;
+  const uint32_t* wq;
+  void* y;
+  int M, N, K, gs;
+  float* ws;        // split-K partial tiles and arrival counters
+  unsigned* cnt;
+};
 
 namespace {
 
@@ -84,8 +97,9 @@ template <class T, int BITS, int DEPTH, bool RING>
 __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, uint32_t m2, int xu, int sbu) {
-  // x rows [M][K + 8] f16 (8 halfs of padding per row spread the rows over
+    uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, uint32_t m2, int xu, int sbu,
+    int ks, int sps, float* __restrict__ ws, unsigned* __restrict__ cnt) {
+  // x rows [M][klen + 8] (8 elements of padding per row spread the rows over
   // the LDS banks), then scales [16][G] and biases [16][G]; afterwards the
   // cross-wavefront reduction buffer
   extern __shared__ uint4 smem4[];
@@ -97,11 +111,16 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int rows = N - n0 < 16 ? N - n0 : 16;
+  // split blockIdx.y of ks takes chunks [c0, c1): sps whole 4-chunk steps
   const int nch = K >> 5;
-  const int nsteps = (nch + 3) >> 2;
+  const int split = blockIdx.y;
+  const int c0 = 4 * sps * split;
+  const int c1 = c0 + 4 * sps < nch ? c0 + 4 * sps : nch;
+  const int nsteps = (c1 - c0 + 3) >> 2;
   const int nsw = wave < nsteps ? (nsteps - wave + kMvWaves - 1) / kMvWaves : 0;
   const int G = K >> gs_log2;
-  const int ldx = K + 8;
+  const int klen = (c1 - c0) * 32;
+  const int ldx = klen + 8;
   const uint32_t row_bytes = (uint32_t)K * BITS / 8;
 
   // Buffers over this workgroup's rows of W / scales / biases and over x:
@@ -131,14 +150,23 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   const uint8_t* bsb = reinterpret_cast<const uint8_t*>(bs4) + bd;
 
   // ---- x loads first (the weight loads queue behind them): 16-byte units
-  // u = tid + 1024 i for i < xu
-  const int xrow_units = K >> 3, xunits = M * xrow_units;
+  // u = tid + 1024 i for i < xu of the split's K range of every row
+  // (row m and unit kk of unit u stepped from one division: u grows by 1024)
+  const int xrow_units = klen >> 3, xunits = M * xrow_units;
+  const int dq = kMvThreads / xrow_units, dr = kMvThreads - dq * xrow_units;
   uint4 xl[kMvMaxXu];
-  uint32_t xoff[kMvMaxXu];
+  uint32_t xoff[kMvMaxXu], xlds[kMvMaxXu];
+  {
+    int m = tid / xrow_units, kk = tid - m * xrow_units;
 #pragma unroll
-  for (int i = 0; i < kMvMaxXu; i++) {
-    const int u = tid + kMvThreads * i;
-    xoff[i] = u < xunits ? (uint32_t)u * 16 : kOob;
+    for (int i = 0; i < kMvMaxXu; i++) {
+      const int u = tid + kMvThreads * i;
+      xoff[i] = u < xunits ? ((uint32_t)m * K + c0 * 32 + kk * 8) * 2 : kOob;
+      xlds[i] = (uint32_t)(m * ldx + kk * 8);
+      m += dq;
+      kk += dr;
+      if (kk >= xrow_units) { kk -= xrow_units; m++; }
+    }
   }
 #pragma unroll
   for (int i = 0; i < kMvMaxXu; i++) {
@@ -173,10 +201,10 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   uint32_t wv[DEPTH][BITS];
 
   auto issue = [&](int j, int d) QMM_INLINE {
-    const int c = 4 * (wave + kMvWaves * j) + g;
-    // kOob when c >= nch, else 0 (a mask, not a select: the compiler would
+    const int c = c0 + 4 * (wave + kMvWaves * j) + g;
+    // kOob when c >= c1, else 0 (a mask, not a select: the compiler would
     // turn a select of two offsets into a branch around two loads)
-    const uint32_t oob = (uint32_t)((nch - 1 - c) >> 31) & kOob;
+    const uint32_t oob = (uint32_t)((c1 - 1 - c) >> 31) & kOob;
     load_wchunk_buf<BITS>(wr, (wbase + c * (4 * BITS)) | oob, wv[d]);
   };
 
@@ -192,10 +220,7 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < kMvMaxXu; i++) {
     const int u = tid + kMvThreads * i;
-    if (i < xu && u < xunits) {
-      const int m = u / xrow_units, kk = (u - m * xrow_units) * 8;
-      *reinterpret_cast<uint4*>(xs + m * ldx + kk) = xl[i];
-    }
+    if (i < xu && u < xunits) *reinterpret_cast<uint4*>(xs + xlds[i]) = xl[i];
   }
 #pragma unroll
   for (int i = 0; i < kMvMaxSb; i++) {
@@ -214,9 +239,9 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     // past the end has zero weights)
     // (scale and bias are zeroed too: the chunk's codes read zero, and
     // s*0 + b must be 0 as well)
-    const int c = 4 * (wave + kMvWaves * j) + g;
-    const int cx = c < nch ? c : nch - 1;
-    const uint32_t keep = ~(uint32_t)((nch - 1 - c) >> 31);   // 0 past the row end
+    const int c = c0 + 4 * (wave + kMvWaves * j) + g;
+    const int cx = c < c1 ? c : c1 - 1;
+    const uint32_t keep = ~(uint32_t)((c1 - 1 - c) >> 31);   // 0 past the split's end
     const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
     const uint32_t sh = *reinterpret_cast<const uint16_t*>(ssb + gi) & keep;
     const uint32_t bh = *reinterpret_cast<const uint16_t*>(bsb + gi) & keep;
@@ -224,7 +249,7 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; i++) a[i] = make_uint4(0, 0, 0, 0);
     if (n < M) {
-      const uint4* xp = reinterpret_cast<const uint4*>(xs + n * ldx + cx * 32);
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + n * ldx + (cx - c0) * 32);
 #pragma unroll
       for (int i = 0; i < 4; i++) a[i] = xp[i];
     }
@@ -285,55 +310,81 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 #pragma unroll
   for (int e = 0; e < 4; e++) red[(wave * 64 + lane) * 4 + e] = acc[e];
   __syncthreads();
+  const int ln = tid >> 2, e = tid & 3;
+  const int m = 4 * (ln >> 4) + e, col = n0 + (ln & 15);
+  float v = 0.0f;
   if (tid < 256) {
-    float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < kMvWaves; w++) v += red[w * 256 + tid];
-    const int ln = tid >> 2, e = tid & 3;
-    const int m = 4 * (ln >> 4) + e, col = n0 + (ln & 15);
-    if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, v);
   }
+  if (ks == 1) {
+    if (tid < 256 && m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, v);
+    return;
+  }
+  // ---- K split over ks workgroups: each writes its 16 x 16 partial tile to
+  // the workspace; the last one to arrive at its row block's counter adds
+  // the ks tiles in split order, writes y and resets the counter for the
+  // next call. Tiles and counter use device-scope atomic accesses, which are
+  // coherent across the per-XCD L2 caches (so no fence has to write back a
+  // whole L2): every thread's stores have completed before the barrier that
+  // precedes the counter update, and the last workgroup reads the tiles only
+  // after its update has returned.
+  __shared__ unsigned last;
+  float* wsb = ws + (int64_t)blockIdx.x * ks * 256;
+  if (tid < 256) __hip_atomic_store(wsb + split * 256 + tid, v, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): the stores have completed
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ks - 1);
+  __syncthreads();
+  if (!last) return;
+  if (tid < 256) {
+    float t = 0.0f;
+    for (int sp = 0; sp < ks; sp++)
+      t += __hip_atomic_load(wsb + sp * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, t);
+  }
+  if (tid == 0) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class T, int BITS, int DEPTH, bool RING>
-hipError_t launch_depth(const void* x, const uint32_t* wq, const void* s, const void* b, int M,
-                        int N, int K, int gs, void* y, hipStream_t st) {
+hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st) {
   const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
-  const int xu = (M * (K / 8) + kMvThreads - 1) / kMvThreads;
-  const int sbu = ((15 + 32 * (K / gs) + 15) / 16 + kMvThreads - 1) / kMvThreads;
-  hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING>), dim3((N + 15) / 16), dim3(kMvThreads),
-                     qmv_mfma_lds(M, K, gs), st, static_cast<const uint16_t*>(x),
-                     reinterpret_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(s),
-                     static_cast<const uint16_t*>(b), static_cast<uint16_t*>(y), M, N, K,
-                     ilog2(gs), m2, xu, sbu);
+  const int xu = (L.M * (p.klen / 8) + kMvThreads - 1) / kMvThreads;
+  const int sbu = ((15 + 32 * (L.K / L.gs) + 15) / 16 + kMvThreads - 1) / kMvThreads;
+  hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING>), dim3((L.N + 15) / 16, p.ks),
+                     dim3(kMvThreads), qmv_mfma_lds(L.M, p.klen, L.K, L.gs), st,
+                     static_cast<const uint16_t*>(L.x), reinterpret_cast<const uint8_t*>(L.wq),
+                     static_cast<const uint16_t*>(L.s), static_cast<const uint16_t*>(L.b),
+                     static_cast<uint16_t*>(L.y), L.M, L.N, L.K, ilog2(L.gs), m2, xu, sbu, p.ks,
+                     p.sps, L.ws, L.cnt);
   return hipGetLastError();
 }
 
-// one round when every wavefront has at most 4 steps (K <= 8192), else a
+// one round when every wavefront has at most 4 steps of its split, else a
 // ring of 3 steps
 template <class T, int BITS>
-hipError_t launch_bits(const void* x, const uint32_t* wq, const void* s, const void* b, int M,
-                       int N, int K, int gs, void* y, hipStream_t st) {
-  const int nsteps = (K / 32 + 3) / 4;
-  const int nsw = (nsteps + kMvWaves - 1) / kMvWaves;
-  if (nsw <= 1) return launch_depth<T, BITS, 1, false>(x, wq, s, b, M, N, K, gs, y, st);
-  if (nsw <= 2) return launch_depth<T, BITS, 2, false>(x, wq, s, b, M, N, K, gs, y, st);
-  if (nsw <= 4) return launch_depth<T, BITS, 4, false>(x, wq, s, b, M, N, K, gs, y, st);
-  return launch_depth<T, BITS, 3, true>(x, wq, s, b, M, N, K, gs, y, st);
+hipError_t launch_bits(const MvLaunch& L, hipStream_t st) {
+  const QmvMfmaPlan p = qmv_mfma_plan(L.N, L.K);
+  const int nsw = (p.sps + kMvWaves - 1) / kMvWaves;
+  if (nsw <= 1) return launch_depth<T, BITS, 1, false>(L, p, st);
+  if (nsw <= 2) return launch_depth<T, BITS, 2, false>(L, p, st);
+  if (nsw <= 4) return launch_depth<T, BITS, 4, false>(L, p, st);
+  return launch_depth<T, BITS, 3, true>(L, p, st);
 }
 
 // all widths, one element type
 template <class T>
-hipError_t launch_qmv_mfma_t(int bits, int gs, const void* x, const uint32_t* wq, const void* s,
-                             const void* b, int64_t M, int64_t N, int64_t K, void* y,
-                             hipStream_t st) {
+hipError_t launch_qmv_mfma_t(int bits, const MvLaunch& L, hipStream_t st) {
   switch (bits) {
-    case 2: return launch_bits<T, 2>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 3: return launch_bits<T, 3>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 4: return launch_bits<T, 4>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 5: return launch_bits<T, 5>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    case 6: return launch_bits<T, 6>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-    default: return launch_bits<T, 8>(x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    case 2: return launch_bits<T, 2>(L, st);
+    case 3: return launch_bits<T, 3>(L, st);
+    case 4: return launch_bits<T, 4>(L, st);
+    case 5: return launch_bits<T, 5>(L, st);
+    case 6: return launch_bits<T, 6>(L, st);
+    default: return launch_bits<T, 8>(L, st);
   }
 }
 

@@ -39,12 +39,13 @@
  *    the caller's next synchronization.
  *  - Supported: bits in {2,3,4,5,6,8}; group_size in {32,64,128};
  *    K a positive multiple of group_size.
- *  - qmm_t and qconv2d_nhwc may split K over workgroups and keep fp32
- *    partial sums in a library-owned workspace: one static 64 MiB device
- *    array per GPU (nothing is allocated per call). Calls that run
- *    concurrently on one GPU (different streams, or different host threads
- *    without ordering) share it and must not overlap; calls queued on one
- *    stream are ordered and safe.
+ *  - qmm_t, qmv and qconv2d_nhwc may split K over workgroups and keep fp32
+ *    partial sums in library-owned workspaces: static device arrays, one set
+ *    per GPU (64 MiB for the tile kernel, 2 MiB and 256 counters for the
+ *    GEMV; nothing is allocated per call). Calls that run concurrently on
+ *    one GPU (different streams, or different host threads without ordering)
+ *    share them and must not overlap; calls queued on one stream are ordered
+ *    and safe.
  */
 #ifndef LIBQMM_H
 #define LIBQMM_H

@@ -137,6 +137,28 @@ def test_qmv_mfma(orc, dt, M, N, K, gs, bits):
     _run_mm(Q.qmm_t, orc, dt, M, N, K, gs, bits, seed=K + M + 1)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qmv_mfma_split_k_repeat(orc, dt):
+    """Narrow layers split K over workgroups; the last one to finish adds the
+    partial tiles and resets its row block's counter. Calls in a row (same
+    shape, then another, then the first again) must all be exact."""
+    code = orc_code(orc, dt)
+    cases = []
+    for (M, N, K, gs, bits, seed) in [(8, 512, 8192, 64, 4, 1), (5, 96, 4160, 32, 3, 2)]:
+        x = synth.normal((M, K), seed=seed, dt=dt)
+        w = synth.normal((N, K), seed=seed + 1, dt=dt)
+        wq, s, b = orc.quantize(w, code, gs, bits)
+        yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
+        dev = (to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+        cases.append((dev, yo, (M, N, K)))
+    outs = []
+    for i in (0, 0, 1, 0, 1, 1):
+        outs.append((Q.qmv(*cases[i][0]), i))
+    torch.cuda.synchronize()
+    for y, i in outs:
+        assert_parity(from_dev(y), cases[i][1], dt, f"split-K GEMV repeat {cases[i][2]}")
+
+
 def test_qmv_mfma_unaligned_scales(orc):
     """Scales and biases only 2-byte aligned (views at an odd element offset):
     the MFMA GEMV reads them as aligned 16-byte units around the block."""
