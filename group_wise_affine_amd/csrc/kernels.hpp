@@ -83,8 +83,8 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
 // Kernel choice for y = x . dequant(W)^T (measured on MI355X, 4096-wide
 // layers): the MFMA GEMV up to 16 rows when x fits in LDS, for f16 from
 // M = 3 (and M <= 2 when K > 8192 on N >= 4096: long rows make the
-// streaming GEMV's passes slow), for bf16 from M = 8 (4 when K > 4096; any
-// M for 8-bit codes); the
+// streaming GEMV's passes slow), for bf16 from M = 4 (any M for 8-bit
+// codes); the
 // streaming dot2 GEMV for a few rows otherwise; the MFMA tile kernel for the
 // rest. qmv never takes the tile kernel (kRouteNone when neither GEMV
 // accepts the shape).

@@ -124,7 +124,9 @@ __device__ __forceinline__ void dequant_piece_f16_pk(const uint32_t* w, uint32_t
   }(std::make_integer_sequence<int, PC / 2>{});
 }
 
-// codes [C0, C0+8) of a chunk -> bf16 hi/lo pairs (see dequant_chunk_bf16)
+// codes [C0, C0+8) of a chunk -> bf16 hi/lo pairs: w = fl32(s*q + b) (s*q is
+// exact), hi = bf16(w), lo = bf16(w - hi), both rounded to nearest even by
+// the packed hardware conversion (v_cvt_pk_bf16_f32, two values at a time)
 template <int BITS, int C0>
 __device__ __forceinline__ void dequant_piece_bf16(const uint32_t* w, float s, float b,
                                                    uint32_t* hi, uint32_t* lo) {
@@ -132,11 +134,13 @@ __device__ __forceinline__ void dequant_piece_bf16(const uint32_t* w, float s, f
     float f[8] = {fmaf(s, (float)code_at<BITS, C0 + J>(w), b)...};
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
-      const uint16_t h0 = from_f32(BF16{}, f[k]), h1 = from_f32(BF16{}, f[k + 1]);
-      hi[(C0 + k) / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      const uint16_t l0 = from_f32(BF16{}, f[k] - to_f32(BF16{}, h0));
-      const uint16_t l1 = from_f32(BF16{}, f[k + 1] - to_f32(BF16{}, h1));
-      lo[(C0 + k) / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      const bf162_t h = {(__bf16)f[k], (__bf16)f[k + 1]};
+      const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+      hi[(C0 + k) / 2] = hu;
+      const float r0 = f[k] - __builtin_bit_cast(float, hu << 16);
+      const float r1 = f[k + 1] - __builtin_bit_cast(float, hu & 0xffff0000u);
+      const bf162_t l = {(__bf16)r0, (__bf16)r1};
+      lo[(C0 + k) / 2] = __builtin_bit_cast(uint32_t, l);
     }
   }(std::make_integer_sequence<int, 8>{});
 }

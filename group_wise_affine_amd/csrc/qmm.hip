@@ -105,11 +105,9 @@ Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allo
   const bool mfma_ok = qmv_mfma_fits(M, N, K, gs);
   if (dt == 0 && mfma_ok && (M >= 3 || (K > 8192 && N >= 4096) || !dot2_ok)) return kRouteQmvMfma;
   // bf16 dequantizes in fp32 and multiplies hi and lo halves: worth it from
-  // 8 rows (4 on rows longer than 4096, where the streaming GEMV makes more
-  // passes), and always for 8-bit codes, which the streaming GEMV handles in
+  // 4 rows, and always for 8-bit codes, which the streaming GEMV handles in
   // fp32
-  if (dt == 1 && mfma_ok && (M >= 8 || (M >= 4 && K > 4096) || bits == 8 || !dot2_ok))
-    return kRouteQmvMfma;
+  if (dt == 1 && mfma_ok && (M >= 4 || bits == 8 || !dot2_ok)) return kRouteQmvMfma;
   if (!allow_tile) return dot2_ok ? kRouteQmv : kRouteNone;
   // the MFMA GEMV does not take the shape: a few rows on the streaming GEMV
   // (one pass over W per 4 rows at K = 4096), the rest on the tile kernel

@@ -103,22 +103,16 @@ __device__ __forceinline__ void dequant_chunk_f16(const uint32_t* w, float s,
   }
 }
 
-// bf16 dequantization of a chunk, split as hi = bf16(w), lo = bf16(w - hi).
+// bf16 dequantization of a chunk, split as hi = bf16(w), lo = bf16(w - hi)
+// (four 8-code pieces)
 template <int BITS>
 __device__ __forceinline__ void dequant_chunk_bf16(const uint32_t* w, float s,
                                                    float b, uint32_t* hi,
                                                    uint32_t* lo) {
-  [&]<int... J>(std::integer_sequence<int, J...>) {
-    float f[32] = {fmaf(s, (float)code_at<BITS, J>(w), b)...};
-#pragma unroll
-    for (int k = 0; k < 32; k += 2) {
-      const uint16_t h0 = from_f32(BF16{}, f[k]), h1 = from_f32(BF16{}, f[k + 1]);
-      hi[k / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      const uint16_t l0 = from_f32(BF16{}, f[k] - to_f32(BF16{}, h0));
-      const uint16_t l1 = from_f32(BF16{}, f[k + 1] - to_f32(BF16{}, h1));
-      lo[k / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-  }(std::make_integer_sequence<int, 32>{});
+  dequant_piece_bf16<BITS, 0>(w, s, b, hi, lo);
+  dequant_piece_bf16<BITS, 8>(w, s, b, hi, lo);
+  dequant_piece_bf16<BITS, 16>(w, s, b, hi, lo);
+  dequant_piece_bf16<BITS, 24>(w, s, b, hi, lo);
 }
 
 // Instruction interleave for one half step (one basic block): after the
