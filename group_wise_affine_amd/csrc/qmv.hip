@@ -10,6 +10,10 @@
 //  * Each workgroup first stages up to MB rows of x into LDS, already
 //    permuted into the pair order the weight unpacker produces (see
 //    common.hpp), together with the fp32 sum of every 32-element chunk.
+//    When a row fits one batch of lane loads (K <= 16384) and scales and
+//    biases are 16-byte aligned, the scales and biases of the workgroup's
+//    rows (one contiguous run of each array) are staged too, with 16-byte
+//    loads; the W wavefronts then issue nothing but their weight loads.
 //  * A row of W is split over TPR lanes of one wavefront (64/TPR rows per
 //    wavefront); a lane walks the row in 32-code chunks (4*bits bytes,
 //    16 bytes at 4 bits) with stride TPR chunks, so a wavefront load covers
@@ -58,16 +62,51 @@ __device__ __forceinline__ void load_chunk(const uint8_t* p, uint32_t w[BITS]) {
   }
 }
 
-// sum over the chunk of x'_pair . (MAGIC + q*2^o)_pair
-template <class T, int P = 0>
-__device__ __forceinline__ float chunk_dot_pairs(const uint32_t* pairs,
-                                                 const uint32_t* xp, float d) {
-  if constexpr (P == 16) {
-    return d;
-  } else {
-    d = dot2(T{}, pairs[P], xp[P], d);
-    return chunk_dot_pairs<T, P + 1>(pairs, xp, d);
+// d[r] = sum over the chunk of x'_pair . (MAGIC + q*2^o)_pair for each of
+// the R rows of a lane, in fp32. One wavefront per SIMD runs this, so the
+// dot2 instructions form at least four independent chains (NP partial sums
+// per row, interleaved over the rows) rather than one dependent chain.
+template <class T, int R, int NP>
+__device__ __forceinline__ void chunk_dot_rows(const uint32_t (*pairs)[16], const uint32_t* xp,
+                                               float* d) {
+  float part[R][NP];
+#pragma unroll
+  for (int r = 0; r < R; r++)
+#pragma unroll
+    for (int j = 0; j < NP; j++) part[r][j] = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 16; p++)
+#pragma unroll
+    for (int r = 0; r < R; r++) part[r][p % NP] = dot2(T{}, pairs[r][p], xp[p], part[r][p % NP]);
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    float v = part[r][0];
+#pragma unroll
+    for (int j = 1; j < NP; j++) v += part[r][j];
+    d[r] = v;
   }
+}
+
+// v + (v of the lane that the DPP control selects), all lanes active
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return v + __builtin_bit_cast(float, o);
+}
+
+// Sum over each aligned group of tpr lanes (a power of two up to 64),
+// returned in every lane of the group. Within a row of 16 lanes, DPP moves
+// (quad permutes 1-0-3-2 and 2-3-0-1, then the half-row and row mirrors,
+// each of which pairs lanes that hold the same partial sum) avoid the LDS
+// round trip of a lane shuffle; groups of 32 and 64 add the other rows.
+__device__ __forceinline__ float group_sum(float v, int tpr) {
+  if (tpr >= 2) v = dpp_add<0xb1>(v);    // quad_perm [1,0,3,2]
+  if (tpr >= 4) v = dpp_add<0x4e>(v);    // quad_perm [2,3,0,1]
+  if (tpr >= 8) v = dpp_add<0x141>(v);   // row_half_mirror
+  if (tpr >= 16) v = dpp_add<0x140>(v);  // row_mirror
+  if (tpr >= 32) v += __shfl_xor(v, 16);
+  if (tpr >= 64) v += __shfl_xor(v, 32);
+  return v;
 }
 
 template <class T, int BITS, int P = 0>
@@ -79,22 +118,29 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t m2,
   }
 }
 
-constexpr int kWWaves = 4;                        // wavefronts streaming W
 constexpr int kXWaves = 2;                        // wavefronts staging x
-constexpr int kThreads = (kWWaves + kXWaves) * 64;
 
-// One workgroup = 4 W wavefronts + 2 x wavefronts.
-//  x wavefronts: issue the x loads of their first staging task, barrier 1,
-//    then permute / pre-scale / sum into LDS, barrier 2.
+// One workgroup = WW W wavefronts (4 or 8) + 2 x wavefronts.
+//  x wavefronts: issue the x loads of their first staging task (and the
+//    scale / bias loads when staged), barrier 1, then permute / pre-scale /
+//    sum into LDS, barrier 2.
 //  W wavefronts: barrier 1 (so that the x loads are ahead of them in the
-//    CU's memory queue), issue every weight load of the lane, barrier 2
-//    (which does not wait for those loads), then multiply chunk by chunk as
-//    the weight data arrives.
+//    CU's memory queue), issue every weight load of the lane in the order
+//    the chunks are multiplied, barrier 2 (which does not wait for those
+//    loads), then multiply chunk by chunk as the weight data arrives.
+// Staged scales / biases: at most kSbUnits 16-byte units per x lane.
+constexpr int kSbUnits = 4;
+
+// Compiler fence between groups of loads: memory operations are not moved
+// across it, so the loads issue in program order and the wait for one
+// chunk leaves the later chunks in flight.
+__device__ __forceinline__ void chunk_fence() { asm volatile("; chunk fence" ::: "memory"); }
+
 // Lane work: R rows x CPL chunks; lane t of a row group handles chunks
 // c = t + TPR*i (i < CPL) of each of its R rows, so an x chunk read from LDS
 // serves R rows.
-template <class T, int BITS, int MB, int CPL, int R>
-__global__ __launch_bounds__(kThreads) void qmv_kernel(
+template <class T, int BITS, int MB, int CPL, int R, bool SBL, int WW>
+__global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, int tpr_log2,
@@ -111,35 +157,74 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
 
   const int tpr = 1 << tpr_log2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool w_wave = wave < kWWaves;
+  const bool w_wave = wave < WW;
   const int slot = lane >> tpr_log2, t = lane & (tpr - 1);
   const int slots = 64 >> tpr_log2;  // row groups per wavefront
-  const int row0 = ((blockIdx.x * kWWaves + wave) * slots + slot) * R;
+  const int rows_blk = WW * slots * R;
+  const int row0 = ((blockIdx.x * WW + wave) * slots + slot) * R;
 
   const int64_t row_bytes = (int64_t)K * BITS / 8;
   const int G = K >> gs_log2;
+  // staged scales then biases of the workgroup's rows, [2][rows_blk][G]
+  // (16-byte aligned after the x region)
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(smem + ((ntask * (XW + 2) + 3) & ~3));
+  const int sb_units = SBL ? rows_blk * G / 8 : 0;  // 16-byte units per array
   const int batch = tpr * CPL;  // chunks of a row covered by one batch
   uint32_t wv[R][CPL][BITS];
   uint16_t sw[R][CPL], bw[R][CPL];  // raw scale / bias words
   bool ok[R][CPL];
   // Branch-free: out-of-range chunks read a clamped valid address and are
   // zeroed through their scale and bias, so all loads issue back to back.
+  // Chunk-major, so that chunk i of every row is in before chunk i + 1.
   auto load_batch = [&](int cb) {
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      const int row = row0 + r;
-      const int rowc = row < N ? row : N - 1;
+    for (int i = 0; i < CPL; i++) {
 #pragma unroll
-      for (int i = 0; i < CPL; i++) {
+      for (int r = 0; r < R; r++) {
+        const int row = row0 + r;
+        const int rowc = row < N ? row : N - 1;
         const int c = cb + t + i * tpr;
         const int cc = c < nch ? c : nch - 1;
         ok[r][i] = (row < N) && (c < nch);
         load_chunk<BITS>(wq + (int64_t)rowc * row_bytes + (int64_t)cc * (4 * BITS), wv[r][i]);
-        const int g = (cc << 5) >> gs_log2;
-        sw[r][i] = scales[(int64_t)rowc * G + g];
-        bw[r][i] = biases[(int64_t)rowc * G + g];
+        if constexpr (!SBL) {
+          const int g = (cc << 5) >> gs_log2;
+          sw[r][i] = scales[(int64_t)rowc * G + g];
+          bw[r][i] = biases[(int64_t)rowc * G + g];
+        }
+      }
+      chunk_fence();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // staged scales / biases of this lane's chunks, read from LDS
+  auto read_sb = [&]() {
+    const int lr0 = (wave * slots + slot) * R;  // row of the workgroup
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+      const int c = t + i * tpr;
+      const int cc = c < nch ? c : nch - 1;
+      const int g = (cc << 5) >> gs_log2;
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        sw[r][i] = sbl[(lr0 + r) * G + g];
+        bw[r][i] = sbl[(rows_blk + lr0 + r) * G + g];
       }
     }
+  };
+  // x lanes: 16-byte unit u of the staged scales (u < sb_units) or biases;
+  // a unit that crosses the end of the array is read element by element
+  auto sb_load = [&](int u) -> uint4 {
+    const bool bias = u >= sb_units;
+    const int uu = bias ? u - sb_units : u;
+    const uint16_t* src = bias ? biases : scales;
+    const int64_t e0 = (int64_t)blockIdx.x * rows_blk * G + 8 * (int64_t)uu;
+    const int64_t total = (int64_t)N * G;
+    if (e0 + 8 <= total) return *reinterpret_cast<const uint4*>(src + e0);
+    uint32_t h[4] = {0, 0, 0, 0};
+    for (int e = 0; e < 8; e++)
+      if (e0 + e < total) h[e / 2] |= (uint32_t)src[e0 + e] << (16 * (e % 2));
+    return make_uint4(h[0], h[1], h[2], h[3]);
   };
 
   // x staging: task = (row of x, chunk); activations permuted into pair
@@ -197,13 +282,29 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
     __syncthreads();  // 1: the x loads of this workgroup are queued first
     load_batch(0);
     __syncthreads();  // 2: x staged (does not wait for the weight loads)
+    if constexpr (SBL) read_sb();
   } else {
-    const int xl = (wave - kWWaves) * 64 + lane;
+    const int xl = (wave - WW) * 64 + lane;
     uint4 raw4[4];
     x_load(xl, raw4);
+    uint4 sbu[SBL ? kSbUnits : 1];
+    if constexpr (SBL) {
+#pragma unroll
+      for (int j = 0; j < kSbUnits; j++) {
+        const int u = xl + j * kXWaves * 64;
+        if (u < 2 * sb_units) sbu[j] = sb_load(u);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // 1
     if (xl < ntask) stage(xl, raw4);
+    if constexpr (SBL) {
+#pragma unroll
+      for (int j = 0; j < kSbUnits; j++) {
+        const int u = xl + j * kXWaves * 64;
+        if (u < 2 * sb_units) reinterpret_cast<uint4*>(sbl)[u] = sbu[j];
+      }
+    }
     for (int task = xl + kXWaves * 64; task < ntask; task += kXWaves * 64) {
       x_load(task, raw4);
       stage(task, raw4);
@@ -269,27 +370,28 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
             }
             const float xsm = xsum[m * nch + c];
             const float d0 = xd0[m * nch + c];
+            // partial sums per row: rows x partials >= 4 (rows of x give
+            // independent chains as well)
+            constexpr int NP = R * MB >= 4 ? 1 : 4 / (R * MB);
+            float d[R];
+            chunk_dot_rows<T, R, NP>(pr, xp, d);
 #pragma unroll
-            for (int r = 0; r < R; r++) {
-              const float d = chunk_dot_pairs<T>(pr[r], xp, 0.0f) - d0;
-              acc[r][m] = fmaf(sf[r], d, fmaf(bf[r], xsm, acc[r][m]));
-            }
+            for (int r = 0; r < R; r++)
+              acc[r][m] = fmaf(sf[r], d[r] - d0, fmaf(bf[r], xsm, acc[r][m]));
           }
         }
       }
     }
     cb += batch;
     if (cb >= nch) break;
-    load_batch(cb);  // rows longer than one batch (very large K)
+    load_batch(cb);  // rows longer than one batch (very large K; never staged)
   }
 
   // ---- reduce the TPR partial sums of each row
-  for (int o = tpr >> 1; o >= 1; o >>= 1) {
 #pragma unroll
-    for (int r = 0; r < R; r++)
+  for (int r = 0; r < R; r++)
 #pragma unroll
-      for (int m = 0; m < MB; m++) acc[r][m] += __shfl_xor(acc[r][m], o);
-  }
+    for (int m = 0; m < MB; m++) acc[r][m] = group_sum(acc[r][m], tpr);
   if (t == 0) {
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -306,11 +408,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
 
 static constexpr int kMaxLds = 64 * 1024;
 
-// Lane work shapes (chunks per lane, rows per lane) compiled in.
+// Lane work shapes (chunks per lane, rows per lane, W wavefronts) compiled in.
 struct Shape {
-  int cpl, r;
+  int cpl, r, ww;
 };
-static constexpr Shape kShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}};
+static constexpr Shape kShapes[] = {{2, 1, 4}, {4, 1, 4}, {4, 2, 4}, {8, 1, 4}, {4, 1, 8}};
 
 // Threads per row for a lane shape: enough lanes that CPL chunks each cover
 // the row (a power of two, at most 64).
@@ -320,24 +422,38 @@ static int tpr_for(int nch, int cpl) {
   return tpr;
 }
 
-template <class T, int BITS, int MB, int CPL, int R>
+template <class T, int BITS, int MB, int CPL, int R, int WW>
 static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
                                const void* b, int M, int N, int K, int gs,
                                int tpr, void* y, hipStream_t st) {
   using Cfg = QmvCfg<T, BITS>;
-  const int nch = K / 32;
-  const int rows_per_block = kWWaves * (64 / tpr) * R;
+  const int nch = K / 32, G = K / gs;
+  const int rows_per_block = WW * (64 / tpr) * R;
+  const dim3 block((WW + kXWaves) * 64);
   const dim3 grid((N + rows_per_block - 1) / rows_per_block, (M + MB - 1) / MB);
-  const size_t lds = (size_t)MB * nch * (Cfg::kXWords + 2) * 4;
+  const size_t lds_x = (size_t)MB * nch * (Cfg::kXWords + 2) * 4;
+  // staged scales / biases: one batch covers a row, the block's run of each
+  // array is whole 16-byte units at 16-byte aligned addresses, the x lanes
+  // copy it with kSbUnits loads each and it fits in LDS
+  const size_t lds_sb = ((lds_x + 15) & ~(size_t)15) + (size_t)rows_per_block * G * 4;
+  const bool sbl = tpr * CPL >= nch && ((int64_t)rows_per_block * G) % 8 == 0 &&
+                   (int64_t)rows_per_block * G / 4 <= (int64_t)kSbUnits * kXWaves * 64 &&
+                   ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0 &&
+                   lds_sb <= (size_t)kMaxLds;
   const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
   uint32_t magic = 0;
   if constexpr (!Cfg::kF32) magic = T::kMagic;
-  hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R>), grid, dim3(kThreads), lds, st,
-                     static_cast<const uint16_t*>(x),
-                     reinterpret_cast<const uint8_t*>(wq),
-                     static_cast<const uint16_t*>(s),
-                     static_cast<const uint16_t*>(b),
-                     static_cast<uint16_t*>(y), M, N, K, ilog2(gs), ilog2(tpr), m2, magic);
+  const auto xp = static_cast<const uint16_t*>(x);
+  const auto wp = reinterpret_cast<const uint8_t*>(wq);
+  const auto sp = static_cast<const uint16_t*>(s);
+  const auto bp = static_cast<const uint16_t*>(b);
+  const auto yp = static_cast<uint16_t*>(y);
+  if (sbl)
+    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, true, WW>), grid, block, lds_sb, st,
+                       xp, wp, sp, bp, yp, M, N, K, ilog2(gs), ilog2(tpr), m2, magic);
+  else
+    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, false, WW>), grid, block, lds_x, st,
+                       xp, wp, sp, bp, yp, M, N, K, ilog2(gs), ilog2(tpr), m2, magic);
   return hipGetLastError();
 }
 
@@ -346,20 +462,32 @@ static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
                             const void* b, int M, int N, int K, int gs,
                             void* y, hipStream_t st) {
   const int nch = K / 32;
-  // Pick the lane shape: 4 chunks x 2 rows per lane while that gives at
-  // least 256 workgroups (one per CU; measured best at M = 1 for 4096- and
-  // 11008-wide layers, also when a row needs several batches), else the
-  // shape with the most workgroups.
+  auto blocks_of = [&](const Shape& sh) {
+    const int rows_per_block = sh.ww * (64 / tpr_for(nch, sh.cpl)) * sh.r;
+    return (int64_t)((N + rows_per_block - 1) / rows_per_block) * ((M + MB - 1) / MB);
+  };
+  // One row of x: 8 W wavefronts with 4 chunks of one row per lane, so that
+  // two wavefronts per SIMD share the arithmetic that follows the weight
+  // data, when that makes one round of 256 to 320 workgroups (such a
+  // workgroup fills a CU's registers: more would run in a second round).
+  if (MB == 1) {
+    const int64_t b8 = blocks_of(kShapes[4]);
+    if (b8 >= 256 && b8 <= 320) {
+      if constexpr (MB == 1)
+        return launch_shape<T, BITS, MB, 4, 1, 8>(x, wq, s, b, M, N, K, gs,
+                                                  tpr_for(nch, 4), y, st);
+    }
+  }
+  // Otherwise the first 4-wavefront shape in order of preference that gives
+  // at least 256 workgroups (one per CU), else the one with the most: 4
+  // chunks x 2 rows per lane first (measured best for several rows of x and
+  // for layers of many row blocks).
   static constexpr int kOrder[] = {2, 1, 3, 0};
   int best = -1;
   int64_t best_blocks = -1;
   for (int oi = 0; oi < 4; oi++) {
     const int i = kOrder[oi];
-    const Shape sh = kShapes[i];
-    const int tpr = tpr_for(nch, sh.cpl);
-    const int rows_per_block = kWWaves * (64 / tpr) * sh.r;
-    const int64_t blocks = (int64_t)((N + rows_per_block - 1) / rows_per_block) *
-                           ((M + MB - 1) / MB);
+    const int64_t blocks = blocks_of(kShapes[i]);
     if (blocks >= 256) { best = i; break; }
     if (blocks > best_blocks) { best_blocks = blocks; best = i; }
   }
@@ -367,10 +495,10 @@ static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
   const Shape sh = kShapes[best];
   const int tpr = tpr_for(nch, sh.cpl);
   switch (best) {
-    case 0: return launch_shape<T, BITS, MB, 2, 1>(x, wq, s, b, M, N, K, gs, tpr, y, st);
-    case 1: return launch_shape<T, BITS, MB, 4, 1>(x, wq, s, b, M, N, K, gs, tpr, y, st);
-    case 2: return launch_shape<T, BITS, MB, 4, 2>(x, wq, s, b, M, N, K, gs, tpr, y, st);
-    default: return launch_shape<T, BITS, MB, 8, 1>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    case 0: return launch_shape<T, BITS, MB, 2, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    case 1: return launch_shape<T, BITS, MB, 4, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    case 2: return launch_shape<T, BITS, MB, 4, 2, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    default: return launch_shape<T, BITS, MB, 8, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
   }
 }
 

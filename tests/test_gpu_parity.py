@@ -159,24 +159,40 @@ def test_qmv_mfma_split_k_repeat(orc, dt):
         assert_parity(from_dev(y), cases[i][1], dt, f"split-K GEMV repeat {cases[i][2]}")
 
 
-def test_qmv_mfma_unaligned_scales(orc):
-    """Scales and biases only 2-byte aligned (views at an odd element offset):
-    the MFMA GEMV reads them as aligned 16-byte units around the block."""
-    code = orc_code(orc, "f16")
-    M, N, K, gs, bits = 5, 70, 1024, 32, 4
-    x = synth.normal((M, K), seed=3, dt="f16")
-    w = synth.normal((N, K), seed=4, dt="f16")
+@pytest.mark.parametrize("dt,M", [("f16", 5), ("f16", 1), ("bf16", 2)])
+def test_qmv_unaligned_scales(orc, dt, M):
+    """Scales and biases only 2-byte aligned (views at an odd element offset).
+    The MFMA GEMV (f16, 5 rows) reads them as aligned 16-byte units around
+    the block; the streaming GEMV (1 and 2 rows) cannot stage them with
+    16-byte loads and reads them per lane."""
+    code = orc_code(orc, dt)
+    N, K, gs, bits = 70, 1024, 32, 4
+    x = synth.normal((M, K), seed=3, dt=dt)
+    w = synth.normal((N, K), seed=4, dt=dt)
     wq, s, b = orc.quantize(w, code, gs, bits)
     yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
-    sd, bd = to_dev(s, "f16"), to_dev(b, "f16")
+    sd, bd = to_dev(s, dt), to_dev(b, dt)
     s_big = torch.zeros(sd.numel() + 1, dtype=sd.dtype, device=sd.device)
     b_big = torch.zeros(bd.numel() + 3, dtype=bd.dtype, device=bd.device)
     s_big[1:].copy_(sd.reshape(-1))
     b_big[3:].copy_(bd.reshape(-1))
-    y = Q.qmv(to_dev(x, "f16"), bytes_to_words_dev(wq), s_big[1:].view(sd.shape),
+    y = Q.qmv(to_dev(x, dt), bytes_to_words_dev(wq), s_big[1:].view(sd.shape),
               b_big[3:].view(bd.shape), gs, bits)
     torch.cuda.synchronize()
-    assert_parity(from_dev(y), yo, "f16", "qmv unaligned scales")
+    assert_parity(from_dev(y), yo, dt, "qmv unaligned scales")
+
+
+@pytest.mark.parametrize("dt,N,K,gs,bits", [
+    ("bf16", 4100, 4096, 32, 3),    # ragged last workgroup (4 of 16 rows)
+    ("f16", 8192, 2048, 128, 5),
+    ("bf16", 4096, 4096, 64, 6),
+    ("f16", 2560, 4160, 64, 4),     # 64 lanes per row, the last chunks past the row end
+])
+def test_qmv_decode_wide(orc, dt, N, K, gs, bits):
+    """One row of x over layers that make one round of 256 to 320 workgroups
+    in the 8-wavefront lane shape (one W row per lane), with staged scales
+    and biases."""
+    _run_mm(Q.qmv, orc, dt, 1, N, K, gs, bits, seed=N + bits)
 
 
 def test_qmv_max_k(orc):
