@@ -8,7 +8,8 @@ Headline (one step = one decode GEMV through the C ABI):
   algorithmic bytes are packed W + scales + biases + x + y.
 
 The other rows of the hot path are measured in the same run and reported
-under "rows": quantize, dequantize, qmv at bits 2/8 and M <= 16, the chained
+under "rows": quantize, dequantize, qmv at bits 2/8 and M <= 16, the gathered
+GEMV on a mixture-of-experts decode step (4 tokens, top-2 of 8 experts), the chained
 qmm_t bench (10 loops of x = qmm(qmm(x, W1), W2), M=1024), the quantized
 conv2d (x [1,64,64,320], 3x3, groups 1 and 2) and the bf16 small-M sweep.
 
@@ -116,6 +117,41 @@ def bench_qmv(torch, Q, synth, timer, dt, M, N, K, bits, gs, steps, warmup, fn=N
     return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
             "pool_copies": P}
+
+
+def bench_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096, K=4096,
+                 bits=4, gs=64):
+    """Mixture-of-experts decode through the gathered GEMV: T tokens x [1, K]
+    f16, each routed to topk of E experts W_e [N, K] (4-bit g64), one call for
+    the T*topk products. The routing is a seeded permutation of the experts
+    (T*topk == E), so every expert is read once per step. Every step reads a
+    different copy of the expert stack from a >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    import numpy as np
+    assert T * topk == E
+    layers = [make_layer(torch, Q, synth, "f16", N, K, gs, bits, 100 + e) for e in range(E)]
+    stack = tuple(torch.stack([l[i] for l in layers]) for i in range(3))
+    del layers
+    wqs, ss, bs, P = pooled(torch, stack)
+    x = to_dev(np.stack([synth.normal((1, K), seed=7 + t) for t in range(T)]), "f16")
+    lhs = torch.tensor([t for t in range(T) for _ in range(topk)], dtype=torch.int32,
+                       device="cuda")
+    rhs = torch.tensor(np.random.default_rng(5).permutation(E).tolist(), dtype=torch.int32,
+                       device="cuda")
+    y = torch.empty((E, 1, N), dtype=torch.float16, device="cuda")
+
+    def launch(i):
+        j = i % P
+        Q.gather_qmv(x, wqs[j], ss[j], bs[j], lhs, rhs, gs, bits, out=y)
+
+    ms = timer.run(launch, steps, warmup)
+    nbytes = E * (N * K * bits // 8 + N * (K // gs) * 4) + T * K * 2 + E * N * 2
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "pool_copies": P,
+            "workload": f"{T} tokens x top-{topk} of {E} experts [{N},{K}] {bits}-bit g{gs} f16"}
 
 
 def bench_quantize(torch, Q, synth, timer, steps, warmup):
@@ -311,6 +347,10 @@ def main():
                                            for k, v in r.items()}
         rows["qmv_decode_4096x4096_f16_g64"] = dec
         log("decode rows done")
+        rows["gather_qmv_moe_decode_f16_g64"] = {
+            k: round(v, 4) if isinstance(v, float) else v
+            for k, v in bench_gather(torch, Q, synth, timer, n_small, 20).items()}
+        log("gather row done")
         ch = {}
         for bits in (2, 4, 8):
             ch[f"bits{bits}"] = {k: round(v, 4) for k, v in

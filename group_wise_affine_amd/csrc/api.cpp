@@ -161,6 +161,40 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                   "qmv");
 }
 
+qmm_status qmm_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_indices,
+                          const uint32_t* wq, const void* scales, const void* biases,
+                          int64_t w_batches, const int32_t* rhs_indices, int64_t batches,
+                          qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
+                          int bits, void* y, void* stream) {
+  qmm_status st = check_matmul("qmm_gather_qmv", x, wq, scales, biases, dt, M, N, K,
+                               group_size, bits, y);
+  if (st) return st;
+  if (batches < 1 || batches > 65535)
+    return fail(QMM_E_SHAPE, "qmm_gather_qmv: batches (%lld) must be in [1, 65535]",
+                (long long)batches);
+  if (x_batches < 1 || w_batches < 1 || x_batches > kI32 || w_batches > kI32)
+    return fail(QMM_E_SHAPE, "qmm_gather_qmv: x_batches (%lld) and w_batches (%lld) must be >= 1",
+                (long long)x_batches, (long long)w_batches);
+  if (!lhs_indices && x_batches < batches)
+    return fail(QMM_E_SHAPE, "qmm_gather_qmv: without lhs_indices, x needs one batch per output "
+                "batch (%lld < %lld)", (long long)x_batches, (long long)batches);
+  if (!rhs_indices && w_batches < batches)
+    return fail(QMM_E_SHAPE, "qmm_gather_qmv: without rhs_indices, W needs one batch per output "
+                "batch (%lld < %lld)", (long long)w_batches, (long long)batches);
+  if (!aligned(lhs_indices, 4) || !aligned(rhs_indices, 4))
+    return fail(QMM_E_ALIGN, "qmm_gather_qmv: index arrays must be 4-byte aligned");
+  if (x_batches * M * K > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40) ||
+      batches * M * N > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_gather_qmv: problem too large");
+  if (K > qmm::qmv_max_k(bits, (int)dt))
+    return fail(QMM_E_SHAPE, "qmm_gather_qmv: K (%lld) exceeds the streaming GEMV's limit (%lld "
+                "for this bits/dtype)", (long long)K, (long long)qmm::qmv_max_k(bits, (int)dt));
+  return launched(qmm::launch_gather_qmv((int)dt, bits, group_size, x, x_batches, lhs_indices,
+                                         wq, scales, biases, w_batches, rhs_indices, batches, M,
+                                         N, K, y, (hipStream_t)stream),
+                  "qmm_gather_qmv");
+}
+
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
                  const void* biases, qmm_dtype dt, int64_t M, int64_t N,
                  int64_t K, int group_size, int bits, void* y, void* stream) {

@@ -56,6 +56,13 @@ inline bool qmv_mfma_fits(int64_t M, int64_t N, int64_t K, int gs) {
   return qmv_mfma_lds(M, p.klen, K, gs) <= kQmvMfmaMaxLds && M * (p.klen / 8) <= 8 * 1024 &&
          (15 + 32 * (K / gs) + 15) / 16 <= 2 * 1024;
 }
+// Gathered streaming GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T
+// with x [nxb, M, K], W [nwb, N, K] (scales / biases [nwb, N, K/gs]) and
+// y [B, M, N]; a null index array means z. Indices are clamped into range.
+hipError_t launch_gather_qmv(int dt, int bits, int gs, const void* x, int64_t nxb,
+                             const int32_t* lidx, const uint32_t* wq, const void* s,
+                             const void* b, int64_t nwb, const int32_t* ridx, int64_t B,
+                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
 hipError_t launch_qmv_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                            const void* s, const void* b, int64_t M, int64_t N,
                            int64_t K, void* y, hipStream_t st);

@@ -139,16 +139,33 @@ __device__ __forceinline__ void chunk_fence() { asm volatile("; chunk fence" :::
 // Lane work: R rows x CPL chunks; lane t of a row group handles chunks
 // c = t + TPR*i (i < CPL) of each of its R rows, so an x chunk read from LDS
 // serves R rows.
-template <class T, int BITS, int MB, int CPL, int R, bool SBL, int WW>
+template <class T, int BITS, int MB, int CPL, int R, bool SBL, int WW, bool GATHER>
 __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, int tpr_log2,
-    uint32_t m2, uint32_t magic) {
+    uint32_t m2, uint32_t magic, const int32_t* __restrict__ lidx,
+    const int32_t* __restrict__ ridx, int nxb, int nwb) {
   using Cfg = QmvCfg<T, BITS>;
   constexpr int XW = Cfg::kXWords;
   extern __shared__ uint32_t smem[];
   const int nch = K >> 5;
+  // Batch z (gathered products): x batch lidx[z] and weight batch ridx[z]
+  // (z itself where an index array is absent), clamped into range so that
+  // no index can move an access outside the arrays; output batch z. (A
+  // compile-time switch: the plain GEMV starts without these dependent
+  // scalar loads.)
+  if constexpr (GATHER) {
+    const int z = blockIdx.z;
+    int li = lidx ? lidx[z] : z, ri = ridx ? ridx[z] : z;
+    li = li < 0 ? 0 : (li >= nxb ? nxb - 1 : li);
+    ri = ri < 0 ? 0 : (ri >= nwb ? nwb - 1 : ri);
+    x += (int64_t)li * M * K;
+    wq += (int64_t)ri * N * ((int64_t)K * BITS / 8);
+    scales += (int64_t)ri * N * (K >> gs_log2);
+    biases += (int64_t)ri * N * (K >> gs_log2);
+    y += (int64_t)z * M * N;
+  }
   const int ntask = MB * nch;
   uint32_t* xs = smem;                                            // [MB*nch][XW]
   float* xsum = reinterpret_cast<float*>(smem + ntask * XW);       // [MB*nch]
@@ -406,6 +423,19 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
 
 // ----------------------------------------------------------------- launch
 
+// Batches of a gathered GEMV: output batch z of B multiplies x batch
+// lidx[z] (of nxb) by weight batch ridx[z] (of nwb); null index arrays mean
+// z. One plain GEMV is the single batch with no index arrays.
+struct QmvBatch {
+  const int32_t* lidx;
+  const int32_t* ridx;
+  int nxb, nwb, B;
+};
+static constexpr QmvBatch kOneBatch{nullptr, nullptr, 1, 1, 1};
+static bool gathered(const QmvBatch& bt) {
+  return bt.lidx || bt.ridx || bt.B != 1 || bt.nxb != 1 || bt.nwb != 1;
+}
+
 static constexpr int kMaxLds = 64 * 1024;
 
 // Lane work shapes (chunks per lane, rows per lane, W wavefronts) compiled in.
@@ -425,12 +455,12 @@ static int tpr_for(int nch, int cpl) {
 template <class T, int BITS, int MB, int CPL, int R, int WW>
 static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
                                const void* b, int M, int N, int K, int gs,
-                               int tpr, void* y, hipStream_t st) {
+                               int tpr, void* y, hipStream_t st, const QmvBatch& bt) {
   using Cfg = QmvCfg<T, BITS>;
   const int nch = K / 32, G = K / gs;
   const int rows_per_block = WW * (64 / tpr) * R;
   const dim3 block((WW + kXWaves) * 64);
-  const dim3 grid((N + rows_per_block - 1) / rows_per_block, (M + MB - 1) / MB);
+  const dim3 grid((N + rows_per_block - 1) / rows_per_block, (M + MB - 1) / MB, bt.B);
   const size_t lds_x = (size_t)MB * nch * (Cfg::kXWords + 2) * 4;
   // staged scales / biases: one batch covers a row, the block's run of each
   // array is whole 16-byte units at 16-byte aligned addresses, the x lanes
@@ -439,6 +469,7 @@ static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
   const bool sbl = tpr * CPL >= nch && ((int64_t)rows_per_block * G) % 8 == 0 &&
                    (int64_t)rows_per_block * G / 4 <= (int64_t)kSbUnits * kXWaves * 64 &&
                    ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0 &&
+                   (bt.nwb == 1 || ((int64_t)N * G) % 8 == 0) &&   // every weight batch aligned
                    lds_sb <= (size_t)kMaxLds;
   const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
   uint32_t magic = 0;
@@ -448,23 +479,32 @@ static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
   const auto sp = static_cast<const uint16_t*>(s);
   const auto bp = static_cast<const uint16_t*>(b);
   const auto yp = static_cast<uint16_t*>(y);
-  if (sbl)
-    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, true, WW>), grid, block, lds_sb, st,
-                       xp, wp, sp, bp, yp, M, N, K, ilog2(gs), ilog2(tpr), m2, magic);
-  else
-    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, false, WW>), grid, block, lds_x, st,
-                       xp, wp, sp, bp, yp, M, N, K, ilog2(gs), ilog2(tpr), m2, magic);
+  auto go = [&]<bool S, bool GA>() {
+    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, S, WW, GA>), grid, block,
+                       S ? lds_sb : lds_x, st, xp, wp, sp, bp, yp, M, N, K, ilog2(gs),
+                       ilog2(tpr), m2, magic, bt.lidx, bt.ridx, bt.nxb, bt.nwb);
+  };
+  // gathered launches come with one row of x per pass (launch_t)
+  if constexpr (MB == 1) {
+    if (gathered(bt)) {
+      if (sbl) go.template operator()<true, true>();
+      else go.template operator()<false, true>();
+      return hipGetLastError();
+    }
+  }
+  if (sbl) go.template operator()<true, false>();
+  else go.template operator()<false, false>();
   return hipGetLastError();
 }
 
 template <class T, int BITS, int MB>
 static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
                             const void* b, int M, int N, int K, int gs,
-                            void* y, hipStream_t st) {
+                            void* y, hipStream_t st, const QmvBatch& bt) {
   const int nch = K / 32;
   auto blocks_of = [&](const Shape& sh) {
     const int rows_per_block = sh.ww * (64 / tpr_for(nch, sh.cpl)) * sh.r;
-    return (int64_t)((N + rows_per_block - 1) / rows_per_block) * ((M + MB - 1) / MB);
+    return (int64_t)((N + rows_per_block - 1) / rows_per_block) * ((M + MB - 1) / MB) * bt.B;
   };
   // One row of x: 8 W wavefronts with 4 chunks of one row per lane, so that
   // two wavefronts per SIMD share the arithmetic that follows the weight
@@ -475,7 +515,7 @@ static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
     if (b8 >= 256 && b8 <= 320) {
       if constexpr (MB == 1)
         return launch_shape<T, BITS, MB, 4, 1, 8>(x, wq, s, b, M, N, K, gs,
-                                                  tpr_for(nch, 4), y, st);
+                                                  tpr_for(nch, 4), y, st, bt);
     }
   }
   // Otherwise the first 4-wavefront shape in order of preference that gives
@@ -495,41 +535,42 @@ static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
   const Shape sh = kShapes[best];
   const int tpr = tpr_for(nch, sh.cpl);
   switch (best) {
-    case 0: return launch_shape<T, BITS, MB, 2, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
-    case 1: return launch_shape<T, BITS, MB, 4, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
-    case 2: return launch_shape<T, BITS, MB, 4, 2, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
-    default: return launch_shape<T, BITS, MB, 8, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st);
+    case 0: return launch_shape<T, BITS, MB, 2, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st, bt);
+    case 1: return launch_shape<T, BITS, MB, 4, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st, bt);
+    case 2: return launch_shape<T, BITS, MB, 4, 2, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st, bt);
+    default: return launch_shape<T, BITS, MB, 8, 1, 4>(x, wq, s, b, M, N, K, gs, tpr, y, st, bt);
   }
 }
 
 template <class T, int BITS>
 static hipError_t launch_t(const void* x, const uint32_t* wq, const void* s,
                            const void* b, int M, int N, int K, int gs, void* y,
-                           hipStream_t st) {
+                           hipStream_t st, const QmvBatch& bt) {
   using Cfg = QmvCfg<T, BITS>;
   const int64_t per_row = (int64_t)(K / 32) * (Cfg::kXWords + 2) * 4;
   int mb_max = (int)(kMaxLds / per_row);
   int want = 1;  // smallest of 1, 2, 4 covering M (4 at most)
   while (want < M && want < 4) want *= 2;
   while (want > 1 && want > mb_max) want /= 2;
+  if (gathered(bt)) want = 1;  // gathered products: one row of x per pass
   switch (want) {
-    case 4: return launch_mb<T, BITS, 4>(x, wq, s, b, M, N, K, gs, y, st);
-    case 2: return launch_mb<T, BITS, 2>(x, wq, s, b, M, N, K, gs, y, st);
-    default: return launch_mb<T, BITS, 1>(x, wq, s, b, M, N, K, gs, y, st);
+    case 4: return launch_mb<T, BITS, 4>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    case 2: return launch_mb<T, BITS, 2>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    default: return launch_mb<T, BITS, 1>(x, wq, s, b, M, N, K, gs, y, st, bt);
   }
 }
 
 template <class T>
 static hipError_t launch_bits(int bits, const void* x, const uint32_t* wq,
                               const void* s, const void* b, int M, int N,
-                              int K, int gs, void* y, hipStream_t st) {
+                              int K, int gs, void* y, hipStream_t st, const QmvBatch& bt) {
   switch (bits) {
-    case 2: return launch_t<T, 2>(x, wq, s, b, M, N, K, gs, y, st);
-    case 3: return launch_t<T, 3>(x, wq, s, b, M, N, K, gs, y, st);
-    case 4: return launch_t<T, 4>(x, wq, s, b, M, N, K, gs, y, st);
-    case 5: return launch_t<T, 5>(x, wq, s, b, M, N, K, gs, y, st);
-    case 6: return launch_t<T, 6>(x, wq, s, b, M, N, K, gs, y, st);
-    default: return launch_t<T, 8>(x, wq, s, b, M, N, K, gs, y, st);
+    case 2: return launch_t<T, 2>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    case 3: return launch_t<T, 3>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    case 4: return launch_t<T, 4>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    case 5: return launch_t<T, 5>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    case 6: return launch_t<T, 6>(x, wq, s, b, M, N, K, gs, y, st, bt);
+    default: return launch_t<T, 8>(x, wq, s, b, M, N, K, gs, y, st, bt);
   }
 }
 
@@ -540,8 +581,18 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
   if (route(dt, bits, gs, M, N, K, false) == kRouteQmvMfma)
     return launch_qmv_mfma(dt, bits, gs, x, wq, s, b, M, N, K, y, st);
   if (dt == 0)
-    return launch_bits<F16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
-  return launch_bits<BF16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st);
+    return launch_bits<F16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st, kOneBatch);
+  return launch_bits<BF16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st, kOneBatch);
+}
+
+hipError_t launch_gather_qmv(int dt, int bits, int gs, const void* x, int64_t nxb,
+                             const int32_t* lidx, const uint32_t* wq, const void* s,
+                             const void* b, int64_t nwb, const int32_t* ridx, int64_t B,
+                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
+  const QmvBatch bt{lidx, ridx, (int)nxb, (int)nwb, (int)B};
+  if (dt == 0)
+    return launch_bits<F16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st, bt);
+  return launch_bits<BF16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st, bt);
 }
 
 }  // namespace qmm

@@ -19,7 +19,7 @@ QMM_OK, QMM_E_NULL, QMM_E_BITS, QMM_E_GROUP, QMM_E_SHAPE, QMM_E_DTYPE, \
     QMM_E_ALIGN, QMM_E_LAUNCH = range(8)
 STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
-EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qconv2d_nhwc",
+EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qconv2d_nhwc", "qmm_gather_qmv",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -50,7 +50,10 @@ def lib():
         L.qconv2d_nhwc.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, i64, i32,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, vp]
-        for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qconv2d_nhwc"):
+        L.qmm_gather_qmv.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, i64,
+                                     i64, i64, i32, i32, vp, vp]
+        for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qconv2d_nhwc",
+                  "qmm_gather_qmv"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -131,6 +134,32 @@ def qmm_t(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
 def qmv(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
     """Same as qmm_t, always on the streaming GEMV."""
     return _matmul(lib().qmv, x, wq, scales, biases, group_size, bits, out, stream)
+
+
+def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_size=64,
+               bits=4, out=None, stream=None):
+    """y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T.
+
+    x [Bx, M, K]; wq [E, N, K*bits/32] (uint32 words); scales, biases
+    [E, N, K/group_size]; indices int32 device tensors of one length B (None:
+    z itself). Returns y [B, M, N]."""
+    Bx, M, K = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    if lhs_indices is not None:
+        B = lhs_indices.numel()
+    elif rhs_indices is not None:
+        B = rhs_indices.numel()
+    else:
+        B = Bx
+    for t in (lhs_indices, rhs_indices):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != B):
+            raise ValueError("indices must be int32 tensors of one length")
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    _check(lib().qmm_gather_qmv(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales),
+                                _ptr(biases), E, _ptr(rhs_indices), B, _dt(x.dtype), M, N, K,
+                                group_size, bits, _ptr(out), _stream(stream)))
+    return out
 
 
 def conv_out_hw(H, W, kh, kw, stride, padding):

@@ -124,6 +124,33 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                int64_t K, int group_size, int bits, void* y, void* stream);
 
 /*
+ * Gathered GEMV (one quantized weight per product, e.g. the experts of a
+ * mixture-of-experts layer at decode): for z in [0, batches),
+ *   y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T,
+ * where x is [x_batches, M, K], wq [w_batches, N, K*bits/32], scales and
+ * biases [w_batches, N, K/group_size], y [batches, M, N]; every product is
+ * the qmv/qmm_t product above with fp32 accumulation. lhs_indices and
+ * rhs_indices are DEVICE arrays of `batches` int32 (4-byte aligned); a NULL
+ * array means index z (then x, resp. W, needs at least `batches` batches).
+ * Index values are read on the device, so they cannot be checked here: a
+ * value outside [0, x_batches) or [0, w_batches) is clamped into range (no
+ * access leaves the arrays; that product then uses the clamped batch).
+ * Runs on the streaming GEMV (one pass over each selected W per up to 4
+ * rows of x), so K must be within its limit (QMM_E_SHAPE otherwise); meant
+ * for small M. batches <= 65535.
+ * (Source: "Add the 3bit packed qmm_t", ops.cpp gather_qmm: optional
+ * lhs_indices / rhs_indices, defaulting to the batch position, one product
+ * per index pair, one element type for x, scales, biases and y.)
+ */
+qmm_status qmm_gather_qmv(const void* x, int64_t x_batches,
+                          const int32_t* lhs_indices, const uint32_t* wq,
+                          const void* scales, const void* biases,
+                          int64_t w_batches, const int32_t* rhs_indices,
+                          int64_t batches, qmm_dtype dt, int64_t M, int64_t N,
+                          int64_t K, int group_size, int bits, void* y,
+                          void* stream);
+
+/*
  * Quantized 2-D convolution, NHWC, dilation 1, no bias:
  *   x [B,H,W,C] (dt), y [B,OH,OW,O] (dt), OH = (H + 2*pad_h - kh)/stride_h + 1,
  *   OW likewise. The weight [O, kh, kw, C/groups] is reshaped to

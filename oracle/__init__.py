@@ -205,6 +205,34 @@ def qmm_t(x, wq, scales, biases, dt, group_size=64, bits=4, nthreads=1,
     return y32, yo
 
 
+def gather_qmm(x, wq, scales, biases, lhs, rhs, dt, group_size=64, bits=4,
+               nthreads=1):
+    """Gathered products, "Add the 3bit packed qmm_t", ops.cpp gather_qmm:
+    one product per index pair, output z = x[lhs[z]] . dequant(W[rhs[z]])^T,
+    each computed by qmm_t above. A missing index array (None) means z.
+
+    x: [Bx, M, K] words; wq: [E, N, row bytes]; scales, biases: [E, N, K/gs]
+    words; lhs, rhs: int sequences (or None) of one length B. Indices must
+    lie in range. Returns (y32 [B,M,N], y_T [B,M,N])."""
+    x = np.asarray(x)
+    wq = np.asarray(wq)
+    Bx, M, _ = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    B = len(lhs) if lhs is not None else (len(rhs) if rhs is not None else Bx)
+    lhs = list(range(B)) if lhs is None else [int(v) for v in lhs]
+    rhs = list(range(B)) if rhs is None else [int(v) for v in rhs]
+    if len(lhs) != B or len(rhs) != B:
+        raise ValueError("gather_qmm: index arrays of different lengths")
+    y32 = np.zeros((B, M, N), np.float32)
+    yo = np.zeros((B, M, N), storage_dtype(dt))
+    for z in range(B):
+        if not (0 <= lhs[z] < Bx and 0 <= rhs[z] < E):
+            raise IndexError(f"gather_qmm: index pair ({lhs[z]}, {rhs[z]}) out of range")
+        y32[z], yo[z] = qmm_t(x[lhs[z]], wq[rhs[z]], scales[rhs[z]], biases[rhs[z]], dt,
+                              group_size, bits, nthreads)
+    return y32, yo
+
+
 def conv_out_hw(H, W, kh, kw, stride, pad):
     return ((H + 2 * pad[0] - kh) // stride[0] + 1,
             (W + 2 * pad[1] - kw) // stride[1] + 1)

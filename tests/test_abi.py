@@ -158,3 +158,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         Q.lib()
+
+
+def test_gather_arguments(L):
+    def g(x=P, nxb=2, li=None, wq=P, s=P, b=P, nwb=3, ri=None, B=2, dt=0, M=1, N=8, K=64,
+          gs=64, bits=4, y=P):
+        return _st(L, "qmm_gather_qmv", x, nxb, li, wq, s, b, nwb, ri, B, dt, M, N, K, gs,
+                   bits, y, None)
+    assert g(x=None) == Q.QMM_E_NULL
+    assert g(y=None) == Q.QMM_E_NULL
+    assert g(bits=7) == Q.QMM_E_BITS
+    assert g(gs=16) == Q.QMM_E_GROUP
+    assert g(dt=2) == Q.QMM_E_DTYPE
+    assert g(B=0) == Q.QMM_E_SHAPE
+    assert g(B=65536, li=P, ri=P) == Q.QMM_E_SHAPE
+    assert g(nxb=0) == Q.QMM_E_SHAPE
+    assert g(nwb=0, ri=P) == Q.QMM_E_SHAPE
+    assert g(nxb=1) == Q.QMM_E_SHAPE          # no lhs_indices: one x batch per output
+    assert g(nwb=1) == Q.QMM_E_SHAPE          # no rhs_indices: one W batch per output
+    assert b"batch" in L.qmm_last_error()
+    assert g(li=ctypes.c_void_p(0x10002)) == Q.QMM_E_ALIGN
+    assert g(ri=ctypes.c_void_p(0x10001)) == Q.QMM_E_ALIGN
+    assert g(x=P2) == Q.QMM_E_ALIGN
+    assert g(K=1 << 20) == Q.QMM_E_SHAPE      # beyond the streaming GEMV's K limit
+    assert b"K" in L.qmm_last_error()

@@ -389,3 +389,68 @@ def test_conv_config(orc, groups):
                        320, 3, 3, (1, 1), (1, 1), groups, gs, bits)
     torch.cuda.synchronize()
     assert_parity(from_dev(y), yo, dt, f"conv config groups={groups}")
+
+
+# ------------------------------------------------------------ gathered GEMV
+
+def _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed):
+    code = orc_code(orc, dt)
+    x = np.stack([synth.normal((M, K), seed=seed + i, dt=dt) for i in range(Bx)])
+    parts = [orc.quantize(synth.normal((N, K), seed=seed + 100 + e, dt=dt), code, gs, bits)
+             for e in range(E)]
+    wq = np.stack([p[0] for p in parts])
+    s = np.stack([p[1] for p in parts])
+    b = np.stack([p[2] for p in parts])
+    return code, x, wq, s, b
+
+
+def _idx_dev(v):
+    return None if v is None else torch.tensor(v, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("dt,Bx,E,M,N,K,gs,bits,lhs,rhs", [
+    ("f16", 4, 6, 1, 70, 640, 32, 4, [3, 0, 2, 2, 1], [5, 1, 1, 0, 4]),   # ragged N
+    ("bf16", 3, 3, 2, 96, 1024, 64, 3, None, None),                     # identity
+    ("f16", 1, 8, 3, 200, 2048, 128, 6, [0] * 6, [7, 3, 3, 0, 6, 1]),     # one token, 6 experts
+    ("bf16", 2, 4, 5, 33, 4160, 32, 2, [1, 0, 1, 0], [3, 2, 1, 0]),      # 2 row blocks of x;
+                                                                         # N*G % 8 != 0
+    ("f16", 1, 2, 1, 4096, 4096, 64, 4, [0, 0], [1, 0]),                 # 8-wavefront shape
+    ("f16", 2, 2, 1, 64, 11008, 64, 4, [1, 0], None),                    # rows over 1 batch
+    ("bf16", 2, 3, 1, 48, 512, 32, 8, [0, 1, 1], [2, 0, 2]),             # 8-bit bf16 (fp32)
+])
+def test_gather_qmv(orc, dt, Bx, E, M, N, K, gs, bits, lhs, rhs):
+    code, x, wq, s, b = _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed=K + E)
+    yo, _ = orc.gather_qmm(x, wq, s, b, lhs, rhs, code, gs, bits, nthreads=8)
+    y = Q.gather_qmv(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                     _idx_dev(lhs), _idx_dev(rhs), gs, bits)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == yo.shape
+    for z in range(yo.shape[0]):
+        assert_parity(from_dev(y[z]), yo[z], dt, f"gather_qmv batch {z}")
+
+
+def test_gather_qmv_clamps_indices(orc):
+    """Index values outside the batch ranges are clamped on the device."""
+    dt, Bx, E, M, N, K, gs, bits = "f16", 2, 3, 1, 40, 256, 32, 4
+    code, x, wq, s, b = _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed=5)
+    lhs, rhs = [-4, 1, 9], [2, 7, -1]
+    yo, _ = orc.gather_qmm(x, wq, s, b, [0, 1, 1], [2, 2, 0], code, gs, bits)
+    y = Q.gather_qmv(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                     _idx_dev(lhs), _idx_dev(rhs), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, "gather_qmv clamped")
+
+
+def test_gather_qmv_rejects_bad_arguments():
+    x = torch.zeros((2, 1, 64), dtype=torch.float16, device="cuda")
+    wq = torch.zeros((3, 8, 8), dtype=torch.int32, device="cuda")
+    s = torch.zeros((3, 8, 2), dtype=torch.float16, device="cuda")
+    with pytest.raises(Q.QmmError) as e:        # 3 outputs without lhs need 3 x batches
+        Q.gather_qmv(x, wq, s, s, None, _idx_dev([0, 1, 2]), 32, 4)
+    assert e.value.status == Q.QMM_E_SHAPE
+    with pytest.raises(Q.QmmError) as e:        # K beyond the streaming GEMV's limit
+        big = torch.zeros((1, 1, 65536), dtype=torch.float16, device="cuda")
+        wb = torch.zeros((1, 8, 65536 // 8), dtype=torch.int32, device="cuda")
+        sb = torch.zeros((1, 8, 2048), dtype=torch.float16, device="cuda")
+        Q.gather_qmv(big, wb, sb, sb, None, None, 32, 4)
+    assert e.value.status == Q.QMM_E_SHAPE
