@@ -220,7 +220,8 @@ def test_qmm_t_shapes(orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,gs,bits", [
-    (130, 200, 1536, 64, 4),    # 24 steps: three whole stages over two splits
+    (130, 200, 1536, 64, 4),    # 24 steps: too few to split (unsplit 64 x 64 tiles)
+    (200, 300, 4096, 32, 3),    # split 4 ways
     (64, 64, 2080, 32, 4),      # 33 steps: last split a single step, K % 64 == 32
     (257, 130, 4160, 64, 8),    # ragged M and N, K not a multiple of a stage
     (40, 300, 4096, 128, 2),
@@ -258,7 +259,7 @@ def test_qmm_t_split_k_back_to_back(orc):
     (smaller) result must not see the first one's partial sums."""
     code = orc_code(orc, "f16")
     outs = []
-    for (M, N, K, seed) in [(96, 256, 4096, 5), (40, 128, 1024, 6)]:
+    for (M, N, K, seed) in [(96, 256, 4096, 5), (40, 64, 2048, 6)]:
         x = synth.normal((M, K), seed=seed, dt="f16")
         w = synth.normal((N, K), seed=seed + 1, dt="f16")
         wq, s, b = orc.quantize(w, code, 64, 4)
