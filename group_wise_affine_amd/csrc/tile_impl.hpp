@@ -1188,10 +1188,12 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ncols, hipStream_t st) {
 // partial sums within the workspace. Returns 1 when K is not split.
 // gemm: for the plain 128 x 128 GEMM, each split also keeps >= 16 steps
 // (shorter ones spend most of their time filling and draining the copy
-// pipeline), and K is split only when the split grid offers at least the
-// parallelism of unsplit 64 x 64 tiles, counting a 128-row tile as half a
-// workgroup when M <= 64 (half its rows are padding). Measured on 512 x
-// 2048 x 2048: 22.1 us split 4 ways, 15.4 us unsplit on 64 x 64 tiles.
+// pipeline), and a split grid below 192 workgroups is used only when it
+// offers at least the parallelism of unsplit 64 x 64 tiles, counting a
+// 128-row tile as half a workgroup when M <= 64 (half its rows are
+// padding). Measured: 512 x 2048 x 2048 22.1 us split 4 ways, 15.4 us on
+// 64 x 64 tiles; 4096 x 320 x 2880 24.7 us split 2 ways (192 workgroups),
+// 27.0 us on 64 x 64 tiles.
 static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm = false) {
   const int nk = (a.K + 63) / 64;
   *ksteps = ((nk + kStageSteps - 1) / kStageSteps) * kStageSteps;
@@ -1202,7 +1204,7 @@ static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm 
   if (gemm) {
     if (s > nk / 16) s = nk / 16;
     const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64);
-    if (s >= 2 && tiles * s * (a.M <= 64 ? 1 : 2) < 2 * t64) return 1;
+    if (s >= 2 && tiles * s < 192 && tiles * s * (a.M <= 64 ? 1 : 2) < 2 * t64) return 1;
   }
   while (s > 1 && (int64_t)s * a.M * a.ldy > kSplitWsFloats) s--;
   if (s < 2) return 1;
