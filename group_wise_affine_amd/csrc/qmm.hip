@@ -75,6 +75,11 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
   a.kh = cg.kh; a.kw = cg.kw; a.sh = cg.sh; a.sw = cg.sw;
   a.ph = cg.ph; a.pw = cg.pw;
   a.Cg = (int)cg.Cg; a.Og = (int)cg.Og; a.K_true = (int)cg.K_true;
+  // exact for dividends below 2^16 (steps and taps here are far fewer)
+  auto div_mul = [](int d) { return d > 1 ? 0xffffffffu / (uint32_t)d + 1u : 0u; };
+  a.cu = (int)(cg.Cg / 64);
+  a.cu_mul = div_mul(a.cu);
+  a.kw_mul = div_mul(cg.kw);
   // the DMA path needs 16-byte x pieces (8 channels of one tap) and a k
   // table (one entry per 8 channels, dy and dx below 256) that fits in LDS
   const int64_t nk = (cg.K_pad + 63) / 64;

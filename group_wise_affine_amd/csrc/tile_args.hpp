@@ -18,6 +18,12 @@ struct GemmArgs {
   int64_t ldy;       // row stride of y in elements
   // implicit im2col (conv only)
   int H, W, C, OH, OW, kh, kw, sh, sw, ph, pw, Cg, Og, K_true;
+  // conv with Cg % 64 == 0: step t lies in tap t / cu (cu = Cg / 64) and tap
+  // u in kernel row u / kw; quotients of such small numbers are
+  // umulhi(n, mul) with mul = floor((2^32 - 1) / d) + 1 (0 for d == 1: the
+  // quotient is n)
+  int cu;
+  uint32_t cu_mul, kw_mul;
   // split K (tile kernel only): blockIdx.y takes K steps [y*ksteps,
   // (y+1)*ksteps) and, with ksplit > 1, writes fp32 partial sums to the
   // split-K workspace ws ([split][M][ldy], kSplitWsFloats floats) instead of y

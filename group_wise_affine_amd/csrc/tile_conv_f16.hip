@@ -5,8 +5,11 @@ namespace qmm {
 
 hipError_t launch_tile_conv_f16(int bits, const GemmArgs& a, int groups, bool dma,
                                 hipStream_t st) {
-  return dma ? launch_bits<F16, true, true>(bits, a, groups, st)
-             : launch_bits<F16, true, false>(bits, a, groups, st);
+  // channel counts per group that are a multiple of 64 keep every K step in
+  // one tap: those pieces are addressed without the k table
+  if (dma && a.Cg % 64 == 0) return launch_bits<F16, 2, true>(bits, a, groups, st);
+  return dma ? launch_bits<F16, 1, true>(bits, a, groups, st)
+             : launch_bits<F16, 1, false>(bits, a, groups, st);
 }
 
 }  // namespace qmm

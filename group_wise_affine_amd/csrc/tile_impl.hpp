@@ -569,7 +569,11 @@ constexpr int filler_slot(int f, int nf, int nm, int lead) {
   return lead + (f * (nm - lead)) / nf;
 }
 
-template <class T, int BITS, int BM, int BN, bool CONV>
+// CONV: 0 plain GEMM; 1 convolution, x pieces addressed through a k table in
+// LDS; 2 convolution whose per-group channel count is a multiple of 64, so
+// that the 64 codes of a K step lie in one tap and every piece of the step
+// is addressed from the step's tap and channel (no table, no LDS read).
+template <class T, int BITS, int BM, int BN, int CONV>
 __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   using G = DmaGeo<BM, BN, BITS>;
   constexpr bool kSplit = __is_same(T, BF16);
@@ -591,7 +595,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sl3[kSlotBytes];
   __shared__ uint32_t sct[2 * BN * 17];
-  __shared__ uint32_t ktab[CONV ? kKtabMax : 1];
+  __shared__ uint32_t ktab[CONV == 1 ? kKtabMax : 1];
   // target of the filler W copies of wavefronts with one block fewer
   __shared__ __attribute__((aligned(16))) uint8_t wjunk[G::W_BLOCKS % 4 ? 64 * WU : 16];
 
@@ -643,7 +647,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(a.magic));
 
   // ---- conv: k-unit table (dy, dx, channel) of every 8-channel unit
-  if constexpr (CONV) {
+  if constexpr (CONV == 1) {
     for (int ku = tid; ku < nk * 8; ku += 256) {
       const int k = ku * 8;
       uint32_t e = 0xffffffffu;
@@ -673,6 +677,10 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   int xcol[G::A_PER_WAVE];
   int pix_b[CONV ? G::A_PER_WAVE : 1], pix_y[CONV ? G::A_PER_WAVE : 1],
       pix_x[CONV ? G::A_PER_WAVE : 1];
+  // CONV == 2: element offset of the piece at tap (0, 0) of the row's output
+  // pixel, modulo 2^32 (it may lie outside the image: only taps inside it
+  // are read, and for those the sum below is the true offset)
+  uint32_t pix_o[CONV == 2 ? G::A_PER_WAVE : 1];
 #pragma unroll
   for (int i = 0; i < G::A_PER_WAVE; i++) {
     const int blk = 4 * i + wave;
@@ -691,6 +699,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       // rows past M get an impossible y so that every tap reads zeros
       pix_y[i] = m < a.M ? oy * a.sh - a.ph : -(1 << 28);
       pix_x[i] = ox * a.sw - a.pw;
+      if constexpr (CONV == 2)
+        pix_o[i] = (((uint32_t)pix_b[i] + (uint32_t)pix_y[i]) * (uint32_t)a.W +
+                    (uint32_t)pix_x[i]) * (uint32_t)a.C + (uint32_t)xcol[i];
       xoff[i] = 0;
     }
   }
@@ -727,7 +738,19 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       constexpr int i = D;
       const int blk = 4 * i + wave;
       uint16_t* xd = xslot.template operator()<S>() + blk * 512;
-      if constexpr (CONV) {
+      if constexpr (CONV == 2) {
+        // the step's 64 codes are channels [c0, c0 + 64) of tap (dy, dx)
+        const int k0 = 64 * tt;
+        const int tap = a.cu_mul ? (int)__umulhi((uint32_t)tt, a.cu_mul) : tt;
+        const int c0 = k0 - 64 * tap * a.cu;
+        const int dy = a.kw_mul ? (int)__umulhi((uint32_t)tap, a.kw_mul) : tap;
+        const int dx = tap - dy * a.kw;
+        const uint32_t dstep = (uint32_t)((dy * a.W + dx) * a.C + c0);   // uniform
+        const int iy = pix_y[i] + dy, ix = pix_x[i] + dx;
+        const bool in = k0 < a.K_true && (unsigned)iy < (unsigned)a.H &&
+                        (unsigned)ix < (unsigned)a.W;
+        dma_lds<16>(xr, xd, in ? (pix_o[i] + dstep) * 2u : kOob, 0);
+      } else if constexpr (CONV) {
         const int ku = 8 * tt + (xcol[i] >> 3);
         const uint32_t e = ku < nk * 8 ? ktab[ku] : 0xffffffffu;
         const int dy = (int)(e >> 24), dx = (int)((e >> 16) & 0xff);
@@ -1070,7 +1093,8 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int m = m_blk + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < a.M && n < a.N) ws[(int64_t)m * a.ldy + n] = acc[i][j][r];
+          // m * ldy + n < kSplitWsFloats = 2^24 floats per split: 24-bit product
+          if (m < a.M && n < a.N) ws[__umul24((uint32_t)m, (uint32_t)a.ldy) + n] = acc[i][j][r];
         }
       }
     return;
@@ -1129,7 +1153,7 @@ static hipError_t launch_gather(const GemmArgs& a, int groups, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class T, int BITS, int BM, int BN, bool CONV>
+template <class T, int BITS, int BM, int BN, int CONV>
 static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   const dim3 grid(tiles, 1, groups);
@@ -1216,7 +1240,7 @@ static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm 
 
 // tile kernel over a BM x BN tiling with K split by plan (fp32 partials +
 // reduction when split)
-template <class T, int BITS, int BM, int BN, bool CONV>
+template <class T, int BITS, int BM, int BN, int CONV>
 static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   int ksteps = 0;
@@ -1229,7 +1253,7 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   return launch_splitk_reduce<T>(a, (int)a.ldy, st);   // every column of y (all conv groups)
 }
 
-template <class T, int BITS, bool CONV, bool DMA>
+template <class T, int BITS, int CONV, bool DMA>
 static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
   const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
   if constexpr (DMA) {
@@ -1251,7 +1275,7 @@ static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
   }
 }
 
-template <class T, bool CONV, bool DMA>
+template <class T, int CONV, bool DMA>
 static hipError_t launch_bits(int bits, const GemmArgs& a, int groups,
                               hipStream_t st) {
   switch (bits) {
