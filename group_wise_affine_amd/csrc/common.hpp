@@ -37,12 +37,10 @@ __device__ __forceinline__ float to_f32(F32, float f) { return f; }
 __device__ __forceinline__ uint16_t from_f32(F16, float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to
+// nearest even under the default rounding mode; NaN stays a NaN).
 __device__ __forceinline__ uint16_t from_f32(BF16, float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ float from_f32(F32, float f) { return f; }
 
