@@ -1210,7 +1210,9 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ncols, hipStream_t st) {
 // workgroups within one wave over the 256 CUs (a second, partial wave costs
 // more than it saves), each split a whole number of 8-step stages, and the
 // partial sums within the workspace. Returns 1 when K is not split.
-// gemm: for the plain 128 x 128 GEMM, each split also keeps >= 16 steps
+// gemm (the plain f16 128 x 128 GEMM; bf16 runs two MFMAs per fragment and
+// more dequantization per step, and its 64 x 64 tiles measured slower: M =
+// 64, 2048 x 2048 25.3 us against 17.7 us split): each split also keeps >= 16 steps
 // (shorter ones spend most of their time filling and draining the copy
 // pipeline), and a split grid below 192 workgroups is used only when it
 // offers at least the parallelism of unsplit 64 x 64 tiles, counting a
@@ -1244,7 +1246,8 @@ template <class T, int BITS, int BM, int BN, int CONV>
 static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   int ksteps = 0;
-  a.ksplit = splitk_plan(a, (int64_t)tiles * groups, &ksteps, !CONV && BM == 128);
+  a.ksplit = splitk_plan(a, (int64_t)tiles * groups, &ksteps,
+                         !CONV && BM == 128 && __is_same(T, F16));
   a.ksteps = ksteps;
   hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV>), dim3(tiles, a.ksplit, groups),
                      dim3(256), 0, st, a);
@@ -1266,7 +1269,7 @@ static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
     if (a.N % 128 != 0 && a.N % 128 < 64) return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
     if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
     int ks;
-    if (splitk_plan(a, tiles128, &ks, !CONV) > 1)
+    if (splitk_plan(a, tiles128, &ks, !CONV && __is_same(T, F16)) > 1)
       return launch_dma_split<T, BITS, 128, 128, CONV>(a, groups, st);
     return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
   } else {
