@@ -138,10 +138,33 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     bias = edge;
   }
 
+  // Codes rint((w - bias) / scale) with the correctly rounded quotient, at
+  // the cost of a multiplication: t = d * fl(1/scale) lies within 3 * 2^-24
+  // * |t| of the rounded quotient fl(d / scale), so both round to the same
+  // integer unless t is that close to the half-integer between its floor and
+  // ceiling (ties included); there the quotient itself is computed (a branch
+  // a wavefront takes only when one of its lanes is that close; the margin
+  // used is 16 times the bound).
+  const float rscale = 1.0f / scale;
+  float d[8], t[8];
+  unsigned fix = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    d[i] = v[i] - bias;
+    t[i] = d[i] * rscale;
+    if (fabsf(t[i] - (floorf(t[i]) + 0.5f)) <= 0x1p-20f * fabsf(t[i])) fix |= 1u << i;
+  }
+  // a branch on the whole wavefront, so that the divisions are not computed
+  // speculatively for every element
+  if (__builtin_amdgcn_ballot_w64(fix != 0) != 0) {
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if ((fix >> i) & 1u) t[i] = d[i] / scale;
+  }
   uint64_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    float q = __builtin_rintf((v[i] - bias) / scale);
+    float q = __builtin_rintf(t[i]);
     q = q < 0.0f ? 0.0f : q;
     q = q > n_bins ? n_bins : q;
     packed |= (uint64_t)(uint32_t)q << (i * BITS);
