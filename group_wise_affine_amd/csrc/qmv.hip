@@ -23,7 +23,10 @@
 //    activation pairs in fp32. The MAGIC offset is removed through the chunk
 //    sum: s*sum(x*(MAGIC+q)) + (b - MAGIC*s)*sum(x) = sum(x*(s*q + b)).
 //  * Every W byte is read once per MB rows of x; one pass serves all of them.
-//  * Lanes of a row reduce with cross-lane shuffles; lane 0 writes y.
+//  * Lanes of a row reduce with DPP moves inside a 16-lane row and lane
+//    shuffles across rows; lane 0 writes y.
+//  * Gathered products (a compile-time variant): a third grid dimension over
+//    products, each with its own batch of x and of W (scales, biases) and y.
 #include "common.hpp"
 #include "kernels.hpp"
 
