@@ -61,6 +61,8 @@ def _declare(L):
     L.orc_qmm_t_rows.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32,
                                  i64, i64, vp, vp, i32]
     L.orc_qmm_t_rows.restype = i32
+    L.orc_qmm_n.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp, i32]
+    L.orc_qmm_n.restype = i32
     L.orc_qconv2d_nhwc.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, i64, i32,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, vp, i32]
@@ -202,6 +204,25 @@ def qmm_t(x, wq, scales, biases, dt, group_size=64, bits=4, nthreads=1,
                               K, group_size, bits, m0, m1, _p(y32), _p(yo),
                               nthreads)
     _chk(rc, "orc_qmm_t")
+    return y32, yo
+
+
+def qmm_n(x, wq, scales, biases, dt, group_size=64, bits=4, nthreads=1):
+    """Non-transposed product (mlx CPU backend _qmm): y = x . dequant(W)
+    with W [K, N] quantized along N. x: [M,K] words; wq: [K, N*bits/8]
+    bytes; scales, biases: [K, N/gs] words. Returns (y32, y_T)."""
+    x = _words(x, dt)
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    scales, biases = _words(scales, dt), _words(biases, dt)
+    M, K = x.shape
+    N = wq.shape[1] * 8 // bits
+    if wq.shape[0] != K:
+        raise ValueError("qmm_n: W must have K rows")
+    y32 = np.zeros((M, N), np.float32)
+    yo = np.zeros((M, N), storage_dtype(dt))
+    rc = lib().orc_qmm_n(_p(x), _p(wq), _p(scales), _p(biases), dt, M, N, K,
+                         group_size, bits, _p(y32), _p(yo), nthreads)
+    _chk(rc, "orc_qmm_n")
     return y32, yo
 
 

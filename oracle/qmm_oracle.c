@@ -319,6 +319,38 @@ int orc_qmm_t(const void* x, const uint8_t* wq, const void* scales,
 }
 
 /* ------------------------------------------------------------------ */
+/* Non-transposed product ([P4] _qmm): W [K, N] quantized along its rows  */
+/* (groups of N), y[m,n] = sum over k ascending of x[m,k] * w[k,n].      */
+/* ------------------------------------------------------------------ */
+
+int orc_qmm_n(const void* x, const uint8_t* wq, const void* scales,
+              const void* biases, int dtype, int64_t M, int64_t N, int64_t K,
+              int group_size, int bits, float* y32, void* y_out,
+              int nthreads) {
+  int rc = check_args(dtype, N, group_size, bits);
+  if (rc) return rc;
+  if (M < 1 || K < 1) return -3;
+  /* the K stored rows, each N long with its groups along N */
+  float* w32 = dequant_all(wq, scales, biases, dtype, K, N, group_size, bits);
+  if (!w32) return -5;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t n = 0; n < N; n++) {
+      float acc = 0.0f;
+      for (int64_t k = 0; k < K; k++) {
+        float prod = load_t(x, dtype, m * K + k) * w32[k * N + n];
+        acc = acc + prod;
+      }
+      if (y32) y32[m * N + n] = acc;
+      if (y_out) store_t(y_out, dtype, m * N + n, acc);
+    }
+  }
+  free(w32);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Quantized conv2d, NHWC, implicit im2col ([P1] img2col + forward).    */
 /* Patch element k of output pixel (b, oy, ox) in conv group g is       */
 /* (dy, dx, c) with k = (dy*kw + dx)*Cg + c, reading                    */

@@ -85,6 +85,15 @@ int orc_qmm_t_rows(const void* x, const uint8_t* wq, const void* scales,
                    int64_t K, int group_size, int bits, int64_t m0, int64_t m1,
                    float* y32, void* y_out, int nthreads);
 
+/* Non-transposed product ("mlx 1.0.0 backend/cpu/quantized.cpp", _qmm):
+ * W is [K, N], quantized along N (wq [K, N*bits/8] bytes, scales/biases
+ * [K, N/gs]): y32[M,N] = sum_k x[m,k] * w32[k,n], fp32, k ascending, no
+ * fused multiply-add; y_out = T(y32). Either output may be NULL. */
+int orc_qmm_n(const void* x, const uint8_t* wq, const void* scales,
+              const void* biases, int dtype, int64_t M, int64_t N, int64_t K,
+              int group_size, int bits, float* y32, void* y_out,
+              int nthreads);
+
 /* Quantized 2-D convolution, NHWC, via the implicit im2col of [P1]:
  *   x  [B,H,W,C] (T), wq/scales/biases quantize the weight
  *   [O, kh, kw, C/groups] reshaped to [O, K_true] and zero-padded to
