@@ -9,7 +9,8 @@ Headline (one step = one decode GEMV through the C ABI):
 
 The other rows of the hot path are measured in the same run and reported
 under "rows": quantize, dequantize, qmv at bits 2/8 and M <= 16, the gathered
-GEMV on a mixture-of-experts decode step (4 tokens, top-2 of 8 experts), the chained
+GEMV on a mixture-of-experts decode step (4 tokens, top-2 of 8 experts), the
+non-transposed decode product (W [4096, 4096] quantized along N), the chained
 qmm_t bench (10 loops of x = qmm(qmm(x, W1), W2), M=1024), the quantized
 conv2d (x [1,64,64,320], 3x3, groups 1 and 2) and the bf16 small-M sweep.
 
@@ -152,6 +153,27 @@ def bench_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
             "pool_copies": P,
             "workload": f"{T} tokens x top-{topk} of {E} experts [{N},{K}] {bits}-bit g{gs} f16"}
+
+
+def bench_qmm_n(torch, Q, synth, timer, steps, warmup, M=1, K=4096, N=4096, bits=4, gs=64):
+    """Non-transposed decode product y = x . dequant(W), W [K, N] quantized
+    along N (4-bit g64, f16); every step reads a different copy of W from a
+    >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    w = to_dev(synth.normal((K, N), seed=1), "f16")
+    layer = Q.qmm_quantize(w, gs, bits)
+    del w
+    wqs, ss, bs, P = pooled(torch, layer)
+    x = to_dev(synth.normal((M, K), seed=0), "f16")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.qmm_n(x, wqs[i % P], ss[i % P], bs[i % P], gs, bits, out=y),
+                   steps, warmup)
+    nbytes = alg_bytes(M, N, K, bits, gs)
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "pool_copies": P, "workload": f"x f16 [{M},{K}], W [{K},{N}] {bits}-bit g{gs} along N"}
 
 
 def bench_quantize(torch, Q, synth, timer, steps, warmup):
@@ -351,6 +373,10 @@ def main():
             k: round(v, 4) if isinstance(v, float) else v
             for k, v in bench_gather(torch, Q, synth, timer, n_small, 20).items()}
         log("gather row done")
+        rows["qmm_n_decode_4096x4096_f16_g64"] = {
+            k: round(v, 4) if isinstance(v, float) else v
+            for k, v in bench_qmm_n(torch, Q, synth, timer, n_small, 20).items()}
+        log("qmm_n row done")
         ch = {}
         for bits in (2, 4, 8):
             ch[f"bits{bits}"] = {k: round(v, 4) for k, v in

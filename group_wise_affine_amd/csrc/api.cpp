@@ -12,6 +12,7 @@
 
 #include "../../include/libqmm.h"
 #include "kernels.hpp"
+#include "tile_args.hpp"
 
 namespace {
 
@@ -159,6 +160,42 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
   return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                   biases, M, N, K, y, (hipStream_t)stream),
                   "qmv");
+}
+
+qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const void* biases,
+                 qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size, int bits,
+                 void* y, void* stream) {
+  if (!x || !wq || !scales || !biases || !y)
+    return fail(QMM_E_NULL, "qmm_n: x, wq, scales, biases and y must be non-NULL");
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qmm_n: only float16 and bfloat16 are supported (got dtype %d)",
+                (int)dt);
+  if (M < 1 || K < 1)
+    return fail(QMM_E_SHAPE, "qmm_n: M (%lld) and K (%lld) must be >= 1", (long long)M,
+                (long long)K);
+  if (N < 1 || N % group_size != 0)
+    return fail(QMM_E_SHAPE,
+                "qmm_n: N (%lld) must be a positive multiple of group_size (%d): the weight "
+                "[K, N] is quantized along N",
+                (long long)N, group_size);
+  const int64_t S = qmm::qmm_n_splits(K);
+  if (M > 65535 || S > 65535 || N > kI32 || M * K > ((int64_t)1 << 40) ||
+      N * K > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_n: problem too large (M <= 65535 rows of x per call)");
+  if (S > 1 && S * M * N > qmm::kSplitWsFloats)
+    return fail(QMM_E_SHAPE,
+                "qmm_n: the %lld K ranges x M x N partial sums exceed the split-K workspace "
+                "(%lld floats); pass fewer rows of x per call",
+                (long long)S, (long long)qmm::kSplitWsFloats);
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qmm_n: x, wq and y must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(biases, 2))
+    return fail(QMM_E_ALIGN, "qmm_n: scales and biases must be 2-byte aligned");
+  return launched(qmm::launch_qmm_n((int)dt, bits, group_size, x, wq, scales, biases, M, N, K,
+                                    y, (hipStream_t)stream),
+                  "qmm_n");
 }
 
 qmm_status qmm_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_indices,

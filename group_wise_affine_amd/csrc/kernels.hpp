@@ -56,6 +56,17 @@ inline bool qmv_mfma_fits(int64_t M, int64_t N, int64_t K, int gs) {
   return qmv_mfma_lds(M, p.klen, K, gs) <= kQmvMfmaMaxLds && M * (p.klen / 8) <= 8 * 1024 &&
          (15 + 32 * (K / gs) + 15) / 16 <= 2 * 1024;
 }
+// Non-transposed GEMV: y[M,N] = x[M,K] . dequant(W[K,N]) with W quantized
+// along N (N % gs == 0). K is split into qmm_n_splits(K) ranges; with more
+// than one, fp32 partial rows go to the split-K workspace
+// ([split][M][N], within kSplitWsFloats) and a second kernel adds them.
+int64_t qmm_n_splits(int64_t K);
+hipError_t launch_qmm_n(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                        const void* s, const void* b, int64_t M, int64_t N, int64_t K, void* y,
+                        hipStream_t st);
+// the current device's split-K workspace (a static device array), or null
+float* splitk_workspace();
+
 // Gathered streaming GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T
 // with x [nxb, M, K], W [nwb, N, K] (scales / biases [nwb, N, K/gs]) and
 // y [B, M, N]; a null index array means z. Indices are clamped into range.

@@ -35,6 +35,8 @@ float* splitk_ws() {
 
 }  // namespace
 
+float* splitk_workspace() { return splitk_ws(); }
+
 hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,
                            int64_t M, int64_t N, int64_t K, void* y,

@@ -19,7 +19,8 @@ QMM_OK, QMM_E_NULL, QMM_E_BITS, QMM_E_GROUP, QMM_E_SHAPE, QMM_E_DTYPE, \
     QMM_E_ALIGN, QMM_E_LAUNCH = range(8)
 STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
-EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qconv2d_nhwc", "qmm_gather_qmv",
+EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
+           "qmm_gather_qmv",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -50,9 +51,10 @@ def lib():
         L.qconv2d_nhwc.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, i64, i32,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, vp]
+        L.qmm_n.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
         L.qmm_gather_qmv.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, i64,
                                      i64, i64, i32, i32, vp, vp]
-        for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qconv2d_nhwc",
+        for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
                   "qmm_gather_qmv"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
@@ -134,6 +136,20 @@ def qmm_t(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
 def qmv(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
     """Same as qmm_t, always on the streaming GEMV."""
     return _matmul(lib().qmv, x, wq, scales, biases, group_size, bits, out, stream)
+
+
+def qmm_n(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
+    """y = x . dequant(W) with W [K, N] quantized along N: x [M, K], wq
+    [K, N*bits/32] (uint32 words), scales, biases [K, N/group_size]."""
+    M, K = x.shape
+    if wq.shape[0] != K:
+        raise ValueError("qmm_n: W must have K rows")
+    N = wq.shape[1] * 32 // bits
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(lib().qmm_n(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _dt(x.dtype), M, N, K,
+                       group_size, bits, _ptr(out), _stream(stream)))
+    return out
 
 
 def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_size=64,

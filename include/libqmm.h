@@ -124,6 +124,24 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                int64_t K, int group_size, int bits, void* y, void* stream);
 
 /*
+ * Non-transposed product: y[M,N] = x[M,K] . dequant(W)[K,N], where the
+ * weight W [K, N] is quantized along N (qmm_quantize of the K rows):
+ *   y[m,n] = sum_k x[m,k] * (scale[k,n/gs] * q[k,n] + bias[k,n/gs]),
+ * fp32 accumulation, y rounded to nearest even in dt. wq is [K, N*bits/32]
+ * uint32, scales and biases [K, N/group_size]; N must be a multiple of
+ * group_size (QMM_E_SHAPE otherwise). Meant for small M (decode): one pass
+ * over W per row of x, K split over workgroups; the fp32 partial sums of
+ * the K ranges (ceil(K/32) of them) go to the library's split-K workspace
+ * (shared with qmm_t on the device), so ceil(K/32) * M * N must stay within
+ * 16M floats when K > 32 (QMM_E_SHAPE otherwise). M <= 65535.
+ * (Source: "mlx 1.0.0 backend/cpu/quantized.cpp", _qmm, the non-transposed
+ * branch of quantized_matmul.)
+ */
+qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales,
+                 const void* biases, qmm_dtype dt, int64_t M, int64_t N,
+                 int64_t K, int group_size, int bits, void* y, void* stream);
+
+/*
  * Gathered GEMV (one quantized weight per product, e.g. the experts of a
  * mixture-of-experts layer at decode): for z in [0, batches),
  *   y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T,

@@ -182,3 +182,21 @@ def test_gather_arguments(L):
     assert g(x=P2) == Q.QMM_E_ALIGN
     assert g(K=1 << 20) == Q.QMM_E_SHAPE      # beyond the streaming GEMV's K limit
     assert b"K" in L.qmm_last_error()
+
+
+def test_qmm_n_arguments(L):
+    def f(x=P, wq=P, s=P, b=P, dt=0, M=1, N=64, K=64, gs=64, bits=4, y=P):
+        return _st(L, "qmm_n", x, wq, s, b, dt, M, N, K, gs, bits, y, None)
+    assert f(x=None) == Q.QMM_E_NULL
+    assert f(bits=7) == Q.QMM_E_BITS
+    assert f(gs=48) == Q.QMM_E_GROUP
+    assert f(dt=2) == Q.QMM_E_DTYPE
+    assert f(N=96) == Q.QMM_E_SHAPE           # W [K, N] is quantized along N
+    assert b"N" in L.qmm_last_error()
+    assert f(M=0) == Q.QMM_E_SHAPE
+    assert f(K=0) == Q.QMM_E_SHAPE
+    assert f(M=65536) == Q.QMM_E_SHAPE
+    assert f(M=64, N=8192, K=4096) == Q.QMM_E_SHAPE   # partial sums beyond the workspace
+    assert b"workspace" in L.qmm_last_error()
+    assert f(x=P2) == Q.QMM_E_ALIGN
+    assert f(s=ctypes.c_void_p(0x10001)) == Q.QMM_E_ALIGN

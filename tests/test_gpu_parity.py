@@ -455,3 +455,45 @@ def test_gather_qmv_rejects_bad_arguments():
         sb = torch.zeros((1, 8, 2048), dtype=torch.float16, device="cuda")
         Q.gather_qmv(big, wb, sb, sb, None, None, 32, 4)
     assert e.value.status == Q.QMM_E_SHAPE
+
+
+# ------------------------------------------------------------ non-transposed GEMV
+
+@pytest.mark.parametrize("dt,M,K,N,gs,bits", [
+    ("f16", 1, 4096, 4096, 64, 4),
+    ("bf16", 2, 640, 96, 32, 3),        # 3 chunks: a partial block of columns
+    ("f16", 3, 30, 256, 128, 5),        # one K range (direct write), K % 4 != 0
+    ("bf16", 1, 1000, 2112, 64, 6),     # 66 chunks: the second block holds 2
+    ("f16", 4, 2048, 512, 32, 2),
+    ("f16", 1, 11008, 4096, 64, 8),     # 344 K ranges
+    ("bf16", 1, 4096, 4096, 128, 8),
+])
+def test_qmm_n(orc, dt, M, K, N, gs, bits):
+    """y = x . dequant(W), W [K, N] quantized along N, against the oracle."""
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=K + N, dt=dt)
+    w = synth.normal((K, N), seed=K + N + 1, dt=dt)
+    wq, s, b = orc.quantize(w, code, gs, bits)
+    yo, _ = orc.qmm_n(x, wq, s, b, code, gs, bits, nthreads=8)
+    y = Q.qmm_n(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (M, N)
+    assert_parity(from_dev(y), yo, dt, f"qmm_n {M}x{K}x{N}")
+
+
+def test_qmm_n_repeat(orc):
+    """Calls in a row reuse the split-K workspace: a larger then a smaller
+    problem, both exact."""
+    code = orc_code(orc, "f16")
+    outs = []
+    for (M, K, N, seed) in [(2, 4096, 2048, 1), (1, 1024, 512, 2)]:
+        x = synth.normal((M, K), seed=seed, dt="f16")
+        w = synth.normal((K, N), seed=seed + 1, dt="f16")
+        wq, s, b = orc.quantize(w, code, 64, 4)
+        yo, _ = orc.qmm_n(x, wq, s, b, code, 64, 4, nthreads=8)
+        y = Q.qmm_n(to_dev(x, "f16"), bytes_to_words_dev(wq), to_dev(s, "f16"),
+                    to_dev(b, "f16"), 64, 4)
+        outs.append((y, yo, (M, K, N)))
+    torch.cuda.synchronize()
+    for y, yo, shape in outs:
+        assert_parity(from_dev(y), yo, "f16", f"qmm_n repeat {shape}")
