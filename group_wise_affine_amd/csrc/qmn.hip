@@ -6,18 +6,20 @@
 //
 // MI355X design (wave64):
 //  * The sum runs along the stored rows, so K is split over workgroups: a
-//    workgroup owns 64 chunks of 32 columns (lane l: chunk 64*blockIdx.x +
-//    l) and 32 rows of K; wavefront w of 8 streams rows w, w+8, ... of them
-//    (two wavefronts per SIMD issue arithmetic better than one). Every
-//    weight load of a lane (one 32-code chunk per row, 4*bits bytes) is
-//    issued before any arithmetic.
+//    workgroup owns 16 chunks of 32 columns and 128 rows of K. Lane l of
+//    wavefront w (8 of them: two per SIMD issue arithmetic better than one)
+//    takes chunk l % 16 and rows 4w + l/16 + 32i, i < 4, so one load
+//    instruction covers four rows of 16 chunks. Every weight load of a lane
+//    (one 32-code chunk per row, 4*bits bytes) is issued before any
+//    arithmetic.
 //  * A chunk lies in one group (gs >= 32), so per row a lane needs one scale
 //    and one bias: acc[j] += (x*s) * q_j for its 32 columns and one bias sum
 //    x*b shared by them.
-//  * The 8 wavefronts' partial chunks are added through LDS (in wavefront
-//    order); with several K ranges each writes its fp32 partial row to the
-//    split-K workspace and a second kernel adds the ranges in a fixed order
-//    (16 threads per output, each with its loads in flight together).
+//  * The 32 partial sums of a column (8 wavefronts x 4 row phases) are
+//    added through LDS in a fixed order. With several K ranges, each
+//    workgroup writes its fp32 partial row to the split-K workspace and a
+//    second kernel adds the ranges in a fixed order (16 threads per output,
+//    each with its loads in flight together).
 #include <utility>
 
 #include "common.hpp"
@@ -27,8 +29,10 @@ namespace qmm {
 namespace {
 
 constexpr int kQnWaves = 8;        // two wavefronts per SIMD
-constexpr int kQnRowsPerWave = 4;
-constexpr int kQnRows = kQnWaves * kQnRowsPerWave;   // rows of K per workgroup
+constexpr int kQnPhases = 4;       // row phases of a wavefront (lanes / 16)
+constexpr int kQnRowsPerLane = 4;
+constexpr int kQnChunks = 16;      // chunks of 32 columns per workgroup
+constexpr int kQnRows = kQnWaves * kQnPhases * kQnRowsPerLane;   // 128 rows of K
 
 // chunk of 32 codes (4*BITS bytes, 4-byte aligned) as BITS little-endian words
 template <int BITS>
@@ -97,21 +101,22 @@ __global__ __launch_bounds__(kQnWaves * 64) void qmn_kernel(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K, int gs_log2) {
   __shared__ float red[kQnWaves][64][33];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = N >> 5;
-  const int c = blockIdx.x * 64 + lane;
+  const int c = blockIdx.x * kQnChunks + (lane & 15);
   const int cc = c < nch ? c : nch - 1;          // lanes past N re-read a chunk
   const int split = blockIdx.y, m = blockIdx.z;
   const int G = N >> gs_log2;
   const int g = (cc << 5) >> gs_log2;            // the chunk's group
   const int64_t row_bytes = (int64_t)N * BITS / 8;
+  const int r0 = split * kQnRows + wave * kQnPhases + (lane >> 4);
 
-  uint32_t w[kQnRowsPerWave][BITS];
-  uint16_t sw[kQnRowsPerWave], bw[kQnRowsPerWave];
-  float xv[kQnRowsPerWave];
+  uint32_t w[kQnRowsPerLane][BITS];
+  uint16_t sw[kQnRowsPerLane], bw[kQnRowsPerLane];
+  float xv[kQnRowsPerLane];
 #pragma unroll
-  for (int i = 0; i < kQnRowsPerWave; i++) {
-    const int k = split * kQnRows + wave + kQnWaves * i;
+  for (int i = 0; i < kQnRowsPerLane; i++) {
+    const int k = r0 + kQnWaves * kQnPhases * i;
     const int kc = k < K ? k : K - 1;              // rows past K: x = 0
     load_chunk_n<BITS>(wq + (int64_t)kc * row_bytes + (int64_t)cc * (4 * BITS), w[i]);
     sw[i] = scales[(int64_t)kc * G + g];
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(kQnWaves * 64) void qmn_kernel(
   for (int j = 0; j < 32; j++) acc[j] = 0.0f;
   float bacc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kQnRowsPerWave; i++) {
+  for (int i = 0; i < kQnRowsPerLane; i++) {
     const float xs = xv[i] * to_f32(T{}, sw[i]);
     bacc = fmaf(xv[i], to_f32(T{}, bw[i]), bacc);
     fma_chunk<BITS>(w[i], xs, acc);
@@ -133,21 +138,22 @@ __global__ __launch_bounds__(kQnWaves * 64) void qmn_kernel(
   for (int j = 0; j < 32; j++) red[wave][lane][j] = acc[j] + bacc;
   __syncthreads();
 
-  // thread t adds the 8 wavefronts' values of 4 columns of chunk t / 8
-  const int tc = threadIdx.x >> 3, j0 = (threadIdx.x & 7) * 4;
-  const int c_out = blockIdx.x * 64 + tc;
-  if (c_out >= nch) return;
-  const int64_t n0 = (int64_t)c_out * 32 + j0;
+  // thread t: column t of the block (chunk t / 32), its 32 partial sums in
+  // wavefront then row-phase order
+  const int cj = tid >> 5, jj = tid & 31;
+  const int c_out = blockIdx.x * kQnChunks + cj;
+  const bool col_ok = c_out < nch;
+  const int64_t n = (int64_t)c_out * 32 + jj;
+  float v = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    float v = red[0][tc][j0 + j];
+  for (int wv = 0; wv < kQnWaves; wv++)
 #pragma unroll
-    for (int wv = 1; wv < kQnWaves; wv++) v += red[wv][tc][j0 + j];
-    if (gridDim.y == 1)
-      y[(int64_t)m * N + n0 + j] = from_f32(T{}, v);
-    else
-      ws[((int64_t)split * M + m) * N + n0 + j] = v;
+    for (int ph = 0; ph < kQnPhases; ph++) v += red[wv][16 * ph + cj][jj];
+  if (gridDim.y == 1) {
+    if (col_ok) y[(int64_t)m * N + n] = from_f32(T{}, v);
+    return;
   }
+  if (col_ok) ws[((int64_t)split * M + m) * N + n] = v;
 }
 
 // y[m, n] = sum over the S K ranges of the partial rows, in a fixed order: a
@@ -189,7 +195,7 @@ hipError_t launch_qmn_t(const void* x, const uint32_t* wq, const void* s, const 
                         int M, int N, int K, int gs, void* y, float* ws, hipStream_t st) {
   const int nch = N / 32;
   const int S = (K + kQnRows - 1) / kQnRows;
-  const dim3 grid((nch + 63) / 64, S, M);
+  const dim3 grid((nch + kQnChunks - 1) / kQnChunks, S, M);
   hipLaunchKernelGGL((qmn_kernel<T, BITS>), grid, dim3(kQnWaves * 64), 0, st,
                      static_cast<const uint16_t*>(x), reinterpret_cast<const uint8_t*>(wq),
                      static_cast<const uint16_t*>(s), static_cast<const uint16_t*>(b),

@@ -130,10 +130,11 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
  * fp32 accumulation, y rounded to nearest even in dt. wq is [K, N*bits/32]
  * uint32, scales and biases [K, N/group_size]; N must be a multiple of
  * group_size (QMM_E_SHAPE otherwise). Meant for small M (decode): one pass
- * over W per row of x, K split over workgroups; the fp32 partial sums of
- * the K ranges (ceil(K/32) of them) go to the library's split-K workspace
- * (shared with qmm_t on the device), so ceil(K/32) * M * N must stay within
- * 16M floats when K > 32 (QMM_E_SHAPE otherwise). M <= 65535.
+ * over W per row of x, K split over workgroups; when K > 128 the fp32
+ * partial sums of the ceil(K/128) K ranges go to the library's split-K
+ * workspace (shared with qmm_t on the device: calls that overlap on one
+ * device share it), so ceil(K/128) * M * N must stay within 16M floats
+ * (QMM_E_SHAPE otherwise). M <= 65535.
  * (Source: "mlx 1.0.0 backend/cpu/quantized.cpp", _qmm, the non-transposed
  * branch of quantized_matmul.)
  */

@@ -196,7 +196,7 @@ def test_qmm_n_arguments(L):
     assert f(M=0) == Q.QMM_E_SHAPE
     assert f(K=0) == Q.QMM_E_SHAPE
     assert f(M=65536) == Q.QMM_E_SHAPE
-    assert f(M=64, N=8192, K=4096) == Q.QMM_E_SHAPE   # partial sums beyond the workspace
+    assert f(M=64, N=8192, K=8192) == Q.QMM_E_SHAPE   # 64 K ranges x 64 x 8192 > 16M floats
     assert b"workspace" in L.qmm_last_error()
     assert f(x=P2) == Q.QMM_E_ALIGN
     assert f(s=ctypes.c_void_p(0x10001)) == Q.QMM_E_ALIGN
