@@ -155,6 +155,28 @@ def bench_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096
             "workload": f"{T} tokens x top-{topk} of {E} experts [{N},{K}] {bits}-bit g{gs} f16"}
 
 
+def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, bits=4, gs=64):
+    """Batched product with one weight per batch: y[b] = x[b] . dequant(W_b)^T,
+    x [B, M, K] f16, W_b [N, K] 4-bit g64 (qmm_t_batched). Every step reads a
+    different copy of the weight stack from a >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    layers = [make_layer(torch, Q, synth, "f16", N, K, gs, bits, 200 + e) for e in range(B)]
+    stack = tuple(torch.stack([l[i] for l in layers]) for i in range(3))
+    del layers
+    wqs, ss, bs, P = pooled(torch, stack)
+    x = to_dev(synth.normal((B, M, K), seed=9), "f16")
+    y = torch.empty((B, M, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.qmm_t_batched(x, wqs[i % P], ss[i % P], bs[i % P], gs, bits,
+                                             out=y), steps, warmup)
+    nbytes = B * alg_bytes(M, N, K, bits, gs)
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "TFLOP/s": 2 * B * M * N * K / (ms * 1e-3) / 1e12, "pool_copies": P,
+            "workload": f"{B} batches of x f16 [{M},{K}] x W_b [{N},{K}] {bits}-bit g{gs}"}
+
+
 def bench_qmm_n(torch, Q, synth, timer, steps, warmup, M=1, K=4096, N=4096, bits=4, gs=64):
     """Non-transposed decode product y = x . dequant(W), W [K, N] quantized
     along N (4-bit g64, f16); every step reads a different copy of W from a
@@ -377,6 +399,12 @@ def main():
             k: round(v, 4) if isinstance(v, float) else v
             for k, v in bench_qmm_n(torch, Q, synth, timer, n_small, 20).items()}
         log("qmm_n row done")
+        rows["qmm_t_batched_4096x4096_f16_g64"] = {
+            f"B{B}_M{M}": {k: round(v, 4) if isinstance(v, float) else v
+                           for k, v in bench_batched(torch, Q, synth, timer, n_small if M == 1
+                                                     else 20, 5, B, M).items()}
+            for (B, M) in [(8, 1), (4, 256)]}
+        log("batched rows done")
         ch = {}
         for bits in (2, 4, 8):
             ch[f"bits{bits}"] = {k: round(v, 4) for k, v in

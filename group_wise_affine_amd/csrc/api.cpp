@@ -162,6 +162,69 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                   "qmv");
 }
 
+qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
+                         const void* biases, int64_t batches, int64_t w_batches, qmm_dtype dt,
+                         int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
+                         void* stream) {
+  qmm_status st = check_matmul("qmm_t_batched", x, wq, scales, biases, dt, M, N, K, group_size,
+                               bits, y);
+  if (st) return st;
+  if (batches < 1 || batches > 65535)
+    return fail(QMM_E_SHAPE, "qmm_t_batched: batches (%lld) must be in [1, 65535]",
+                (long long)batches);
+  if (w_batches != 1 && w_batches != batches)
+    return fail(QMM_E_SHAPE,
+                "qmm_t_batched: w_batches (%lld) must be 1 (one weight for every batch) or "
+                "batches (%lld)",
+                (long long)w_batches, (long long)batches);
+  if (batches * M > kI32 || batches * M * K > ((int64_t)1 << 40) ||
+      batches * M * N > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_t_batched: problem too large");
+  // one weight for every batch: the batches are the rows of one product
+  if (w_batches == 1)
+    return qmm_t(x, wq, scales, biases, dt, batches * M, N, K, group_size, bits, y, stream);
+  const hipStream_t hs = (hipStream_t)stream;
+  const int64_t es = 2;   // element bytes (f16 / bf16)
+  const int64_t xs = M * K * es, ys = M * N * es, ws = N * (K * bits / 8),
+                ss = N * (K / group_size) * es;
+  const qmm::Route r = qmm::route((int)dt, bits, group_size, M, N, K, true);
+  // the streaming GEMV's rows: one gathered launch (batch b with weight b)
+  if (r == qmm::kRouteQmv)
+    return launched(qmm::launch_gather_qmv((int)dt, bits, group_size, x, batches, nullptr, wq,
+                                           scales, biases, batches, nullptr, batches, M, N, K, y,
+                                           hs),
+                    "qmm_t_batched");
+  if (r == qmm::kRouteTile && K >= qmm::kTileMaxK) {
+    return fail(QMM_E_SHAPE, "qmm_t_batched: K (%lld) must be below %lld for the MFMA tile kernel",
+                (long long)K, (long long)qmm::kTileMaxK);
+  }
+  // the MFMA GEMV's or the tile kernel's rows: one launch per batch, at the
+  // batch's offsets (which keep x, wq and y 16-byte aligned)
+  if (xs % 16 != 0 || ys % 16 != 0 || ws % 16 != 0)
+    return fail(QMM_E_ALIGN,
+                "qmm_t_batched: per-batch offsets of x (%lld B), y (%lld B) and wq (%lld B) must be "
+                "multiples of 16 bytes",
+                (long long)xs, (long long)ys, (long long)ws);
+  const char* xb = static_cast<const char*>(x);
+  const char* wb = reinterpret_cast<const char*>(wq);
+  const char* sb = static_cast<const char*>(scales);
+  const char* bb = static_cast<const char*>(biases);
+  char* yb = static_cast<char*>(y);
+  for (int64_t i = 0; i < batches; i++) {
+    const void* xi = xb + i * xs;
+    const uint32_t* wi = reinterpret_cast<const uint32_t*>(wb + i * ws);
+    const void* si = sb + i * ss;
+    const void* bi = bb + i * ss;
+    void* yi = yb + i * ys;
+    const hipError_t e =
+        (r == qmm::kRouteTile)
+            ? qmm::launch_qmm_mfma((int)dt, bits, group_size, xi, wi, si, bi, M, N, K, yi, hs)
+            : qmm::launch_qmv((int)dt, bits, group_size, xi, wi, si, bi, M, N, K, yi, hs);
+    if (e != hipSuccess) return launched(e, "qmm_t_batched");
+  }
+  return launched(hipSuccess, "qmm_t_batched");
+}
+
 qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const void* biases,
                  qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size, int bits,
                  void* y, void* stream) {

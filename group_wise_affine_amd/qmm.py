@@ -20,7 +20,7 @@ QMM_OK, QMM_E_NULL, QMM_E_BITS, QMM_E_GROUP, QMM_E_SHAPE, QMM_E_DTYPE, \
 STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
-           "qmm_gather_qmv",
+           "qmm_gather_qmv", "qmm_t_batched",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -54,8 +54,10 @@ def lib():
         L.qmm_n.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
         L.qmm_gather_qmv.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, i64,
                                      i64, i64, i32, i32, vp, vp]
+        L.qmm_t_batched.argtypes = [vp, vp, vp, vp, i64, i64, i32, i64, i64, i64, i32, i32,
+                                    vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
-                  "qmm_gather_qmv"):
+                  "qmm_gather_qmv", "qmm_t_batched"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -175,6 +177,20 @@ def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_
     _check(lib().qmm_gather_qmv(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales),
                                 _ptr(biases), E, _ptr(rhs_indices), B, _dt(x.dtype), M, N, K,
                                 group_size, bits, _ptr(out), _stream(stream)))
+    return out
+
+
+def qmm_t_batched(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
+    """y[b] = x[b] . dequant(W[b])^T, or the one W for every b: x [B, M, K];
+    wq [B or 1, N, K*bits/32] (uint32 words); scales, biases [B or 1, N,
+    K/group_size]. Returns y [B, M, N]."""
+    B, M, K = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    _check(lib().qmm_t_batched(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), B, E,
+                               _dt(x.dtype), M, N, K, group_size, bits, _ptr(out),
+                               _stream(stream)))
     return out
 
 

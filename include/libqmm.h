@@ -124,6 +124,29 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                int64_t K, int group_size, int bits, void* y, void* stream);
 
 /*
+ * Batched qmm_t: for b in [0, batches),
+ *   y[b] = x[b] . dequant(W[w_batches == 1 ? 0 : b])^T,
+ * with x [batches, M, K], wq [w_batches, N, K*bits/32], scales and biases
+ * [w_batches, N, K/group_size], y [batches, M, N], all contiguous, and
+ * w_batches either 1 (one weight for every batch: the batches' rows form
+ * one product of batches*M rows, as qmm_t) or batches (QMM_E_SHAPE
+ * otherwise). Every product is the qmm_t product above. With one weight per
+ * batch: few rows per batch run as one gathered GEMV launch (qmm_gather_qmv
+ * with no index arrays); otherwise one qmv/qmm_t launch per batch, which
+ * needs the per-batch sizes of x (M*K), y (M*N) and wq (N*K*bits/8 bytes)
+ * to be multiples of 16 bytes (QMM_E_ALIGN otherwise). batches <= 65535;
+ * the other rules are those of qmm_t.
+ * (Source: "Add the 3bit packed qmm_t", the batched adjust_matrix_offsets
+ * in quantized.h and the dispatch in quantized.cpp: a weight with batch
+ * dimensions selects one weight per batch, a 2-D weight takes every row of
+ * x as one product.)
+ */
+qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
+                         const void* biases, int64_t batches, int64_t w_batches,
+                         qmm_dtype dt, int64_t M, int64_t N, int64_t K,
+                         int group_size, int bits, void* y, void* stream);
+
+/*
  * Non-transposed product: y[M,N] = x[M,K] . dequant(W)[K,N], where the
  * weight W [K, N] is quantized along N (qmm_quantize of the K rows):
  *   y[m,n] = sum_k x[m,k] * (scale[k,n/gs] * q[k,n] + bias[k,n/gs]),
@@ -154,8 +177,8 @@ qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales,
  * Index values are read on the device, so they cannot be checked here: a
  * value outside [0, x_batches) or [0, w_batches) is clamped into range (no
  * access leaves the arrays; that product then uses the clamped batch).
- * Runs on the streaming GEMV (one pass over each selected W per up to 4
- * rows of x), so K must be within its limit (QMM_E_SHAPE otherwise); meant
+ * Runs on the streaming GEMV (one pass over each selected W per row of x),
+ * so K must be within its limit (QMM_E_SHAPE otherwise); meant
  * for small M. batches <= 65535.
  * (Source: "Add the 3bit packed qmm_t", ops.cpp gather_qmm: optional
  * lhs_indices / rhs_indices, defaulting to the batch position, one product

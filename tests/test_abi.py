@@ -184,6 +184,26 @@ def test_gather_arguments(L):
     assert b"K" in L.qmm_last_error()
 
 
+def test_batched_arguments(L):
+    def f(x=P, wq=P, s=P, b=P, B=2, E=2, dt=0, M=1, N=8, K=64, gs=64, bits=4, y=P):
+        return _st(L, "qmm_t_batched", x, wq, s, b, B, E, dt, M, N, K, gs, bits, y, None)
+    assert f(x=None) == Q.QMM_E_NULL
+    assert f(bits=7) == Q.QMM_E_BITS
+    assert f(gs=16) == Q.QMM_E_GROUP
+    assert f(dt=2) == Q.QMM_E_DTYPE
+    assert f(B=0) == Q.QMM_E_SHAPE
+    assert f(B=65536, E=65536) == Q.QMM_E_SHAPE
+    assert f(E=3) == Q.QMM_E_SHAPE            # one weight, or one per batch
+    assert b"w_batches" in L.qmm_last_error()
+    assert f(E=0) == Q.QMM_E_SHAPE
+    assert f(B=65535, E=1, M=65535) == Q.QMM_E_SHAPE   # batches * M rows beyond int32
+    assert f(x=P2) == Q.QMM_E_ALIGN
+    assert f(M=3, N=7) == Q.QMM_E_ALIGN       # MFMA GEMV per batch: y batch of 42 bytes
+    assert b"16 bytes" in L.qmm_last_error()
+    assert f(M=100, N=7) == Q.QMM_E_ALIGN     # tile kernel per batch: y batch of 1400 bytes
+    assert f(M=100, K=1 << 22) == Q.QMM_E_SHAPE   # beyond the tile kernel's K
+
+
 def test_qmm_n_arguments(L):
     def f(x=P, wq=P, s=P, b=P, dt=0, M=1, N=64, K=64, gs=64, bits=4, y=P):
         return _st(L, "qmm_n", x, wq, s, b, dt, M, N, K, gs, bits, y, None)

@@ -457,6 +457,38 @@ def test_gather_qmv_rejects_bad_arguments():
     assert e.value.status == Q.QMM_E_SHAPE
 
 
+# ------------------------------------------------------------ batched weights
+
+@pytest.mark.parametrize("dt,B,E,M,N,K,gs,bits", [
+    ("f16", 3, 3, 1, 520, 1024, 64, 4),      # per-batch W, streaming GEMV (one launch)
+    ("bf16", 4, 4, 2, 256, 512, 32, 3),      # per-batch W, bf16 streaming GEMV
+    ("f16", 3, 3, 8, 512, 2048, 128, 5),     # per-batch W, MFMA GEMV per batch
+    ("f16", 2, 2, 96, 384, 512, 64, 4),      # per-batch W, tile kernel per batch
+    ("bf16", 3, 3, 200, 256, 1024, 32, 8),   # per-batch W, ragged M tiles, 8-bit
+    ("f16", 4, 1, 5, 256, 512, 64, 6),       # one W for every batch: 20 rows, tile kernel
+    ("bf16", 3, 1, 1, 136, 768, 64, 2),      # one W for every batch: 3 rows, GEMV
+])
+def test_qmm_t_batched(orc, dt, B, E, M, N, K, gs, bits):
+    code, x, wq, s, b = _gather_inputs(orc, dt, B, E, M, N, K, gs, bits, seed=M + N + E)
+    yo, _ = orc.gather_qmm(x, wq, s, b, None, None if E == B else [0] * B, code, gs, bits,
+                           nthreads=8)
+    y = Q.qmm_t_batched(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                        gs, bits)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == yo.shape
+    for z in range(B):
+        assert_parity(from_dev(y[z]), yo[z], dt, f"qmm_t_batched batch {z}")
+
+
+def test_qmm_t_batched_rejects_unaligned_batches():
+    x = torch.zeros((2, 3, 64), dtype=torch.float16, device="cuda")
+    wq = torch.zeros((2, 7, 8), dtype=torch.int32, device="cuda")
+    s = torch.zeros((2, 7, 1), dtype=torch.float16, device="cuda")
+    with pytest.raises(Q.QmmError) as e:        # y batches of 3 x 7 halves: 42 bytes
+        Q.qmm_t_batched(x, wq, s, s, 64, 4)
+    assert e.value.status == Q.QMM_E_ALIGN
+
+
 # ------------------------------------------------------------ non-transposed GEMV
 
 @pytest.mark.parametrize("dt,M,K,N,gs,bits", [
