@@ -198,13 +198,19 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
     return fail(QMM_E_SHAPE, "qmm_t_batched: K (%lld) must be below %lld for the MFMA tile kernel",
                 (long long)K, (long long)qmm::kTileMaxK);
   }
-  // the MFMA GEMV's or the tile kernel's rows: one launch per batch, at the
-  // batch's offsets (which keep x, wq and y 16-byte aligned)
+  // the MFMA GEMV's or the tile kernel's rows: the batches start at offsets
+  // that keep x, wq and y 16-byte aligned
   if (xs % 16 != 0 || ys % 16 != 0 || ws % 16 != 0)
     return fail(QMM_E_ALIGN,
                 "qmm_t_batched: per-batch offsets of x (%lld B), y (%lld B) and wq (%lld B) must be "
                 "multiples of 16 bytes",
                 (long long)xs, (long long)ys, (long long)ws);
+  // tile kernel: one launch over all batches
+  if (r == qmm::kRouteTile)
+    return launched(qmm::launch_qmm_mfma((int)dt, bits, group_size, x, wq, scales, biases, M, N,
+                                         K, y, hs, batches),
+                    "qmm_t_batched");
+  // MFMA GEMV: one launch per batch
   const char* xb = static_cast<const char*>(x);
   const char* wb = reinterpret_cast<const char*>(wq);
   const char* sb = static_cast<const char*>(scales);
@@ -217,9 +223,7 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
     const void* bi = bb + i * ss;
     void* yi = yb + i * ys;
     const hipError_t e =
-        (r == qmm::kRouteTile)
-            ? qmm::launch_qmm_mfma((int)dt, bits, group_size, xi, wi, si, bi, M, N, K, yi, hs)
-            : qmm::launch_qmv((int)dt, bits, group_size, xi, wi, si, bi, M, N, K, yi, hs);
+        qmm::launch_qmv((int)dt, bits, group_size, xi, wi, si, bi, M, N, K, yi, hs);
     if (e != hipSuccess) return launched(e, "qmm_t_batched");
   }
   return launched(hipSuccess, "qmm_t_batched");

@@ -80,12 +80,16 @@ hipError_t launch_qmv_mfma(int dt, int bits, int gs, const void* x, const uint32
 
 // MFMA tile GEMM: y[M,N] = x[M,K] . dequant(W)[N,K]^T. K must be below
 // kTileMaxK (byte offsets inside a tile stay below 2^30, in range of the
-// buffer resources the tile kernel reads through).
+// buffer resources the tile kernel reads through). With batches > 1 (at most
+// 65535), one launch computes y[g] = x[g] . dequant(W[g])^T for every batch
+// g of contiguous x [batches, M, K], W [batches, N, K] and y [batches, M, N]
+// (every batch's x, wq and y 16-byte aligned; the split-K partial sums of
+// all batches within the workspace).
 constexpr int64_t kTileMaxK = (int64_t)1 << 22;
 hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,
                            int64_t M, int64_t N, int64_t K, void* y,
-                           hipStream_t st);
+                           hipStream_t st, int64_t batches = 1);
 
 // Implicit-im2col conv on the MFMA tile GEMM.
 struct ConvGeom {

@@ -40,7 +40,7 @@ float* splitk_workspace() { return splitk_ws(); }
 hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,
                            int64_t M, int64_t N, int64_t K, void* y,
-                           hipStream_t st) {
+                           hipStream_t st, int64_t batches) {
   GemmArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.wq = reinterpret_cast<const uint8_t*>(wq);
@@ -53,7 +53,8 @@ hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
   a.magic = F16::kMagic;
   a.ws = splitk_ws();
   if (!a.ws) return hipErrorInvalidSymbol;
-  return dt == 0 ? launch_tile_gemm_f16(bits, a, st) : launch_tile_gemm_bf16(bits, a, st);
+  return dt == 0 ? launch_tile_gemm_f16(bits, a, (int)batches, st)
+                 : launch_tile_gemm_bf16(bits, a, (int)batches, st);
 }
 
 hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,

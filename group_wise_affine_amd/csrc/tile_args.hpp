@@ -26,7 +26,8 @@ struct GemmArgs {
   uint32_t cu_mul, kw_mul;
   // split K (tile kernel only): blockIdx.y takes K steps [y*ksteps,
   // (y+1)*ksteps) and, with ksplit > 1, writes fp32 partial sums to the
-  // split-K workspace ws ([split][M][ldy], kSplitWsFloats floats) instead of y
+  // split-K workspace ws ([split][M][ldy], for a batched GEMM
+  // [split][batch][M][ldy]; kSplitWsFloats floats) instead of y
   int ksplit, ksteps;
   float* ws;
 };
@@ -38,9 +39,12 @@ constexpr int kKtabMax = 4096;      // conv k-unit table entries (K_pad <= 32768
 
 // Tile kernel launchers, one translation unit each (they compile in
 // parallel): plain GEMM and convolution, f16 and bf16. dma selects the
-// buffer-load kernel for convolutions (else the gather kernel).
-hipError_t launch_tile_gemm_f16(int bits, const GemmArgs& a, hipStream_t st);
-hipError_t launch_tile_gemm_bf16(int bits, const GemmArgs& a, hipStream_t st);
+// buffer-load kernel for convolutions (else the gather kernel). The GEMM
+// runs `batches` products of the same shape at once (blockIdx.z): batch g
+// reads x + g*M*K, wq + g*N*K*bits/8 bytes, scales and biases + g*N*K/gs,
+// and writes y + g*M*ldy.
+hipError_t launch_tile_gemm_f16(int bits, const GemmArgs& a, int batches, hipStream_t st);
+hipError_t launch_tile_gemm_bf16(int bits, const GemmArgs& a, int batches, hipStream_t st);
 hipError_t launch_tile_conv_f16(int bits, const GemmArgs& a, int groups, bool dma,
                                 hipStream_t st);
 hipError_t launch_tile_conv_bf16(int bits, const GemmArgs& a, int groups, bool dma,

@@ -616,7 +616,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   const int lane = tid & 63, h = lane >> 5, rr = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
-  const int g = CONV ? blockIdx.z : 0;
+  // blockIdx.z: the conv group, or the batch of a batched plain GEMM (x, W,
+  // scales, biases and y of batch g follow those of batch g - 1)
+  const int g = blockIdx.z;
   int tile = blockIdx.x;
   {
     // workgroup i runs on XCD i % 8: give each XCD a contiguous band of tiles
@@ -640,6 +642,10 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     wq += (int64_t)g * a.Og * row_bytes;
     sp += (int64_t)g * a.Og * n_groups;
     bp += (int64_t)g * a.Og * n_groups;
+  } else {
+    wq += (int64_t)g * a.N * row_bytes;
+    sp += (int64_t)g * a.N * n_groups;
+    bp += (int64_t)g * a.N * n_groups;
   }
 
   uint32_t magic_v;
@@ -667,7 +673,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // row M-1; their results are not stored). Conv: offsets from channel g*Cg
   // of the image, computed per step from the k table.
   const char* xbase = reinterpret_cast<const char*>(a.x) +
-                      (CONV ? (int64_t)g * a.Cg * 2 : (int64_t)m_blk * a.K * 2);
+                      (CONV ? (int64_t)g * a.Cg * 2 : ((int64_t)g * a.M + m_blk) * a.K * 2);
   const int64_t x_bytes =
       CONV ? (int64_t)(a.M / (a.OH * a.OW)) * a.H * a.W * a.C * 2 - (int64_t)g * a.Cg * 2
            : (int64_t)(a.M - m_blk) * a.K * 2;
@@ -1084,7 +1090,10 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // each store instruction covers two 128-byte row pieces)
   if (a.ksplit > 1) {
     wait_vmcnt<0>();   // no copy may still be landing in LDS when the wave ends
-    float* ws = a.ws + (int64_t)sk * a.M * a.ldy + (CONV ? (int64_t)g * a.Og : 0);
+    // conv: [split][M][ldy], the groups side by side in a row; batched GEMM:
+    // [split][batch][M][ldy]
+    float* ws = a.ws + (CONV ? (int64_t)sk * a.M * a.ldy + (int64_t)g * a.Og
+                             : ((int64_t)sk * gridDim.z + g) * a.M * a.ldy);
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -1120,7 +1129,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       }
     }
   __syncthreads();
-  uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : 0);
+  uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : (int64_t)g * a.M * a.ldy);
   constexpr int VPR = WTN / 8;
   const bool vec_ok = (a.N % 8 == 0) && (a.ldy % 8 == 0);
 #pragma unroll
@@ -1220,7 +1229,8 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ncols, hipStream_t st) {
 // padding). Measured: 512 x 2048 x 2048 22.1 us split 4 ways, 15.4 us on
 // 64 x 64 tiles; 4096 x 320 x 2880 24.7 us split 2 ways (192 workgroups),
 // 27.0 us on 64 x 64 tiles.
-static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm = false) {
+static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm = false,
+                       int batches = 1) {
   const int nk = (a.K + 63) / 64;
   *ksteps = ((nk + kStageSteps - 1) / kStageSteps) * kStageSteps;
   if (tiles >= 192 || a.ldy % 4 != 0) return 1;
@@ -1229,10 +1239,10 @@ static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm 
   if (s > nk / kStageSteps) s = nk / kStageSteps;
   if (gemm) {
     if (s > nk / 16) s = nk / 16;
-    const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64);
+    const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64) * batches;
     if (s >= 2 && tiles * s < 192 && tiles * s * (a.M <= 64 ? 1 : 2) < 2 * t64) return 1;
   }
-  while (s > 1 && (int64_t)s * a.M * a.ldy > kSplitWsFloats) s--;
+  while (s > 1 && (int64_t)s * batches * a.M * a.ldy > kSplitWsFloats) s--;
   if (s < 2) return 1;
   int per = (nk + s - 1) / s;
   per = ((per + kStageSteps - 1) / kStageSteps) * kStageSteps;
@@ -1247,13 +1257,15 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   int ksteps = 0;
   a.ksplit = splitk_plan(a, (int64_t)tiles * groups, &ksteps,
-                         !CONV && BM == 128 && __is_same(T, F16));
+                         !CONV && BM == 128 && __is_same(T, F16), CONV ? 1 : groups);
   a.ksteps = ksteps;
   hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV>), dim3(tiles, a.ksplit, groups),
                      dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
-  return launch_splitk_reduce<T>(a, (int)a.ldy, st);   // every column of y (all conv groups)
+  // every column of y (all conv groups); the batches of a GEMM as consecutive rows
+  if constexpr (!CONV) a.M *= groups;
+  return launch_splitk_reduce<T>(a, (int)a.ldy, st);
 }
 
 template <class T, int BITS, int CONV, bool DMA>
@@ -1269,7 +1281,7 @@ static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
     if (a.N % 128 != 0 && a.N % 128 < 64) return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
     if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
     int ks;
-    if (splitk_plan(a, tiles128, &ks, !CONV && __is_same(T, F16)) > 1)
+    if (splitk_plan(a, tiles128, &ks, !CONV && __is_same(T, F16), CONV ? 1 : groups) > 1)
       return launch_dma_split<T, BITS, 128, 128, CONV>(a, groups, st);
     return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
   } else {

@@ -131,11 +131,14 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
  * w_batches either 1 (one weight for every batch: the batches' rows form
  * one product of batches*M rows, as qmm_t) or batches (QMM_E_SHAPE
  * otherwise). Every product is the qmm_t product above. With one weight per
- * batch: few rows per batch run as one gathered GEMV launch (qmm_gather_qmv
- * with no index arrays); otherwise one qmv/qmm_t launch per batch, which
- * needs the per-batch sizes of x (M*K), y (M*N) and wq (N*K*bits/8 bytes)
- * to be multiples of 16 bytes (QMM_E_ALIGN otherwise). batches <= 65535;
- * the other rules are those of qmm_t.
+ * batch, by the qmm_t route for M rows: the streaming GEMV's rows run as
+ * one gathered GEMV launch (qmm_gather_qmv with no index arrays), the MFMA
+ * tile kernel's as one launch over all batches (its K split, if any, keeps
+ * the partial sums of every batch in the split-K workspace), the MFMA
+ * GEMV's as one launch per batch. The last two need the per-batch sizes of
+ * x (M*K), y (M*N) and wq (N*K*bits/8 bytes) to be multiples of 16 bytes
+ * (QMM_E_ALIGN otherwise). batches <= 65535; the other rules are those of
+ * qmm_t.
  * (Source: "Add the 3bit packed qmm_t", the batched adjust_matrix_offsets
  * in quantized.h and the dispatch in quantized.cpp: a weight with batch
  * dimensions selects one weight per batch, a 2-D weight takes every row of

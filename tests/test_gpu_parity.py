@@ -463,8 +463,11 @@ def test_gather_qmv_rejects_bad_arguments():
     ("f16", 3, 3, 1, 520, 1024, 64, 4),      # per-batch W, streaming GEMV (one launch)
     ("bf16", 4, 4, 2, 256, 512, 32, 3),      # per-batch W, bf16 streaming GEMV
     ("f16", 3, 3, 8, 512, 2048, 128, 5),     # per-batch W, MFMA GEMV per batch
-    ("f16", 2, 2, 96, 384, 512, 64, 4),      # per-batch W, tile kernel per batch
+    ("f16", 2, 2, 96, 384, 512, 64, 4),      # per-batch W, one tile launch (z = batch)
     ("bf16", 3, 3, 200, 256, 1024, 32, 8),   # per-batch W, ragged M tiles, 8-bit
+    ("f16", 2, 2, 64, 512, 4096, 64, 4),     # per-batch W, tile kernel, K split 4 ways
+    ("f16", 3, 3, 20, 256, 2048, 32, 3),     # 32-row tiles, K split, 3 batches
+    ("bf16", 2, 2, 24, 320, 1024, 128, 6),   # bf16 32-row tiles, N % 128 = 64
     ("f16", 4, 1, 5, 256, 512, 64, 6),       # one W for every batch: 20 rows, tile kernel
     ("bf16", 3, 1, 1, 136, 768, 64, 2),      # one W for every batch: 3 rows, GEMV
 ])
