@@ -155,6 +155,35 @@ def bench_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096
             "workload": f"{T} tokens x top-{topk} of {E} experts [{N},{K}] {bits}-bit g{gs} f16"}
 
 
+def bench_gather_prefill(torch, Q, synth, timer, steps, warmup, E=8, M=128, N=4096, K=4096,
+                         bits=4, gs=64):
+    """Mixture-of-experts prefill through the gathered tile GEMM: E blocks of
+    M tokens x [M, K] f16 (tokens grouped by expert), block z multiplied by
+    expert rhs[z] (a seeded permutation of the E experts W_e [N, K], 4-bit
+    g64), one qmm_gather_qmm call. Every step reads a different copy of the
+    expert stack from a >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    import numpy as np
+    layers = [make_layer(torch, Q, synth, "f16", N, K, gs, bits, 100 + e) for e in range(E)]
+    stack = tuple(torch.stack([l[i] for l in layers]) for i in range(3))
+    del layers
+    wqs, ss, bs, P = pooled(torch, stack)
+    x = to_dev(synth.normal((E, M, K), seed=11), "f16")
+    rhs = torch.tensor(np.random.default_rng(6).permutation(E).tolist(), dtype=torch.int32,
+                       device="cuda")
+    y = torch.empty((E, M, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.gather_qmm(x, wqs[i % P], ss[i % P], bs[i % P], None, rhs, gs,
+                                          bits, out=y), steps, warmup)
+    nbytes = E * alg_bytes(M, N, K, bits, gs)
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "TFLOP/s": 2 * E * M * N * K / (ms * 1e-3) / 1e12,
+            "mfma_frac": 2 * E * M * N * K / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "GB/s": nbytes / (ms * 1e-3) / 1e9, "pool_copies": P,
+            "workload": f"{E} blocks of {M} tokens, each x one of {E} experts [{N},{K}] "
+                        f"{bits}-bit g{gs} f16"}
+
+
 def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, bits=4, gs=64):
     """Batched product with one weight per batch: y[b] = x[b] . dequant(W_b)^T,
     x [B, M, K] f16, W_b [N, K] 4-bit g64 (qmm_t_batched). Every step reads a
@@ -395,6 +424,10 @@ def main():
             k: round(v, 4) if isinstance(v, float) else v
             for k, v in bench_gather(torch, Q, synth, timer, n_small, 20).items()}
         log("gather row done")
+        rows["gather_qmm_moe_prefill_f16_g64"] = {
+            k: round(v, 4) if isinstance(v, float) else v
+            for k, v in bench_gather_prefill(torch, Q, synth, timer, 20, 5).items()}
+        log("gather prefill row done")
         rows["qmm_n_decode_4096x4096_f16_g64"] = {
             k: round(v, 4) if isinstance(v, float) else v
             for k, v in bench_qmm_n(torch, Q, synth, timer, n_small, 20).items()}

@@ -265,31 +265,83 @@ qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const vo
                   "qmm_n");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the gathered products (qmm_gather_qmv, qmm_gather_qmm).
+qmm_status check_gather(const char* tag, const void* x, int64_t x_batches,
+                        const int32_t* lhs_indices, const uint32_t* wq, const void* scales,
+                        const void* biases, int64_t w_batches, const int32_t* rhs_indices,
+                        int64_t batches, qmm_dtype dt, int64_t M, int64_t N, int64_t K,
+                        int group_size, int bits, const void* y) {
+  qmm_status st = check_matmul(tag, x, wq, scales, biases, dt, M, N, K, group_size, bits, y);
+  if (st) return st;
+  if (batches < 1 || batches > 65535)
+    return fail(QMM_E_SHAPE, "%s: batches (%lld) must be in [1, 65535]", tag,
+                (long long)batches);
+  if (x_batches < 1 || w_batches < 1 || x_batches > kI32 || w_batches > kI32)
+    return fail(QMM_E_SHAPE, "%s: x_batches (%lld) and w_batches (%lld) must be >= 1", tag,
+                (long long)x_batches, (long long)w_batches);
+  if (!lhs_indices && x_batches < batches)
+    return fail(QMM_E_SHAPE, "%s: without lhs_indices, x needs one batch per output "
+                "batch (%lld < %lld)", tag, (long long)x_batches, (long long)batches);
+  if (!rhs_indices && w_batches < batches)
+    return fail(QMM_E_SHAPE, "%s: without rhs_indices, W needs one batch per output "
+                "batch (%lld < %lld)", tag, (long long)w_batches, (long long)batches);
+  if (!aligned(lhs_indices, 4) || !aligned(rhs_indices, 4))
+    return fail(QMM_E_ALIGN, "%s: index arrays must be 4-byte aligned", tag);
+  if (x_batches * M * K > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40) ||
+      batches * M * N > ((int64_t)1 << 40) || batches * M > kI32)
+    return fail(QMM_E_SHAPE, "%s: problem too large", tag);
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_gather_qmm(const void* x, int64_t x_batches, const int32_t* lhs_indices,
+                          const uint32_t* wq, const void* scales, const void* biases,
+                          int64_t w_batches, const int32_t* rhs_indices, int64_t batches,
+                          qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
+                          int bits, void* y, void* stream) {
+  qmm_status st = check_gather("qmm_gather_qmm", x, x_batches, lhs_indices, wq, scales, biases,
+                               w_batches, rhs_indices, batches, dt, M, N, K, group_size, bits,
+                               y);
+  if (st) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  // few rows per product: the gathered streaming GEMV
+  if (qmm::route((int)dt, bits, group_size, M, N, K, true) == qmm::kRouteQmv)
+    return launched(qmm::launch_gather_qmv((int)dt, bits, group_size, x, x_batches, lhs_indices,
+                                           wq, scales, biases, w_batches, rhs_indices, batches,
+                                           M, N, K, y, hs),
+                    "qmm_gather_qmm");
+  // the rest: the MFMA tile kernel, one launch, batch z in the grid
+  if (K >= qmm::kTileMaxK)
+    return fail(QMM_E_SHAPE, "qmm_gather_qmm: K (%lld) must be below %lld for the MFMA tile kernel",
+                (long long)K, (long long)qmm::kTileMaxK);
+  const int64_t xs = M * K * 2, ys = M * N * 2, ws = N * (K * bits / 8);
+  if (xs % 16 != 0 || ys % 16 != 0 || ws % 16 != 0)
+    return fail(QMM_E_ALIGN,
+                "qmm_gather_qmm: per-batch sizes of x (%lld B), y (%lld B) and wq (%lld B) must be "
+                "multiples of 16 bytes",
+                (long long)xs, (long long)ys, (long long)ws);
+  return launched(qmm::launch_gather_qmm_mfma((int)dt, bits, group_size, x, x_batches,
+                                              lhs_indices, wq, scales, biases, w_batches,
+                                              rhs_indices, batches, M, N, K, y, hs),
+                  "qmm_gather_qmm");
+}
+
 qmm_status qmm_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_indices,
                           const uint32_t* wq, const void* scales, const void* biases,
                           int64_t w_batches, const int32_t* rhs_indices, int64_t batches,
                           qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
                           int bits, void* y, void* stream) {
-  qmm_status st = check_matmul("qmm_gather_qmv", x, wq, scales, biases, dt, M, N, K,
-                               group_size, bits, y);
+  qmm_status st = check_gather("qmm_gather_qmv", x, x_batches, lhs_indices, wq, scales, biases,
+                               w_batches, rhs_indices, batches, dt, M, N, K, group_size, bits,
+                               y);
   if (st) return st;
-  if (batches < 1 || batches > 65535)
-    return fail(QMM_E_SHAPE, "qmm_gather_qmv: batches (%lld) must be in [1, 65535]",
-                (long long)batches);
-  if (x_batches < 1 || w_batches < 1 || x_batches > kI32 || w_batches > kI32)
-    return fail(QMM_E_SHAPE, "qmm_gather_qmv: x_batches (%lld) and w_batches (%lld) must be >= 1",
-                (long long)x_batches, (long long)w_batches);
-  if (!lhs_indices && x_batches < batches)
-    return fail(QMM_E_SHAPE, "qmm_gather_qmv: without lhs_indices, x needs one batch per output "
-                "batch (%lld < %lld)", (long long)x_batches, (long long)batches);
-  if (!rhs_indices && w_batches < batches)
-    return fail(QMM_E_SHAPE, "qmm_gather_qmv: without rhs_indices, W needs one batch per output "
-                "batch (%lld < %lld)", (long long)w_batches, (long long)batches);
-  if (!aligned(lhs_indices, 4) || !aligned(rhs_indices, 4))
-    return fail(QMM_E_ALIGN, "qmm_gather_qmv: index arrays must be 4-byte aligned");
-  if (x_batches * M * K > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40) ||
-      batches * M * N > ((int64_t)1 << 40))
-    return fail(QMM_E_SHAPE, "qmm_gather_qmv: problem too large");
   if (K > qmm::qmv_max_k(bits, (int)dt))
     return fail(QMM_E_SHAPE, "qmm_gather_qmv: K (%lld) exceeds the streaming GEMV's limit (%lld "
                 "for this bits/dtype)", (long long)K, (long long)qmm::qmv_max_k(bits, (int)dt));

@@ -91,6 +91,15 @@ hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            int64_t M, int64_t N, int64_t K, void* y,
                            hipStream_t st, int64_t batches = 1);
 
+// Gathered MFMA tile GEMM: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T
+// with x [nxb, M, K], W [nwb, N, K], y [B, M, N] (a null index array means
+// z; indices are clamped into range). Same limits as launch_qmm_mfma with
+// batches = B.
+hipError_t launch_gather_qmm_mfma(int dt, int bits, int gs, const void* x, int64_t nxb,
+                                  const int32_t* lidx, const uint32_t* wq, const void* s,
+                                  const void* b, int64_t nwb, const int32_t* ridx, int64_t B,
+                                  int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
+
 // Implicit-im2col conv on the MFMA tile GEMM.
 struct ConvGeom {
   int64_t B, H, W, C, O, OH, OW;

@@ -41,6 +41,14 @@ hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,
                            int64_t M, int64_t N, int64_t K, void* y,
                            hipStream_t st, int64_t batches) {
+  return launch_gather_qmm_mfma(dt, bits, gs, x, batches, nullptr, wq, s, b, batches, nullptr,
+                                batches, M, N, K, y, st);
+}
+
+hipError_t launch_gather_qmm_mfma(int dt, int bits, int gs, const void* x, int64_t nxb,
+                                  const int32_t* lidx, const uint32_t* wq, const void* s,
+                                  const void* b, int64_t nwb, const int32_t* ridx, int64_t B,
+                                  int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
   GemmArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.wq = reinterpret_cast<const uint8_t*>(wq);
@@ -51,10 +59,12 @@ hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
   a.gs_log2 = ilog2(gs);
   a.ldy = N;
   a.magic = F16::kMagic;
+  a.lidx = lidx; a.ridx = ridx;
+  a.nxb = (int)nxb; a.nwb = (int)nwb;
   a.ws = splitk_ws();
   if (!a.ws) return hipErrorInvalidSymbol;
-  return dt == 0 ? launch_tile_gemm_f16(bits, a, (int)batches, st)
-                 : launch_tile_gemm_bf16(bits, a, (int)batches, st);
+  return dt == 0 ? launch_tile_gemm_f16(bits, a, (int)B, st)
+                 : launch_tile_gemm_bf16(bits, a, (int)B, st);
 }
 
 hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,

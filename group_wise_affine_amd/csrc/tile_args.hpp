@@ -30,6 +30,12 @@ struct GemmArgs {
   // [split][batch][M][ldy]; kSplitWsFloats floats) instead of y
   int ksplit, ksteps;
   float* ws;
+  // gathered GEMM (plain GEMM only): batch g multiplies x batch lidx[g] (of
+  // nxb) by weight batch ridx[g] (of nwb), indices clamped into range; a
+  // null array means g
+  const int32_t* lidx;
+  const int32_t* ridx;
+  int nxb, nwb;
 };
 
 // Split-K workspace size: [split][M][ldy] fp32 partial sums, library-owned

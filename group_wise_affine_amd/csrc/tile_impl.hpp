@@ -617,7 +617,8 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
   // blockIdx.z: the conv group, or the batch of a batched plain GEMM (x, W,
-  // scales, biases and y of batch g follow those of batch g - 1)
+  // scales, biases and y of batch g follow those of batch g - 1; a gathered
+  // GEMM takes x and W from the batches its index arrays name)
   const int g = blockIdx.z;
   int tile = blockIdx.x;
   {
@@ -638,14 +639,24 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   const uint8_t* wq = a.wq;
   const uint16_t* sp = a.s;
   const uint16_t* bp = a.b;
+  int gx = g;   // x batch of a batched GEMM
   if constexpr (CONV) {
     wq += (int64_t)g * a.Og * row_bytes;
     sp += (int64_t)g * a.Og * n_groups;
     bp += (int64_t)g * a.Og * n_groups;
   } else {
-    wq += (int64_t)g * a.N * row_bytes;
-    sp += (int64_t)g * a.N * n_groups;
-    bp += (int64_t)g * a.N * n_groups;
+    int gw = g;
+    if (a.lidx) {
+      const int v = a.lidx[g];
+      gx = v < 0 ? 0 : (v >= a.nxb ? a.nxb - 1 : v);
+    }
+    if (a.ridx) {
+      const int v = a.ridx[g];
+      gw = v < 0 ? 0 : (v >= a.nwb ? a.nwb - 1 : v);
+    }
+    wq += (int64_t)gw * a.N * row_bytes;
+    sp += (int64_t)gw * a.N * n_groups;
+    bp += (int64_t)gw * a.N * n_groups;
   }
 
   uint32_t magic_v;
@@ -673,7 +684,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // row M-1; their results are not stored). Conv: offsets from channel g*Cg
   // of the image, computed per step from the k table.
   const char* xbase = reinterpret_cast<const char*>(a.x) +
-                      (CONV ? (int64_t)g * a.Cg * 2 : ((int64_t)g * a.M + m_blk) * a.K * 2);
+                      (CONV ? (int64_t)g * a.Cg * 2 : ((int64_t)gx * a.M + m_blk) * a.K * 2);
   const int64_t x_bytes =
       CONV ? (int64_t)(a.M / (a.OH * a.OW)) * a.H * a.W * a.C * 2 - (int64_t)g * a.Cg * 2
            : (int64_t)(a.M - m_blk) * a.K * 2;

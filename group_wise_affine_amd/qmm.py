@@ -20,7 +20,7 @@ QMM_OK, QMM_E_NULL, QMM_E_BITS, QMM_E_GROUP, QMM_E_SHAPE, QMM_E_DTYPE, \
 STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
-           "qmm_gather_qmv", "qmm_t_batched",
+           "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -54,10 +54,11 @@ def lib():
         L.qmm_n.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
         L.qmm_gather_qmv.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, i64,
                                      i64, i64, i32, i32, vp, vp]
+        L.qmm_gather_qmm.argtypes = L.qmm_gather_qmv.argtypes
         L.qmm_t_batched.argtypes = [vp, vp, vp, vp, i64, i64, i32, i64, i64, i64, i32, i32,
                                     vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
-                  "qmm_gather_qmv", "qmm_t_batched"):
+                  "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -155,8 +156,9 @@ def qmm_n(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
 
 
 def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_size=64,
-               bits=4, out=None, stream=None):
-    """y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T.
+               bits=4, out=None, stream=None, _fn="qmm_gather_qmv"):
+    """y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T on the
+    gathered streaming GEMV (small M).
 
     x [Bx, M, K]; wq [E, N, K*bits/32] (uint32 words); scales, biases
     [E, N, K/group_size]; indices int32 device tensors of one length B (None:
@@ -174,10 +176,17 @@ def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_
             raise ValueError("indices must be int32 tensors of one length")
     if out is None:
         out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
-    _check(lib().qmm_gather_qmv(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales),
-                                _ptr(biases), E, _ptr(rhs_indices), B, _dt(x.dtype), M, N, K,
-                                group_size, bits, _ptr(out), _stream(stream)))
+    _check(getattr(lib(), _fn)(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales),
+                               _ptr(biases), E, _ptr(rhs_indices), B, _dt(x.dtype), M, N, K,
+                               group_size, bits, _ptr(out), _stream(stream)))
     return out
+
+
+def gather_qmm(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_size=64,
+               bits=4, out=None, stream=None):
+    """Same as gather_qmv for any M (the MFMA tile kernel beyond a few rows)."""
+    return gather_qmv(x, wq, scales, biases, lhs_indices, rhs_indices, group_size, bits, out,
+                      stream, _fn="qmm_gather_qmm")
 
 
 def qmm_t_batched(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):

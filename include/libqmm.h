@@ -196,6 +196,28 @@ qmm_status qmm_gather_qmv(const void* x, int64_t x_batches,
                           void* stream);
 
 /*
+ * Gathered product for any M (e.g. the experts of a mixture-of-experts
+ * layer with many tokens per expert): same operation, arguments, index
+ * rules and clamping as qmm_gather_qmv. Few rows per product (the qmm_t
+ * route's streaming GEMV rows) run on the gathered streaming GEMV; the rest
+ * on the MFMA tile kernel in one launch, which needs K below its limit and
+ * the per-batch sizes of x (M*K), y (M*N) and wq (N*K*bits/8 bytes) to be
+ * multiples of 16 bytes (QMM_E_SHAPE / QMM_E_ALIGN otherwise); a K split
+ * keeps the partial sums of all products in the split-K workspace.
+ * batches <= 65535 and batches*M < 2^31.
+ * (Source: "Add the 3bit packed qmm_t", ops.cpp gather_qmm, as for
+ * qmm_gather_qmv; the per-batch offsets of the batched
+ * adjust_matrix_offsets in quantized.h.)
+ */
+qmm_status qmm_gather_qmm(const void* x, int64_t x_batches,
+                          const int32_t* lhs_indices, const uint32_t* wq,
+                          const void* scales, const void* biases,
+                          int64_t w_batches, const int32_t* rhs_indices,
+                          int64_t batches, qmm_dtype dt, int64_t M, int64_t N,
+                          int64_t K, int group_size, int bits, void* y,
+                          void* stream);
+
+/*
  * Quantized 2-D convolution, NHWC, dilation 1, no bias:
  *   x [B,H,W,C] (dt), y [B,OH,OW,O] (dt), OH = (H + 2*pad_h - kh)/stride_h + 1,
  *   OW likewise. The weight [O, kh, kw, C/groups] is reshaped to

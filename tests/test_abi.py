@@ -184,6 +184,28 @@ def test_gather_arguments(L):
     assert b"K" in L.qmm_last_error()
 
 
+def test_gather_qmm_arguments(L):
+    def g(x=P, nxb=2, li=None, wq=P, s=P, b=P, nwb=3, ri=None, B=2, dt=0, M=3, N=8, K=64,
+          gs=64, bits=4, y=P):
+        return _st(L, "qmm_gather_qmm", x, nxb, li, wq, s, b, nwb, ri, B, dt, M, N, K, gs,
+                   bits, y, None)
+    assert g(x=None) == Q.QMM_E_NULL
+    assert g(bits=7) == Q.QMM_E_BITS
+    assert g(gs=16) == Q.QMM_E_GROUP
+    assert g(dt=2) == Q.QMM_E_DTYPE
+    assert g(B=0) == Q.QMM_E_SHAPE
+    assert g(B=65536, li=P, ri=P) == Q.QMM_E_SHAPE
+    assert g(nxb=1) == Q.QMM_E_SHAPE          # no lhs_indices: one x batch per output
+    assert g(nwb=1) == Q.QMM_E_SHAPE          # no rhs_indices: one W batch per output
+    assert g(li=ctypes.c_void_p(0x10002)) == Q.QMM_E_ALIGN
+    assert g(B=65535, li=P, ri=P, M=65535) == Q.QMM_E_SHAPE   # batches * M beyond int32
+    assert g(x=P2) == Q.QMM_E_ALIGN
+    assert g(N=7) == Q.QMM_E_ALIGN            # tile kernel: y batches of 42 bytes
+    assert b"16 bytes" in L.qmm_last_error()
+    assert g(M=100, K=1 << 22) == Q.QMM_E_SHAPE   # beyond the tile kernel's K
+    assert b"K" in L.qmm_last_error()
+
+
 def test_batched_arguments(L):
     def f(x=P, wq=P, s=P, b=P, B=2, E=2, dt=0, M=1, N=8, K=64, gs=64, bits=4, y=P):
         return _st(L, "qmm_t_batched", x, wq, s, b, B, E, dt, M, N, K, gs, bits, y, None)

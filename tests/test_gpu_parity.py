@@ -457,6 +457,37 @@ def test_gather_qmv_rejects_bad_arguments():
     assert e.value.status == Q.QMM_E_SHAPE
 
 
+@pytest.mark.parametrize("dt,Bx,E,M,N,K,gs,bits,lhs,rhs", [
+    ("f16", 4, 6, 64, 256, 512, 64, 4, [3, 0, 2, 2, 1], [5, 1, 1, 0, 4]),  # tile kernel
+    ("bf16", 2, 3, 40, 320, 1024, 32, 3, [1, 0, 1], [2, 2, 0]),          # ragged M, bf16
+    ("f16", 1, 8, 16, 512, 2048, 128, 6, [0] * 4, [7, 3, 3, 0]),         # 32-row tiles, K split
+    ("f16", 3, 4, 128, 384, 4096, 64, 4, [2, 1, 0, 2], [3, 2, 1, 0]),    # K split 4 ways
+    ("bf16", 2, 2, 200, 128, 256, 32, 8, None, [1, 0]),                  # 8-bit, rhs only
+    ("f16", 2, 3, 2, 96, 512, 32, 5, [1, 0], [2, 2]),                    # gathered GEMV rows
+])
+def test_gather_qmm(orc, dt, Bx, E, M, N, K, gs, bits, lhs, rhs):
+    code, x, wq, s, b = _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed=M + K + E)
+    yo, _ = orc.gather_qmm(x, wq, s, b, lhs, rhs, code, gs, bits, nthreads=8)
+    y = Q.gather_qmm(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                     _idx_dev(lhs), _idx_dev(rhs), gs, bits)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == yo.shape
+    for z in range(yo.shape[0]):
+        assert_parity(from_dev(y[z]), yo[z], dt, f"gather_qmm batch {z}")
+
+
+def test_gather_qmm_clamps_indices(orc):
+    """Index values outside the batch ranges are clamped in the tile kernel."""
+    dt, Bx, E, M, N, K, gs, bits = "f16", 2, 3, 48, 128, 512, 64, 4
+    code, x, wq, s, b = _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed=15)
+    lhs, rhs = [-3, 1, 5], [9, 0, -1]
+    yo, _ = orc.gather_qmm(x, wq, s, b, [0, 1, 1], [2, 0, 0], code, gs, bits)
+    y = Q.gather_qmm(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                     _idx_dev(lhs), _idx_dev(rhs), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, "gather_qmm clamped")
+
+
 # ------------------------------------------------------------ batched weights
 
 @pytest.mark.parametrize("dt,B,E,M,N,K,gs,bits", [
