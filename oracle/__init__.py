@@ -67,6 +67,25 @@ def _declare(L):
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, vp, i32]
     L.orc_qconv2d_nhwc.restype = i32
+    u8, f32 = ctypes.c_uint8, ctypes.c_float
+    L.orc_fp4_value.argtypes = [u8]
+    L.orc_fp4_value.restype = f32
+    L.orc_fp4_encode.argtypes = [f32]
+    L.orc_fp4_encode.restype = u8
+    L.orc_fp8_e4m3_value.argtypes = [u8]
+    L.orc_fp8_e4m3_value.restype = f32
+    L.orc_fp8_e4m3_encode.argtypes = [f32]
+    L.orc_fp8_e4m3_encode.restype = u8
+    L.orc_e8m0_encode.argtypes = [f32]
+    L.orc_e8m0_encode.restype = u8
+    L.orc_fp_scale.argtypes = [u8, i32, i32]
+    L.orc_fp_scale.restype = f32
+    L.orc_fp_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
+    L.orc_fp_quantize.restype = i32
+    L.orc_fp_dequantize.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp, vp]
+    L.orc_fp_dequantize.restype = i32
+    L.orc_fp_qmm_t.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp, i32]
+    L.orc_fp_qmm_t.restype = i32
 
 
 class OracleError(RuntimeError):
@@ -289,3 +308,73 @@ def conv_weight_matrix(w, groups, group_size):
     out = np.zeros((O, K_pad), w.dtype)
     out[:, :K_true] = w.reshape(O, K_true)
     return out
+
+
+# ------------------------------------------------- floating-point modes
+# (bits, group size): (4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8; see
+# fp_oracle.c ("mlx 1.0.0 backend/cpu/quantized.cpp": FP4_LUT, to_fp4_e2m1,
+# to_fp8_e8m0, dequantize_scale, fp_quantize_dequantize, fp_qmm_t).
+
+FP_MODES = {"mxfp4": (4, 32), "nvfp4": (4, 16), "mxfp8": (8, 32)}
+
+
+def fp4_value(code):
+    return lib().orc_fp4_value(int(code))
+
+
+def fp4_encode(x):
+    return lib().orc_fp4_encode(float(x))
+
+
+def e4m3_value(b):
+    return lib().orc_fp8_e4m3_value(int(b))
+
+
+def e4m3_encode(x):
+    return lib().orc_fp8_e4m3_encode(float(x))
+
+
+def e8m0_encode(x):
+    return lib().orc_e8m0_encode(float(x))
+
+
+def fp_scale(s, group_size, dt):
+    return lib().orc_fp_scale(int(s), group_size, dt)
+
+
+def fp_quantize(w, dt, group_size=32, bits=4):
+    """w: [rows, K] storage words. Returns (wq bytes [rows, K*bits/8],
+    scales uint8 [rows, K/gs])."""
+    w = _words(w, dt)
+    rows, K = w.shape
+    wq = np.zeros((rows, row_bytes(K, bits)), np.uint8)
+    sc = np.zeros((rows, max(K // group_size, 1)), np.uint8)
+    _chk(lib().orc_fp_quantize(_p(w), dt, rows, K, group_size, bits, _p(wq), _p(sc)),
+         "orc_fp_quantize")
+    return wq, sc
+
+
+def fp_dequantize(wq, scales, dt, K, group_size=32, bits=4):
+    """Returns (w32 [rows,K] float32, w_out [rows,K] storage words)."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = wq.shape[0]
+    w32 = np.zeros((rows, K), np.float32)
+    wo = np.zeros((rows, K), storage_dtype(dt))
+    _chk(lib().orc_fp_dequantize(_p(wq), _p(scales), dt, rows, K, group_size, bits, _p(w32),
+                                 _p(wo)), "orc_fp_dequantize")
+    return w32, wo
+
+
+def fp_qmm_t(x, wq, scales, dt, group_size=32, bits=4, nthreads=1):
+    """y = x . dequant(W)^T in an fp mode. x: [M,K] words. Returns (y32, y_T)."""
+    x = _words(x, dt)
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M, K = x.shape
+    N = wq.shape[0]
+    y32 = np.zeros((M, N), np.float32)
+    yo = np.zeros((M, N), storage_dtype(dt))
+    _chk(lib().orc_fp_qmm_t(_p(x), _p(wq), _p(scales), dt, M, N, K, group_size, bits, _p(y32),
+                            _p(yo), nthreads), "orc_fp_qmm_t")
+    return y32, yo

@@ -16,9 +16,9 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
 
 
 def build(verbose=False):
-    src = os.path.join(HERE, "qmm_oracle.c")
+    srcs = [os.path.join(HERE, f) for f in ("qmm_oracle.c", "fp_oracle.c")]
     tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, src, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, *srcs, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)

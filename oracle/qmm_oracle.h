@@ -107,6 +107,31 @@ int orc_qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
                      int groups, int dtype, int group_size, int bits,
                      float* y32, void* y_out, int nthreads);
 
+/* ---- Floating-point modes (fp_oracle.c; "mlx 1.0.0
+ * backend/cpu/quantized.cpp": FP4_LUT, to_fp4_e2m1, to_fp8_e8m0,
+ * dequantize_scale, fp_quantize_dequantize, fp_qmm_t). (bits, group size):
+ * (4, 32) mxfp4 = E2M1 codes + e8m0 scale; (4, 16) nvfp4 = E2M1 + E4M3
+ * scale; (8, 32) mxfp8 = E4M3 codes + e8m0 scale. wq: rows * K*bits/8 bytes
+ * (4-bit codes two per byte, first in the low nibble); scales: one byte per
+ * group, [rows, K/gs]. */
+float orc_fp4_value(uint8_t code);
+uint8_t orc_fp4_encode(float x);
+float orc_fp8_e4m3_value(uint8_t b);
+uint8_t orc_fp8_e4m3_encode(float x);
+uint8_t orc_e8m0_encode(float x);
+/* decoded scale of byte s rounded to T (dtype), as the products use it */
+float orc_fp_scale(uint8_t s, int group_size, int dtype);
+int orc_fp_quantize(const void* w, int dtype, int64_t rows, int64_t K, int group_size,
+                    int bits, uint8_t* wq, uint8_t* scales);
+/* w32 = fl32(scale_T * value) (exact), w_out = T(w32); either may be NULL */
+int orc_fp_dequantize(const uint8_t* wq, const uint8_t* scales, int dtype, int64_t rows,
+                      int64_t K, int group_size, int bits, float* w32, void* w_out);
+/* y[m,n] = sum_g scale_T[n,g] * sum_{k in g} x[m,k] * value[n,k], fp32,
+ * ascending, no fused multiply-add; either output may be NULL */
+int orc_fp_qmm_t(const void* x, const uint8_t* wq, const uint8_t* scales, int dtype, int64_t M,
+                 int64_t N, int64_t K, int group_size, int bits, float* y32, void* y_out,
+                 int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
