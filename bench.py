@@ -184,6 +184,29 @@ def bench_gather_prefill(torch, Q, synth, timer, steps, warmup, E=8, M=128, N=40
                         f"{bits}-bit g{gs} f16"}
 
 
+def bench_fp(torch, Q, synth, timer, steps, warmup, bits, gs, M=1, N=4096, K=4096):
+    """Decode GEMV in a floating-point mode (mxfp4 / nvfp4 / mxfp8) on an
+    f16 [4096, 4096] weight; every step reads a different copy of W from a
+    >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    w = to_dev(synth.normal((N, K), seed=1), "f16")
+    wq, sc = Q.fp_quantize(w, gs, bits)
+    del w
+    per = wq.numel() * 4 + sc.numel()
+    P = max(2, -(-POOL_BYTES // per))
+    wqs = wq.unsqueeze(0).expand(P, *wq.shape).contiguous()
+    scs = sc.unsqueeze(0).expand(P, *sc.shape).contiguous()
+    x = to_dev(synth.normal((M, K), seed=0), "f16")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.fp_qmv(x, wqs[i % P], scs[i % P], gs, bits, out=y), steps, warmup)
+    nbytes = N * K * bits // 8 + N * (K // gs) + M * K * 2 + M * N * 2
+    del wqs, scs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "pool_copies": P}
+
+
 def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, bits=4, gs=64):
     """Batched product with one weight per batch: y[b] = x[b] . dequant(W_b)^T,
     x [B, M, K] f16, W_b [N, K] 4-bit g64 (qmm_t_batched). Every step reads a
@@ -438,6 +461,11 @@ def main():
                                                      else 20, 5, B, M).items()}
             for (B, M) in [(8, 1), (4, 256)]}
         log("batched rows done")
+        rows["fp_qmv_decode_4096x4096_f16"] = {
+            name: {k: round(v, 4) if isinstance(v, float) else v
+                   for k, v in bench_fp(torch, Q, synth, timer, n_small, 20, bits, gs).items()}
+            for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32))}
+        log("fp rows done")
         ch = {}
         for bits in (2, 4, 8):
             ch[f"bits{bits}"] = {k: round(v, 4) for k, v in

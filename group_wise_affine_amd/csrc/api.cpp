@@ -351,6 +351,91 @@ qmm_status qmm_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_i
                   "qmm_gather_qmv");
 }
 
+}  // extern "C"
+
+namespace {
+
+qmm_status check_fp_mode(const char* tag, int bits, int gs) {
+  if (bits != 4 && bits != 8)
+    return fail(QMM_E_BITS, "%s: floating-point modes take bits 4 (mxfp4, nvfp4) or 8 (mxfp8), "
+                "got %d", tag, bits);
+  if (!(gs == 32 || (bits == 4 && gs == 16)))
+    return fail(QMM_E_GROUP, "%s: group_size must be 32 (mxfp4, mxfp8) or 16 (nvfp4, bits 4), "
+                "got %d with bits %d", tag, gs, bits);
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_fp_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
+                           int group_size, int bits, uint32_t* wq, uint8_t* scales,
+                           void* stream) {
+  if (!w || !wq || !scales)
+    return fail(QMM_E_NULL, "qmm_fp_quantize: w, wq and scales must be non-NULL");
+  qmm_status st = check_fp_mode("qmm_fp_quantize", bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16 && dt != QMM_F32)
+    return fail(QMM_E_DTYPE, "qmm_fp_quantize: only floating point inputs are supported");
+  if (rows < 1) return fail(QMM_E_SHAPE, "qmm_fp_quantize: rows must be >= 1");
+  st = check_k(K, group_size);
+  if (st) return st;
+  if (rows * K > ((int64_t)1 << 42))
+    return fail(QMM_E_SHAPE, "qmm_fp_quantize: problem too large");
+  if (!aligned(w, 16) || !aligned(wq, 16))
+    return fail(QMM_E_ALIGN, "qmm_fp_quantize: w and wq must be 16-byte aligned");
+  return launched(qmm::launch_fp_quantize((int)dt, bits, group_size, w, rows, K, wq, scales,
+                                          (hipStream_t)stream),
+                  "qmm_fp_quantize");
+}
+
+qmm_status qmm_fp_dequantize(const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
+                             int64_t rows, int64_t K, int group_size, int bits, void* w_out,
+                             void* stream) {
+  if (!wq || !scales || !w_out)
+    return fail(QMM_E_NULL, "qmm_fp_dequantize: wq, scales and w_out must be non-NULL");
+  qmm_status st = check_fp_mode("qmm_fp_dequantize", bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16 && dt != QMM_F32)
+    return fail(QMM_E_DTYPE, "qmm_fp_dequantize: only floating point outputs are supported");
+  if (rows < 1) return fail(QMM_E_SHAPE, "qmm_fp_dequantize: rows must be >= 1");
+  st = check_k(K, group_size);
+  if (st) return st;
+  if (rows * K > ((int64_t)1 << 42))
+    return fail(QMM_E_SHAPE, "qmm_fp_dequantize: problem too large");
+  if (!aligned(wq, 16) || !aligned(w_out, 16))
+    return fail(QMM_E_ALIGN, "qmm_fp_dequantize: wq and w_out must be 16-byte aligned");
+  return launched(qmm::launch_fp_dequantize((int)dt, bits, group_size, wq, scales, rows, K,
+                                            w_out, (hipStream_t)stream),
+                  "qmm_fp_dequantize");
+}
+
+qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
+                      int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
+                      void* stream) {
+  if (!x || !wq || !scales || !y)
+    return fail(QMM_E_NULL, "qmm_fp_qmv: x, wq, scales and y must be non-NULL");
+  qmm_status st = check_fp_mode("qmm_fp_qmv", bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qmm_fp_qmv: only float16 and bfloat16 are supported (got dtype %d)",
+                (int)dt);
+  if (M < 1 || N < 1 || M > 65535 || N > kI32)
+    return fail(QMM_E_SHAPE, "qmm_fp_qmv: M (%lld) must be in [1, 65535] and N (%lld) >= 1",
+                (long long)M, (long long)N);
+  if (K < 32 || K % 32 != 0 || K > qmm::kFpMaxK)
+    return fail(QMM_E_SHAPE, "qmm_fp_qmv: K (%lld) must be a positive multiple of 32 up to %lld",
+                (long long)K, (long long)qmm::kFpMaxK);
+  if (N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_fp_qmv: problem too large");
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qmm_fp_qmv: x, wq and y must be 16-byte aligned");
+  return launched(qmm::launch_fp_qmv((int)dt, bits, group_size, x, wq, scales, M, N, K, y,
+                                     (hipStream_t)stream),
+                  "qmm_fp_qmv");
+}
+
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
                  const void* biases, qmm_dtype dt, int64_t M, int64_t N,
                  int64_t K, int group_size, int bits, void* y, void* stream) {

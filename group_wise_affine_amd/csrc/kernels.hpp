@@ -100,6 +100,20 @@ hipError_t launch_gather_qmm_mfma(int dt, int bits, int gs, const void* x, int64
                                   const void* b, int64_t nwb, const int32_t* ridx, int64_t B,
                                   int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
 
+// Floating-point modes, (bits, gs) in {(4, 32) mxfp4, (4, 16) nvfp4, (8, 32)
+// mxfp8}: codes [rows, K*bits/8] bytes, one scale byte per group.
+hipError_t launch_fp_quantize(int dt, int bits, int gs, const void* w, int64_t rows, int64_t K,
+                              uint32_t* wq, uint8_t* scales, hipStream_t st);
+hipError_t launch_fp_dequantize(int dt, int bits, int gs, const uint32_t* wq,
+                                const uint8_t* scales, int64_t rows, int64_t K, void* out,
+                                hipStream_t st);
+// GEMV, f16 / bf16: K % 32 == 0, K <= kFpMaxK (x row staged in LDS as fp32),
+// M <= 65535 (one pass over W per row of x).
+constexpr int64_t kFpMaxK = 16384;
+hipError_t launch_fp_qmv(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                         const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
+                         hipStream_t st);
+
 // Implicit-im2col conv on the MFMA tile GEMM.
 struct ConvGeom {
   int64_t B, H, W, C, O, OH, OW;

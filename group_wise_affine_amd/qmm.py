@@ -21,6 +21,7 @@ STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
+           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -57,8 +58,12 @@ def lib():
         L.qmm_gather_qmm.argtypes = L.qmm_gather_qmv.argtypes
         L.qmm_t_batched.argtypes = [vp, vp, vp, vp, i64, i64, i32, i64, i64, i64, i32, i32,
                                     vp, vp]
+        L.qmm_fp_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
+        L.qmm_fp_dequantize.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp, vp]
+        L.qmm_fp_qmv.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
-                  "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched"):
+                  "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched", "qmm_fp_quantize",
+                  "qmm_fp_dequantize", "qmm_fp_qmv"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -200,6 +205,37 @@ def qmm_t_batched(x, wq, scales, biases, group_size=64, bits=4, out=None, stream
     _check(lib().qmm_t_batched(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), B, E,
                                _dt(x.dtype), M, N, K, group_size, bits, _ptr(out),
                                _stream(stream)))
+    return out
+
+
+def fp_quantize(w, group_size=32, bits=4, stream=None):
+    """Floating-point mode ((4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8):
+    w [rows, K] -> (wq int32 [rows, K*bits/32], scales uint8 [rows, K/gs])."""
+    rows, K = w.shape
+    wq = torch.empty((rows, max(K * bits // 32, 1)), dtype=torch.int32, device=w.device)
+    sc = torch.empty((rows, max(K // group_size, 1)), dtype=torch.uint8, device=w.device)
+    _check(lib().qmm_fp_quantize(_ptr(w), _dt(w.dtype), rows, K, group_size, bits, _ptr(wq),
+                                 _ptr(sc), _stream(stream)))
+    return wq, sc
+
+
+def fp_dequantize(wq, scales, dtype=torch.float16, group_size=32, bits=4, stream=None):
+    rows = wq.shape[0]
+    K = wq.shape[1] * 32 // bits
+    out = torch.empty((rows, K), dtype=dtype, device=wq.device)
+    _check(lib().qmm_fp_dequantize(_ptr(wq), _ptr(scales), _dt(dtype), rows, K, group_size,
+                                   bits, _ptr(out), _stream(stream)))
+    return out
+
+
+def fp_qmv(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
+    """y [M,N] = x [M,K] . dequant(W)^T for a floating-point mode."""
+    M, K = x.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(lib().qmm_fp_qmv(_ptr(x), _ptr(wq), _ptr(scales), _dt(x.dtype), M, N, K, group_size,
+                            bits, _ptr(out), _stream(stream)))
     return out
 
 

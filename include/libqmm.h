@@ -150,6 +150,51 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
                          int group_size, int bits, void* y, void* stream);
 
 /*
+ * Floating-point modes (no bias; one scale byte per group): (bits,
+ * group_size) = (4, 32) mxfp4: E2M1 codes, e8m0 scale 2^(s-127);
+ * (4, 16) nvfp4: E2M1 codes, E4M3 scale; (8, 32) mxfp8: E4M3 codes (OCP,
+ * no infinities), e8m0 scale. Other pairs: QMM_E_BITS / QMM_E_GROUP.
+ * Quantize w[rows, K] (f16, bf16 or f32) per group of group_size: scale =
+ * max|w| / (6 for E2M1, 448 for E4M3) encoded in one byte (e8m0: n =
+ * round(log2 scale), exact, clamped to [-127, 127]; E4M3: round to nearest
+ * even, saturating at 448), then each w divided by the decoded scale and
+ * encoded (E2M1: nearest value, ties to the even code, beyond 6 -> 6;
+ * E4M3: nearest even, saturating at 448). All fp32, IEEE division.
+ * Outputs: wq [rows, K*bits/32] uint32 (the row's bytes; 4-bit codes two per
+ * byte, code k in the low nibble of byte k/2 when k is even), scales
+ * [rows, K/group_size] uint8 (any alignment). K % group_size == 0.
+ * (Source: "mlx 1.0.0 backend/cpu/quantized.cpp": FP4_LUT, to_fp4_e2m1,
+ * to_fp8_e8m0, dequantize_scale and the per-group steps of
+ * fp_quantize_dequantize.)
+ */
+qmm_status qmm_fp_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
+                           int group_size, int bits, uint32_t* wq,
+                           uint8_t* scales, void* stream);
+
+/*
+ * Dequantize a floating-point mode: w_out[n,k] = dt(scale_T * value), where
+ * scale_T is the decoded scale rounded to dt (for f16, e8m0 scales below
+ * 2^-24 become 0 and above 2^15 infinity; every other case is exact) and
+ * the product is exact. (Source: as qmm_fp_quantize; dequantize_scale<T>.)
+ */
+qmm_status qmm_fp_dequantize(const uint32_t* wq, const uint8_t* scales,
+                             qmm_dtype dt, int64_t rows, int64_t K,
+                             int group_size, int bits, void* w_out,
+                             void* stream);
+
+/*
+ * y[M,N] = x[M,K] . dequant(W)^T for a floating-point mode: y[m,n] =
+ * sum over groups g of scale_T[n,g] * sum_{k in g} x[m,k] * value[n,k],
+ * fp32 accumulation, y rounded to nearest even in dt (f16 or bf16). A GEMV
+ * (one pass over W per row of x): K a multiple of 32 up to 16384, M <=
+ * 65535. (Source: "mlx 1.0.0 backend/cpu/quantized.cpp", fp_qmm_t and
+ * fp_qmm_t_simd.)
+ */
+qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales,
+                      qmm_dtype dt, int64_t M, int64_t N, int64_t K,
+                      int group_size, int bits, void* y, void* stream);
+
+/*
  * Non-transposed product: y[M,N] = x[M,K] . dequant(W)[K,N], where the
  * weight W [K, N] is quantized along N (qmm_quantize of the K rows):
  *   y[m,n] = sum_k x[m,k] * (scale[k,n/gs] * q[k,n] + bias[k,n/gs]),

@@ -206,6 +206,35 @@ def test_gather_qmm_arguments(L):
     assert b"K" in L.qmm_last_error()
 
 
+def test_fp_arguments(L):
+    def q(w=P, dt=0, rows=4, K=64, gs=32, bits=4, wq=P, sc=P):
+        return _st(L, "qmm_fp_quantize", w, dt, rows, K, gs, bits, wq, sc, None)
+
+    def d(wq=P, sc=P, dt=0, rows=4, K=64, gs=32, bits=4, out=P):
+        return _st(L, "qmm_fp_dequantize", wq, sc, dt, rows, K, gs, bits, out, None)
+
+    def v(x=P, wq=P, sc=P, dt=0, M=1, N=8, K=64, gs=32, bits=4, y=P):
+        return _st(L, "qmm_fp_qmv", x, wq, sc, dt, M, N, K, gs, bits, y, None)
+    for f in (q, d, v):
+        assert f(bits=3) == Q.QMM_E_BITS
+        assert f(bits=2) == Q.QMM_E_BITS
+        assert f(gs=64) == Q.QMM_E_GROUP
+        assert f(bits=8, gs=16) == Q.QMM_E_GROUP    # nvfp4 is 4-bit only
+        assert f(K=48) == Q.QMM_E_SHAPE             # not a multiple of the group size
+    assert q(w=None) == Q.QMM_E_NULL and q(sc=None) == Q.QMM_E_NULL
+    assert q(dt=5) == Q.QMM_E_DTYPE
+    assert q(rows=0) == Q.QMM_E_SHAPE
+    assert q(w=P2) == Q.QMM_E_ALIGN
+    assert d(out=None) == Q.QMM_E_NULL
+    assert d(out=P2) == Q.QMM_E_ALIGN
+    assert v(y=None) == Q.QMM_E_NULL
+    assert v(dt=2) == Q.QMM_E_DTYPE             # the GEMV takes f16 / bf16
+    assert v(K=16, gs=16) == Q.QMM_E_SHAPE      # K must be a multiple of 32
+    assert v(K=32768) == Q.QMM_E_SHAPE          # beyond the LDS-staged row of x
+    assert v(M=65536) == Q.QMM_E_SHAPE
+    assert v(x=P2) == Q.QMM_E_ALIGN
+
+
 def test_batched_arguments(L):
     def f(x=P, wq=P, s=P, b=P, B=2, E=2, dt=0, M=1, N=8, K=64, gs=64, bits=4, y=P):
         return _st(L, "qmm_t_batched", x, wq, s, b, B, E, dt, M, N, K, gs, bits, y, None)

@@ -1,0 +1,135 @@
+"""GPU parity of the floating-point modes (mxfp4, nvfp4, mxfp8) against the
+oracle ("mlx 1.0.0 backend/cpu/quantized.cpp": to_fp4_e2m1, to_fp8_e8m0,
+dequantize_scale, fp_quantize_dequantize, fp_qmm_t): quantize and dequantize
+bit-exact, the GEMV within the floating-point gate."""
+import numpy as np
+import pytest
+import torch
+
+from group_wise_affine_amd import qmm as Q
+from group_wise_affine_amd import synth
+from tests.helpers import (assert_parity, bytes_to_words_dev, from_dev, orc_code, to_dev,
+                           words_dev_to_bytes)
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)]
+
+
+def _weights(rows, K, gs, dt, seed, big=2.0 ** 8):
+    """Normal rows, plus structured groups (zeros, constants, ramps, outliers,
+    tiny values) and rows scaled far down (2^-12) and up (big)."""
+    w = synth.normal((rows, K), seed=seed, sigma=2.0, dt=dt)
+    n = min(rows, 12)
+    w[:n] = synth.structured_rows(n, K, gs, seed=seed + 1, dt=dt)
+    f = synth.words_to_f32(w, dt)
+    if rows > n + 2:
+        f[n] *= 2.0 ** -12      # tiny groups: small e8m0 / E4M3 scales, E4M3 subnormals
+        f[n + 1] *= big         # large groups
+    return synth.to_words(f, dt)
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_fp_quantize_bit_exact(orc, name, bits, gs, dt):
+    rows, K = 33, gs * 6
+    w = _weights(rows, K, gs, dt, seed=20 + bits + gs)
+    wq_o, sc_o = orc.fp_quantize(w, orc_code(orc, dt), gs, bits)
+    wq, sc = Q.fp_quantize(to_dev(w, dt), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_dev_to_bytes(wq), wq_o)
+    assert np.array_equal(sc.cpu().numpy(), sc_o)
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+def test_fp_quantize_large(orc, name, bits, gs):
+    """A 4096 x 4096 f16 weight, bit-exact."""
+    w = synth.normal((4096, 4096), seed=1)
+    wq_o, sc_o = orc.fp_quantize(w, orc.F16, gs, bits)
+    wq, sc = Q.fp_quantize(to_dev(w, "f16"), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_dev_to_bytes(wq), wq_o)
+    assert np.array_equal(sc.cpu().numpy(), sc_o)
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_fp_dequantize_bit_exact(orc, name, bits, gs, dt):
+    """Every code value and a wide range of scale bytes (for f16, e8m0 scales
+    below 2^-24 round to 0; bytes whose scale leaves f16 are left out, their
+    zero codes would give NaN)."""
+    rows, K = 24, gs * 8
+    rng = np.random.default_rng(bits + gs)
+    if bits == 4:
+        wq = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    else:
+        wq = rng.integers(0, 256, (rows, K), dtype=np.uint8)
+        wq[(wq & 0x7f) == 0x7f] = 0x11                   # no NaN codes
+    if gs == 16:
+        sc = rng.integers(0, 256, (rows, K // gs), dtype=np.uint8)
+        sc[(sc & 0x7f) == 0x7f] = 0x30
+        sc &= 0x7f                                        # positive E4M3 scales
+    else:
+        top = 142 if dt == "f16" else 254
+        sc = rng.integers(0, top + 1, (rows, K // gs), dtype=np.uint8)
+        sc[0, :3] = [0, 102, 103]                          # 2^-127, 2^-25, 2^-24
+    _, w_o = orc.fp_dequantize(wq, sc, orc_code(orc, dt), K, gs, bits)
+    out = Q.fp_dequantize(bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), synth_dt(dt), gs,
+                          bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), w_o)
+
+
+def synth_dt(dt):
+    return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt,M,N,K", [
+    ("f16", 1, 4096, 4096),      # decode layer
+    ("bf16", 1, 4096, 4096),
+    ("f16", 3, 70, 1024),        # N % 16 != 0: a partial block of rows
+    ("bf16", 2, 257, 96),        # 3 units of 32 codes: most lanes idle
+    ("f16", 1, 64, 16384),       # the largest K (x in 64 KB of LDS)
+    ("bf16", 5, 200, 2080),      # K % 64 == 32
+])
+def test_fp_qmv(orc, name, bits, gs, dt, M, N, K):
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=M + K, dt=dt)
+    w = _weights(N, K, gs, dt, seed=N + bits, big=16.0)   # keeps y within f16 at K = 16384
+    wq, sc = orc.fp_quantize(w, code, gs, bits)
+    yo, _ = orc.fp_qmm_t(x, wq, sc, code, gs, bits, nthreads=8)
+    y = Q.fp_qmv(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"fp_qmv {name} {dt} M{M} N{N} K{K}")
+
+
+def test_fp_quantize_then_qmv_end_to_end(orc):
+    """Quantize on the GPU, multiply on the GPU, compare with the oracle's
+    product over the oracle's codes (identical by the bit-exact quantizer)."""
+    dt, M, N, K, gs, bits = "f16", 2, 512, 2048, 32, 4
+    x = synth.normal((M, K), seed=3, dt=dt)
+    w = synth.normal((N, K), seed=4, dt=dt)
+    wq, sc = Q.fp_quantize(to_dev(w, dt), gs, bits)
+    y = Q.fp_qmv(to_dev(x, dt), wq, sc, gs, bits)
+    wq_o, sc_o = orc.fp_quantize(w, orc.F16, gs, bits)
+    yo, _ = orc.fp_qmm_t(x, wq_o, sc_o, orc.F16, gs, bits, nthreads=8)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, "fp quantize + qmv")
+
+
+def test_fp_rejects_bad_arguments():
+    x = torch.zeros((1, 64), dtype=torch.float16, device="cuda")
+    wq = torch.zeros((8, 8), dtype=torch.int32, device="cuda")
+    sc = torch.zeros((8, 2), dtype=torch.uint8, device="cuda")
+    with pytest.raises(Q.QmmError) as e:          # nvfp4 takes bits 4 only
+        Q.fp_qmv(x, torch.zeros((8, 16), dtype=torch.int32, device="cuda"), sc, 16, 8)
+    assert e.value.status == Q.QMM_E_GROUP
+    with pytest.raises(Q.QmmError) as e:          # K beyond the LDS-staged row
+        big = torch.zeros((1, 32768), dtype=torch.float16, device="cuda")
+        Q.fp_qmv(big, torch.zeros((8, 4096), dtype=torch.int32, device="cuda"),
+                 torch.zeros((8, 1024), dtype=torch.uint8, device="cuda"), 32, 4)
+    assert e.value.status == Q.QMM_E_SHAPE
+    with pytest.raises(Q.QmmError) as e:
+        Q.fp_qmv(x, wq, sc, 32, 3)
+    assert e.value.status == Q.QMM_E_BITS
