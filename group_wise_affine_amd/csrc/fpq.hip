@@ -226,14 +226,13 @@ __global__ __launch_bounds__(256) void fp_dequantize_kernel(const uint8_t* __res
 
 // ---------------------------------------------------------------- GEMV
 // y[m, n] = T(sum over groups g of scale_T[n, g] * sum_{k in g} x[m, k] *
-// value[n, k]) with fp32 accumulation. Workgroup = 4 wavefronts x kFpRows
-// rows of W for one row m of x (blockIdx.y); x[m] is staged in LDS as fp32.
-// Each lane takes 16-byte units of a row (32 E2M1 or 16 E4M3 codes), unit
-// u at lane u % 64, for kFpRows rows at once so that their loads overlap.
-constexpr int kFpRows = 4;
+// value[n, k]) with fp32 accumulation. Workgroup = 4 wavefronts x R rows of
+// W for one row m of x (blockIdx.y); x[m] is staged in LDS as fp32. Each
+// lane takes 16-byte units of a row (32 E2M1 or 16 E4M3 codes), unit u at
+// lane u % 64, for R rows at once so that their loads overlap.
 constexpr int kFpWaves = 4;
 
-template <class T, int BITS, int GS>
+template <class T, int BITS, int GS, int kFpRows>
 __global__ __launch_bounds__(256) void fp_qmv_kernel(const typename T::word* __restrict__ x,
                                                      const uint8_t* __restrict__ wq,
                                                      const uint8_t* __restrict__ sc,
@@ -319,15 +318,30 @@ hipError_t fp_dequantize_t(const uint32_t* wq, const uint8_t* sc, int64_t rows, 
   return hipGetLastError();
 }
 
-template <class T, int BITS, int GS>
-hipError_t fp_qmv_t(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
+template <class T, int BITS, int GS, int R>
+hipError_t fp_qmv_r(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
                     int64_t K, void* y, hipStream_t st) {
-  const int64_t rows_per_block = kFpWaves * kFpRows;
+  const int64_t rows_per_block = kFpWaves * R;
   const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)M);
-  hipLaunchKernelGGL((fp_qmv_kernel<T, BITS, GS>), grid, dim3(256), (size_t)K * 4, st,
+  hipLaunchKernelGGL((fp_qmv_kernel<T, BITS, GS, R>), grid, dim3(256), (size_t)K * 4, st,
                      static_cast<const typename T::word*>(x), reinterpret_cast<const uint8_t*>(wq),
                      sc, static_cast<typename T::word*>(y), (int)N, (int)K);
   return hipGetLastError();
+}
+
+// Rows per wavefront: the most (of 4, 2, 1) that still give 512 workgroups
+// (1024 for 8-bit codes, whose rows are twice as long) over the rows of W
+// and x. Measured on 4096 x 4096 at M = 1: 4-bit 7.4 / 6.2 / 7.6 us and
+// 8-bit 10.1 / 7.6 / 7.3 us for 4 / 2 / 1 rows; M = 4 (4-bit) 9.7 / 12.7 /
+// 21.4 us.
+template <class T, int BITS, int GS>
+hipError_t fp_qmv_t(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
+                    int64_t K, void* y, hipStream_t st) {
+  const int64_t want = BITS == 8 ? 1024 : 512;
+  auto blocks = [&](int64_t r) { return (N + kFpWaves * r - 1) / (kFpWaves * r) * M; };
+  if (blocks(4) >= want) return fp_qmv_r<T, BITS, GS, 4>(x, wq, sc, M, N, K, y, st);
+  if (blocks(2) >= want) return fp_qmv_r<T, BITS, GS, 2>(x, wq, sc, M, N, K, y, st);
+  return fp_qmv_r<T, BITS, GS, 1>(x, wq, sc, M, N, K, y, st);
 }
 
 // mode dispatch: (4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8
