@@ -398,6 +398,9 @@ def main():
                     help="run the PMC calibration copy and headline launches, print nothing else")
     ap.add_argument("--mfma-only", action="store_true",
                     help="time only the MFMA tile rows (chained 4-bit layers, conv), for profiling")
+    ap.add_argument("--next-only", action="store_true",
+                    help="time only the gathered, batched, non-transposed and fp-mode rows, "
+                         "for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the path is measured on a single "
@@ -420,6 +423,16 @@ def main():
              "conv_groups1": bench_conv(torch, Q, synth, timer, 1, 50, 5),
              "conv_groups2": bench_conv(torch, Q, synth, timer, 2, 50, 5)}
         print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r.items()}))
+        return
+    if args.next_only:
+        r = {"gather_qmv_moe_decode": bench_gather(torch, Q, synth, timer, 200, 20),
+             "gather_qmm_moe_prefill": bench_gather_prefill(torch, Q, synth, timer, 20, 5),
+             "qmm_t_batched_B4_M256": bench_batched(torch, Q, synth, timer, 20, 5, 4, 256),
+             "qmm_n_decode": bench_qmm_n(torch, Q, synth, timer, 200, 20)}
+        for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)):
+            r[f"fp_qmv_{name}"] = bench_fp(torch, Q, synth, timer, 200, 20, bits, gs)
+        print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items() if isinstance(vv, float)}
+                          for k, v in r.items()}))
         return
 
     log("headline: qmv 4-bit g64 f16 M=1 4096x4096")
