@@ -404,7 +404,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the path is measured on a single "
-              "MI355X (multi-GPU sharding is described in DESIGN.md, not run).",
+              "MI355X; the path shards over rows of W without communication, which "
+              "this benchmark does not run.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -68,7 +68,7 @@ def test_dequantize_bit_exact(orc, dt, bits):
 
 
 def test_quantize_large_rows(orc):
-    """configs-scale weight (4096 x 4096, 4-bit g64 f16), bit-exact."""
+    """A full-size decode weight (4096 x 4096, 4-bit g64 f16), bit-exact."""
     w = synth.normal((4096, 4096), seed=1)
     wq_o, s_o, b_o = orc.quantize(w, orc.F16, 64, 4)
     wq, s, b = Q.qmm_quantize(to_dev(w, "f16"), 64, 4)
