@@ -248,21 +248,40 @@ qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const vo
                 "[K, N] is quantized along N",
                 (long long)N, group_size);
   const int64_t S = qmm::qmm_n_splits(K);
-  if (M > 65535 || S > 65535 || N > kI32 || M * K > ((int64_t)1 << 40) ||
-      N * K > ((int64_t)1 << 40))
-    return fail(QMM_E_SHAPE, "qmm_n: problem too large (M <= 65535 rows of x per call)");
-  if (S > 1 && S * M * N > qmm::kSplitWsFloats)
-    return fail(QMM_E_SHAPE,
-                "qmm_n: the %lld K ranges x M x N partial sums exceed the split-K workspace "
-                "(%lld floats); pass fewer rows of x per call",
-                (long long)S, (long long)qmm::kSplitWsFloats);
+  if (M > kI32 || S > 65535 || N > kI32 || M * K > ((int64_t)1 << 40) ||
+      N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_n: problem too large");
+  // rows of x per launch: at most 65535, and with K split the partial sums of
+  // a launch's rows must fit the split-K workspace
+  int64_t chunk = 65535;
+  if (S > 1) {
+    const int64_t fit = qmm::kSplitWsFloats / (S * N);
+    if (fit < 1)
+      return fail(QMM_E_SHAPE,
+                  "qmm_n: one row's %lld K ranges x N (%lld) partial sums exceed the split-K "
+                  "workspace (%lld floats)",
+                  (long long)S, (long long)N, (long long)qmm::kSplitWsFloats);
+    chunk = fit < chunk ? fit : chunk;
+  }
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
     return fail(QMM_E_ALIGN, "qmm_n: x, wq and y must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(biases, 2))
     return fail(QMM_E_ALIGN, "qmm_n: scales and biases must be 2-byte aligned");
-  return launched(qmm::launch_qmm_n((int)dt, bits, group_size, x, wq, scales, biases, M, N, K,
-                                    y, (hipStream_t)stream),
-                  "qmm_n");
+  if (M > chunk && ((chunk * K * 2) % 16 != 0 || (chunk * N * 2) % 16 != 0))
+    return fail(QMM_E_ALIGN,
+                "qmm_n: with more than %lld rows of x the rows are taken %lld at a time, whose "
+                "x and y blocks must stay 16-byte aligned (K and N multiples of 8)",
+                (long long)chunk, (long long)chunk);
+  const char* xb = static_cast<const char*>(x);
+  char* yb = static_cast<char*>(y);
+  for (int64_t m0 = 0; m0 < M; m0 += chunk) {
+    const int64_t mc = M - m0 < chunk ? M - m0 : chunk;
+    const hipError_t e = qmm::launch_qmm_n((int)dt, bits, group_size, xb + m0 * K * 2, wq, scales,
+                                           biases, mc, N, K, yb + m0 * N * 2,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return launched(e, "qmm_n");
+  }
+  return launched(hipSuccess, "qmm_n");
 }
 
 }  // extern "C"

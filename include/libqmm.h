@@ -204,8 +204,11 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales,
  * over W per row of x, K split over workgroups; when K > 128 the fp32
  * partial sums of the ceil(K/128) K ranges go to the library's split-K
  * workspace (shared with qmm_t on the device: calls that overlap on one
- * device share it), so ceil(K/128) * M * N must stay within 16M floats
- * (QMM_E_SHAPE otherwise). M <= 65535.
+ * device share it), so the rows of x are taken in blocks of at most
+ * floor(16M / (ceil(K/128) * N)) (and 65535) rows, one launch pair each;
+ * QMM_E_SHAPE when a single row does not fit, QMM_E_ALIGN when a block's x
+ * or y would not start 16-byte aligned (K or N not a multiple of 8 with
+ * more rows than one block).
  * (Source: "mlx 1.0.0 backend/cpu/quantized.cpp", _qmm, the non-transposed
  * branch of quantized_matmul.)
  */

@@ -266,8 +266,8 @@ def test_qmm_n_arguments(L):
     assert b"N" in L.qmm_last_error()
     assert f(M=0) == Q.QMM_E_SHAPE
     assert f(K=0) == Q.QMM_E_SHAPE
-    assert f(M=65536) == Q.QMM_E_SHAPE
-    assert f(M=64, N=8192, K=8192) == Q.QMM_E_SHAPE   # 64 K ranges x 64 x 8192 > 16M floats
+    assert f(M=1, N=262208, K=8192) == Q.QMM_E_SHAPE  # one row: 64 K ranges x N > 16M floats
     assert b"workspace" in L.qmm_last_error()
+    assert f(M=300, N=4160, K=2047) == Q.QMM_E_ALIGN  # x blocks of 252 rows x 2047 halves
     assert f(x=P2) == Q.QMM_E_ALIGN
     assert f(s=ctypes.c_void_p(0x10001)) == Q.QMM_E_ALIGN

@@ -533,6 +533,8 @@ def test_qmm_t_batched_rejects_unaligned_batches():
     ("f16", 4, 2048, 512, 32, 2),
     ("f16", 1, 11008, 4096, 64, 8),     # 344 K ranges
     ("bf16", 1, 4096, 4096, 128, 8),
+    ("f16", 300, 2048, 8192, 64, 4),    # rows taken 128 at a time (workspace): 3 launches
+    ("bf16", 150, 8192, 2048, 32, 3),   # 128 + 22 rows
 ])
 def test_qmm_n(orc, dt, M, K, N, gs, bits):
     """y = x . dequant(W), W [K, N] quantized along N, against the oracle."""
