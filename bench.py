@@ -207,6 +207,39 @@ def bench_fp(torch, Q, synth, timer, steps, warmup, bits, gs, M=1, N=4096, K=409
             "pool_copies": P}
 
 
+def bench_fp_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096, K=4096):
+    """Mixture-of-experts decode with mxfp4 experts: T tokens x [1, K] f16,
+    each routed to topk of E experts W_e [N, K] (a seeded permutation, every
+    expert read once per step), one qmm_fp_gather_qmv call. Every step reads a
+    different copy of the expert stack from a >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    import numpy as np
+    parts = [Q.fp_quantize(to_dev(synth.normal((N, K), seed=100 + e), "f16"), 32, 4)
+             for e in range(E)]
+    wq = torch.stack([p[0] for p in parts])
+    sc = torch.stack([p[1] for p in parts])
+    del parts
+    per = wq.numel() * 4 + sc.numel()
+    P = max(2, -(-POOL_BYTES // per))
+    wqs = wq.unsqueeze(0).expand(P, *wq.shape).contiguous()
+    scs = sc.unsqueeze(0).expand(P, *sc.shape).contiguous()
+    x = to_dev(np.stack([synth.normal((1, K), seed=7 + t) for t in range(T)]), "f16")
+    lhs = torch.tensor([t for t in range(T) for _ in range(topk)], dtype=torch.int32,
+                       device="cuda")
+    rhs = torch.tensor(np.random.default_rng(5).permutation(E).tolist(), dtype=torch.int32,
+                       device="cuda")
+    y = torch.empty((E, 1, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.fp_gather_qmv(x, wqs[i % P], scs[i % P], lhs, rhs, 32, 4, out=y),
+                   steps, warmup)
+    nbytes = E * (N * K // 2 + N * (K // 32)) + T * K * 2 + E * N * 2
+    del wqs, scs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "pool_copies": P,
+            "workload": f"{T} tokens x top-{topk} of {E} mxfp4 experts [{N},{K}] f16"}
+
+
 def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, bits=4, gs=64):
     """Batched product with one weight per batch: y[b] = x[b] . dequant(W_b)^T,
     x [B, M, K] f16, W_b [N, K] 4-bit g64 (qmm_t_batched). Every step reads a
@@ -432,6 +465,7 @@ def main():
              "qmm_n_decode": bench_qmm_n(torch, Q, synth, timer, 200, 20)}
         for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)):
             r[f"fp_qmv_{name}"] = bench_fp(torch, Q, synth, timer, 200, 20, bits, gs)
+        r["fp_gather_qmv_moe_decode_mxfp4"] = bench_fp_gather(torch, Q, synth, timer, 200, 20)
         print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items() if isinstance(vv, float)}
                           for k, v in r.items()}))
         return
@@ -480,6 +514,10 @@ def main():
                    for k, v in bench_fp(torch, Q, synth, timer, n_small, 20, bits, gs).items()}
             for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32))}
         log("fp rows done")
+        rows["fp_gather_qmv_moe_decode_mxfp4"] = {
+            k: round(v, 4) if isinstance(v, float) else v
+            for k, v in bench_fp_gather(torch, Q, synth, timer, n_small, 20).items()}
+        log("fp gather row done")
         ch = {}
         for bits in (2, 4, 8):
             ch[f"bits{bits}"] = {k: round(v, 4) for k, v in

@@ -455,6 +455,48 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales, 
                   "qmm_fp_qmv");
 }
 
+qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_indices,
+                             const uint32_t* wq, const uint8_t* scales, int64_t w_batches,
+                             const int32_t* rhs_indices, int64_t batches, qmm_dtype dt, int64_t M,
+                             int64_t N, int64_t K, int group_size, int bits, void* y,
+                             void* stream) {
+  if (!x || !wq || !scales || !y)
+    return fail(QMM_E_NULL, "qmm_fp_gather_qmv: x, wq, scales and y must be non-NULL");
+  qmm_status st = check_fp_mode("qmm_fp_gather_qmv", bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qmm_fp_gather_qmv: only float16 and bfloat16 are supported");
+  if (M < 1 || N < 1 || M > 65535 || N > kI32)
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: M (%lld) must be in [1, 65535] and N (%lld) >= 1",
+                (long long)M, (long long)N);
+  if (K < 32 || K % 32 != 0 || K > qmm::kFpMaxK)
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: K (%lld) must be a positive multiple of 32 up "
+                "to %lld", (long long)K, (long long)qmm::kFpMaxK);
+  if (batches < 1 || batches > 65535)
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: batches (%lld) must be in [1, 65535]",
+                (long long)batches);
+  if (x_batches < 1 || w_batches < 1 || x_batches > kI32 || w_batches > kI32)
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: x_batches (%lld) and w_batches (%lld) must be "
+                ">= 1", (long long)x_batches, (long long)w_batches);
+  if (!lhs_indices && x_batches < batches)
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: without lhs_indices, x needs one batch per "
+                "output batch (%lld < %lld)", (long long)x_batches, (long long)batches);
+  if (!rhs_indices && w_batches < batches)
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: without rhs_indices, W needs one batch per "
+                "output batch (%lld < %lld)", (long long)w_batches, (long long)batches);
+  if (x_batches * M * K > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40) ||
+      batches * M * N > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_fp_gather_qmv: problem too large");
+  if (!aligned(lhs_indices, 4) || !aligned(rhs_indices, 4))
+    return fail(QMM_E_ALIGN, "qmm_fp_gather_qmv: index arrays must be 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qmm_fp_gather_qmv: x, wq and y must be 16-byte aligned");
+  return launched(qmm::launch_fp_gather_qmv((int)dt, bits, group_size, x, x_batches, lhs_indices,
+                                            wq, scales, w_batches, rhs_indices, batches, M, N, K,
+                                            y, (hipStream_t)stream),
+                  "qmm_fp_gather_qmv");
+}
+
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
                  const void* biases, qmm_dtype dt, int64_t M, int64_t N,
                  int64_t K, int group_size, int bits, void* y, void* stream) {

@@ -232,14 +232,39 @@ __global__ __launch_bounds__(256) void fp_dequantize_kernel(const uint8_t* __res
 // lane u % 64, for R rows at once so that their loads overlap.
 constexpr int kFpWaves = 4;
 
-template <class T, int BITS, int GS, int kFpRows>
+// Gathered products (GA): output batch z = blockIdx.z multiplies x batch
+// lidx[z] (of nxb, M rows each) by weight batch ridx[z] (of nwb), indices
+// clamped into range; a null array means z.
+struct FpBatch {
+  const int32_t* lidx;
+  const int32_t* ridx;
+  int nxb, nwb, M, B;
+};
+
+template <class T, int BITS, int GS, int kFpRows, bool GA>
 __global__ __launch_bounds__(256) void fp_qmv_kernel(const typename T::word* __restrict__ x,
                                                      const uint8_t* __restrict__ wq,
                                                      const uint8_t* __restrict__ sc,
                                                      typename T::word* __restrict__ y, int N,
-                                                     int K) {
+                                                     int K, FpBatch bt) {
   extern __shared__ float xs[];
   const int m = blockIdx.y;
+  if constexpr (GA) {
+    const int z = blockIdx.z;
+    int zx = z, zw = z;
+    if (bt.lidx) {
+      const int v = bt.lidx[z];
+      zx = v < 0 ? 0 : (v >= bt.nxb ? bt.nxb - 1 : v);
+    }
+    if (bt.ridx) {
+      const int v = bt.ridx[z];
+      zw = v < 0 ? 0 : (v >= bt.nwb ? bt.nwb - 1 : v);
+    }
+    x += (int64_t)zx * bt.M * K;
+    wq += (int64_t)zw * N * ((int64_t)K * BITS / 8);
+    sc += (int64_t)zw * N * (K / GS);
+    y += (int64_t)z * bt.M * N;
+  }
   const typename T::word* xr = x + (int64_t)m * K;
   for (int k = threadIdx.x; k < K; k += 256) xs[k] = to_f32(T{}, xr[k]);
   __syncthreads();
@@ -320,12 +345,18 @@ hipError_t fp_dequantize_t(const uint32_t* wq, const uint8_t* sc, int64_t rows, 
 
 template <class T, int BITS, int GS, int R>
 hipError_t fp_qmv_r(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
-                    int64_t K, void* y, hipStream_t st) {
+                    int64_t K, void* y, hipStream_t st, const FpBatch* bt) {
   const int64_t rows_per_block = kFpWaves * R;
-  const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)M);
-  hipLaunchKernelGGL((fp_qmv_kernel<T, BITS, GS, R>), grid, dim3(256), (size_t)K * 4, st,
-                     static_cast<const typename T::word*>(x), reinterpret_cast<const uint8_t*>(wq),
-                     sc, static_cast<typename T::word*>(y), (int)N, (int)K);
+  const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)M,
+                  bt ? (unsigned)bt->B : 1u);
+  auto go = [&](auto kern, const FpBatch& b) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), (size_t)K * 4, st,
+                       static_cast<const typename T::word*>(x),
+                       reinterpret_cast<const uint8_t*>(wq), sc,
+                       static_cast<typename T::word*>(y), (int)N, (int)K, b);
+  };
+  if (bt) go(fp_qmv_kernel<T, BITS, GS, R, true>, *bt);
+  else go(fp_qmv_kernel<T, BITS, GS, R, false>, FpBatch{nullptr, nullptr, 1, 1, (int)M, 1});
   return hipGetLastError();
 }
 
@@ -336,12 +367,12 @@ hipError_t fp_qmv_r(const void* x, const uint32_t* wq, const uint8_t* sc, int64_
 // 21.4 us.
 template <class T, int BITS, int GS>
 hipError_t fp_qmv_t(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
-                    int64_t K, void* y, hipStream_t st) {
-  const int64_t want = BITS == 8 ? 1024 : 512;
-  auto blocks = [&](int64_t r) { return (N + kFpWaves * r - 1) / (kFpWaves * r) * M; };
-  if (blocks(4) >= want) return fp_qmv_r<T, BITS, GS, 4>(x, wq, sc, M, N, K, y, st);
-  if (blocks(2) >= want) return fp_qmv_r<T, BITS, GS, 2>(x, wq, sc, M, N, K, y, st);
-  return fp_qmv_r<T, BITS, GS, 1>(x, wq, sc, M, N, K, y, st);
+                    int64_t K, void* y, hipStream_t st, const FpBatch* bt) {
+  const int64_t want = BITS == 8 ? 1024 : 512, nb = bt ? bt->B : 1;
+  auto blocks = [&](int64_t r) { return (N + kFpWaves * r - 1) / (kFpWaves * r) * M * nb; };
+  if (blocks(4) >= want) return fp_qmv_r<T, BITS, GS, 4>(x, wq, sc, M, N, K, y, st, bt);
+  if (blocks(2) >= want) return fp_qmv_r<T, BITS, GS, 2>(x, wq, sc, M, N, K, y, st, bt);
+  return fp_qmv_r<T, BITS, GS, 1>(x, wq, sc, M, N, K, y, st, bt);
 }
 
 // mode dispatch: (4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8
@@ -370,8 +401,19 @@ hipError_t launch_fp_dequantize(int dt, int bits, int gs, const uint32_t* wq,
 hipError_t launch_fp_qmv(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                          const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
                          hipStream_t st) {
-  if (dt == 0) return FP_DISPATCH(F16, fp_qmv_t, x, wq, scales, M, N, K, y, st);
-  return FP_DISPATCH(BF16, fp_qmv_t, x, wq, scales, M, N, K, y, st);
+  const FpBatch* none = nullptr;
+  if (dt == 0) return FP_DISPATCH(F16, fp_qmv_t, x, wq, scales, M, N, K, y, st, none);
+  return FP_DISPATCH(BF16, fp_qmv_t, x, wq, scales, M, N, K, y, st, none);
+}
+
+hipError_t launch_fp_gather_qmv(int dt, int bits, int gs, const void* x, int64_t nxb,
+                                const int32_t* lidx, const uint32_t* wq, const uint8_t* scales,
+                                int64_t nwb, const int32_t* ridx, int64_t B, int64_t M, int64_t N,
+                                int64_t K, void* y, hipStream_t st) {
+  const FpBatch bt{lidx, ridx, (int)nxb, (int)nwb, (int)M, (int)B};
+  const FpBatch* p = &bt;
+  if (dt == 0) return FP_DISPATCH(F16, fp_qmv_t, x, wq, scales, M, N, K, y, st, p);
+  return FP_DISPATCH(BF16, fp_qmv_t, x, wq, scales, M, N, K, y, st, p);
 }
 
 }  // namespace qmm

@@ -113,6 +113,13 @@ constexpr int64_t kFpMaxK = 16384;
 hipError_t launch_fp_qmv(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                          const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
                          hipStream_t st);
+// Gathered fp GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T with
+// x [nxb, M, K], W [nwb, N, K] (codes and scale bytes), y [B, M, N]; a null
+// index array means z, indices are clamped into range. B <= 65535.
+hipError_t launch_fp_gather_qmv(int dt, int bits, int gs, const void* x, int64_t nxb,
+                                const int32_t* lidx, const uint32_t* wq, const uint8_t* scales,
+                                int64_t nwb, const int32_t* ridx, int64_t B, int64_t M, int64_t N,
+                                int64_t K, void* y, hipStream_t st);
 
 // Implicit-im2col conv on the MFMA tile GEMM.
 struct ConvGeom {

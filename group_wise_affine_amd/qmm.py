@@ -21,7 +21,7 @@ STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
-           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv",
+           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -61,9 +61,11 @@ def lib():
         L.qmm_fp_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
         L.qmm_fp_dequantize.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp, vp]
         L.qmm_fp_qmv.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
+        L.qmm_fp_gather_qmv.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i32, i64, i64, i64,
+                                        i32, i32, vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
                   "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched", "qmm_fp_quantize",
-                  "qmm_fp_dequantize", "qmm_fp_qmv"):
+                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -236,6 +238,25 @@ def fp_qmv(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(lib().qmm_fp_qmv(_ptr(x), _ptr(wq), _ptr(scales), _dt(x.dtype), M, N, K, group_size,
                             bits, _ptr(out), _stream(stream)))
+    return out
+
+
+def fp_gather_qmv(x, wq, scales, lhs_indices=None, rhs_indices=None, group_size=32, bits=4,
+                  out=None, stream=None):
+    """y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T in a floating-point
+    mode: x [Bx, M, K]; wq [E, N, K*bits/32]; scales uint8 [E, N, K/gs]."""
+    Bx, M, K = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    B = (lhs_indices.numel() if lhs_indices is not None else
+         rhs_indices.numel() if rhs_indices is not None else Bx)
+    for t in (lhs_indices, rhs_indices):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != B):
+            raise ValueError("indices must be int32 tensors of one length")
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    _check(lib().qmm_fp_gather_qmv(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales), E,
+                                   _ptr(rhs_indices), B, _dt(x.dtype), M, N, K, group_size, bits,
+                                   _ptr(out), _stream(stream)))
     return out
 
 

@@ -195,6 +195,25 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales,
                       int group_size, int bits, void* y, void* stream);
 
 /*
+ * Gathered product in a floating-point mode (e.g. mixture-of-experts decode
+ * with mxfp4 experts): for z in [0, batches),
+ *   y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T,
+ * x [x_batches, M, K], wq [w_batches, N, K*bits/32], scales [w_batches, N,
+ * K/group_size] bytes, y [batches, M, N]; index arrays, their defaults and
+ * the clamping of out-of-range values as for qmm_gather_qmv; every product
+ * is the qmm_fp_qmv product (same limits on K and M). batches <= 65535.
+ * (Source: "Add the 3bit packed qmm_t", ops.cpp gather_qmm, which takes the
+ * quantization mode like quantized_matmul; "mlx 1.0.0 backend/cpu/
+ * quantized.cpp", fp_qmm_t.)
+ */
+qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches,
+                             const int32_t* lhs_indices, const uint32_t* wq,
+                             const uint8_t* scales, int64_t w_batches,
+                             const int32_t* rhs_indices, int64_t batches,
+                             qmm_dtype dt, int64_t M, int64_t N, int64_t K,
+                             int group_size, int bits, void* y, void* stream);
+
+/*
  * Non-transposed product: y[M,N] = x[M,K] . dequant(W)[K,N], where the
  * weight W [K, N] is quantized along N (qmm_quantize of the K rows):
  *   y[m,n] = sum_k x[m,k] * (scale[k,n/gs] * q[k,n] + bias[k,n/gs]),

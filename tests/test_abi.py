@@ -235,6 +235,25 @@ def test_fp_arguments(L):
     assert v(x=P2) == Q.QMM_E_ALIGN
 
 
+def test_fp_gather_arguments(L):
+    def g(x=P, nxb=2, li=None, wq=P, sc=P, nwb=3, ri=None, B=2, dt=0, M=1, N=8, K=64, gs=32,
+          bits=4, y=P):
+        return _st(L, "qmm_fp_gather_qmv", x, nxb, li, wq, sc, nwb, ri, B, dt, M, N, K, gs, bits,
+                   y, None)
+    assert g(x=None) == Q.QMM_E_NULL
+    assert g(bits=3) == Q.QMM_E_BITS
+    assert g(gs=64) == Q.QMM_E_GROUP
+    assert g(dt=2) == Q.QMM_E_DTYPE
+    assert g(K=48) == Q.QMM_E_SHAPE
+    assert g(K=32768) == Q.QMM_E_SHAPE
+    assert g(B=0) == Q.QMM_E_SHAPE
+    assert g(B=65536, li=P, ri=P) == Q.QMM_E_SHAPE
+    assert g(nxb=1) == Q.QMM_E_SHAPE          # no lhs_indices: one x batch per output
+    assert g(nwb=1) == Q.QMM_E_SHAPE          # no rhs_indices: one W batch per output
+    assert g(li=ctypes.c_void_p(0x10002)) == Q.QMM_E_ALIGN
+    assert g(y=P2) == Q.QMM_E_ALIGN
+
+
 def test_batched_arguments(L):
     def f(x=P, wq=P, s=P, b=P, B=2, E=2, dt=0, M=1, N=8, K=64, gs=64, bits=4, y=P):
         return _st(L, "qmm_t_batched", x, wq, s, b, B, E, dt, M, N, K, gs, bits, y, None)

@@ -105,6 +105,52 @@ def test_fp_qmv(orc, name, bits, gs, dt, M, N, K):
     assert_parity(from_dev(y), yo, dt, f"fp_qmv {name} {dt} M{M} N{N} K{K}")
 
 
+def _idx(v):
+    return None if v is None else torch.tensor(v, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt,Bx,E,M,N,K,lhs,rhs", [
+    ("f16", 4, 8, 1, 512, 1024, [3, 0, 2, 2, 1, 0], [5, 1, 1, 0, 7, 6]),   # MoE decode routing
+    ("bf16", 2, 2, 3, 70, 256, None, None),                               # identity, ragged N
+    ("f16", 1, 3, 2, 4096, 2048, [0, 0, 0], [2, 0, 1]),                    # one token, 3 experts
+])
+def test_fp_gather_qmv(orc, name, bits, gs, dt, Bx, E, M, N, K, lhs, rhs):
+    code = orc_code(orc, dt)
+    x = np.stack([synth.normal((M, K), seed=30 + i, dt=dt) for i in range(Bx)])
+    parts = [orc.fp_quantize(synth.normal((N, K), seed=40 + e, dt=dt), code, gs, bits)
+             for e in range(E)]
+    wq = np.stack([p[0] for p in parts])
+    sc = np.stack([p[1] for p in parts])
+    y = Q.fp_gather_qmv(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(),
+                        _idx(lhs), _idx(rhs), gs, bits)
+    torch.cuda.synchronize()
+    B = len(lhs) if lhs is not None else (len(rhs) if rhs is not None else Bx)
+    assert tuple(y.shape) == (B, M, N)
+    yg = from_dev(y)
+    for z in range(B):
+        lz = lhs[z] if lhs is not None else z
+        rz = rhs[z] if rhs is not None else z
+        yo, _ = orc.fp_qmm_t(x[lz], wq[rz], sc[rz], code, gs, bits, nthreads=8)
+        assert_parity(yg[z], yo, dt, f"fp_gather {name} batch {z}")
+
+
+def test_fp_gather_qmv_clamps_indices(orc):
+    dt, gs, bits, M, N, K = "f16", 32, 4, 1, 96, 512
+    x = np.stack([synth.normal((M, K), seed=50 + i, dt=dt) for i in range(2)])
+    parts = [orc.fp_quantize(synth.normal((N, K), seed=60 + e, dt=dt), orc.F16, gs, bits)
+             for e in range(3)]
+    wq = np.stack([p[0] for p in parts])
+    sc = np.stack([p[1] for p in parts])
+    y = Q.fp_gather_qmv(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(),
+                        _idx([-2, 1, 7]), _idx([5, 0, -1]), gs, bits)
+    torch.cuda.synchronize()
+    yg = from_dev(y)
+    for z, (lz, rz) in enumerate([(0, 2), (1, 0), (1, 0)]):
+        yo, _ = orc.fp_qmm_t(x[lz], wq[rz], sc[rz], orc.F16, gs, bits)
+        assert_parity(yg[z], yo, dt, f"fp_gather clamped {z}")
+
+
 def test_fp_quantize_then_qmv_end_to_end(orc):
     """Quantize on the GPU, multiply on the GPU, compare with the oracle's
     product over the oracle's codes (identical by the bit-exact quantizer)."""
