@@ -135,6 +135,26 @@ def test_fp_gather_qmv(orc, name, bits, gs, dt, Bx, E, M, N, K, lhs, rhs):
         assert_parity(yg[z], yo, dt, f"fp_gather {name} batch {z}")
 
 
+def test_fp_gather_max_batches(orc):
+    """65535 products (the largest batch count), random routing, sampled."""
+    dt, gs, bits, M, N, K, Bx, E, B = "f16", 32, 4, 1, 32, 64, 5, 6, 65535
+    rng = np.random.default_rng(11)
+    lhs = rng.integers(0, Bx, B).tolist()
+    rhs = rng.integers(0, E, B).tolist()
+    x = np.stack([synth.normal((M, K), seed=70 + i, dt=dt) for i in range(Bx)])
+    parts = [orc.fp_quantize(synth.normal((N, K), seed=80 + e, dt=dt), orc.F16, gs, bits)
+             for e in range(E)]
+    wq = np.stack([p[0] for p in parts])
+    sc = np.stack([p[1] for p in parts])
+    y = Q.fp_gather_qmv(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(),
+                        _idx(lhs), _idx(rhs), gs, bits)
+    torch.cuda.synchronize()
+    yg = from_dev(y)
+    for z in list(range(0, B, 97)) + [B - 1]:
+        yo, _ = orc.fp_qmm_t(x[lhs[z]], wq[rhs[z]], sc[rhs[z]], orc.F16, gs, bits)
+        assert_parity(yg[z], yo, dt, f"fp_gather batch {z}")
+
+
 def test_fp_gather_qmv_clamps_indices(orc):
     dt, gs, bits, M, N, K = "f16", 32, 4, 1, 96, 512
     x = np.stack([synth.normal((M, K), seed=50 + i, dt=dt) for i in range(2)])

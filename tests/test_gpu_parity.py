@@ -442,6 +442,28 @@ def test_gather_qmv_clamps_indices(orc):
     assert_parity(from_dev(y), yo, dt, "gather_qmv clamped")
 
 
+def test_gather_max_batches(orc):
+    """65535 products (the largest batch count) on the GEMV and on the tile kernel,
+    random routing; every product checked against the oracle on a sample."""
+    dt, Bx, E, gs, bits, B = "f16", 7, 5, 32, 4, 65535
+    rng = np.random.default_rng(9)
+    lhs = rng.integers(0, Bx, B).tolist()
+    rhs = rng.integers(0, E, B).tolist()
+    for M, N, K, fn in ((1, 32, 64, Q.gather_qmv), (32, 128, 64, Q.gather_qmm)):
+        code, x, wq, s, b = _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed=M + 3)
+        y = fn(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+               _idx_dev(lhs), _idx_dev(rhs), gs, bits)
+        torch.cuda.synchronize()
+        yg = from_dev(y)
+        # every (x batch, expert) pair's product, then each output against its pair
+        pairs = {}
+        for lz in range(Bx):
+            for rz in range(E):
+                pairs[lz, rz], _ = orc.qmm_t(x[lz], wq[rz], s[rz], b[rz], code, gs, bits)
+        for z in list(range(0, B, 97)) + [B - 1]:
+            assert_parity(yg[z], pairs[lhs[z], rhs[z]], dt, f"{fn.__name__} batch {z}")
+
+
 def test_gather_qmv_rejects_bad_arguments():
     x = torch.zeros((2, 1, 64), dtype=torch.float16, device="cuda")
     wq = torch.zeros((3, 8, 8), dtype=torch.int32, device="cuda")
