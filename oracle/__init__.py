@@ -378,3 +378,35 @@ def fp_qmm_t(x, wq, scales, dt, group_size=32, bits=4, nthreads=1):
     _chk(lib().orc_fp_qmm_t(_p(x), _p(wq), _p(scales), dt, M, N, K, group_size, bits, _p(y32),
                             _p(yo), nthreads), "orc_fp_qmm_t")
     return y32, yo
+
+
+# ---------------------------------------------------- affine-packed layout
+# "Add the 3bit packed qmm_t", ops.cpp quantize with QuantizationType::
+# AffinePacked: after the affine quantizer, rows are taken in blocks of RP =
+# 4 (power-of-two bits) or 2 (3, 5, 6 bits); each block's scales and biases
+# become one row holding, per group, the RP scales then the RP biases; for
+# power-of-two bits the block's weight words are interleaved (word w of row r
+# at position w*RP + r). The steps below follow the page's order: unflatten
+# the row axis, concatenate scales and biases, move the block axis last,
+# flatten.
+
+def affine_pack(wq, scales, biases, bits):
+    """wq: [N, K*bits/8] bytes; scales, biases: [N, G] words. Returns
+    (wq_packed bytes [N/RP, RP*K*bits/8] for power-of-two bits, else wq
+    unchanged; sb_packed words [N/RP, G*2*RP])."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    N = wq.shape[0]
+    pow2 = (bits & (bits - 1)) == 0
+    rp = 4 if pow2 else 2
+    if N % rp:
+        raise ValueError(f"affine_pack: rows ({N}) must be a multiple of {rp}")
+    s = scales.reshape(N // rp, rp, -1)                  # unflatten(-2, {-1, rp})
+    b = biases.reshape(N // rp, rp, -1)
+    sb = np.concatenate([s, b], axis=-2)                 # [N/rp, 2rp, G]
+    sb = np.moveaxis(sb, -2, -1)                         # [N/rp, G, 2rp]
+    sb = np.ascontiguousarray(sb).reshape(N // rp, -1)   # flatten(-2, -1)
+    if pow2:
+        words = wq.view(np.uint32).reshape(N // rp, rp, -1)
+        words = np.ascontiguousarray(np.moveaxis(words, -2, -1))   # [N/rp, Kw, rp]
+        wq = words.reshape(N // rp, -1).view(np.uint8)
+    return wq, sb
