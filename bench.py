@@ -240,6 +240,30 @@ def bench_fp_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4
             "workload": f"{T} tokens x top-{topk} of {E} mxfp4 experts [{N},{K}] f16"}
 
 
+def bench_affine_packed(torch, Q, synth, timer, steps, warmup, M=1, N=4096, K=4096, bits=4,
+                        gs=64):
+    """Decode GEMV on the affine-packed layout (4-bit g64 f16, [4096, 4096]); every
+    step reads a different copy of the packed weight from a >= 1 GiB pool."""
+    from tests.helpers import to_dev
+    wq, s, b = make_layer(torch, Q, synth, "f16", N, K, gs, bits, 1)
+    wp, sbp = Q.affine_pack(wq, s, b, gs, bits)
+    del wq, s, b
+    per = wp.numel() * 4 + sbp.numel() * 2
+    P = max(2, -(-POOL_BYTES // per))
+    wps = wp.unsqueeze(0).expand(P, *wp.shape).contiguous()
+    sbps = sbp.unsqueeze(0).expand(P, *sbp.shape).contiguous()
+    x = to_dev(synth.normal((M, K), seed=0), "f16")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.qmv_affine_packed(x, wps[i % P], sbps[i % P], N, gs, bits, out=y),
+                   steps, warmup)
+    nbytes = alg_bytes(M, N, K, bits, gs)
+    del wps, sbps
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "pool_copies": P}
+
+
 def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, bits=4, gs=64):
     """Batched product with one weight per batch: y[b] = x[b] . dequant(W_b)^T,
     x [B, M, K] f16, W_b [N, K] 4-bit g64 (qmm_t_batched). Every step reads a
@@ -466,6 +490,7 @@ def main():
         for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)):
             r[f"fp_qmv_{name}"] = bench_fp(torch, Q, synth, timer, 200, 20, bits, gs)
         r["fp_gather_qmv_moe_decode_mxfp4"] = bench_fp_gather(torch, Q, synth, timer, 200, 20)
+        r["qmv_affine_packed_4bit"] = bench_affine_packed(torch, Q, synth, timer, 200, 20)
         print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items() if isinstance(vv, float)}
                           for k, v in r.items()}))
         return
@@ -518,6 +543,12 @@ def main():
             k: round(v, 4) if isinstance(v, float) else v
             for k, v in bench_fp_gather(torch, Q, synth, timer, n_small, 20).items()}
         log("fp gather row done")
+        rows["qmv_affine_packed_decode_4096x4096_f16_g64"] = {
+            f"bits{bits}": {k: round(v, 4) if isinstance(v, float) else v
+                            for k, v in bench_affine_packed(torch, Q, synth, timer, n_small, 20,
+                                                            bits=bits).items()}
+            for bits in (4, 8)}
+        log("affine-packed rows done")
         ch = {}
         for bits in (2, 4, 8):
             ch[f"bits{bits}"] = {k: round(v, 4) for k, v in

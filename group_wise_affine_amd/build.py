@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "quantize.hip", "qmv.hip", "qmn.hip", "fpq.hip", "qmv_mfma_f16.hip", "qmv_mfma_bf16.hip", "qmm.hip",
+SOURCES = ["api.cpp", "quantize.hip", "qmv.hip", "qmn.hip", "fpq.hip", "apk.hip", "qmv_mfma_f16.hip", "qmv_mfma_bf16.hip", "qmm.hip",
            "tile_gemm_f16.hip", "tile_gemm_bf16.hip", "tile_conv_f16.hip", "tile_conv_bf16.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

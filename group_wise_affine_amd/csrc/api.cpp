@@ -497,6 +497,63 @@ qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches, const int32_t* lh
                   "qmm_fp_gather_qmv");
 }
 
+qmm_status qmm_affine_pack(const uint32_t* wq, const void* scales, const void* biases,
+                           qmm_dtype dt, int64_t N, int64_t K, int group_size, int bits,
+                           uint32_t* wq_packed, void* sb_packed, void* stream) {
+  const bool pow2 = (bits & (bits - 1)) == 0;
+  if (!wq || !scales || !biases || !sb_packed || (pow2 && !wq_packed))
+    return fail(QMM_E_NULL, "qmm_affine_pack: wq, scales, biases, sb_packed (and wq_packed for "
+                "power-of-two bits) must be non-NULL");
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16 && dt != QMM_F32)
+    return fail(QMM_E_DTYPE, "qmm_affine_pack: scales must be float16, bfloat16 or float32");
+  st = check_k(K, group_size);
+  if (st) return st;
+  const int rp = pow2 ? 4 : 2;
+  if (N < 1 || N % rp != 0)
+    return fail(QMM_E_SHAPE, "qmm_affine_pack: N (%lld) must be a positive multiple of %d for "
+                "%d-bit codes", (long long)N, rp, bits);
+  if (N * K > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_affine_pack: problem too large");
+  if ((pow2 && (!aligned(wq, 16) || !aligned(wq_packed, 16))) ||
+      !aligned(scales, elem_bytes(dt)) || !aligned(biases, elem_bytes(dt)) ||
+      !aligned(sb_packed, elem_bytes(dt)))
+    return fail(QMM_E_ALIGN, "qmm_affine_pack: wq and wq_packed must be 16-byte aligned, the "
+                "scale arrays aligned to their element size");
+  return launched(qmm::launch_affine_pack((int)dt, bits, group_size, wq, scales, biases, N, K,
+                                          wq_packed, sb_packed, (hipStream_t)stream),
+                  "qmm_affine_pack");
+}
+
+qmm_status qmv_affine_packed(const void* x, const uint32_t* wq_packed, const void* sb_packed,
+                             qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
+                             int bits, void* y, void* stream) {
+  if (!x || !wq_packed || !sb_packed || !y)
+    return fail(QMM_E_NULL, "qmv_affine_packed: x, wq_packed, sb_packed and y must be non-NULL");
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(QMM_E_BITS, "qmv_affine_packed: the interleaved weight layout exists for bits "
+                "2, 4 and 8 only (got %d)", bits);
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qmv_affine_packed: only float16 and bfloat16 are supported");
+  st = check_k(K, group_size);
+  if (st) return st;
+  if (M < 1 || M > 65535 || N < 4 || N % 4 != 0 || N > kI32 || K > qmm::kFpMaxK)
+    return fail(QMM_E_SHAPE, "qmv_affine_packed: M (%lld) must be in [1, 65535], N (%lld) a "
+                "positive multiple of 4, K (%lld) at most %lld", (long long)M, (long long)N,
+                (long long)K, (long long)qmm::kFpMaxK);
+  if (N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmv_affine_packed: problem too large");
+  if (!aligned(x, 16) || !aligned(wq_packed, 16) || !aligned(sb_packed, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qmv_affine_packed: x, wq_packed, sb_packed and y must be 16-byte "
+                "aligned");
+  return launched(qmm::launch_affine_packed_qmv((int)dt, bits, group_size, x, wq_packed,
+                                                sb_packed, M, N, K, y, (hipStream_t)stream),
+                  "qmv_affine_packed");
+}
+
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
                  const void* biases, qmm_dtype dt, int64_t M, int64_t N,
                  int64_t K, int group_size, int bits, void* y, void* stream) {

@@ -121,6 +121,16 @@ hipError_t launch_fp_gather_qmv(int dt, int bits, int gs, const void* x, int64_t
                                 int64_t nwb, const int32_t* ridx, int64_t B, int64_t M, int64_t N,
                                 int64_t K, void* y, hipStream_t st);
 
+// Affine-packed layout: pack the affine-quantized wq / scales / biases of N
+// rows (N % RP == 0, RP = 4 for power-of-two bits, else 2) and the GEMV on
+// the packed layout (power-of-two bits, f16 / bf16, K <= kFpMaxK).
+hipError_t launch_affine_pack(int dt, int bits, int gs, const uint32_t* wq, const void* s,
+                              const void* b, int64_t N, int64_t K, uint32_t* wq_packed,
+                              void* sb_packed, hipStream_t st);
+hipError_t launch_affine_packed_qmv(int dt, int bits, int gs, const void* x,
+                                    const uint32_t* wq_packed, const void* sb_packed, int64_t M,
+                                    int64_t N, int64_t K, void* y, hipStream_t st);
+
 // Implicit-im2col conv on the MFMA tile GEMM.
 struct ConvGeom {
   int64_t B, H, W, C, O, OH, OW;

@@ -22,6 +22,7 @@ STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
            "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv",
+           "qmm_affine_pack", "qmv_affine_packed",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -56,6 +57,8 @@ def lib():
         L.qmm_gather_qmv.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, i64,
                                      i64, i64, i32, i32, vp, vp]
         L.qmm_gather_qmm.argtypes = L.qmm_gather_qmv.argtypes
+        L.qmm_affine_pack.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, vp, vp, vp]
+        L.qmv_affine_packed.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
         L.qmm_t_batched.argtypes = [vp, vp, vp, vp, i64, i64, i32, i64, i64, i64, i32, i32,
                                     vp, vp]
         L.qmm_fp_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
@@ -65,7 +68,8 @@ def lib():
                                         i32, i32, vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
                   "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched", "qmm_fp_quantize",
-                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv"):
+                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv",
+                  "qmm_affine_pack", "qmv_affine_packed"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -257,6 +261,32 @@ def fp_gather_qmv(x, wq, scales, lhs_indices=None, rhs_indices=None, group_size=
     _check(lib().qmm_fp_gather_qmv(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales), E,
                                    _ptr(rhs_indices), B, _dt(x.dtype), M, N, K, group_size, bits,
                                    _ptr(out), _stream(stream)))
+    return out
+
+
+def affine_pack(wq, scales, biases, group_size=64, bits=4, stream=None):
+    """Affine-packed layout of (wq [N, K*bits/32], scales, biases [N, K/gs]):
+    returns (wq_packed [N/4, 4*K*bits/32] for bits 2/4/8, else wq itself;
+    sb_packed [N/RP, K/gs*2*RP])."""
+    N = wq.shape[0]
+    K = wq.shape[1] * 32 // bits
+    pow2 = (bits & (bits - 1)) == 0
+    rp = 4 if pow2 else 2
+    wp = torch.empty((N // rp, rp * wq.shape[1]), dtype=torch.int32,
+                     device=wq.device) if pow2 else None
+    sbp = torch.empty((N // rp, scales.shape[1] * 2 * rp), dtype=scales.dtype, device=wq.device)
+    _check(lib().qmm_affine_pack(_ptr(wq), _ptr(scales), _ptr(biases), _dt(scales.dtype), N, K,
+                                 group_size, bits, _ptr(wp), _ptr(sbp), _stream(stream)))
+    return (wp if pow2 else wq), sbp
+
+
+def qmv_affine_packed(x, wq_packed, sb_packed, N, group_size=64, bits=4, out=None, stream=None):
+    """y [M,N] = x [M,K] . dequant(W)^T from the affine-packed layout."""
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(lib().qmv_affine_packed(_ptr(x), _ptr(wq_packed), _ptr(sb_packed), _dt(x.dtype), M, N,
+                                   K, group_size, bits, _ptr(out), _stream(stream)))
     return out
 
 

@@ -214,6 +214,34 @@ qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches,
                              int group_size, int bits, void* y, void* stream);
 
 /*
+ * Affine-packed layout of an affine-quantized weight (wq [N, K*bits/32],
+ * scales and biases [N, K/group_size] as qmm_quantize writes them): rows in
+ * blocks of RP = 4 (bits 2, 4, 8) or 2 (bits 3, 5, 6), N % RP == 0.
+ * sb_packed [N/RP, (K/group_size)*2*RP] in dt: per block and group, the RP
+ * scales then the RP biases. For bits 2, 4, 8, wq_packed [N/4, 4*K*bits/32]
+ * uint32: word w of row 4i+r at [i, 4w + r]; for 3, 5, 6 the weight rows
+ * keep their layout and wq_packed is not written (may be NULL).
+ * (Source: "Add the 3bit packed qmm_t", ops.cpp quantize with
+ * QuantizationType::AffinePacked.)
+ */
+qmm_status qmm_affine_pack(const uint32_t* wq, const void* scales,
+                           const void* biases, qmm_dtype dt, int64_t N,
+                           int64_t K, int group_size, int bits,
+                           uint32_t* wq_packed, void* sb_packed, void* stream);
+
+/*
+ * y[M,N] = x[M,K] . dequant(W)^T read from the affine-packed layout (bits 2,
+ * 4 or 8; f16 / bf16; N % 4 == 0; K <= 16384; M <= 65535): the same product
+ * as qmv, y[m,n] = sum over groups of s * sum x*q + b * sum x in fp32, one
+ * pass over W per row of x. (Source: "Add the 3bit packed qmm_t",
+ * affine_packed_qmv_fast_impl: a wide load per row block.)
+ */
+qmm_status qmv_affine_packed(const void* x, const uint32_t* wq_packed,
+                             const void* sb_packed, qmm_dtype dt, int64_t M,
+                             int64_t N, int64_t K, int group_size, int bits,
+                             void* y, void* stream);
+
+/*
  * Non-transposed product: y[M,N] = x[M,K] . dequant(W)[K,N], where the
  * weight W [K, N] is quantized along N (qmm_quantize of the K rows):
  *   y[m,n] = sum_k x[m,k] * (scale[k,n/gs] * q[k,n] + bias[k,n/gs]),

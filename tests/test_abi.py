@@ -254,6 +254,30 @@ def test_fp_gather_arguments(L):
     assert g(y=P2) == Q.QMM_E_ALIGN
 
 
+def test_affine_packed_arguments(L):
+    def pk(wq=P, s=P, b=P, dt=0, N=8, K=64, gs=64, bits=4, wp=P, sbp=P):
+        return _st(L, "qmm_affine_pack", wq, s, b, dt, N, K, gs, bits, wp, sbp, None)
+
+    def mv(x=P, wp=P, sbp=P, dt=0, M=1, N=8, K=64, gs=64, bits=4, y=P):
+        return _st(L, "qmv_affine_packed", x, wp, sbp, dt, M, N, K, gs, bits, y, None)
+    assert pk(wq=None) == Q.QMM_E_NULL
+    assert pk(wp=None) == Q.QMM_E_NULL          # needed for power-of-two bits
+    assert pk(bits=7) == Q.QMM_E_BITS
+    assert pk(gs=16) == Q.QMM_E_GROUP
+    assert pk(dt=5) == Q.QMM_E_DTYPE
+    assert pk(N=6) == Q.QMM_E_SHAPE             # blocks of 4 rows
+    assert pk(N=5, bits=3, wp=None) == Q.QMM_E_SHAPE   # blocks of 2 rows
+    assert pk(K=48) == Q.QMM_E_SHAPE
+    assert pk(wq=P2) == Q.QMM_E_ALIGN
+    assert mv(x=None) == Q.QMM_E_NULL
+    assert mv(bits=3) == Q.QMM_E_BITS           # no interleaved words for 3 bits
+    assert mv(dt=2) == Q.QMM_E_DTYPE
+    assert mv(N=6) == Q.QMM_E_SHAPE
+    assert mv(K=32768) == Q.QMM_E_SHAPE
+    assert mv(M=0) == Q.QMM_E_SHAPE
+    assert mv(sbp=P2) == Q.QMM_E_ALIGN
+
+
 def test_batched_arguments(L):
     def f(x=P, wq=P, s=P, b=P, B=2, E=2, dt=0, M=1, N=8, K=64, gs=64, bits=4, y=P):
         return _st(L, "qmm_t_batched", x, wq, s, b, B, E, dt, M, N, K, gs, bits, y, None)

@@ -510,6 +510,40 @@ def test_gather_qmm_clamps_indices(orc):
     assert_parity(from_dev(y), yo, dt, "gather_qmm clamped")
 
 
+# ------------------------------------------------------------ affine-packed layout
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_affine_pack_bit_exact(orc, dt, bits):
+    N, K, gs = 24, 256, 64
+    w = synth.normal((N, K), seed=bits, dt=dt)
+    wq, s, b = orc.quantize(w, orc_code(orc, dt), gs, bits)
+    wp_o, sbp_o = orc.affine_pack(wq, s, b, bits)
+    wp, sbp = Q.affine_pack(bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_dev_to_bytes(wp), wp_o)
+    assert np.array_equal(from_dev(sbp), sbp_o)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt,M,N,K,gs", [
+    ("f16", 1, 4096, 4096, 64),
+    ("bf16", 1, 4096, 4096, 64),
+    ("f16", 3, 72, 640, 32),       # 18 row blocks: a partial workgroup; few words per lane
+    ("bf16", 2, 8, 16384, 128),    # the largest K
+])
+def test_qmv_affine_packed(orc, dt, M, N, K, gs, bits):
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=M + N, dt=dt)
+    w = synth.normal((N, K), seed=N + K, dt=dt)
+    wq, s, b = orc.quantize(w, code, gs, bits)
+    yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
+    wp, sbp = Q.affine_pack(bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    y = Q.qmv_affine_packed(to_dev(x, dt), wp, sbp, N, gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"qmv_affine_packed {dt} M{M} N{N} K{K} b{bits}")
+
+
 # ------------------------------------------------------------ batched weights
 
 @pytest.mark.parametrize("dt,B,E,M,N,K,gs,bits", [
