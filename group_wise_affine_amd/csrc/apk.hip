@@ -47,17 +47,18 @@ __global__ __launch_bounds__(256) void apk_scales_kernel(const W* __restrict__ s
 
 // ---------------------------------------------------------------- GEMV
 // y[m, n] = sum over groups of s * sum x*q + b * sum x (fp32), power-of-two
-// bits. Workgroup = 4 wavefronts; kApkSplit of them share a row block of 4
-// rows, taking alternate runs of 64 words; one row m of x (blockIdx.y) is
-// staged in LDS as fp32. A 16-byte load gives word w of all 4 rows of a
-// block (32/BITS codes each), one 16-byte load the block's 4 scales and 4
-// biases of the group; the wavefronts' sums meet in LDS. Measured (4096 x
-// 4096, 4-bit g64, M = 1): 1 / 2 / 4 wavefronts per block 9.85 / 7.65 /
-// 7.03 us.
+// bits. Workgroup = kApkWaves wavefronts; kApkSplit of them share a row
+// block of 4 rows, taking alternate runs of 64 words; one row m of x
+// (blockIdx.y) is staged in LDS as fp32. A 16-byte load gives word w of all
+// 4 rows of a block (32/BITS codes each), one 16-byte load the block's 4
+// scales and 4 biases of the group; the wavefronts' sums meet in LDS.
+// Measured (4096 x 4096, 4-bit g64, M = 1; waves per workgroup / per
+// block): 4/1 9.85, 4/2 7.65, 4/4 6.97, 8/8 6.67, 8/4 6.20 us.
 constexpr int kApkSplit = 4;   // wavefronts per row block
+constexpr int kApkWaves = 8;   // wavefronts per workgroup (2 row blocks)
 
 template <class T, int BITS>
-__global__ __launch_bounds__(256) void apk_qmv_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kApkWaves) void apk_qmv_kernel(const uint16_t* __restrict__ x,
                                                       const uint32_t* __restrict__ wp,
                                                       const uint16_t* __restrict__ sbp,
                                                       uint16_t* __restrict__ y, int N, int K,
@@ -65,12 +66,12 @@ __global__ __launch_bounds__(256) void apk_qmv_kernel(const uint16_t* __restrict
   extern __shared__ float xs[];
   const int m = blockIdx.y;
   const uint16_t* xr = x + (int64_t)m * K;
-  for (int k = threadIdx.x; k < K; k += 256) xs[k] = to_f32(T{}, xr[k]);
+  for (int k = threadIdx.x; k < K; k += 64 * kApkWaves) xs[k] = to_f32(T{}, xr[k]);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = wave % kApkSplit;               // which runs of 64 words
-  const int blk = blockIdx.x * (4 / kApkSplit) + wave / kApkSplit;
+  const int blk = blockIdx.x * (kApkWaves / kApkSplit) + wave / kApkSplit;
   const bool live = blk < N / 4;
   constexpr int kCpw = 32 / BITS;                 // codes per word
   constexpr uint32_t kMask = (1u << BITS) - 1u;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void apk_qmv_kernel(const uint16_t* __restrict
       acc[r] = fmaf(s, qs, fmaf(b, sumx, acc[r]));
     }
   }
-  __shared__ float red[4][4];
+  __shared__ float red[kApkWaves][4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
     float v = acc[r];
@@ -124,18 +125,18 @@ __global__ __launch_bounds__(256) void apk_qmv_kernel(const uint16_t* __restrict
 template <class T>
 hipError_t apk_qmv_t(int bits, int gs, const void* x, const uint32_t* wp, const void* sbp,
                      int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
-  constexpr int kBlocks = 4 / kApkSplit;          // row blocks per workgroup
+  constexpr int kBlocks = kApkWaves / kApkSplit;  // row blocks per workgroup
   const dim3 grid((unsigned)((N / 4 + kBlocks - 1) / kBlocks), (unsigned)M);
   const auto xp = static_cast<const uint16_t*>(x);
   const auto sp = static_cast<const uint16_t*>(sbp);
   const auto yp = static_cast<uint16_t*>(y);
   const size_t lds = (size_t)K * 4;
   switch (bits) {
-    case 2: hipLaunchKernelGGL((apk_qmv_kernel<T, 2>), grid, dim3(256), lds, st, xp, wp, sp, yp,
+    case 2: hipLaunchKernelGGL((apk_qmv_kernel<T, 2>), grid, dim3(64 * kApkWaves), lds, st, xp, wp, sp, yp,
                                (int)N, (int)K, ilog2(gs)); break;
-    case 4: hipLaunchKernelGGL((apk_qmv_kernel<T, 4>), grid, dim3(256), lds, st, xp, wp, sp, yp,
+    case 4: hipLaunchKernelGGL((apk_qmv_kernel<T, 4>), grid, dim3(64 * kApkWaves), lds, st, xp, wp, sp, yp,
                                (int)N, (int)K, ilog2(gs)); break;
-    default: hipLaunchKernelGGL((apk_qmv_kernel<T, 8>), grid, dim3(256), lds, st, xp, wp, sp, yp,
+    default: hipLaunchKernelGGL((apk_qmv_kernel<T, 8>), grid, dim3(64 * kApkWaves), lds, st, xp, wp, sp, yp,
                                 (int)N, (int)K, ilog2(gs)); break;
   }
   return hipGetLastError();
