@@ -226,15 +226,15 @@ __global__ __launch_bounds__(256) void fp_dequantize_kernel(const uint8_t* __res
 
 // ---------------------------------------------------------------- GEMV
 // y[m, n] = T(sum over groups g of scale_T[n, g] * sum_{k in g} x[m, k] *
-// value[n, k]) with fp32 accumulation. Workgroup = fp_waves wavefronts x R rows of
+// value[n, k]) with fp32 accumulation. Workgroup = WV wavefronts x R rows of
 // W for one row m of x (blockIdx.y); x[m] is staged in LDS as fp32. Each
 // lane takes 16-byte units of a row (32 E2M1 or 16 E4M3 codes), unit u at
 // lane u % 64, for R rows at once so that their loads overlap.
-// Wavefronts per workgroup: 8 for E4M3 codes, 4 for E2M1 (measured on 4096 x
-// 4096, M = 1: mxfp8 6.44 / 7.21 us and mxfp4 6.76 / 6.19 us with 8 / 4;
-// 2 wavefronts: 9.2 - 9.3 us).
-template <int BITS>
-constexpr int fp_waves() { return BITS == 8 ? 8 : 4; }
+// Wavefronts per workgroup (WV): 8 for E4M3 codes; for E2M1, 8 when that
+// still gives 512 workgroups at 4 rows per wavefront (several rows of x or
+// gathered products), else 4. Measured on 4096 x 4096: M = 1 mxfp8 6.44 /
+// 7.21 us and mxfp4 6.76 / 6.19 us with 8 / 4; mxfp4 M = 4 8.57 / 9.57 us;
+// 2 wavefronts 9.2 - 9.3 us.
 
 // Gathered products (GA): output batch z = blockIdx.z multiplies x batch
 // lidx[z] (of nxb, M rows each) by weight batch ridx[z] (of nwb), indices
@@ -245,8 +245,8 @@ struct FpBatch {
   int nxb, nwb, M, B;
 };
 
-template <class T, int BITS, int GS, int kFpRows, bool GA>
-__global__ __launch_bounds__(64 * fp_waves<BITS>()) void fp_qmv_kernel(const typename T::word* __restrict__ x,
+template <class T, int BITS, int GS, int kFpRows, bool GA, int WV>
+__global__ __launch_bounds__(64 * WV) void fp_qmv_kernel(const typename T::word* __restrict__ x,
                                                      const uint8_t* __restrict__ wq,
                                                      const uint8_t* __restrict__ sc,
                                                      typename T::word* __restrict__ y, int N,
@@ -270,11 +270,11 @@ __global__ __launch_bounds__(64 * fp_waves<BITS>()) void fp_qmv_kernel(const typ
     y += (int64_t)z * bt.M * N;
   }
   const typename T::word* xr = x + (int64_t)m * K;
-  for (int k = threadIdx.x; k < K; k += 64 * fp_waves<BITS>()) xs[k] = to_f32(T{}, xr[k]);
+  for (int k = threadIdx.x; k < K; k += 64 * WV) xs[k] = to_f32(T{}, xr[k]);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * fp_waves<BITS>() + wave) * kFpRows;
+  const int n0 = (blockIdx.x * WV + wave) * kFpRows;
   constexpr int kCodes = 128 / BITS;            // codes per 16-byte unit
   const int units = K / kCodes;
   const int64_t rb = (int64_t)K * BITS / 8, G = K / GS;
@@ -347,20 +347,20 @@ hipError_t fp_dequantize_t(const uint32_t* wq, const uint8_t* sc, int64_t rows, 
   return hipGetLastError();
 }
 
-template <class T, int BITS, int GS, int R>
+template <class T, int BITS, int GS, int R, int WV>
 hipError_t fp_qmv_r(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
                     int64_t K, void* y, hipStream_t st, const FpBatch* bt) {
-  const int64_t rows_per_block = fp_waves<BITS>() * R;
+  const int64_t rows_per_block = WV * R;
   const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)M,
                   bt ? (unsigned)bt->B : 1u);
   auto go = [&](auto kern, const FpBatch& b) {
-    hipLaunchKernelGGL(kern, grid, dim3(64 * fp_waves<BITS>()), (size_t)K * 4, st,
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WV), (size_t)K * 4, st,
                        static_cast<const typename T::word*>(x),
                        reinterpret_cast<const uint8_t*>(wq), sc,
                        static_cast<typename T::word*>(y), (int)N, (int)K, b);
   };
-  if (bt) go(fp_qmv_kernel<T, BITS, GS, R, true>, *bt);
-  else go(fp_qmv_kernel<T, BITS, GS, R, false>, FpBatch{nullptr, nullptr, 1, 1, (int)M, 1});
+  if (bt) go(fp_qmv_kernel<T, BITS, GS, R, true, WV>, *bt);
+  else go(fp_qmv_kernel<T, BITS, GS, R, false, WV>, FpBatch{nullptr, nullptr, 1, 1, (int)M, 1});
   return hipGetLastError();
 }
 
@@ -373,11 +373,17 @@ template <class T, int BITS, int GS>
 hipError_t fp_qmv_t(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
                     int64_t K, void* y, hipStream_t st, const FpBatch* bt) {
   const int64_t want = BITS == 8 ? 1024 : 512, nb = bt ? bt->B : 1;
-  constexpr int64_t kW = fp_waves<BITS>();
-  auto blocks = [&](int64_t r) { return (N + kW * r - 1) / (kW * r) * M * nb; };
-  if (blocks(4) >= want) return fp_qmv_r<T, BITS, GS, 4>(x, wq, sc, M, N, K, y, st, bt);
-  if (blocks(2) >= want) return fp_qmv_r<T, BITS, GS, 2>(x, wq, sc, M, N, K, y, st, bt);
-  return fp_qmv_r<T, BITS, GS, 1>(x, wq, sc, M, N, K, y, st, bt);
+  auto blocks = [&](int64_t w, int64_t r) { return (N + w * r - 1) / (w * r) * M * nb; };
+  if constexpr (BITS == 8) {
+    if (blocks(8, 4) >= want) return fp_qmv_r<T, BITS, GS, 4, 8>(x, wq, sc, M, N, K, y, st, bt);
+    if (blocks(8, 2) >= want) return fp_qmv_r<T, BITS, GS, 2, 8>(x, wq, sc, M, N, K, y, st, bt);
+    return fp_qmv_r<T, BITS, GS, 1, 8>(x, wq, sc, M, N, K, y, st, bt);
+  } else {
+    if (blocks(8, 4) >= want) return fp_qmv_r<T, BITS, GS, 4, 8>(x, wq, sc, M, N, K, y, st, bt);
+    if (blocks(4, 4) >= want) return fp_qmv_r<T, BITS, GS, 4, 4>(x, wq, sc, M, N, K, y, st, bt);
+    if (blocks(4, 2) >= want) return fp_qmv_r<T, BITS, GS, 2, 4>(x, wq, sc, M, N, K, y, st, bt);
+    return fp_qmv_r<T, BITS, GS, 1, 4>(x, wq, sc, M, N, K, y, st, bt);
+  }
 }
 
 // mode dispatch: (4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8

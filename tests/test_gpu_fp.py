@@ -88,7 +88,8 @@ def synth_dt(dt):
 @pytest.mark.parametrize("dt,M,N,K", [
     ("f16", 1, 4096, 4096),      # decode layer
     ("bf16", 1, 4096, 4096),
-    ("f16", 4, 4096, 1024),      # 4 rows of W per wavefront (enough workgroups)
+    ("f16", 4, 4096, 1024),      # 4 rows of W per wavefront, 8 wavefronts (4-bit)
+    ("bf16", 2, 4096, 512),      # 4 rows of W per wavefront, 4 wavefronts (4-bit)
     ("f16", 3, 70, 1024),        # N % 16 != 0: a partial block of rows
     ("bf16", 2, 257, 96),        # 3 units of 32 codes: most lanes idle
     ("f16", 1, 64, 16384),       # the largest K (x in 64 KB of LDS)
