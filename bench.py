@@ -10,9 +10,13 @@ Headline (one step = one decode GEMV through the C ABI):
 The other rows of the hot path are measured in the same run and reported
 under "rows": quantize, dequantize, qmv at bits 2/8 and M <= 16, the gathered
 GEMV on a mixture-of-experts decode step (4 tokens, top-2 of 8 experts), the
-non-transposed decode product (W [4096, 4096] quantized along N), the chained
-qmm_t bench (10 loops of x = qmm(qmm(x, W1), W2), M=1024), the quantized
-conv2d (x [1,64,64,320], 3x3, groups 1 and 2) and the bf16 small-M sweep.
+gathered tile GEMM on a mixture-of-experts prefill step (8 blocks of 128
+tokens), the non-transposed decode product (W [4096, 4096] quantized along N),
+batched weights (8 batches at M = 1, 4 at M = 256), the floating-point modes'
+decode GEMV (mxfp4, nvfp4, mxfp8) and their gathered form (mxfp4 experts), the
+GEMV on the affine-packed layout, the chained qmm_t bench (10 loops of x =
+qmm(qmm(x, W1), W2), M=1024), the quantized conv2d (x [1,64,64,320], 3x3,
+groups 1 and 2) and the bf16 small-M sweep.
 
 Timing: the K timed launches are captured in one HIP graph and replayed
 between two HIP events on the launch stream, after a synchronize; a warmup
