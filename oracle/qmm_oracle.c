@@ -266,12 +266,23 @@ int orc_dequantize(const uint8_t* wq, const void* scales, const void* biases,
 /* y = x . dequant(W)^T with fp32 accumulation ([P4] _qmm_t_simd).      */
 /* ------------------------------------------------------------------ */
 
+/* Every weight of W dequantized to fp32 (as orc_dequantize, rows split over
+ * threads; each element's arithmetic is the same). */
 static float* dequant_all(const uint8_t* wq, const void* scales,
                           const void* biases, int dtype, int64_t N, int64_t K,
-                          int gs, int bits) {
+                          int gs, int bits, int nthreads) {
   float* w32 = (float*)malloc(sizeof(float) * (size_t)(N * K));
   if (!w32) return NULL;
-  orc_dequantize(wq, scales, biases, dtype, N, K, gs, bits, w32, NULL);
+  const int64_t rb = orc_row_bytes(K, bits);
+  const int64_t G = K / gs;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t k = 0; k < K; k++) {
+      const int64_t g = n * G + k / gs;
+      w32[n * K + k] = deq(load_t(scales, dtype, g), load_t(biases, dtype, g),
+                           orc_unpack_code(wq + n * rb, k, bits));
+    }
   return w32;
 }
 
@@ -282,7 +293,7 @@ int orc_qmm_t_rows(const void* x, const uint8_t* wq, const void* scales,
   int rc = check_args(dtype, K, group_size, bits);
   if (rc) return rc;
   if (M < 1 || N < 1 || m0 < 0 || m1 > M || m1 <= m0) return -3;
-  float* w32 = dequant_all(wq, scales, biases, dtype, N, K, group_size, bits);
+  float* w32 = dequant_all(wq, scales, biases, dtype, N, K, group_size, bits, nthreads);
   if (!w32) return -5;
   const int64_t rows = m1 - m0;
   float* xr = (float*)malloc(sizeof(float) * (size_t)(rows * K));
@@ -293,7 +304,9 @@ int orc_qmm_t_rows(const void* x, const uint8_t* wq, const void* scales,
   for (int64_t r = 0; r < rows; r++)
     for (int64_t k = 0; k < K; k++) xr[r * K + k] = load_t(x, dtype, (m0 + r) * K + k);
   if (nthreads < 1) nthreads = 1;
-#pragma omp parallel for num_threads(nthreads) schedule(static)
+  /* threads split the (row, column) pairs, so one row of x also spreads
+     over every thread; each output's sum keeps its k-ascending order */
+#pragma omp parallel for collapse(2) num_threads(nthreads) schedule(static)
   for (int64_t r = 0; r < rows; r++) {
     for (int64_t n = 0; n < N; n++) {
       float acc = 0.0f;
@@ -331,10 +344,10 @@ int orc_qmm_n(const void* x, const uint8_t* wq, const void* scales,
   if (rc) return rc;
   if (M < 1 || K < 1) return -3;
   /* the K stored rows, each N long with its groups along N */
-  float* w32 = dequant_all(wq, scales, biases, dtype, K, N, group_size, bits);
+  float* w32 = dequant_all(wq, scales, biases, dtype, K, N, group_size, bits, nthreads);
   if (!w32) return -5;
   if (nthreads < 1) nthreads = 1;
-#pragma omp parallel for num_threads(nthreads) schedule(static)
+#pragma omp parallel for collapse(2) num_threads(nthreads) schedule(static)
   for (int64_t m = 0; m < M; m++) {
     for (int64_t n = 0; n < N; n++) {
       float acc = 0.0f;
@@ -375,7 +388,7 @@ int orc_qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
   const int64_t OH = (H + 2 * pad_h - kh) / stride_h + 1;
   const int64_t OW = (W + 2 * pad_w - kw) / stride_w + 1;
   if (OH < 1 || OW < 1) return -3;
-  float* w32 = dequant_all(wq, scales, biases, dtype, O, K_pad, group_size, bits);
+  float* w32 = dequant_all(wq, scales, biases, dtype, O, K_pad, group_size, bits, nthreads);
   if (!w32) return -5;
   const int64_t npix = B * OH * OW;
   if (nthreads < 1) nthreads = 1;

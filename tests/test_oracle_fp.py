@@ -213,3 +213,61 @@ def test_fp_qmm_t_tiny_bruteforce(orc):
                 acc += float(xf[m, k]) * v
                 mag += abs(float(xf[m, k]) * v)
             assert abs(y32[m, n] - acc) <= (K + 2) * U32 * mag * 1.01 + 1e-30
+
+
+# ---------------------------------------------------- the scale as the product uses it
+# "mlx 1.0.0 backend/cpu/quantized.cpp", dequantize_scale<T>: the decoded
+# group scale is converted to the element type T before it multiplies the
+# codes. Expected values come from numpy / torch casts of the exact scale.
+
+E8M0_BYTES = [0, 1, 100, 101, 102, 103, 104, 112, 113, 127, 141, 142, 143, 144, 200, 254]
+
+
+def _cast_scale(v, dt):
+    """Exact scale (a Python float) rounded to T by numpy / torch, as float."""
+    if dt == "f16":
+        with np.errstate(over="ignore"):
+            return float(np.float64(v).astype(np.float16))
+    if dt == "bf16":
+        return float(torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).double())
+    return float(np.float32(v))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_fp_scale_e8m0_rounded_to_t(orc, dt):
+    """2^(s-127) rounded to T: f16 flushes bytes <= 102 to 0 (2^-25 ties to
+    even, down to 0), keeps 2^-24 (byte 103) as a subnormal and overflows from
+    byte 143 (2^16); bf16 and f32 hold every byte exactly."""
+    for s in E8M0_BYTES:
+        want = _cast_scale(math.ldexp(1.0, s - 127), dt)
+        got = orc.fp_scale(s, 32, _code(orc, dt))
+        assert got == want, (dt, s, got, want)
+    if dt == "f16":
+        assert orc.fp_scale(102, 32, orc.F16) == 0.0
+        assert orc.fp_scale(103, 32, orc.F16) == 2.0 ** -24
+        assert orc.fp_scale(142, 32, orc.F16) == 32768.0
+        assert math.isinf(orc.fp_scale(143, 32, orc.F16))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_fp_scale_e4m3(orc, dt):
+    """Group size 16 (nvfp4): the scale byte is an E4M3 value (torch's
+    float8_e4m3fn), which f16, bf16 and f32 all hold exactly."""
+    vals = torch.arange(128, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for s in range(127):          # 0x7f is NaN, outside the contract
+        want = _cast_scale(float(vals[s]), dt)
+        assert want == float(vals[s])
+        assert orc.fp_scale(s, 16, _code(orc, dt)) == want, (dt, s)
+
+
+def test_fp_dequantize_uses_rounded_scale(orc):
+    """Dequantization with the E2M1 code for 1.0 returns the scale as T holds
+    it: byte 102 gives 0 in f16 (2^-25 rounds to 0) but 2^-25 in bf16; byte 143
+    gives inf in f16 and 65536 in bf16."""
+    K, gs = 32, 32
+    wq = np.full((2, K // 2), 0x22, np.uint8)         # every code 0b0010 = 1.0
+    sc = np.array([[102], [143]], np.uint8)
+    w16, _ = orc.fp_dequantize(wq, sc, orc.F16, K, gs, 4)
+    wbf, _ = orc.fp_dequantize(wq, sc, orc.BF16, K, gs, 4)
+    assert np.all(w16[0] == 0.0) and np.all(np.isinf(w16[1]))
+    assert np.all(wbf[0] == 2.0 ** -25) and np.all(wbf[1] == 65536.0)
