@@ -90,12 +90,14 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w) {
 // "magic number" trick: a code field q*2^o (q < 2^BITS) OR-ed into the
 // mantissa of MAGIC = 1024.0 (f16) or 128.0 (bf16) is exactly the float
 // MAGIC + q*2^o, provided q*2^o fits the mantissa (10 bits for f16, 7 for
-// bf16). Two codes go into one 32-bit register as (low half, high half),
-// and a v_dot2 instruction multiplies them with a pair of activations that
-// were pre-scaled by 2^-o, so each product is x*q plus an offset x*MAGIC*2^-o
-// that depends on x only (removed through a per-chunk constant).
-// A field at in-half offset o <= kMaxOff needs no shift; for f16 the offset
-// is capped at 4 so that pre-scaled activations rarely reach subnormals.
+// bf16). Two codes go into one 32-bit register as (low half, high half).
+// The streaming GEMV multiplies them with a pair of unscaled activations
+// (v_dot2, fp32 sums kept apart per offset o) and scales each sum by 2^-o in
+// fp32, which is exact; each product is then x*q plus an offset x*MAGIC*2^-o
+// that depends on x only (removed through a per-chunk constant). The matrix
+// kernels map MAGIC + q*2^o back to q with the same exact power-of-two factor.
+// A field at in-half offset o <= max_off needs no shift; for f16 the offset
+// is capped at 4.
 // The order in which codes land in pairs depends on the width:
 //  * power-of-two widths: inside each 32-bit word, field f of the low half
 //    pairs with field f of the high half, i.e. code (word*V + f) with code
@@ -144,6 +146,18 @@ __host__ __device__ constexpr int pair_half(int k) {
   }
 }
 
+// code of the low half of pair p (pair_index(pair_code(p)) == p)
+template <int BITS>
+__host__ __device__ constexpr int pair_code(int p) {
+  if constexpr (Pack<BITS>::kPow2) {
+    constexpr int V = Pack<BITS>::kVals, H = V / 2;
+    return (p / H) * V + p % H;
+  } else {
+    constexpr int V = Pack<BITS>::kVals;
+    return (p / V) * 2 * V + p % V;
+  }
+}
+
 // window geometry of code j of a non-power-of-two pack
 template <int BITS>
 __host__ __device__ constexpr int win_start(int j) {
@@ -166,6 +180,47 @@ __host__ __device__ constexpr int pair_off(int k) {
     const int off = win_off<BITS>(k % Pack<BITS>::kVals);
     return off <= max_off<T, BITS>() ? off : 0;
   }
+}
+
+// Offset classes: the distinct offsets o of a chunk's 16 pairs (at most 4;
+// offset 0 is always present and is class 0). The streaming GEMV sums the
+// products of each class apart and scales the sums by 2^-o in fp32.
+template <class T, int BITS>
+__host__ __device__ constexpr unsigned off_set() {
+  unsigned m = 0;
+  for (int p = 0; p < 16; p++) m |= 1u << pair_off<T, BITS>(pair_code<BITS>(p));
+  return m;
+}
+template <class T, int BITS>
+__host__ __device__ constexpr int n_off_classes() {
+  int n = 0;
+  for (int o = 0; o < 8; o++) n += (off_set<T, BITS>() >> o) & 1u;
+  return n;
+}
+// class of pair p: rank of its offset among the offsets present
+template <class T, int BITS>
+__host__ __device__ constexpr int off_class(int p) {
+  const int o = pair_off<T, BITS>(pair_code<BITS>(p));
+  int c = 0;
+  for (int i = 0; i < o; i++) c += (off_set<T, BITS>() >> i) & 1u;
+  return c;
+}
+// offset of class c
+template <class T, int BITS>
+__host__ __device__ constexpr int class_off(int c) {
+  for (int o = 0; o < 8; o++)
+    if ((off_set<T, BITS>() >> o) & 1u) {
+      if (c == 0) return o;
+      c--;
+    }
+  return 0;
+}
+// position of pair p among the pairs of its class (pairs in index order)
+template <class T, int BITS>
+__host__ __device__ constexpr int rank_in_class(int p) {
+  int r = 0;
+  for (int q = 0; q < p; q++) r += off_class<T, BITS>(q) == off_class<T, BITS>(p);
+  return r;
 }
 
 // Pair P (0..15) of a chunk as two magic floats (see above). m2 must hold

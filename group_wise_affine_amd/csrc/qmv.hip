@@ -18,15 +18,20 @@
 //    wavefront); a lane walks the row in 32-code chunks (4*bits bytes,
 //    16 bytes at 4 bits) with stride TPR chunks, so a wavefront load covers
 //    64/TPR contiguous row segments of TPR*4*bits bytes each.
-//  * Codes become exact f16/bf16 values MAGIC + q with one shift and one
-//    and-or per pair, and v_dot2_f32_{f16,bf16} multiplies them with the
-//    activation pairs in fp32. The MAGIC offset is removed through the chunk
-//    sum: s*sum(x*(MAGIC+q)) + (b - MAGIC*s)*sum(x) = sum(x*(s*q + b)).
+//  * Codes become exact f16/bf16 values MAGIC + q*2^o with at most one
+//    shift and one and-or per pair, and v_dot2_f32_{f16,bf16} multiplies
+//    them with the unscaled activation pairs in fp32, one set of partial
+//    sums per field offset o, each scaled by 2^-o in fp32 (exact). The MAGIC
+//    offset is removed through a per-chunk constant: sum(x*(MAGIC*2^-o + q))
+//    - MAGIC*sum(x*2^-o) = sum(x*q). Activations are never rounded again, so
+//    small f16 inputs keep every bit.
 //  * Every W byte is read once per MB rows of x; one pass serves all of them.
 //  * Lanes of a row reduce with DPP moves inside a 16-lane row and lane
 //    shuffles across rows; lane 0 writes y.
 //  * Gathered products (a compile-time variant): a third grid dimension over
 //    products, each with its own batch of x and of W (scales, biases) and y.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,27 +70,45 @@ __device__ __forceinline__ void load_chunk(const uint8_t* p, uint32_t w[BITS]) {
   }
 }
 
-// d[r] = sum over the chunk of x'_pair . (MAGIC + q*2^o)_pair for each of
-// the R rows of a lane, in fp32. One wavefront per SIMD runs this, so the
-// dot2 instructions form at least four independent chains (NP partial sums
-// per row, interleaved over the rows) rather than one dependent chain.
-template <class T, int R, int NP>
+// d[r] = sum over the chunk of x_pair . (MAGIC + q*2^o)_pair * 2^-o for each
+// of the R rows of a lane, in fp32. The products of each offset class are
+// summed apart (dot2 sums of unscaled activations) and the class sums are
+// scaled by 2^-o in fp32, which is exact, so no activation is ever rounded
+// again. One wavefront per SIMD runs this, so the dot2 instructions form at
+// least NP independent chains per row (split over the classes) rather than
+// one dependent chain.
+template <class T, int BITS, int R, int NP>
 __device__ __forceinline__ void chunk_dot_rows(const uint32_t (*pairs)[16], const uint32_t* xp,
                                                float* d) {
-  float part[R][NP];
+  constexpr int NC = n_off_classes<T, BITS>();
+  constexpr int NPC = NP / NC >= 1 ? NP / NC : 1;  // chains per class
+  float part[R][NC][NPC];
 #pragma unroll
   for (int r = 0; r < R; r++)
 #pragma unroll
-    for (int j = 0; j < NP; j++) part[r][j] = 0.0f;
+    for (int c = 0; c < NC; c++)
 #pragma unroll
-  for (int p = 0; p < 16; p++)
+      for (int j = 0; j < NPC; j++) part[r][c][j] = 0.0f;
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    ([&]() {
+       constexpr int c = off_class<T, BITS>(P), j = rank_in_class<T, BITS>(P) % NPC;
 #pragma unroll
-    for (int r = 0; r < R; r++) part[r][p % NP] = dot2(T{}, pairs[r][p], xp[p], part[r][p % NP]);
+       for (int r = 0; r < R; r++) part[r][c][j] = dot2(T{}, pairs[r][P], xp[P], part[r][c][j]);
+     }(),
+     ...);
+  }(std::make_integer_sequence<int, 16>{});
 #pragma unroll
   for (int r = 0; r < R; r++) {
-    float v = part[r][0];
+    float v = part[r][0][0];
 #pragma unroll
-    for (int j = 1; j < NP; j++) v += part[r][j];
+    for (int j = 1; j < NPC; j++) v += part[r][0][j];
+#pragma unroll
+    for (int c = 1; c < NC; c++) {
+      float u = part[r][c][0];
+#pragma unroll
+      for (int j = 1; j < NPC; j++) u += part[r][c][j];
+      v = fmaf(u, __builtin_bit_cast(float, (uint32_t)(127 - class_off<T, BITS>(c)) << 23), v);
+    }
     d[r] = v;
   }
 }
@@ -125,7 +148,7 @@ constexpr int kXWaves = 2;                        // wavefronts staging x
 
 // One workgroup = WW W wavefronts (4 or 8) + 2 x wavefronts.
 //  x wavefronts: issue the x loads of their first staging task (and the
-//    scale / bias loads when staged), barrier 1, then permute / pre-scale /
+//    scale / bias loads when staged), barrier 1, then permute /
 //    sum into LDS, barrier 2.
 //  W wavefronts: barrier 1 (so that the x loads are ahead of them in the
 //    CU's memory queue), issue every weight load of the lane in the order
@@ -248,7 +271,7 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
   };
 
   // x staging: task = (row of x, chunk); activations permuted into pair
-  // order and pre-scaled by 2^-o, plus the chunk's sum and magic offset
+  // order, plus the chunk's sum and magic offset
   auto x_load = [&](int task, uint4* raw4) {
     const int tk = task < ntask ? task : ntask - 1;
     const int m = tk / nch, c = tk - m * nch;
@@ -278,15 +301,15 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     } else {
 #pragma unroll
       for (int p = 0; p < 16; p++) px[p] = 0;
+      // activations keep their own bits (permuted into pair order); the
+      // magic offset sum(x * MAGIC * 2^-o) is formed in fp32 (exact scaling)
 #pragma unroll
       for (int k = 0; k < 32; k++) {
-        const float f = live ? to_f32(T{}, (uint16_t)(raw[k / 2] >> (16 * (k % 2)))) : 0.0f;
-        constexpr float kScale[8] = {1.f, 0.5f, 0.25f, 0.125f, 0.0625f, 0.03125f,
-                                     0.015625f, 0.0078125f};
-        const uint16_t h = from_f32(T{}, f * kScale[pair_off<T, BITS>(k)]);
+        const uint16_t h = live ? (uint16_t)(raw[k / 2] >> (16 * (k % 2))) : (uint16_t)0;
+        const float f = to_f32(T{}, h);
         px[pair_index<BITS>(k)] |= (uint32_t)h << (16 * pair_half<BITS>(k));
         sum += f;
-        d0 += to_f32(T{}, h);
+        d0 += f * __builtin_bit_cast(float, (uint32_t)(127 - pair_off<T, BITS>(k)) << 23);
       }
       d0 *= T::kMagicF;
     }
@@ -394,7 +417,7 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
             // independent chains as well)
             constexpr int NP = R * MB >= 4 ? 1 : 4 / (R * MB);
             float d[R];
-            chunk_dot_rows<T, R, NP>(pr, xp, d);
+            chunk_dot_rows<T, BITS, R, NP>(pr, xp, d);
 #pragma unroll
             for (int r = 0; r < R; r++)
               acc[r][m] = fmaf(sf[r], d[r] - d0, fmaf(bf[r], xsm, acc[r][m]));

@@ -47,11 +47,24 @@ def normal(shape, seed, sigma=1.0, dt="f16"):
     return to_words(a, dt)
 
 
-def structured_rows(rows, K, group_size, seed, dt="f16"):
+def mixed_magnitude(shape, seed, lo=1e-5, hi=1e2, block=16, dt="f16"):
+    """Normal values whose magnitude alternates between ``lo`` and ``hi`` in
+    blocks of ``block`` consecutive elements along the last axis (one float32
+    multiply per element, then rounded into the storage type)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    k = np.arange(shape[-1])
+    mag = np.where((k // block) % 2 == 0, np.float32(lo), np.float32(hi)).astype(np.float32)
+    return to_words(a * mag, dt)
+
+
+def structured_rows(rows, K, group_size, seed, dt="f16", sigma=1.0):
     """Weight rows whose groups cover the quantizer's special cases: all-zero
     groups, constant groups, integer ramps, groups holding exact zeros among
     normal values, sign-symmetric extremes (|min| == |max|), a single
-    outlier, tiny magnitudes, and plain normal groups."""
+    outlier, tiny magnitudes, and plain normal groups. ``sigma`` scales every
+    row (one float32 multiply) so that they sit among weights of that
+    spread."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal(size=(rows, K), dtype=np.float32)
     G = K // group_size
@@ -82,4 +95,6 @@ def structured_rows(rows, K, group_size, seed, dt="f16"):
             elif kind == 7:
                 a[r, sl] = a[r, sl] * np.float32(1e-3)
             # kind 8: plain normal
+    if sigma != 1.0:
+        a = a * np.float32(sigma)
     return to_words(a, dt)

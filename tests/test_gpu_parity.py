@@ -31,10 +31,15 @@ def _gpu():
 
 
 def _quantized(orc, dt, N, K, gs, bits, seed=2, sigma=1.0, structured=False):
+    """Seeded normal weights, quantized by the oracle; with ``structured`` the
+    first rows (up to 9, at most a quarter of the rows) hold the quantizer's
+    special groups (zeros, constants, ramps, exact zeros, symmetric extremes,
+    an outlier, tiny values) at the same spread."""
     code = orc_code(orc, dt)
     w = synth.normal((N, K), seed=seed, sigma=sigma, dt=dt)
     if structured:
-        w[: min(N, 9)] = synth.structured_rows(min(N, 9), K, gs, seed=seed + 1, dt=dt)
+        ns = min(9, max(N // 4, 1))
+        w[:ns] = synth.structured_rows(ns, K, gs, seed=seed + 1, dt=dt, sigma=sigma)
     wq, s, b = orc.quantize(w, code, gs, bits)
     return w, wq, s, b
 
@@ -79,10 +84,15 @@ def test_quantize_large_rows(orc):
 
 # ------------------------------------------------------------ qmv
 
-def _run_mm(fn, orc, dt, M, N, K, gs, bits, seed=0, sigma_w=1.0, rows=None):
+def _run_mm(fn, orc, dt, M, N, K, gs, bits, seed=0, sigma_w=1.0, rows=None, x=None,
+            structured=True):
+    """fn (qmv / qmm_t) against the oracle on seeded x (N(0,1) unless given)
+    and seeded weights with structured rows."""
     code = orc_code(orc, dt)
-    x = synth.normal((M, K), seed=seed, dt=dt)
-    w, wq, s, b = _quantized(orc, dt, N, K, gs, bits, seed=seed + 1, sigma=sigma_w)
+    if x is None:
+        x = synth.normal((M, K), seed=seed, dt=dt)
+    w, wq, s, b = _quantized(orc, dt, N, K, gs, bits, seed=seed + 1, sigma=sigma_w,
+                             structured=structured)
     y = fn(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
     torch.cuda.synchronize()
     yg = from_dev(y)
@@ -200,6 +210,67 @@ def test_qmv_max_k(orc):
     _run_mm(Q.qmv, orc, "f16", 1, 3, 29120, 32, 4, seed=3)
 
 
+# ------------------------------------------------------------ small activations
+
+def _x_of(kind, M, K, seed, dt):
+    """Activations that f16 holds only as small normals or subnormals:
+    N(0, 1e-4), N(0, 3e-5), and rows mixing 1e-5 and 1e2 magnitudes."""
+    if kind == "mixed":
+        return synth.mixed_magnitude((M, K), seed=seed, dt=dt)
+    return synth.normal((M, K), seed=seed, sigma={"n1e-4": 1e-4, "n3e-5": 3e-5}[kind], dt=dt)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("kind", ["n1e-4", "n3e-5", "mixed"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_small_activations(orc, dt, kind, bits):
+    """Every kernel that takes x: the streaming GEMV (M = 1, 2), the MFMA GEMV
+    (M = 5), the tile kernel (M = 100), through qmv and qmm_t."""
+    N, K, gs = 96, 1024, 64
+    for M in (1, 2, 5, 100):
+        x = _x_of(kind, M, K, seed=M + bits, dt=dt)
+        fns = (Q.qmv, Q.qmm_t) if M <= 16 else (Q.qmm_t,)
+        for fn in fns:
+            _run_mm(fn, orc, dt, M, N, K, gs, bits, seed=M + 7, x=x)
+
+
+@pytest.mark.parametrize("kind", ["n1e-4", "n3e-5", "mixed"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_small_activations_decode_shape(orc, kind, bits):
+    """x f16 [1, 4096] of small magnitude on the 4096 x 4096 decode layer
+    (the 8-wavefront lane shape of the streaming GEMV)."""
+    x = _x_of(kind, 1, 4096, seed=bits, dt="f16")
+    _run_mm(Q.qmm_t, orc, "f16", 1, 4096, 4096, 64, bits, seed=0, x=x)
+
+
+@pytest.mark.parametrize("kind", ["n1e-4", "n3e-5", "mixed"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_small_activations_gather_batched(orc, dt, kind):
+    """Gathered GEMV and batched weights at M = 1 with small activations and
+    structured weight rows."""
+    code = orc_code(orc, dt)
+    Bx, E, M, N, K, gs, bits = 3, 4, 1, 72, 1024, 64, 4
+    x = np.stack([_x_of(kind, M, K, seed=20 + i, dt=dt) for i in range(Bx)])
+    parts = [_quantized(orc, dt, N, K, gs, bits, seed=30 + e, structured=True)[1:]
+             for e in range(E)]
+    wq = np.stack([p[0] for p in parts])
+    s = np.stack([p[1] for p in parts])
+    b = np.stack([p[2] for p in parts])
+    lhs, rhs = [2, 0, 1, 1], [3, 1, 0, 2]
+    yo, _ = orc.gather_qmm(x, wq, s, b, lhs, rhs, code, gs, bits, nthreads=8)
+    y = Q.gather_qmv(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt),
+                     _idx_dev(lhs), _idx_dev(rhs), gs, bits)
+    torch.cuda.synchronize()
+    for z in range(len(lhs)):
+        assert_parity(from_dev(y[z]), yo[z], dt, f"gather_qmv small x batch {z}")
+    yo, _ = orc.gather_qmm(x, wq[:Bx], s[:Bx], b[:Bx], None, None, code, gs, bits, nthreads=8)
+    y = Q.qmm_t_batched(to_dev(x, dt), bytes_to_words_dev(wq[:Bx]), to_dev(s[:Bx], dt),
+                        to_dev(b[:Bx], dt), gs, bits)
+    torch.cuda.synchronize()
+    for z in range(Bx):
+        assert_parity(from_dev(y[z]), yo[z], dt, f"qmm_t_batched small x batch {z}")
+
+
 # ------------------------------------------------------------ qmm_t (MFMA)
 
 @pytest.mark.parametrize("bits", BITS)
@@ -304,6 +375,10 @@ def test_qconv2d_parity(orc, dt, case):
     code = orc_code(orc, dt)
     x = synth.normal((B, H, W, C), seed=12, dt=dt)
     wconv = synth.normal((O, kh, kw, C // groups), seed=13, sigma=0.5, dt=dt)
+    # structured groups in the first output channels (along the flattened taps)
+    ns, kt = min(9, max(O // 4, 1)), kh * kw * (C // groups)
+    wconv[:ns] = synth.structured_rows(ns, kt, gs, seed=14, dt=dt, sigma=0.5).reshape(
+        ns, kh, kw, C // groups)
     wm = orc.conv_weight_matrix(wconv, groups, gs)
     wq, s, b = orc.quantize(wm, code, gs, bits)
     yo, _ = orc.qconv2d_nhwc(x, wq, s, b, code, O, kh, kw, stride, pad, groups, gs, bits,
@@ -397,7 +472,7 @@ def test_conv_config(orc, groups):
 def _gather_inputs(orc, dt, Bx, E, M, N, K, gs, bits, seed):
     code = orc_code(orc, dt)
     x = np.stack([synth.normal((M, K), seed=seed + i, dt=dt) for i in range(Bx)])
-    parts = [orc.quantize(synth.normal((N, K), seed=seed + 100 + e, dt=dt), code, gs, bits)
+    parts = [_quantized(orc, dt, N, K, gs, bits, seed=seed + 100 + e, structured=True)[1:]
              for e in range(E)]
     wq = np.stack([p[0] for p in parts])
     s = np.stack([p[1] for p in parts])
