@@ -7,8 +7,8 @@ namespace qmm {
 
 // Split-K workspace of the MFMA GEMV: 16 x 16 fp32 partial tiles of at most
 // 256 row blocks x 8 splits, and one arrival counter per row block (zero at
-// load; the last workgroup of a row block resets its counter). Calls that
-// overlap on one device share them.
+// load; a wrapping increment brings it back to zero on the last arrival of
+// each call). Calls that overlap on one device share them.
 constexpr int kMvWsFloats = 256 * 8 * 256;
 __device__ float g_mv_ws[kMvWsFloats];
 __device__ unsigned g_mv_cnt[256];

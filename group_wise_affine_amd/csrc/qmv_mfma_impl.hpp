@@ -323,8 +323,11 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   }
   // ---- K split over ks workgroups: each writes its 16 x 16 partial tile to
   // the workspace; the last one to arrive at its row block's counter adds
-  // the ks tiles in split order, writes y and resets the counter for the
-  // next call. Tiles and counter use device-scope atomic accesses, which are
+  // the ks tiles in split order and writes y. The counter update is a
+  // wrapping increment with limit ks - 1 (0, 1, ..., ks - 1, then back to 0),
+  // so the last arrival itself leaves the counter at zero for the next call:
+  // there is no separate reset store for an overlapping call to race with.
+  // Tiles and counter use device-scope atomic accesses, which are
   // coherent across the per-XCD L2 caches (so no fence has to write back a
   // whole L2): every thread's stores have completed before the barrier that
   // precedes the counter update, and the last workgroup reads the tiles only
@@ -336,8 +339,8 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): the stores have completed
   __syncthreads();
   if (tid == 0)
-    last = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ks - 1);
+    last = __builtin_amdgcn_atomic_inc32(cnt + blockIdx.x, (unsigned)(ks - 1), __ATOMIC_RELAXED,
+                                         "agent") == (unsigned)(ks - 1);
   __syncthreads();
   if (!last) return;
   if (tid < 256) {
@@ -346,7 +349,6 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       t += __hip_atomic_load(wsb + sp * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, t);
   }
-  if (tid == 0) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class T, int BITS, int DEPTH, bool RING>

@@ -108,8 +108,61 @@ def packed_words(K, bits):
     return K * bits // 32
 
 
+# ---------------------------------------------------------------- validation
+# The C ABI takes plain pointers and sizes, so it cannot see a tensor's
+# extent: the binding checks every tensor's shape, element type, layout and
+# device against the sizes it passes before anything is launched ("Add the
+# 3bit packed qmm_t", ops.cpp extract_quantized_matmul_dims: the packed
+# width, scales and biases of one shape, the inner dimension of x). Sizes the
+# library itself rejects (bits, group size, K not a multiple of the group)
+# are left to its status codes.
+
+_BITS = (2, 3, 4, 5, 6, 8)
+_GS = (32, 64, 128)
+
+
+def _sizes_ok(K, group_size, bits):
+    """True when the packed shapes below are defined (else the library rejects
+    the call with its own status)."""
+    return bits in _BITS and group_size in _GS and K >= 1 and K % group_size == 0
+
+
+def _check_tensor(t, name, shape=None, dtype=None, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(*named):
+    """Every given tensor on one ROCm device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _check_indices(t, name, B):
+    if t is None:
+        return
+    _check_tensor(t, name, shape=(B,), dtype=torch.int32)
+
+
 def qmm_quantize(w, group_size=64, bits=4, out=None, stream=None):
     """w [rows, K] -> (wq int32 [rows, K*bits/32], scales, biases [rows, K/gs])."""
+    _check_tensor(w, "w", dims=2)
     rows, K = w.shape
     if out is None:
         G = max(K // group_size, 1) if group_size > 0 else 1
@@ -117,26 +170,52 @@ def qmm_quantize(w, group_size=64, bits=4, out=None, stream=None):
                torch.empty((rows, G), dtype=w.dtype, device=w.device),
                torch.empty((rows, G), dtype=w.dtype, device=w.device))
     wq, s, b = out
+    if _sizes_ok(K, group_size, bits):
+        _check_tensor(wq, "wq", (rows, packed_words(K, bits)), torch.int32)
+        _check_tensor(s, "scales", (rows, K // group_size), w.dtype)
+        _check_tensor(b, "biases", (rows, K // group_size), w.dtype)
+    _check_device(("w", w), ("wq", wq), ("scales", s), ("biases", b))
     _check(lib().qmm_quantize(_ptr(w), _dt(w.dtype), rows, K, group_size, bits,
                               _ptr(wq), _ptr(s), _ptr(b), _stream(stream)))
     return wq, s, b
 
 
 def qmm_dequantize(wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
+    _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
     rows = wq.shape[0]
-    K = wq.shape[1] * 32 // bits
+    K = wq.shape[1] * 32 // bits if bits in _BITS else 0
     if out is None:
         out = torch.empty((rows, K), dtype=scales.dtype, device=wq.device)
+    if _sizes_ok(K, group_size, bits):
+        _check_tensor(scales, "scales", (rows, K // group_size))
+        _check_tensor(biases, "biases", (rows, K // group_size), scales.dtype)
+        _check_tensor(out, "out", (rows, K), scales.dtype)
+    _check_device(("wq", wq), ("scales", scales), ("biases", biases), ("out", out))
     _check(lib().qmm_dequantize(_ptr(wq), _ptr(scales), _ptr(biases), _dt(scales.dtype),
                                 rows, K, group_size, bits, _ptr(out), _stream(stream)))
     return out
 
 
+def _check_mm(x, wq, scales, biases, out, lead, M, N, K, group_size, bits, nw=None):
+    """x [*lead, M, K]; wq [*nw, N, K*bits/32]; scales, biases [*nw, N, K/gs];
+    out [*lead, M, N]; one element type for x, scales, biases and out."""
+    nw = lead if nw is None else nw
+    if _sizes_ok(K, group_size, bits):
+        _check_tensor(wq, "wq", (*nw, N, packed_words(K, bits)), torch.int32)
+        _check_tensor(scales, "scales", (*nw, N, K // group_size), x.dtype)
+        _check_tensor(biases, "biases", (*nw, N, K // group_size), x.dtype)
+    _check_tensor(out, "out", (*lead, M, N), x.dtype)
+    _check_device(("x", x), ("wq", wq), ("scales", scales), ("biases", biases), ("out", out))
+
+
 def _matmul(fn, x, wq, scales, biases, group_size, bits, out, stream):
+    _check_tensor(x, "x", dims=2)
+    _check_tensor(wq, "wq", dims=2)
     M, K = x.shape
     N = wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check_mm(x, wq, scales, biases, out, (), M, N, K, group_size, bits)
     _check(fn(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _dt(x.dtype), M, N, K,
               group_size, bits, _ptr(out), _stream(stream)))
     return out
@@ -155,12 +234,19 @@ def qmv(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
 def qmm_n(x, wq, scales, biases, group_size=64, bits=4, out=None, stream=None):
     """y = x . dequant(W) with W [K, N] quantized along N: x [M, K], wq
     [K, N*bits/32] (uint32 words), scales, biases [K, N/group_size]."""
+    _check_tensor(x, "x", dims=2)
+    _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
     M, K = x.shape
     if wq.shape[0] != K:
         raise ValueError("qmm_n: W must have K rows")
-    N = wq.shape[1] * 32 // bits
+    N = wq.shape[1] * 32 // bits if bits in _BITS else 0
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if _sizes_ok(N, group_size, bits):
+        _check_tensor(scales, "scales", (K, N // group_size), x.dtype)
+        _check_tensor(biases, "biases", (K, N // group_size), x.dtype)
+    _check_tensor(out, "out", (M, N), x.dtype)
+    _check_device(("x", x), ("wq", wq), ("scales", scales), ("biases", biases), ("out", out))
     _check(lib().qmm_n(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _dt(x.dtype), M, N, K,
                        group_size, bits, _ptr(out), _stream(stream)))
     return out
@@ -174,6 +260,8 @@ def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_
     x [Bx, M, K]; wq [E, N, K*bits/32] (uint32 words); scales, biases
     [E, N, K/group_size]; indices int32 device tensors of one length B (None:
     z itself). Returns y [B, M, N]."""
+    _check_tensor(x, "x", dims=3)
+    _check_tensor(wq, "wq", dims=3)
     Bx, M, K = x.shape
     E, N = wq.shape[0], wq.shape[1]
     if lhs_indices is not None:
@@ -185,8 +273,12 @@ def gather_qmv(x, wq, scales, biases, lhs_indices=None, rhs_indices=None, group_
     for t in (lhs_indices, rhs_indices):
         if t is not None and (t.dtype != torch.int32 or t.numel() != B):
             raise ValueError("indices must be int32 tensors of one length")
+    _check_indices(lhs_indices, "lhs_indices", B)
+    _check_indices(rhs_indices, "rhs_indices", B)
     if out is None:
         out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    _check_mm(x, wq, scales, biases, out, (B,), M, N, K, group_size, bits, nw=(E,))
+    _check_device(("x", x), ("lhs_indices", lhs_indices), ("rhs_indices", rhs_indices))
     _check(getattr(lib(), _fn)(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales),
                                _ptr(biases), E, _ptr(rhs_indices), B, _dt(x.dtype), M, N, K,
                                group_size, bits, _ptr(out), _stream(stream)))
@@ -204,10 +296,13 @@ def qmm_t_batched(x, wq, scales, biases, group_size=64, bits=4, out=None, stream
     """y[b] = x[b] . dequant(W[b])^T, or the one W for every b: x [B, M, K];
     wq [B or 1, N, K*bits/32] (uint32 words); scales, biases [B or 1, N,
     K/group_size]. Returns y [B, M, N]."""
+    _check_tensor(x, "x", dims=3)
+    _check_tensor(wq, "wq", dims=3)
     B, M, K = x.shape
     E, N = wq.shape[0], wq.shape[1]
     if out is None:
         out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    _check_mm(x, wq, scales, biases, out, (B,), M, N, K, group_size, bits, nw=(E,))
     _check(lib().qmm_t_batched(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), B, E,
                                _dt(x.dtype), M, N, K, group_size, bits, _ptr(out),
                                _stream(stream)))
@@ -217,6 +312,8 @@ def qmm_t_batched(x, wq, scales, biases, group_size=64, bits=4, out=None, stream
 def fp_quantize(w, group_size=32, bits=4, stream=None):
     """Floating-point mode ((4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8):
     w [rows, K] -> (wq int32 [rows, K*bits/32], scales uint8 [rows, K/gs])."""
+    _check_tensor(w, "w", dims=2)
+    _check_device(("w", w))
     rows, K = w.shape
     wq = torch.empty((rows, max(K * bits // 32, 1)), dtype=torch.int32, device=w.device)
     sc = torch.empty((rows, max(K // group_size, 1)), dtype=torch.uint8, device=w.device)
@@ -225,9 +322,17 @@ def fp_quantize(w, group_size=32, bits=4, stream=None):
     return wq, sc
 
 
+def _fp_sizes_ok(K, group_size, bits):
+    return (bits, group_size) in ((4, 32), (4, 16), (8, 32)) and K >= 1 and K % group_size == 0
+
+
 def fp_dequantize(wq, scales, dtype=torch.float16, group_size=32, bits=4, stream=None):
+    _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
     rows = wq.shape[0]
-    K = wq.shape[1] * 32 // bits
+    K = wq.shape[1] * 32 // bits if bits in (4, 8) else 0
+    if _fp_sizes_ok(K, group_size, bits):
+        _check_tensor(scales, "scales", (rows, K // group_size), torch.uint8)
+    _check_device(("wq", wq), ("scales", scales))
     out = torch.empty((rows, K), dtype=dtype, device=wq.device)
     _check(lib().qmm_fp_dequantize(_ptr(wq), _ptr(scales), _dt(dtype), rows, K, group_size,
                                    bits, _ptr(out), _stream(stream)))
@@ -236,10 +341,17 @@ def fp_dequantize(wq, scales, dtype=torch.float16, group_size=32, bits=4, stream
 
 def fp_qmv(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
     """y [M,N] = x [M,K] . dequant(W)^T for a floating-point mode."""
+    _check_tensor(x, "x", dims=2)
+    _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
     M, K = x.shape
     N = wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if _fp_sizes_ok(K, group_size, bits):
+        _check_tensor(wq, "wq", (N, K * bits // 32), torch.int32)
+        _check_tensor(scales, "scales", (N, K // group_size), torch.uint8)
+    _check_tensor(out, "out", (M, N), x.dtype)
+    _check_device(("x", x), ("wq", wq), ("scales", scales), ("out", out))
     _check(lib().qmm_fp_qmv(_ptr(x), _ptr(wq), _ptr(scales), _dt(x.dtype), M, N, K, group_size,
                             bits, _ptr(out), _stream(stream)))
     return out
@@ -249,6 +361,8 @@ def fp_gather_qmv(x, wq, scales, lhs_indices=None, rhs_indices=None, group_size=
                   out=None, stream=None):
     """y[z] = x[lhs_indices[z]] . dequant(W[rhs_indices[z]])^T in a floating-point
     mode: x [Bx, M, K]; wq [E, N, K*bits/32]; scales uint8 [E, N, K/gs]."""
+    _check_tensor(x, "x", dims=3)
+    _check_tensor(wq, "wq", dims=3, dtype=torch.int32)
     Bx, M, K = x.shape
     E, N = wq.shape[0], wq.shape[1]
     B = (lhs_indices.numel() if lhs_indices is not None else
@@ -256,8 +370,16 @@ def fp_gather_qmv(x, wq, scales, lhs_indices=None, rhs_indices=None, group_size=
     for t in (lhs_indices, rhs_indices):
         if t is not None and (t.dtype != torch.int32 or t.numel() != B):
             raise ValueError("indices must be int32 tensors of one length")
+    _check_indices(lhs_indices, "lhs_indices", B)
+    _check_indices(rhs_indices, "rhs_indices", B)
     if out is None:
         out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    if _fp_sizes_ok(K, group_size, bits):
+        _check_tensor(wq, "wq", (E, N, K * bits // 32), torch.int32)
+        _check_tensor(scales, "scales", (E, N, K // group_size), torch.uint8)
+    _check_tensor(out, "out", (B, M, N), x.dtype)
+    _check_device(("x", x), ("wq", wq), ("scales", scales), ("out", out),
+                  ("lhs_indices", lhs_indices), ("rhs_indices", rhs_indices))
     _check(lib().qmm_fp_gather_qmv(_ptr(x), Bx, _ptr(lhs_indices), _ptr(wq), _ptr(scales), E,
                                    _ptr(rhs_indices), B, _dt(x.dtype), M, N, K, group_size, bits,
                                    _ptr(out), _stream(stream)))
@@ -268,10 +390,15 @@ def affine_pack(wq, scales, biases, group_size=64, bits=4, stream=None):
     """Affine-packed layout of (wq [N, K*bits/32], scales, biases [N, K/gs]):
     returns (wq_packed [N/4, 4*K*bits/32] for bits 2/4/8, else wq itself;
     sb_packed [N/RP, K/gs*2*RP])."""
+    _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
     N = wq.shape[0]
-    K = wq.shape[1] * 32 // bits
+    K = wq.shape[1] * 32 // bits if bits in _BITS else 0
     pow2 = (bits & (bits - 1)) == 0
     rp = 4 if pow2 else 2
+    if _sizes_ok(K, group_size, bits):
+        _check_tensor(scales, "scales", (N, K // group_size))
+        _check_tensor(biases, "biases", (N, K // group_size), scales.dtype)
+    _check_device(("wq", wq), ("scales", scales), ("biases", biases))
     wp = torch.empty((N // rp, rp * wq.shape[1]), dtype=torch.int32,
                      device=wq.device) if pow2 else None
     sbp = torch.empty((N // rp, scales.shape[1] * 2 * rp), dtype=scales.dtype, device=wq.device)
@@ -282,9 +409,18 @@ def affine_pack(wq, scales, biases, group_size=64, bits=4, stream=None):
 
 def qmv_affine_packed(x, wq_packed, sb_packed, N, group_size=64, bits=4, out=None, stream=None):
     """y [M,N] = x [M,K] . dequant(W)^T from the affine-packed layout."""
+    _check_tensor(x, "x", dims=2)
     M, K = x.shape
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if _sizes_ok(K, group_size, bits):
+        rp = 4 if (bits & (bits - 1)) == 0 else 2
+        if N % rp == 0:
+            _check_tensor(wq_packed, "wq_packed", (N // rp, rp * packed_words(K, bits))
+                          if rp == 4 else (N, packed_words(K, bits)), torch.int32)
+            _check_tensor(sb_packed, "sb_packed", (N // rp, K // group_size * 2 * rp), x.dtype)
+    _check_tensor(out, "out", (M, N), x.dtype)
+    _check_device(("x", x), ("wq_packed", wq_packed), ("sb_packed", sb_packed), ("out", out))
     _check(lib().qmv_affine_packed(_ptr(x), _ptr(wq_packed), _ptr(sb_packed), _dt(x.dtype), M, N,
                                    K, group_size, bits, _ptr(out), _stream(stream)))
     return out
@@ -298,10 +434,19 @@ def conv_out_hw(H, W, kh, kw, stride, padding):
 def qconv2d_nhwc(x, wq, scales, biases, O, kh, kw, stride=(1, 1), padding=(0, 0),
                  groups=1, group_size=64, bits=4, out=None, stream=None):
     """x [B,H,W,C] -> y [B,OH,OW,O]; wq from quantize_conv_weight."""
+    _check_tensor(x, "x", dims=4)
     B, H, W, C = x.shape
     OH, OW = conv_out_hw(H, W, kh, kw, stride, padding)
     if out is None:
         out = torch.empty((B, OH, OW, O), dtype=x.dtype, device=x.device)
+    if groups >= 1 and C % groups == 0 and bits in _BITS and group_size in _GS:
+        k_true = kh * kw * (C // groups)
+        k_pad = -(-k_true // group_size) * group_size
+        _check_tensor(wq, "wq", (O, packed_words(k_pad, bits)), torch.int32)
+        _check_tensor(scales, "scales", (O, k_pad // group_size), x.dtype)
+        _check_tensor(biases, "biases", (O, k_pad // group_size), x.dtype)
+    _check_tensor(out, "out", (B, OH, OW, O), x.dtype)
+    _check_device(("x", x), ("wq", wq), ("scales", scales), ("biases", biases), ("out", out))
     _check(lib().qconv2d_nhwc(_ptr(x), B, H, W, C, _ptr(wq), _ptr(scales), _ptr(biases),
                               O, kh, kw, stride[0], stride[1], padding[0], padding[1],
                               groups, _dt(x.dtype), group_size, bits, _ptr(out),

@@ -39,13 +39,20 @@
  *    the caller's next synchronization.
  *  - Supported: bits in {2,3,4,5,6,8}; group_size in {32,64,128};
  *    K a positive multiple of group_size.
- *  - qmm_t, qmv and qconv2d_nhwc may split K over workgroups and keep fp32
- *    partial sums in library-owned workspaces: static device arrays, one set
- *    per GPU (64 MiB for the tile kernel, 2 MiB and 256 counters for the
- *    GEMV; nothing is allocated per call). Calls that run concurrently on
- *    one GPU (different streams, or different host threads without ordering)
- *    share them and must not overlap; calls queued on one stream are ordered
- *    and safe.
+ *  - Several entry points split K over workgroups and keep fp32 partial sums
+ *    in library-owned workspaces: static device arrays, one set per GPU,
+ *    holding their last call's contents (nothing is allocated per call):
+ *      * the tile-kernel workspace (64 MiB): qmm_t, qmm_t_batched,
+ *        qmm_gather_qmm and qconv2d_nhwc when they split K, and qmm_n;
+ *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
+ *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
+ *        the MFMA GEMV on a narrow layer.
+ *    Calls queued on one stream are ordered and safe. Calls that run
+ *    concurrently on one GPU (different streams, or host threads without
+ *    ordering) race on these arrays: serialise them. An overlap makes the
+ *    overlapping calls' outputs undefined; the GEMV's counters wrap back to
+ *    zero on each call's last arrival, so once overlapping calls of the same
+ *    shape have finished, later calls are exact again.
  */
 #ifndef LIBQMM_H
 #define LIBQMM_H

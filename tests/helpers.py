@@ -1,10 +1,10 @@
 """Shared test helpers: oracle/GPU plumbing and the parity gates."""
 import numpy as np
-import torch
 
 from group_wise_affine_amd import synth
+from group_wise_affine_amd.devio import (TORCH_DT, bytes_to_words_dev, from_dev,  # noqa: F401
+                                         from_dev_i32, to_dev, words_dev_to_bytes)
 
-TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
 
 # Gates for floating-point outputs, against the oracle's fp32 result y32:
 #   f16 : ||y - y32|| / ||y32|| <= 1e-3   and   max |y - y32| <= 1e-2 max |y32|
@@ -19,36 +19,6 @@ MAX_REL = 1e-2
 
 def orc_code(orc, dt):
     return {"f16": orc.F16, "bf16": orc.BF16, "f32": orc.F32}[dt]
-
-
-def to_dev(words, dt, dev="cuda"):
-    """Storage words (numpy) -> torch tensor of the element type on dev."""
-    if dt == "f32":
-        return torch.from_numpy(np.ascontiguousarray(words, np.float32)).to(dev)
-    t = torch.from_numpy(np.ascontiguousarray(words).view(np.int16))
-    return t.view(TORCH_DT[dt]).to(dev)
-
-
-def from_dev(t):
-    """torch tensor -> storage words (numpy)."""
-    t = t.detach().cpu().contiguous()
-    if t.dtype == torch.float32:
-        return t.numpy()
-    return t.view(torch.int16).numpy().view(np.uint16)
-
-
-def bytes_to_words_dev(wq_bytes, dev="cuda"):
-    """Packed row bytes [rows, K*bits/8] -> int32 tensor [rows, K*bits/32]."""
-    b = np.ascontiguousarray(wq_bytes, np.uint8)
-    return torch.from_numpy(b.view(np.int32).copy()).to(dev)
-
-
-def words_dev_to_bytes(wq):
-    return from_dev_i32(wq).view(np.uint8).reshape(wq.shape[0], -1)
-
-
-def from_dev_i32(t):
-    return t.detach().cpu().contiguous().numpy().view(np.uint32)
 
 
 def _bf16_interval(words):
