@@ -44,12 +44,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def to_dev(words, dt):
+    from group_wise_affine_amd.devio import to_dev as _to_dev
+    return _to_dev(words, dt)
+
+
+def round_rows(d):
+    """Round floats in a (nested) row dict for the JSON line."""
+    if isinstance(d, dict):
+        return {k: round_rows(v) for k, v in d.items()}
+    return round(d, 4) if isinstance(d, float) else d
+
+
 def alg_bytes(M, N, K, bits, gs, esize=2):
     return N * K * bits // 8 + N * (K // gs) * 2 * esize + M * K * esize + M * N * esize
 
 
 class Timer:
-    """Capture `launch(i)` for i in range(n) into a graph; time replays."""
+    """Capture `launch(i)` for i in range(n) into one HIP graph and time its
+    replays: `warmup` untimed replays, then `reps` replays, each between two
+    HIP events recorded on the launch stream (the stream every launch is
+    queued on), with a synchronize before and after the timed replays."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -63,30 +78,36 @@ class Timer:
                 launch(i)
         return g
 
-    def run(self, launch, steps, warmup):
+    def replays(self, launch, n, reps, warmup=1):
+        """ms of each of `reps` timed replays of an n-launch graph."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
-            for i in range(min(2, steps)):  # eager first calls
+            for i in range(min(2, n)):  # eager first calls
                 launch(i)
         torch.cuda.synchronize()
-        gw = self.graph(launch, max(warmup, 1))
-        gt = self.graph(launch, steps)
+        g = self.graph(launch, n)
         with torch.cuda.stream(self.stream):
-            gw.replay()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(self.stream)
-            gt.replay()
-            e1.record(self.stream)
+            for _ in range(max(warmup, 1)):
+                g.replay()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        del gw, gt
-        return ms / steps  # ms per launch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        with torch.cuda.stream(self.stream):
+            ev[0].record(self.stream)
+            for r in range(reps):
+                g.replay()
+                ev[r + 1].record(self.stream)
+        torch.cuda.synchronize()
+        del g
+        return [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+
+    def run(self, launch, n, warmup=1, reps=5):
+        """Median ms per launch over `reps` replays of an n-launch graph, after
+        at least `warmup` untimed launches (whole replays)."""
+        ts = sorted(self.replays(launch, n, reps, -(-max(warmup, 1) // n)))
+        return ts[len(ts) // 2] / n
 
 
 def make_layer(torch, Q, synth, dt, N, K, gs, bits, seed, sigma=1.0):
-    from tests.helpers import to_dev
     w = to_dev(synth.normal((N, K), seed=seed, sigma=sigma, dt=dt), dt)
     return Q.qmm_quantize(w, gs, bits)
 
@@ -104,7 +125,6 @@ def pooled(torch, layer, min_bytes=POOL_BYTES):
 
 def bench_qmv(torch, Q, synth, timer, dt, M, N, K, bits, gs, steps, warmup, fn=None,
               seed=0, sigma=1.0):
-    from tests.helpers import to_dev
     fn = fn or Q.qmv
     layer = make_layer(torch, Q, synth, dt, N, K, gs, bits, seed + 1, sigma)
     wqs, ss, bs, P = pooled(torch, layer)
@@ -124,6 +144,87 @@ def bench_qmv(torch, Q, synth, timer, dt, M, N, K, bits, gs, steps, warmup, fn=N
             "pool_copies": P}
 
 
+def bench_headline(torch, Q, synth, timer, steps, warmup):
+    """The headline: one step = one decode token through a stack of P layers,
+    the decode GEMV qmv(x f16 [1, 4096], W_l [4096, 4096] 4-bit g64) once per
+    layer l, each layer a distinct copy of W in HBM (P copies, >= 1 GiB in
+    all, 4x the 256 MB MALL, so no layer is served from a cache). The P
+    launches of a step are one HIP graph; `warmup` untimed steps, then
+    `steps` timed steps, each between HIP events on the launch stream.
+    Per-launch time = median step time / P."""
+    dt, M, N, K, bits, gs = "f16", 1, 4096, 4096, 4, 64
+    layer = make_layer(torch, Q, synth, dt, N, K, gs, bits, 1)
+    wqs, ss, bs, P = pooled(torch, layer)
+    x = to_dev(synth.normal((M, K), seed=0, dt=dt), dt)
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+
+    def launch(i):
+        Q.qmv(x, wqs[i], ss[i], bs[i], gs, bits, out=y)
+
+    ts = timer.replays(launch, P, max(steps, 1), max(warmup, 1))
+    srt = sorted(ts)
+    med = srt[len(srt) // 2]
+    per = med / P
+    nbytes = alg_bytes(M, N, K, bits, gs)
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": per * 1e3, "GB/s": nbytes / (per * 1e-3) / 1e9, "bytes": nbytes,
+            "layers_per_step": P, "ms_per_step": med,
+            "step_ms_min": srt[0], "step_ms_max": srt[-1],
+            "timed_ms_total": sum(ts)}
+
+
+CEILING_LIB = os.path.join(ROOT, "group_wise_affine_amd", "libqmm_ceiling.so")
+
+
+def bench_ceiling(torch, timer, steps, warmup, nbytes=9453568, gemv_grid=(256, 640)):
+    """Single-launch floor at the headline's size: (a) one launch that only
+    streams `nbytes` (the headline GEMV's algorithmic bytes) from HBM with
+    16-byte nontemporal loads, each launch reading a distinct slice of a
+    >= 1 GiB pool (best of a few grid shapes); (b) an empty kernel of the
+    headline GEMV's grid (256 workgroups of 640 threads) and of one
+    workgroup. Timed like the other rows (median over graph replays)."""
+    import ctypes
+    L = ctypes.CDLL(CEILING_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.qmm_ceiling_read.argtypes = [vp, i64, vp, i32, i32, vp]
+    L.qmm_ceiling_empty.argtypes = [i32, i32, vp]
+    stride = -(-nbytes // 4096) * 4096
+    P = max(2, -(-POOL_BYTES // stride))
+    pool = torch.empty(P * stride, dtype=torch.uint8, device="cuda")
+    pool.fill_(7)
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    base = pool.data_ptr()
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    res = {}
+    best = None
+    for blocks, threads in ((256, 512), (512, 512), (1024, 256), (2048, 256), (256, 1024)):
+        def launch(i, blocks=blocks, threads=threads):
+            rc = L.qmm_ceiling_read(ctypes.c_void_p(base + (i % P) * stride), nbytes,
+                                    ctypes.c_void_p(sink.data_ptr()), blocks, threads, stream())
+            assert rc == 0
+        ms = timer.run(launch, P, warmup)
+        r = {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "blocks": blocks,
+             "threads": threads}
+        if best is None or r["us"] < best["us"]:
+            best = r
+    best["bytes"] = nbytes
+    best["pool_slices"] = P
+    best["hbm_frac"] = best["GB/s"] / HBM_PEAK_GBS
+    res[f"read_{nbytes}B_one_launch"] = best
+    for blocks, threads in (gemv_grid, (1, 64)):
+        def launch(i, blocks=blocks, threads=threads):
+            assert L.qmm_ceiling_empty(blocks, threads, stream()) == 0
+        ms = timer.run(launch, 200, warmup)
+        res[f"empty_kernel_{blocks}x{threads}"] = {"us": ms * 1e3}
+    del pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096, K=4096,
                  bits=4, gs=64):
     """Mixture-of-experts decode through the gathered GEMV: T tokens x [1, K]
@@ -131,7 +232,6 @@ def bench_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096
     the T*topk products. The routing is a seeded permutation of the experts
     (T*topk == E), so every expert is read once per step. Every step reads a
     different copy of the expert stack from a >= 1 GiB pool."""
-    from tests.helpers import to_dev
     import numpy as np
     assert T * topk == E
     layers = [make_layer(torch, Q, synth, "f16", N, K, gs, bits, 100 + e) for e in range(E)]
@@ -166,7 +266,6 @@ def bench_gather_prefill(torch, Q, synth, timer, steps, warmup, E=8, M=128, N=40
     expert rhs[z] (a seeded permutation of the E experts W_e [N, K], 4-bit
     g64), one qmm_gather_qmm call. Every step reads a different copy of the
     expert stack from a >= 1 GiB pool."""
-    from tests.helpers import to_dev
     import numpy as np
     layers = [make_layer(torch, Q, synth, "f16", N, K, gs, bits, 100 + e) for e in range(E)]
     stack = tuple(torch.stack([l[i] for l in layers]) for i in range(3))
@@ -192,7 +291,6 @@ def bench_fp(torch, Q, synth, timer, steps, warmup, bits, gs, M=1, N=4096, K=409
     """Decode GEMV in a floating-point mode (mxfp4 / nvfp4 / mxfp8) on an
     f16 [4096, 4096] weight; every step reads a different copy of W from a
     >= 1 GiB pool."""
-    from tests.helpers import to_dev
     w = to_dev(synth.normal((N, K), seed=1), "f16")
     wq, sc = Q.fp_quantize(w, gs, bits)
     del w
@@ -216,7 +314,6 @@ def bench_fp_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4
     each routed to topk of E experts W_e [N, K] (a seeded permutation, every
     expert read once per step), one qmm_fp_gather_qmv call. Every step reads a
     different copy of the expert stack from a >= 1 GiB pool."""
-    from tests.helpers import to_dev
     import numpy as np
     parts = [Q.fp_quantize(to_dev(synth.normal((N, K), seed=100 + e), "f16"), 32, 4)
              for e in range(E)]
@@ -248,7 +345,6 @@ def bench_affine_packed(torch, Q, synth, timer, steps, warmup, M=1, N=4096, K=40
                         gs=64):
     """Decode GEMV on the affine-packed layout (4-bit g64 f16, [4096, 4096]); every
     step reads a different copy of the packed weight from a >= 1 GiB pool."""
-    from tests.helpers import to_dev
     wq, s, b = make_layer(torch, Q, synth, "f16", N, K, gs, bits, 1)
     wp, sbp = Q.affine_pack(wq, s, b, gs, bits)
     del wq, s, b
@@ -272,7 +368,6 @@ def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, b
     """Batched product with one weight per batch: y[b] = x[b] . dequant(W_b)^T,
     x [B, M, K] f16, W_b [N, K] 4-bit g64 (qmm_t_batched). Every step reads a
     different copy of the weight stack from a >= 1 GiB pool."""
-    from tests.helpers import to_dev
     layers = [make_layer(torch, Q, synth, "f16", N, K, gs, bits, 200 + e) for e in range(B)]
     stack = tuple(torch.stack([l[i] for l in layers]) for i in range(3))
     del layers
@@ -294,7 +389,6 @@ def bench_qmm_n(torch, Q, synth, timer, steps, warmup, M=1, K=4096, N=4096, bits
     """Non-transposed decode product y = x . dequant(W), W [K, N] quantized
     along N (4-bit g64, f16); every step reads a different copy of W from a
     >= 1 GiB pool."""
-    from tests.helpers import to_dev
     w = to_dev(synth.normal((K, N), seed=1), "f16")
     layer = Q.qmm_quantize(w, gs, bits)
     del w
@@ -312,7 +406,6 @@ def bench_qmm_n(torch, Q, synth, timer, steps, warmup, M=1, K=4096, N=4096, bits
 
 
 def bench_quantize(torch, Q, synth, timer, steps, warmup):
-    from tests.helpers import to_dev
     N = K = 4096
     w = to_dev(synth.normal((N, K), seed=1), "f16")
     wq, s, b = Q.qmm_quantize(w, 64, 4)
@@ -331,7 +424,6 @@ def bench_quantize(torch, Q, synth, timer, steps, warmup):
 def bench_chained(torch, Q, synth, timer, bits, steps, warmup):
     """10 loops of x = qmm(qmm(x, W1), W2): x [1024,1024], W1 [4096,1024],
     W2 [1024,4096], g64 f16. One step = the 20 launches of the 10 loops."""
-    from tests.helpers import to_dev
     gs = 64
     x = to_dev(synth.normal((1024, 1024), seed=0), "f16")
     l1 = make_layer(torch, Q, synth, "f16", 4096, 1024, gs, bits, 1)
@@ -351,7 +443,6 @@ def bench_chained(torch, Q, synth, timer, bits, steps, warmup):
 
 
 def bench_conv(torch, Q, synth, timer, groups, steps, warmup):
-    from tests.helpers import to_dev
     gs, bits = 64, 4
     x = to_dev(synth.normal((1, 64, 64, 320), seed=0), "f16")
     wc = to_dev(synth.normal((320, 3, 3, 320 // groups), seed=1, sigma=0.05), "f16")
@@ -364,31 +455,87 @@ def bench_conv(torch, Q, synth, timer, groups, steps, warmup):
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
 
 
-def cpu_baseline(seconds=10.0):
-    """The oracle on the host cores, headline workload, bounded sample."""
-    import numpy as np
+def cpu_threads():
+    """Threads the oracle runs with on all cores: OMP_NUM_THREADS when set,
+    else the CPUs this process may run on."""
+    try:
+        env = os.environ.get("OMP_NUM_THREADS")
+        return max(1, int(env) if env else len(os.sched_getaffinity(0)))
+    except (ValueError, OSError):
+        return max(1, os.cpu_count() or 1)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(seconds=5.0):
+    """The oracle as it stands, on the host cores, on bounded samples of the
+    workloads: the headline decode qmv on one thread and on all threads
+    (threads split the output columns; each output's summation order is
+    unchanged), one loop of the chained qmm_t bench (two products) and the
+    groups = 1 conv, on all threads."""
     import oracle as orc
     from group_wise_affine_amd import synth
+    nt = cpu_threads()
     M, N, K, gs, bits = 1, 4096, 4096, 64, 4
     x = synth.normal((M, K), seed=0)
     w = synth.normal((N, K), seed=1)
     wq, s, b = orc.quantize(w, orc.F16, gs, bits)
-    orc.qmm_t(x, wq, s, b, orc.F16, gs, bits)  # warm
-    n, t0 = 0, time.perf_counter()
-    while True:
-        orc.qmm_t(x, wq, s, b, orc.F16, gs, bits, nthreads=1)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / n
     nbytes = alg_bytes(M, N, K, bits, gs)
-    del np
-    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n} oracle calls of the headline decode qmv (M=1, 4096x4096, "
-                      f"4-bit g64 f16) in {el:.1f} s, {per * 1e3:.1f} ms per call; the "
-                      f"oracle parallelises over rows of x, so M=1 runs on one thread"}
+
+    def timed(fn, budget):
+        fn()  # warm
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+
+    modes = {}
+    for name, threads in (("decode_qmv_1_thread", 1), ("decode_qmv_all_threads", nt)):
+        n, el = timed(lambda: orc.qmm_t(x, wq, s, b, orc.F16, gs, bits, nthreads=threads),
+                      seconds)
+        modes[name] = {"GB/s": round(nbytes / (el / n) / 1e9, 4), "threads": threads,
+                       "calls": n, "s": round(el, 2)}
+    xc = synth.normal((1024, 1024), seed=0)
+    wq1, s1, b1 = orc.quantize(synth.normal((4096, 1024), seed=1), orc.F16, gs, bits)
+    wq2, s2, b2 = orc.quantize(synth.normal((1024, 4096), seed=2), orc.F16, gs, bits)
+    t0 = time.perf_counter()
+    _, h = orc.qmm_t(xc, wq1, s1, b1, orc.F16, gs, bits, nthreads=nt)
+    orc.qmm_t(h, wq2, s2, b2, orc.F16, gs, bits, nthreads=nt)
+    el = time.perf_counter() - t0
+    fl = 2 * (2 * 1024 * 4096 * 1024)
+    modes["chained_qmm_t_one_loop_all_threads"] = {
+        "TFLOP/s": round(fl / el / 1e12, 6), "s": round(el, 2), "threads": nt,
+        "us_per_10_loops_extrapolated": round(el * 10 * 1e6, 1)}
+    xv = synth.normal((1, 64, 64, 320), seed=0)
+    wc = synth.normal((320, 3, 3, 320), seed=1, sigma=0.05)
+    cq, cs, cb = orc.quantize(orc.conv_weight_matrix(wc, 1, gs), orc.F16, gs, bits)
+    t0 = time.perf_counter()
+    orc.qconv2d_nhwc(xv, cq, cs, cb, orc.F16, 320, 3, 3, (1, 1), (1, 1), 1, gs, bits,
+                     nthreads=nt)
+    el = time.perf_counter() - t0
+    fl = 2 * 64 * 64 * 320 * 2880
+    modes["qconv2d_groups1_all_threads"] = {"TFLOP/s": round(fl / el / 1e12, 6),
+                                            "s": round(el, 2), "threads": nt}
+    head = modes["decode_qmv_all_threads"]
+    return {"value": head["GB/s"], "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "sample": f"{head['calls']} oracle calls of the headline decode qmv (M=1, "
+                      f"4096x4096, 4-bit g64 f16) in {head['s']} s on {nt} threads (threads "
+                      f"split the output columns); modes also time one thread, one loop of "
+                      f"the chained bench and the groups=1 conv",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "modes": modes}
 
 
 def kernel_source_hash():
@@ -437,7 +584,6 @@ def traffic_probe(torch, Q, synth, launches=20):
     del bufs
     layer = make_layer(torch, Q, synth, "f16", 4096, 4096, 64, 4, 1)
     wqs, ss, bs, P = pooled(torch, layer)
-    from tests.helpers import to_dev
     x = to_dev(synth.normal((1, 4096), seed=0), "f16")
     y = torch.empty((1, 4096), dtype=x.dtype, device=x.device)
     for i in range(launches):
@@ -450,8 +596,9 @@ def traffic_probe(torch, Q, synth, launches=20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50,
+                    help="timed headline steps (one step = one token through the layer pool)")
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline decode GEMV (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -499,14 +646,18 @@ def main():
                           for k, v in r.items()}))
         return
 
-    log("headline: qmv 4-bit g64 f16 M=1 4096x4096")
+    log("headline: qmv 4-bit g64 f16 M=1 4096x4096, one step = one token through the layer pool")
     torch.cuda.synchronize()
-    head = bench_qmv(torch, Q, synth, timer, "f16", 1, 4096, 4096, 4, 64, K_, W_)
-    log(f"  {head['us']:.3f} us  {head['GB/s']:.1f} GB/s")
+    head = bench_headline(torch, Q, synth, timer, K_, W_)
+    log(f"  {head['us']:.3f} us per launch, {head['GB/s']:.1f} GB/s "
+        f"({head['layers_per_step']} layers per step)")
 
     rows = {}
     if not args.headline_only:
         n_small = max(50, min(K_, 500))
+        rows["single_launch_floor_decode_size"] = round_rows(
+            bench_ceiling(torch, timer, K_, 20))
+        log("ceiling rows done")
         rows.update(bench_quantize(torch, Q, synth, timer, 20, 5))
         log("quantize/dequantize done")
         dec = {}
@@ -581,7 +732,9 @@ def main():
     achieved = head["GB/s"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic()}
+                "traffic": measured_traffic(),
+                "kernel": "qmv_kernel (streaming GEMV), one launch per layer",
+                "us_per_launch": round(head["us"], 4)}
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
@@ -593,18 +746,24 @@ def main():
         "n_gpus": 1,
         "steps": K_,
         "warmup": W_,
-        "ms_per_step": round(head["us"] / 1e3, 6),
+        "ms_per_step": round(head["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "decode qmv: x f16 [1,4096] ~N(0,1), W [4096,4096] ~N(0,1) "
-                               "quantized affine 4-bit g64 with f16 scales/biases; each step "
-                               f"reads a different copy of W from a {head['pool_copies']}-copy "
-                               "(>=1 GiB) pool",
+                               "quantized affine 4-bit g64 with f16 scales/biases; one step = "
+                               f"one token through a stack of {head['layers_per_step']} such "
+                               "layers, each a distinct copy of W (>=1 GiB in all), one GEMV "
+                               "launch per layer",
                    "M": 1, "N": 4096, "K": 4096, "bits": 4, "group_size": 64,
-                   "algorithmic_bytes_per_step": head["bytes"]},
+                   "layers_per_step": head["layers_per_step"],
+                   "algorithmic_bytes_per_launch": head["bytes"],
+                   "algorithmic_bytes_per_step": head["bytes"] * head["layers_per_step"],
+                   "step_ms_min_median_max": [round(head["step_ms_min"], 6),
+                                              round(head["ms_per_step"], 6),
+                                              round(head["step_ms_max"], 6)]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rows": rows,

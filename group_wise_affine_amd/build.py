@@ -18,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmm.so")
+CEILING_LIB = os.path.join(HERE, "libqmm_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "quantize.hip", "qmv.hip", "qmn.hip", "fpq.hip", "apk.hip", "qmv_mfma_f16.hip", "qmv_mfma_bf16.hip", "qmm.hip",
@@ -59,7 +60,20 @@ def build(verbose=False, jobs=None):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_ceiling()
     return LIB
+
+
+def build_ceiling():
+    """libqmm_ceiling.so: the benchmark's single-launch floor kernels
+    (csrc/ceiling.hip, include/qmm_ceiling.h), separate from libqmm."""
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "ceiling.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for ceiling.hip:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
 
 
 if __name__ == "__main__":
