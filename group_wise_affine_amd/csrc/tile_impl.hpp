@@ -498,25 +498,30 @@ __device__ __forceinline__ void keep(const uint4& v) {
 
 constexpr int kStageSteps = 8;      // K steps per scale stage (512 codes)
 
-template <int BM, int BN, int BITS>
+template <int BM, int BN, int BITS, int KW, int SL>
 struct DmaGeo {
-  // wavefront grid: 1 x 4 for 128-wide tiles (each W chunk is dequantized by
-  // exactly one wavefront), 2 x 2 for 64 x 64 tiles
-  static constexpr int WAVES_N = BN >= 128 ? 4 : 2, WAVES_M = 4 / WAVES_N;
+  // SL output slices, KW wavefronts per slice (each taking 1/KW of the codes
+  // of every K step): SL*KW wavefronts
+  static constexpr int NW = SL * KW, NT = 64 * NW;
+  // slice grid (each W chunk is dequantized by exactly one wavefront):
+  //  SL = 4: 1 x 4 slices of 128-wide tiles, 2 x 2 for 64 x 64 tiles;
+  //  SL = 2: 1 x 2 slices (each 64 columns wide), so that every x fragment
+  //  read from LDS feeds two MFMAs and the tile's x reads are halved
+  static constexpr int WAVES_N = SL == 2 ? 2 : (BN >= 128 ? 4 : 2), WAVES_M = SL / WAVES_N;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = BM * 64;          // x tile of one step
   static constexpr int A_BLOCKS = BM / 8;          // 8 rows per DMA instruction
-  static constexpr int A_PER_WAVE = A_BLOCKS / 4;
+  static constexpr int A_PER_WAVE = A_BLOCKS / NW;
   static constexpr int WU = (BITS == 8 || (BITS == 4 && BN == 128)) ? 16 : 4;
   static constexpr int W_ROW = 8 * BITS;           // bytes per W row and step
   static constexpr int W_BYTES = BN * W_ROW;
   static constexpr int UPR = W_ROW / WU;           // DMA units per W row
   static constexpr int W_BLOCKS = W_BYTES / WU / 64;
-  static constexpr int W_HI = (W_BLOCKS + 3) / 4;  // W instructions of wave 0
-  static constexpr int W_LO = W_BLOCKS / 4;        // ... of wave 3
+  static constexpr int W_HI = (W_BLOCKS + NW - 1) / NW;  // W instructions of wave 0
+  static constexpr int W_LO = W_BLOCKS / NW;             // ... of the last wave
   static constexpr int SWZ = WU == 16 ? ilog2(16 / UPR) : 0;
-  static_assert(A_BLOCKS % 4 == 0 && W_BYTES % (64 * WU) == 0, "DMA blocks");
+  static_assert(A_BLOCKS % NW == 0 && W_BYTES % (64 * WU) == 0, "DMA blocks");
 };
 
 // f16 constants of a chunk for every field offset o: s*2^-o and b - 1024*s*2^-o
@@ -573,19 +578,31 @@ constexpr int filler_slot(int f, int nf, int nm, int lead) {
 // LDS; 2 convolution whose per-group channel count is a multiple of 64, so
 // that the 64 codes of a K step lie in one tap and every piece of the step
 // is addressed from the step's tap and channel (no table, no LDS read).
-template <class T, int BITS, int BM, int BN, int CONV>
-__global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
-  using G = DmaGeo<BM, BN, BITS>;
+// KW = 2: two wavefronts per output slice (8 per workgroup, two per SIMD, so
+// that one wavefront's MFMAs run while the other issues its dequantization
+// and copies); wavefront w + 4 takes the upper 16 codes of each lane's
+// 32-code chunk (MFMA slices 2 and 3 of the step), w the lower 16, and the
+// pair's accumulators are added once, through LDS, after the last step.
+template <class T, int BITS, int BM, int BN, int CONV, int KW, int SL>
+__global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
+  using G = DmaGeo<BM, BN, BITS, KW, SL>;
+  constexpr int NW = G::NW, NT = G::NT;
   constexpr bool kSplit = __is_same(T, BF16);
   constexpr int NB = kSplit ? 2 : 1;
   constexpr int FM = G::FM, FN = G::FN, WTM = G::WTM, WTN = G::WTN;
   constexpr int WU = G::WU, UPR = G::UPR;
-  constexpr int NDMA_LO = G::A_PER_WAVE + G::W_LO, NDMA_HI = G::A_PER_WAVE + G::W_HI;
+  constexpr int KK = 4 / KW;                     // MFMA K slices per wavefront and step
+  constexpr int CW = 32 / KW;                    // codes of a lane's chunk per wavefront
   constexpr int PC = kSplit ? 8 : piece_codes<BITS>();
-  constexpr int NP = 32 / PC;                    // pieces per chunk
-  constexpr int kM = 4 * FM * FN * NB;           // MFMAs per step
-  constexpr int kNF = FN + FN * NP + (FM >= 2 ? 0 : 4 * FM);  // fillers per step
+  constexpr int NP = CW / PC;                    // pieces per wavefront and chunk
+  constexpr int kM = KK * FM * FN * NB;          // MFMAs per step
+  // x fragments: with several row blocks per wavefront and all four slices
+  // (kJit) slice kk+2 is read while the MFMAs of slice kk run; otherwise the
+  // next step's fragments are read during the current step (two buffers)
+  constexpr bool kJit = KW == 1 && FM >= 2;
+  constexpr int kNF = FN + FN * NP + (kJit ? 0 : KK * FM);  // fillers per step
   constexpr int kLead = kM >= 16 ? 4 : 1;
+  static_assert(KW == 1 || KW == 2, "one or two wavefronts per slice");
 
   // one LDS array per ring slot (x tile, then W tile): the compiler tracks
   // pending LDS-DMA writes per array for a handful of arrays only
@@ -597,7 +614,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   __shared__ uint32_t sct[2 * BN * 17];
   __shared__ uint32_t ktab[CONV == 1 ? kKtabMax : 1];
   // target of the filler W copies of wavefronts with one block fewer
-  __shared__ __attribute__((aligned(16))) uint8_t wjunk[G::W_BLOCKS % 4 ? 64 * WU : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t wjunk[G::W_BLOCKS % NW ? 64 * WU : 16];
 
   auto slot = [&]<int S>() -> uint8_t* QMM_INLINE {
     if constexpr (S == 0) return sl0;
@@ -615,7 +632,13 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, rr = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+  const int w4 = wave & (SL - 1);                 // output slice
+  const int kh = KW == 2 ? wave / SL : 0;         // part of each chunk
+  const int wm = w4 / G::WAVES_N, wn = w4 % G::WAVES_N;
+  // LDS ring slot k (for the end-of-kernel staging: each slice owns 4/SL)
+  auto slot_at = [&](int k) -> uint8_t* QMM_INLINE {
+    return k == 0 ? sl0 : k == 1 ? sl1 : k == 2 ? sl2 : sl3;
+  };
   // blockIdx.z: the conv group, or the batch of a batched plain GEMM (x, W,
   // scales, biases and y of batch g follow those of batch g - 1; a gathered
   // GEMM takes x and W from the batches its index arrays name)
@@ -700,7 +723,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   uint32_t pix_o[CONV == 2 ? G::A_PER_WAVE : 1];
 #pragma unroll
   for (int i = 0; i < G::A_PER_WAVE; i++) {
-    const int blk = 4 * i + wave;
+    const int blk = NW * i + wave;
     const int r = 8 * blk + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     xcol[i] = 8 * c;
@@ -733,7 +756,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   int wuo[G::W_HI];
 #pragma unroll
   for (int i = 0; i < G::W_HI; i++) {
-    const int blk = 4 * i + wave;
+    const int blk = NW * i + wave;
     const int ui = 64 * (blk < G::W_BLOCKS ? blk : 0) + lane;
     const int r = ui / UPR, p = ui % UPR;
     const int u = WU == 16 ? (p ^ ((r >> G::SWZ) & (UPR - 1))) : p;
@@ -753,7 +776,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   auto issue_one = [&]<int S, int D, bool CHK>(int tt) QMM_INLINE {
     if constexpr (D < G::A_PER_WAVE) {
       constexpr int i = D;
-      const int blk = 4 * i + wave;
+      const int blk = NW * i + wave;
       uint16_t* xd = xslot.template operator()<S>() + blk * 512;
       if constexpr (CONV == 2) {
         // the step's 64 codes are channels [c0, c0 + 64) of tap (dy, dx)
@@ -787,8 +810,8 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       constexpr int i = D - G::A_PER_WAVE;
       uint8_t* wd = wslot.template operator()<S>();
       const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;
-      const int blk = 4 * i + wave;
-      const bool real = G::W_BLOCKS % 4 == 0 || blk < G::W_BLOCKS;
+      const int blk = NW * i + wave;
+      const bool real = G::W_BLOCKS % NW == 0 || blk < G::W_BLOCKS;
       bool ok = real;
       if constexpr (CHK) ok = ok && (int)wsoff + wuo[i] < row_bytes;
       dma_lds<WU>(wr, real ? (void*)(wd + blk * 64 * WU) : (void*)wjunk, ok ? woff[i] : kOob,
@@ -805,7 +828,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // (in steps 1 and 2 of a stage the scale loads issued after step 1's copies
   // may stay in flight too; they must land by the end of step 3)
   auto step_sync = [&]<int U>() QMM_INLINE {
-    constexpr int kSLoads = 2 * (BN * 16 / 256);
+    constexpr int kSLoads = 2 * (BN * 16 / NT);
     wait_vmcnt<G::A_PER_WAVE + G::W_HI + ((U == 1 || U == 2) ? kSLoads : 0)>();
     lds_barrier();
   };
@@ -814,11 +837,11 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   const int sg_log2 = 9 - a.gs_log2;          // groups per stage: 4, 8 or 16
   const int SG = 1 << sg_log2, SGP = SG + 1;
   // Each thread loads kSL scales and kSL biases per stage (element e =
-  // thread + 256 i modulo BN*SG: group e % SG of tile row e / SG; repeats
+  // thread + NT i modulo BN*SG: group e % SG of tile row e / SG; repeats
   // rewrite the same value) through buffer resources over the tile's rows, at
   // loop-invariant lane offsets plus a per-stage scalar offset. Groups past
   // the end of a row read the next row (or zeros): they only meet zero x.
-  constexpr int kSL = BN * 16 / 256;
+  constexpr int kSL = BN * 16 / NT;
   const char* sbase = reinterpret_cast<const char*>(sp + (int64_t)n_blk * n_groups);
   const char* bbase = reinterpret_cast<const char*>(bp + (int64_t)n_blk * n_groups);
   const int64_t s_bytes = (int64_t)(a.N - n_blk) * n_groups * 2;
@@ -828,7 +851,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   int sdst[kSL];
 #pragma unroll
   for (int i = 0; i < kSL; i++) {
-    const int e = (tid + 256 * i) & (BN * SG - 1);
+    const int e = (tid + NT * i) & (BN * SG - 1);
     const int grp = e & (SG - 1), row = e >> sg_log2;
     const int rc = n_blk + row < a.N ? row : a.N - 1 - n_blk;
     soffv[i] = (uint32_t)((rc * n_groups + grp) * 2);
@@ -858,15 +881,11 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     }
   };
 
-  // ---- per-step register state. x fragments: with several row blocks per
-  // wavefront (kJit) slice kk+2 is read while the MFMAs of slice kk run
-  // (slices 0 and 1 of the next step during slices 2 and 3; one buffer);
-  // with one row block the next step's four slices are read during the
-  // current step (two buffers).
-  constexpr bool kJit = FM >= 2;
-  uint4 af[kJit ? 1 : 2][4][FM];
-  uint4 bq[2][FN][NB][4];        // W operands (row block, hi/lo, K slice)
-  uint32_t wc[FN][BITS];         // raw W chunks of the next step
+  // ---- per-step register state (x fragments: see kJit)
+  uint4 af[kJit ? 1 : 2][KK][FM];
+  uint4 bq[2][FN][NB][KK];       // W operands (row block, hi/lo, K slice)
+  uint32_t wc[FN][BITS];         // raw W chunk part of the next step
+  uint32_t wfull[KW == 2 ? FN : 1][BITS];   // KW = 2: the whole chunk, as read
   uint32_t sbw[FN];              // (scale | bias << 16) of the next step
   uint32_t s2v[FN], b2v[FN];      // f16 scale / bias in both halves
   float sf[FN], bf[FN];           // bf16 path: scale / bias in fp32
@@ -884,35 +903,66 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       // (vector-typed 16-byte loads: a load split into words and merged again
       // loses the information that it reads this slot only, and the compiler
       // then waits for every LDS copy in flight)
+      uint32_t full[BITS];
       if constexpr (WU == 16 && BITS == 4) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
             wsl + r * 32 + 16 * (h ^ ((r >> G::SWZ) & 1)));
 #pragma unroll
-        for (int q = 0; q < 4; q++) wc[j][q] = v[q];
+        for (int q = 0; q < 4; q++) full[q] = v[q];
       } else if constexpr (WU == 16 && BITS == 8) {
 #pragma unroll
         for (int e = 0; e < 2; e++) {
           const int u = (2 * h + e) ^ ((r >> G::SWZ) & 3);
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wsl + r * 64 + 16 * u);
 #pragma unroll
-          for (int q = 0; q < 4; q++) wc[j][4 * e + q] = v[q];
+          for (int q = 0; q < 4; q++) full[4 * e + q] = v[q];
         }
       } else {
         const uint32_t* pw =
             reinterpret_cast<const uint32_t*>(wsl + r * (8 * BITS) + 4 * BITS * h);
 #pragma unroll
-        for (int q = 0; q < BITS; q++) wc[j][q] = pw[q];
+        for (int q = 0; q < BITS; q++) full[q] = pw[q];
+      }
+#pragma unroll
+      for (int q = 0; q < BITS; q++) {
+        if constexpr (KW == 1) wc[j][q] = full[q];
+        else wfull[j][q] = full[q];
       }
     }
   };
-  // x fragment (K slice KK, row block I) of slot S
-  auto read_x = [&]<int S, int KK, int I>(uint4 (&afr)[4][FM]) QMM_INLINE {
+  // KW = 2: the wavefront's 16 codes of chunk J as codes 0..15 of a chunk
+  // (the upper half starts at byte 2*BITS, a whole pack boundary for every
+  // width, so the magic pairs of either half stay inside it). Done in the
+  // step's first filler, so that the wait for the chunk's LDS read does not
+  // hold up the step's first MFMA.
+  auto take_part = [&]<int J>() QMM_INLINE {
+    if constexpr (KW == 2) {
+      constexpr int SB = 2 * BITS, NWD = (SB + 3) / 4;
+      const uint32_t* full = wfull[J];
+#pragma unroll
+      for (int q = 0; q < BITS; q++) wc[J][q] = 0;
+      [&]<int... Q>(std::integer_sequence<int, Q...>) QMM_INLINE {
+        ([&]() QMM_INLINE {
+           constexpr int b = SB + 4 * Q, iq = b / 4, sh = 8 * (b % 4);
+           uint32_t up;
+           if constexpr (sh == 0) up = full[iq];
+           else up = __builtin_amdgcn_alignbit(iq + 1 < BITS ? full[iq + 1] : 0u, full[iq], sh);
+           wc[J][Q] = kh ? up : full[Q];
+         }(),
+         ...);
+      }(std::make_integer_sequence<int, NWD>{});
+    }
+  };
+  // x fragment (the wavefront's K slice L, row block I) of slot S: slice
+  // KK*kh + L of the step
+  auto read_x = [&]<int S, int L, int I>(uint4 (&afr)[KK][FM]) QMM_INLINE {
     const uint16_t* xsl = xslot.template operator()<S>();
     const int ra = wm * WTM + 32 * I + rr;
-    const int c = (4 * h + KK) ^ ((ra >> 1) & 7);
-    afr[KK][I] = *reinterpret_cast<const uint4*>(xsl + ra * 64 + 8 * c);
+    const int c = (4 * h + KK * kh + L) ^ ((ra >> 1) & 7);
+    afr[L][I] = *reinterpret_cast<const uint4*>(xsl + ra * 64 + 8 * c);
   };
   auto prep = [&]<int J>() QMM_INLINE {
+    take_part.template operator()<J>();
     if constexpr (kSplit) {
       sf[J] = to_f32(T{}, (uint16_t)sbw[J]);
       bf[J] = to_f32(T{}, (uint16_t)(sbw[J] >> 16));
@@ -921,7 +971,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
       b2v[J] = __builtin_amdgcn_perm(sbw[J], sbw[J], 0x03020302u);
     }
   };
-  auto piece = [&]<int J, int P>(uint4 (&bqn)[FN][NB][4]) QMM_INLINE {
+  auto piece = [&]<int J, int P>(uint4 (&bqn)[FN][NB][KK]) QMM_INLINE {
     uint32_t hi[16], lo[16];
     if constexpr (kSplit) {
       dequant_piece_bf16<BITS, P * 8>(wc[J], sf[J], bf[J], hi, lo);
@@ -936,7 +986,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   };
   // filler F of a step: scale prep, a dequant piece, or (without kJit) an x
   // fragment read of the next step (slot SN)
-  auto filler = [&]<int F, int SN>(uint4 (&afn)[4][FM], uint4 (&bqn)[FN][NB][4]) QMM_INLINE {
+  auto filler = [&]<int F, int SN>(uint4 (&afn)[KK][FM], uint4 (&bqn)[FN][NB][KK]) QMM_INLINE {
     if constexpr (F < FN) {
       prep.template operator()<F>();
     } else if constexpr (F < FN + FN * NP) {
@@ -970,9 +1020,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
     }(std::make_integer_sequence<int, kNF>{});
   };
   constexpr int kSlice = FM * FN * NB;       // MFMAs per K slice
-  auto read_slice = [&]<int S, int KK>() QMM_INLINE {
+  auto read_slice = [&]<int S, int KS>() QMM_INLINE {
     [&]<int... I>(std::integer_sequence<int, I...>) QMM_INLINE {
-      (read_x.template operator()<S, KK, I>(af[0]), ...);
+      (read_x.template operator()<S, KS, I>(af[0]), ...);
     }(std::make_integer_sequence<int, FM>{});
   };
   auto mfma_at = [&]<int MM, int C, int SC, int SN>() QMM_INLINE {
@@ -1044,9 +1094,11 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   issue.template operator()<0>(t0);
   issue.template operator()<1>(t0 + 1);
   issue.template operator()<2>(t0 + 2);
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+  // the stage's scales and step 0 (steps 1 and 2 stay in flight: the first
+  // step's end waits for step 1)
+  wait_vmcnt<2 * kDma>();
   scale_store(js0);
-  wait_vmcnt_barrier<0>();
+  wait_vmcnt_barrier<2 * kDma>();
   read_w.template operator()<0>(t0);
   [&]<int... F>(std::integer_sequence<int, F...>) QMM_INLINE {
     (filler.template operator()<F, 0>(af[0], bq[0]), ...);
@@ -1078,7 +1130,7 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
 #pragma unroll
              for (int e = 0; e < NB; e++)
 #pragma unroll
-               for (int kk = 0; kk < 4; kk++) keep(bq[(U + 1) % 2][j][e][kk]);
+               for (int kk = 0; kk < KK; kk++) keep(bq[(U + 1) % 2][j][e][kk]);
            step_sync.template operator()<U>();
          }
        }()),
@@ -1096,11 +1148,45 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   for (; js < js0 + n_full; js++) stage.template operator()<true, true>(js);
   if ((t1 - t0) % kStageSteps) stage.template operator()<false, true>(js0 + n_full);
 
+  // ---- KW = 2: the upper-half wavefront adds its accumulators to its
+  // pair's through the slice's ring slot (once every wavefront has passed
+  // the first barrier, every copy has landed and every slot read is done);
+  // lane-major, so each store and load instruction covers 256 contiguous
+  // bytes
+  if constexpr (KW == 2) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    // the slice's 32x32 tiles spread over its 4/SL slots
+    constexpr int kTiles = FM * FN, kTps = kTiles / (4 / SL);
+    static_assert(kTps * 16 * 64 * 4 <= kSlotBytes, "partial tiles must fit the slots");
+    auto red = [&](int t) -> float* QMM_INLINE {
+      return reinterpret_cast<float*>(slot_at(w4 * (4 / SL) + t / kTps)) + (t % kTps) * 16 * 64;
+    };
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) red(i * FN + j)[r * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[i][j][r] += red(i * FN + j)[r * 64 + lane];
+    }
+  }
+
   // ---- split K: fp32 partial sums straight from the accumulators (lane:
   // column 32j + lane%32, rows 8(r/4) + 4(lane/32) + r%4 of each 32x32 tile;
   // each store instruction covers two 128-byte row pieces)
   if (a.ksplit > 1) {
     wait_vmcnt<0>();   // no copy may still be landing in LDS when the wave ends
+    if (kh != 0) return;
     // conv: [split][M][ldy], the groups side by side in a row; batched GEMM:
     // [split][batch][M][ldy]
     float* ws = a.ws + (CONV ? (int64_t)sk * a.M * a.ldy + (int64_t)g * a.Og
@@ -1123,11 +1209,14 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
   // ---- epilogue: each wavefront stages its WTM x WTN tile in "its" x slot
   // (all copies have landed and all slot reads are done), then writes rows
   // of 16-byte vectors.
+  // (with KW = 2 the lower-half wavefronts write, the others only take part
+  // in the barriers)
   wait_vmcnt<0>();
   __syncthreads();
-  uint16_t* cs = reinterpret_cast<uint16_t*>(wave == 0 ? sl0 : wave == 1 ? sl1 : wave == 2 ? sl2 : sl3);
+  uint16_t* cs = reinterpret_cast<uint16_t*>(slot_at(w4 * (4 / SL)));
   constexpr int CROW = WTN + 8;
-  static_assert(WTM * CROW <= G::A_ELEMS, "epilogue tile must fit an x slot");
+  static_assert(WTM * CROW * 2 <= kSlotBytes, "epilogue tile must fit a slot");
+  if (kh == 0) {
 #pragma unroll
   for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -1139,7 +1228,9 @@ __global__ __launch_bounds__(256) void qmm_dma_kernel(GemmArgs a) {
         cs[row * CROW + col] = from_f32(T{}, acc[i][j][r]);
       }
     }
+  }
   __syncthreads();
+  if (kh != 0) return;
   uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : (int64_t)g * a.M * a.ldy);
   constexpr int VPR = WTN / 8;
   const bool vec_ok = (a.N % 8 == 0) && (a.ldy % 8 == 0);
@@ -1173,13 +1264,29 @@ static hipError_t launch_gather(const GemmArgs& a, int groups, hipStream_t st) {
   return hipGetLastError();
 }
 
+// wavefronts per output slice of the DMA tile kernel: two (8 per workgroup,
+// two per SIMD) where the x tile has a copy block for each of them
+template <int BM>
+constexpr int dma_kw() {
+  return BM >= 64 ? 2 : 1;
+}
+// output slices of the DMA tile kernel: 4 (1 x 2 slices of 64 columns for
+// 128 x 128 tiles halve the x reads from LDS, but one wavefront per SIMD
+// cannot hide the rest: measured 19.4 against 16.1 us on 1024 x 4096 x 1024)
+template <int BM, int BN>
+constexpr int dma_sl() {
+  return 4;
+}
+
 template <class T, int BITS, int BM, int BN, int CONV>
 static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
+  constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   const dim3 grid(tiles, 1, groups);
   a.ksplit = 1;
   a.ksteps = ((a.K + 63) / 64 + kStageSteps - 1) / kStageSteps * kStageSteps;
-  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL>), grid, dim3(64 * SL * KW), 0,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -1270,8 +1377,9 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   a.ksplit = splitk_plan(a, (int64_t)tiles * groups, &ksteps,
                          !CONV && BM == 128 && __is_same(T, F16), CONV ? 1 : groups);
   a.ksteps = ksteps;
-  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV>), dim3(tiles, a.ksplit, groups),
-                     dim3(256), 0, st, a);
+  constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL>), dim3(tiles, a.ksplit, groups),
+                     dim3(64 * SL * KW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   // every column of y (all conv groups); the batches of a GEMM as consecutive rows
