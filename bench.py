@@ -309,6 +309,28 @@ def bench_fp(torch, Q, synth, timer, steps, warmup, bits, gs, M=1, N=4096, K=409
             "pool_copies": P}
 
 
+def bench_fp_qmm(torch, Q, synth, timer, steps, warmup, bits, gs, M=1024, N=4096, K=4096):
+    """fp-mode product at large M on the MFMA tile kernel (qmm_fp_t): x f16
+    [1024, 4096], W [4096, 4096] quantized on the GPU; every step reads a
+    different copy of W from a >= 1 GiB pool."""
+    w = to_dev(synth.normal((N, K), seed=1), "f16")
+    wq, sc = Q.fp_quantize(w, gs, bits)
+    del w
+    per = wq.numel() * 4 + sc.numel()
+    P = max(2, -(-POOL_BYTES // per))
+    wqs = wq.unsqueeze(0).expand(P, *wq.shape).contiguous()
+    scs = sc.unsqueeze(0).expand(P, *sc.shape).contiguous()
+    x = to_dev(synth.normal((M, K), seed=0), "f16")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ms = timer.run(lambda i: Q.fp_qmm_t(x, wqs[i % P], scs[i % P], gs, bits, out=y), steps, warmup)
+    fl = 2 * M * N * K
+    del wqs, scs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, "pool_copies": P,
+            "workload": f"x f16 [{M},{K}] x W [{N},{K}], fp mode bits {bits} g{gs}"}
+
+
 def bench_fp_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096, K=4096):
     """Mixture-of-experts decode with mxfp4 experts: T tokens x [1, K] f16,
     each routed to topk of E experts W_e [N, K] (a seeded permutation, every
@@ -692,6 +714,9 @@ def main():
         rows["fp_qmv_decode_4096x4096_f16"] = {
             name: {k: round(v, 4) if isinstance(v, float) else v
                    for k, v in bench_fp(torch, Q, synth, timer, n_small, 20, bits, gs).items()}
+            for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32))}
+        rows["fp_qmm_t_1024x4096x4096_f16"] = {
+            name: round_rows(bench_fp_qmm(torch, Q, synth, timer, 20, 5, bits, gs))
             for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32))}
         log("fp rows done")
         rows["fp_gather_qmv_moe_decode_mxfp4"] = {

@@ -455,6 +455,39 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales, 
                   "qmm_fp_qmv");
 }
 
+qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
+                    int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
+                    void* stream) {
+  if (!x || !wq || !scales || !y)
+    return fail(QMM_E_NULL, "qmm_fp_t: x, wq, scales and y must be non-NULL");
+  qmm_status st = check_fp_mode("qmm_fp_t", bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qmm_fp_t: only float16 and bfloat16 are supported (got dtype %d)",
+                (int)dt);
+  if (M < 1 || N < 1 || M > kI32 || N > kI32)
+    return fail(QMM_E_SHAPE, "qmm_fp_t: M (%lld) and N (%lld) must be >= 1", (long long)M,
+                (long long)N);
+  if (K < 32 || K % 32 != 0)
+    return fail(QMM_E_SHAPE, "qmm_fp_t: K (%lld) must be a positive multiple of 32", (long long)K);
+  if (N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_fp_t: problem too large");
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qmm_fp_t: x, wq and y must be 16-byte aligned");
+  const bool gemv = M < qmm::fp_crossover_m(bits, group_size, (int)dt) && M <= 65535 &&
+                    K <= qmm::kFpMaxK;
+  if (gemv)
+    return launched(qmm::launch_fp_qmv((int)dt, bits, group_size, x, wq, scales, M, N, K, y,
+                                       (hipStream_t)stream),
+                    "qmm_fp_t");
+  if (K >= qmm::kTileMaxK)
+    return fail(QMM_E_SHAPE, "qmm_fp_t: K (%lld) must be below %lld for the MFMA tile kernel",
+                (long long)K, (long long)qmm::kTileMaxK);
+  return launched(qmm::launch_fp_qmm_mfma((int)dt, bits, group_size, x, wq, scales, M, N, K, y,
+                                          (hipStream_t)stream),
+                  "qmm_fp_t");
+}
+
 qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_indices,
                              const uint32_t* wq, const uint8_t* scales, int64_t w_batches,
                              const int32_t* rhs_indices, int64_t batches, qmm_dtype dt, int64_t M,

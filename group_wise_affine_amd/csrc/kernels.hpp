@@ -113,6 +113,13 @@ constexpr int64_t kFpMaxK = 16384;
 hipError_t launch_fp_qmv(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                          const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
                          hipStream_t st);
+// fp-mode product on the MFMA tile kernel, any M (same limits as
+// launch_qmm_mfma: K below kTileMaxK, x, wq and y 16-byte aligned).
+hipError_t launch_fp_qmm_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                              const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
+                              hipStream_t st);
+// Rows of x from which qmm_fp_t takes the tile kernel instead of the fp GEMV.
+int fp_crossover_m(int bits, int gs, int dt);
 // Gathered fp GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T with
 // x [nxb, M, K], W [nwb, N, K] (codes and scale bytes), y [B, M, N]; a null
 // index array means z, indices are clamped into range. B <= 65535.

@@ -145,4 +145,84 @@ __device__ __forceinline__ void dequant_piece_bf16(const uint32_t* w, float s, f
   }(std::make_integer_sequence<int, 8>{});
 }
 
+// ------------------------------------------------------------ fp-mode pieces
+// Floating-point modes of the tile kernel: 1 mxfp4 (E2M1 codes, e8m0 scale
+// per 32), 2 nvfp4 (E2M1, E4M3 scale per 16), 3 mxfp8 (E4M3 codes, e8m0 per
+// 32). Codes are OCP E2M1 (two per byte, the first in the low nibble) or
+// E4M3 (one per byte).
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The group scale as the product uses it, rounded to T ("mlx 1.0.0
+// backend/cpu/quantized.cpp", dequantize_scale<T>), as fp32 bits. e8m0 byte
+// s is 2^(s-127) (byte 0 the fp32 subnormal 2^-127); f16 holds 2^-24 ..
+// 2^15 of those, rounds smaller ones to 0 (2^-25 ties to even) and larger
+// ones to infinity; bf16 holds them all. E4M3 values are exact in f16 and
+// bf16.
+template <class T, int FPM>
+__device__ __forceinline__ uint32_t fp_scale_t_bits(uint32_t s) {
+  if constexpr (FPM == 2) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_f32_fp8(s, 1.0f, 0));
+  } else {
+    if constexpr (__is_same(T, F16)) {
+      if (s < 103u) return 0u;
+      if (s > 142u) return 0x7f800000u;
+    }
+    return s == 0u ? 0x00400000u : (s << 23);
+  }
+}
+
+// Eight codes (one word of E2M1 codes or two of E4M3) times the scale sc,
+// as four T pairs in code order. With an e8m0 scale the scaled conversion
+// applies the power of two exactly (the hardware takes only the scale's
+// exponent, which is all an e8m0 value has); with an E4M3 scale the codes
+// are converted at scale 1 and each multiplied by sc in fp32 (exact: at most
+// 2 + 4 significant bits) before the rounding to T.
+template <class T, int FPM>
+__device__ __forceinline__ void fp_piece(const uint32_t* w, float sc, uint32_t* out) {
+  constexpr bool kF16 = __is_same(T, F16);
+  if constexpr (FPM == 3) {
+    if constexpr (kF16) {
+      out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], sc, false));
+      out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], sc, true));
+      out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], sc, false));
+      out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], sc, true));
+    } else {
+      out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false));
+      out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true));
+      out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false));
+      out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true));
+    }
+  } else if constexpr (FPM == 1) {
+    if constexpr (kF16) {
+      out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[0], sc, 0));
+      out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[0], sc, 1));
+      out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[0], sc, 2));
+      out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[0], sc, 3));
+    } else {
+      out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], sc, 0));
+      out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], sc, 1));
+      out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], sc, 2));
+      out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], sc, 3));
+    }
+  } else {
+    f32x2_t v[4];
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 3);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float a0 = v[q].x * sc, a1 = v[q].y * sc;
+      if constexpr (kF16) {
+        const half2_t hv = {(_Float16)a0, (_Float16)a1};
+        out[q] = __builtin_bit_cast(uint32_t, hv);
+      } else {
+        const bf162_t bv = {(__bf16)a0, (__bf16)a1};
+        out[q] = __builtin_bit_cast(uint32_t, bv);
+      }
+    }
+  }
+}
+
 }  // namespace qmm

@@ -67,6 +67,33 @@ hipError_t launch_gather_qmm_mfma(int dt, int bits, int gs, const void* x, int64
                  : launch_tile_gemm_bf16(bits, a, (int)B, st);
 }
 
+hipError_t launch_fp_qmm_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                              const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
+                              hipStream_t st) {
+  GemmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.wq = reinterpret_cast<const uint8_t*>(wq);
+  a.s = reinterpret_cast<const uint16_t*>(scales);   // scale bytes
+  a.b = nullptr;
+  a.y = static_cast<uint16_t*>(y);
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.gs_log2 = ilog2(gs);
+  a.ldy = N;
+  a.nxb = 1; a.nwb = 1;
+  a.ws = splitk_ws();
+  if (!a.ws) return hipErrorInvalidSymbol;
+  return launch_tile_fp(dt, bits, gs, a, st);
+}
+
+// The fp GEMV reads W once per row of x; the tile kernel once per 128 rows.
+// Measured (f16, 4096 x 4096 and 2048 x 8192, hot weights): the GEMV takes
+// 6.9-9.6 us at M = 2 and 8.1-12.4 us at M = 4, the tile kernel 8.1-11.0 us
+// at M = 8 and about the same below; E4M3 codes cost the GEMV more per row.
+int fp_crossover_m(int bits, int gs, int dt) {
+  (void)gs; (void)dt;
+  return bits == 8 ? 3 : 4;
+}
+
 hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
                              const ConvGeom& cg, const uint32_t* wq,
                              const void* s, const void* b, void* y,

@@ -55,5 +55,9 @@ hipError_t launch_tile_conv_f16(int bits, const GemmArgs& a, int groups, bool dm
                                 hipStream_t st);
 hipError_t launch_tile_conv_bf16(int bits, const GemmArgs& a, int groups, bool dma,
                                  hipStream_t st);
+// Floating-point modes ((bits, gs) = (4, 32) mxfp4, (4, 16) nvfp4, (8, 32)
+// mxfp8; dt 0 f16, 1 bf16): a.s points to the scale bytes [N, K/gs], a.b is
+// unused.
+hipError_t launch_tile_fp(int dt, int bits, int gs, const GemmArgs& a, hipStream_t st);
 
 }  // namespace qmm

@@ -583,17 +583,29 @@ constexpr int filler_slot(int f, int nf, int nm, int lead) {
 // and copies); wavefront w + 4 takes the upper 16 codes of each lane's
 // 32-code chunk (MFMA slices 2 and 3 of the step), w the lower 16, and the
 // pair's accumulators are added once, through LDS, after the last step.
-template <class T, int BITS, int BM, int BN, int CONV, int KW, int SL>
+//
+// FPM != 0: a floating-point mode ("mlx 1.0.0 backend/cpu/quantized.cpp",
+// fp_qmm_t): 1 mxfp4 (E2M1 codes, one e8m0 scale byte per 32), 2 nvfp4 (E2M1,
+// one E4M3 scale byte per 16), 3 mxfp8 (E4M3 codes, e8m0 per 32); no bias.
+// The scale rounded to T times a code is exact in T whenever it lies in T's
+// range, so W reaches the MFMA as T values (no bf16 hi/lo split): for e8m0
+// scales one scaled conversion per code pair (v_cvt_scalef32_pk_*, which
+// applies a power-of-two scale exactly), for E4M3 scales the conversion at
+// scale 1 and an fp32 product rounded to T.
+template <class T, int BITS, int BM, int BN, int CONV, int KW, int SL, int FPM>
 __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   using G = DmaGeo<BM, BN, BITS, KW, SL>;
   constexpr int NW = G::NW, NT = G::NT;
-  constexpr bool kSplit = __is_same(T, BF16);
+  constexpr bool kFp = FPM != 0;
+  constexpr bool kSplit = !kFp && __is_same(T, BF16);
+  constexpr int ES = kFp ? 1 : 2;                // bytes per scale element
+  constexpr int kSgMax = FPM == 2 ? 32 : 16;     // groups per 512-code stage, at most
   constexpr int NB = kSplit ? 2 : 1;
   constexpr int FM = G::FM, FN = G::FN, WTM = G::WTM, WTN = G::WTN;
   constexpr int WU = G::WU, UPR = G::UPR;
   constexpr int KK = 4 / KW;                     // MFMA K slices per wavefront and step
   constexpr int CW = 32 / KW;                    // codes of a lane's chunk per wavefront
-  constexpr int PC = kSplit ? 8 : piece_codes<BITS>();
+  constexpr int PC = (kSplit || kFp) ? 8 : piece_codes<BITS>();
   constexpr int NP = CW / PC;                    // pieces per wavefront and chunk
   constexpr int kM = KK * FM * FN * NB;          // MFMAs per step
   // x fragments: with several row blocks per wavefront and all four slices
@@ -611,7 +623,7 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sl1[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sl3[kSlotBytes];
-  __shared__ uint32_t sct[2 * BN * 17];
+  __shared__ uint32_t sct[2 * BN * (kSgMax + 1)];
   __shared__ uint32_t ktab[CONV == 1 ? kKtabMax : 1];
   // target of the filler W copies of wavefronts with one block fewer
   __shared__ __attribute__((aligned(16))) uint8_t wjunk[G::W_BLOCKS % NW ? 64 * WU : 16];
@@ -660,13 +672,13 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   const int row_bytes = K / 8 * BITS;
   const int n_groups = K >> a.gs_log2;
   const uint8_t* wq = a.wq;
-  const uint16_t* sp = a.s;
-  const uint16_t* bp = a.b;
+  const char* sp = reinterpret_cast<const char*>(a.s);   // ES bytes per element
+  const char* bp = reinterpret_cast<const char*>(a.b);
   int gx = g;   // x batch of a batched GEMM
   if constexpr (CONV) {
     wq += (int64_t)g * a.Og * row_bytes;
-    sp += (int64_t)g * a.Og * n_groups;
-    bp += (int64_t)g * a.Og * n_groups;
+    sp += (int64_t)g * a.Og * n_groups * ES;
+    bp += (int64_t)g * a.Og * n_groups * ES;
   } else {
     int gw = g;
     if (a.lidx) {
@@ -678,8 +690,8 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
       gw = v < 0 ? 0 : (v >= a.nwb ? a.nwb - 1 : v);
     }
     wq += (int64_t)gw * a.N * row_bytes;
-    sp += (int64_t)gw * a.N * n_groups;
-    bp += (int64_t)gw * a.N * n_groups;
+    sp += (int64_t)gw * a.N * n_groups * ES;
+    bp += (int64_t)gw * a.N * n_groups * ES;
   }
 
   uint32_t magic_v;
@@ -828,7 +840,7 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   // (in steps 1 and 2 of a stage the scale loads issued after step 1's copies
   // may stay in flight too; they must land by the end of step 3)
   auto step_sync = [&]<int U>() QMM_INLINE {
-    constexpr int kSLoads = 2 * (BN * 16 / NT);
+    constexpr int kSLoads = (kFp ? 1 : 2) * (BN * kSgMax / NT);
     wait_vmcnt<G::A_PER_WAVE + G::W_HI + ((U == 1 || U == 2) ? kSLoads : 0)>();
     lds_barrier();
   };
@@ -841,10 +853,10 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   // rewrite the same value) through buffer resources over the tile's rows, at
   // loop-invariant lane offsets plus a per-stage scalar offset. Groups past
   // the end of a row read the next row (or zeros): they only meet zero x.
-  constexpr int kSL = BN * 16 / NT;
-  const char* sbase = reinterpret_cast<const char*>(sp + (int64_t)n_blk * n_groups);
-  const char* bbase = reinterpret_cast<const char*>(bp + (int64_t)n_blk * n_groups);
-  const int64_t s_bytes = (int64_t)(a.N - n_blk) * n_groups * 2;
+  constexpr int kSL = BN * kSgMax / NT;
+  const char* sbase = sp + (int64_t)n_blk * n_groups * ES;
+  const char* bbase = kFp ? sbase : bp + (int64_t)n_blk * n_groups * ES;
+  const int64_t s_bytes = (int64_t)(a.N - n_blk) * n_groups * ES;
   const uint32_t s_rb = (uint32_t)(s_bytes < 0x7fffffff ? s_bytes : 0x7fffffff);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(sbase, s_rb), br = make_rsrc(bbase, s_rb);
   uint32_t soffv[kSL];
@@ -854,17 +866,21 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
     const int e = (tid + NT * i) & (BN * SG - 1);
     const int grp = e & (SG - 1), row = e >> sg_log2;
     const int rc = n_blk + row < a.N ? row : a.N - 1 - n_blk;
-    soffv[i] = (uint32_t)((rc * n_groups + grp) * 2);
+    soffv[i] = (uint32_t)((rc * n_groups + grp) * ES);
     sdst[i] = row * SGP + grp;
   }
   uint32_t sreg[kSL], breg[kSL];
   constexpr int kSGrp = kSL >= 4 ? 4 : kSL;          // loads of a group (each array)
   auto scale_load_grp = [&]<int GR>(int j) QMM_INLINE {
-    const uint32_t so = (uint32_t)(j * SG * 2);
+    const uint32_t so = (uint32_t)(j * SG * ES);
 #pragma unroll
     for (int i = GR * kSGrp; i < (GR + 1) * kSGrp; i++) {
-      sreg[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soffv[i], so, 0);
-      breg[i] = __builtin_amdgcn_raw_buffer_load_b16(br, soffv[i], so, 0);
+      if constexpr (kFp) {
+        sreg[i] = __builtin_amdgcn_raw_buffer_load_b8(sr, soffv[i], so, 0);
+      } else {
+        sreg[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soffv[i], so, 0);
+        breg[i] = __builtin_amdgcn_raw_buffer_load_b16(br, soffv[i], so, 0);
+      }
     }
   };
   auto scale_load = [&](int j) QMM_INLINE {
@@ -872,12 +888,20 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
       (scale_load_grp.template operator()<GR>(j), ...);
     }(std::make_integer_sequence<int, kSL / kSGrp>{});
   };
+  // affine: (scale | bias << 16) words; fp modes: the scale rounded to T,
+  // as fp32 bits
   auto scale_store = [&](int j) QMM_INLINE {
-    uint16_t* base = reinterpret_cast<uint16_t*>(sct + (j & 1) * BN * SGP);
+    if constexpr (kFp) {
+      uint32_t* base = sct + (j & 1) * BN * SGP;
 #pragma unroll
-    for (int i = 0; i < kSL; i++) {
-      base[2 * sdst[i]] = (uint16_t)sreg[i];
-      base[2 * sdst[i] + 1] = (uint16_t)breg[i];
+      for (int i = 0; i < kSL; i++) base[sdst[i]] = fp_scale_t_bits<T, FPM>(sreg[i]);
+    } else {
+      uint16_t* base = reinterpret_cast<uint16_t*>(sct + (j & 1) * BN * SGP);
+#pragma unroll
+      for (int i = 0; i < kSL; i++) {
+        base[2 * sdst[i]] = (uint16_t)sreg[i];
+        base[2 * sdst[i] + 1] = (uint16_t)breg[i];
+      }
     }
   };
 
@@ -889,14 +913,24 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   uint32_t sbw[FN];              // (scale | bias << 16) of the next step
   uint32_t s2v[FN], b2v[FN];      // f16 scale / bias in both halves
   float sf[FN], bf[FN];           // bf16 path: scale / bias in fp32
+  // fp modes: the scale of the wavefront's codes, and with groups of 16 and
+  // one wavefront per slice the scale of the chunk's second group
+  constexpr bool kTwoGroups = FPM == 2 && KW == 1;
+  uint32_t sbw2[kTwoGroups ? FN : 1];
+  float sfp[FN], sfp2[kTwoGroups ? FN : 1];
 
   // W chunks and scale words of step tt from slot S
   auto read_w = [&]<int S>(int tt) QMM_INLINE {
     const uint8_t* wsl = wslot.template operator()<S>();
     const uint32_t* scs = sct + ((tt >> 3) & 1) * BN * SGP;
-    const int gl = (((tt & 7) << 6) + 32 * h) >> a.gs_log2;
+    // group of the wavefront's first code (groups of 16 split a chunk)
+    const int gl = (((tt & 7) << 6) + 32 * h + CW * kh) >> a.gs_log2;
 #pragma unroll
     for (int j = 0; j < FN; j++) sbw[j] = scs[(wn * WTN + 32 * j + rr) * SGP + gl];
+    if constexpr (kTwoGroups) {
+#pragma unroll
+      for (int j = 0; j < FN; j++) sbw2[j] = scs[(wn * WTN + 32 * j + rr) * SGP + gl + 1];
+    }
 #pragma unroll
     for (int j = 0; j < FN; j++) {
       const int r = wn * WTN + 32 * j + rr;
@@ -963,7 +997,10 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   };
   auto prep = [&]<int J>() QMM_INLINE {
     take_part.template operator()<J>();
-    if constexpr (kSplit) {
+    if constexpr (kFp) {
+      sfp[J] = __builtin_bit_cast(float, sbw[J]);
+      if constexpr (kTwoGroups) sfp2[J] = __builtin_bit_cast(float, sbw2[J]);
+    } else if constexpr (kSplit) {
       sf[J] = to_f32(T{}, (uint16_t)sbw[J]);
       bf[J] = to_f32(T{}, (uint16_t)(sbw[J] >> 16));
     } else {
@@ -973,7 +1010,14 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   };
   auto piece = [&]<int J, int P>(uint4 (&bqn)[FN][NB][KK]) QMM_INLINE {
     uint32_t hi[16], lo[16];
-    if constexpr (kSplit) {
+    if constexpr (kFp) {
+      // codes [8P, 8P + 8) of the wavefront's part: slice P
+      float sc = sfp[J];
+      if constexpr (kTwoGroups) sc = P >= 2 ? sfp2[J] : sfp[J];
+      uint32_t pr[4];
+      fp_piece<T, FPM>(wc[J] + P * BITS / 4, sc, pr);
+      bqn[J][0][P] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+    } else if constexpr (kSplit) {
       dequant_piece_bf16<BITS, P * 8>(wc[J], sf[J], bf[J], hi, lo);
       bqn[J][1][P] = make_uint4(lo[4 * P], lo[4 * P + 1], lo[4 * P + 2], lo[4 * P + 3]);
       bqn[J][0][P] = make_uint4(hi[4 * P], hi[4 * P + 1], hi[4 * P + 2], hi[4 * P + 3]);
@@ -1278,15 +1322,15 @@ constexpr int dma_sl() {
   return 4;
 }
 
-template <class T, int BITS, int BM, int BN, int CONV>
+template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0>
 static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
   constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   const dim3 grid(tiles, 1, groups);
   a.ksplit = 1;
   a.ksteps = ((a.K + 63) / 64 + kStageSteps - 1) / kStageSteps * kStageSteps;
-  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL>), grid, dim3(64 * SL * KW), 0,
-                     st, a);
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM>), grid,
+                     dim3(64 * SL * KW), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1370,16 +1414,16 @@ static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm 
 
 // tile kernel over a BM x BN tiling with K split by plan (fp32 partials +
 // reduction when split)
-template <class T, int BITS, int BM, int BN, int CONV>
+template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0>
 static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   int ksteps = 0;
   a.ksplit = splitk_plan(a, (int64_t)tiles * groups, &ksteps,
-                         !CONV && BM == 128 && __is_same(T, F16), CONV ? 1 : groups);
+                         !CONV && BM == 128 && (__is_same(T, F16) || FPM != 0), CONV ? 1 : groups);
   a.ksteps = ksteps;
   constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
-  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL>), dim3(tiles, a.ksplit, groups),
-                     dim3(64 * SL * KW), 0, st, a);
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM>),
+                     dim3(tiles, a.ksplit, groups), dim3(64 * SL * KW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   // every column of y (all conv groups); the batches of a GEMM as consecutive rows
@@ -1387,22 +1431,26 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   return launch_splitk_reduce<T>(a, (int)a.ldy, st);
 }
 
-template <class T, int BITS, int CONV, bool DMA>
+template <class T, int BITS, int CONV, bool DMA, int FPM = 0>
 static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
   const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
+  // the plain f16 GEMM (and the fp modes, which run one MFMA per fragment in
+  // either type) keep each split at least 16 steps long
+  constexpr bool kGemmPlan = !CONV && (__is_same(T, F16) || FPM != 0);
   if constexpr (DMA) {
     // at most 32 rows: one 32-row block per tile (W is read once)
     if constexpr (!CONV) {
-      if (a.M <= 32) return launch_dma_split<T, BITS, 32, 128, CONV>(a, groups, st);
+      if (a.M <= 32) return launch_dma_split<T, BITS, 32, 128, CONV, FPM>(a, groups, st);
     }
     // 128-wide tiles that would leave more than half a tile of columns idle
     // (e.g. 160-channel conv groups): 64 x 64 tiles
-    if (a.N % 128 != 0 && a.N % 128 < 64) return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
-    if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV>(a, groups, st);
+    if (a.N % 128 != 0 && a.N % 128 < 64)
+      return launch_dma<T, BITS, 64, 64, CONV, FPM>(a, groups, st);
+    if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV, FPM>(a, groups, st);
     int ks;
-    if (splitk_plan(a, tiles128, &ks, !CONV && __is_same(T, F16), CONV ? 1 : groups) > 1)
-      return launch_dma_split<T, BITS, 128, 128, CONV>(a, groups, st);
-    return launch_dma<T, BITS, 64, 64, CONV>(a, groups, st);
+    if (splitk_plan(a, tiles128, &ks, kGemmPlan, CONV ? 1 : groups) > 1)
+      return launch_dma_split<T, BITS, 128, 128, CONV, FPM>(a, groups, st);
+    return launch_dma<T, BITS, 64, 64, CONV, FPM>(a, groups, st);
   } else {
     if (tiles128 >= 256) return launch_gather<T, BITS, 128, 128>(a, groups, st);
     return launch_gather<T, BITS, 64, 64>(a, groups, st);

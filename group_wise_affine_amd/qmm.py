@@ -21,7 +21,7 @@ STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
                 "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
-           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv",
+           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
            "qmm_affine_pack", "qmv_affine_packed",
            "qmm_crossover_m", "qmm_last_error"]
 
@@ -64,11 +64,12 @@ def lib():
         L.qmm_fp_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
         L.qmm_fp_dequantize.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp, vp]
         L.qmm_fp_qmv.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
+        L.qmm_fp_t.argtypes = L.qmm_fp_qmv.argtypes
         L.qmm_fp_gather_qmv.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i32, i64, i64, i64,
                                         i32, i32, vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
                   "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched", "qmm_fp_quantize",
-                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_gather_qmv",
+                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
                   "qmm_affine_pack", "qmv_affine_packed"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
@@ -339,8 +340,8 @@ def fp_dequantize(wq, scales, dtype=torch.float16, group_size=32, bits=4, stream
     return out
 
 
-def fp_qmv(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
-    """y [M,N] = x [M,K] . dequant(W)^T for a floating-point mode."""
+def fp_qmv(x, wq, scales, group_size=32, bits=4, out=None, stream=None, _fn="qmm_fp_qmv"):
+    """y [M,N] = x [M,K] . dequant(W)^T for a floating-point mode (the GEMV)."""
     _check_tensor(x, "x", dims=2)
     _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
     M, K = x.shape
@@ -352,9 +353,15 @@ def fp_qmv(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
         _check_tensor(scales, "scales", (N, K // group_size), torch.uint8)
     _check_tensor(out, "out", (M, N), x.dtype)
     _check_device(("x", x), ("wq", wq), ("scales", scales), ("out", out))
-    _check(lib().qmm_fp_qmv(_ptr(x), _ptr(wq), _ptr(scales), _dt(x.dtype), M, N, K, group_size,
-                            bits, _ptr(out), _stream(stream)))
+    _check(getattr(lib(), _fn)(_ptr(x), _ptr(wq), _ptr(scales), _dt(x.dtype), M, N, K,
+                               group_size, bits, _ptr(out), _stream(stream)))
     return out
+
+
+def fp_qmm_t(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
+    """Same as fp_qmv for any M: the GEMV for a few rows, the MFMA tile kernel
+    beyond."""
+    return fp_qmv(x, wq, scales, group_size, bits, out, stream, _fn="qmm_fp_t")
 
 
 def fp_gather_qmv(x, wq, scales, lhs_indices=None, rhs_indices=None, group_size=32, bits=4,

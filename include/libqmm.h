@@ -43,7 +43,8 @@
  *    in library-owned workspaces: static device arrays, one set per GPU,
  *    holding their last call's contents (nothing is allocated per call):
  *      * the tile-kernel workspace (64 MiB): qmm_t, qmm_t_batched,
- *        qmm_gather_qmm and qconv2d_nhwc when they split K, and qmm_n;
+ *        qmm_gather_qmm, qconv2d_nhwc and qmm_fp_t when they split K, and
+ *        qmm_n;
  *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
  *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
  *        the MFMA GEMV on a narrow layer.
@@ -200,6 +201,21 @@ qmm_status qmm_fp_dequantize(const uint32_t* wq, const uint8_t* scales,
 qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales,
                       qmm_dtype dt, int64_t M, int64_t N, int64_t K,
                       int group_size, int bits, void* y, void* stream);
+
+/*
+ * The same product for any M: the qmm_fp_qmv GEMV for a few rows of x, the
+ * MFMA tile kernel beyond (W dequantized on chip to dt: scale_T * value is
+ * exact in dt whenever it lies in dt's range, which always holds for bf16
+ * and for f16 scales from 2^-14 to 2^14; fp32 accumulation). K a positive
+ * multiple of 32 (below 2^22 on the tile kernel, up to 16384 on the GEMV);
+ * x, wq and y 16-byte aligned; scales any alignment. The tile kernel may
+ * split K and use the library's tile-kernel workspace (see above).
+ * (Source: "mlx 1.0.0 backend/cpu/quantized.cpp", fp_qmm_t and
+ * fp_qmm_t_simd, which serve any number of rows.)
+ */
+qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales,
+                    qmm_dtype dt, int64_t M, int64_t N, int64_t K,
+                    int group_size, int bits, void* y, void* stream);
 
 /*
  * Gathered product in a floating-point mode (e.g. mixture-of-experts decode

@@ -1,7 +1,8 @@
 """GPU parity of the floating-point modes (mxfp4, nvfp4, mxfp8) against the
 oracle ("mlx 1.0.0 backend/cpu/quantized.cpp": to_fp4_e2m1, to_fp8_e8m0,
 dequantize_scale, fp_quantize_dequantize, fp_qmm_t): quantize and dequantize
-bit-exact, the GEMV within the floating-point gate."""
+bit-exact, the GEMV and the any-M product (MFMA tile kernel) within the
+floating-point gate."""
 import numpy as np
 import pytest
 import torch
@@ -104,6 +105,61 @@ def test_fp_qmv(orc, name, bits, gs, dt, M, N, K):
     y = Q.fp_qmv(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs, bits)
     torch.cuda.synchronize()
     assert_parity(from_dev(y), yo, dt, f"fp_qmv {name} {dt} M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt,M,N,K", [
+    ("f16", 64, 256, 512),       # 64 rows: K split over 32-row-free tiles
+    ("bf16", 256, 384, 1024),    # 128 x 128 tiles, split K
+    ("f16", 1024, 512, 1024),    # 128 x 128 tiles, whole K
+    ("bf16", 1024, 256, 2048),
+    ("f16", 100, 200, 2080),     # ragged M and N, K % 64 == 32
+    ("bf16", 20, 136, 4096),     # 32-row tiles, K split
+    ("f16", 9, 64, 512),         # just above the GEMV's rows
+    ("bf16", 3, 96, 640),        # the GEMV
+])
+def test_fp_qmm_t(orc, name, bits, gs, dt, M, N, K):
+    """The fp-mode product for any M (the tile kernel beyond a few rows)
+    against the oracle's fp_qmm_t, with structured groups and rows of small
+    (2^-12) and large (x16) scales."""
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=M + K + 1, dt=dt)
+    w = _weights(N, K, gs, dt, seed=N + K + bits, big=16.0)
+    wq, sc = orc.fp_quantize(w, code, gs, bits)
+    yo, _ = orc.fp_qmm_t(x, wq, sc, code, gs, bits, nthreads=8)
+    y = Q.fp_qmm_t(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"fp_qmm_t {name} {dt} M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+def test_fp_qmm_t_full_size(orc, name, bits, gs):
+    """x f16 [1024, 4096] . W [4096, 4096] quantized on the GPU, checked on
+    sampled rows (the oracle recomputes rows 0..15 and 1000..1023)."""
+    x = synth.normal((1024, 4096), seed=0)
+    w = synth.normal((4096, 4096), seed=1)
+    wq, sc = Q.fp_quantize(to_dev(w, "f16"), gs, bits)
+    y = Q.fp_qmm_t(to_dev(x, "f16"), wq, sc, gs, bits)
+    torch.cuda.synchronize()
+    yg = from_dev(y)
+    wq_o, sc_o = words_dev_to_bytes(wq), sc.cpu().numpy()
+    for r0, r1 in [(0, 16), (1000, 1024)]:
+        yo, _ = orc.fp_qmm_t(x[r0:r1], wq_o, sc_o, orc.F16, gs, bits, nthreads=8)
+        assert_parity(yg[r0:r1], yo, "f16", f"fp_qmm_t {name} 1024x4096x4096 rows {r0}..{r1}")
+
+
+def test_fp_qmm_t_routes_consistently(orc):
+    """Around the GEMV / tile crossover both kernels agree with the oracle."""
+    dt, N, K, gs, bits = "f16", 96, 512, 32, 4
+    w = _weights(N, K, gs, dt, seed=5, big=16.0)
+    wq, sc = orc.fp_quantize(w, orc.F16, gs, bits)
+    for M in (2, 3, 4, 5, 9, 33):
+        x = synth.normal((M, K), seed=M, dt=dt)
+        yo, _ = orc.fp_qmm_t(x, wq, sc, orc.F16, gs, bits, nthreads=8)
+        y = Q.fp_qmm_t(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs,
+                       bits)
+        torch.cuda.synchronize()
+        assert_parity(from_dev(y), yo, dt, f"fp_qmm_t crossover M{M}")
 
 
 def _idx(v):
