@@ -443,20 +443,29 @@ def bench_quantize(torch, Q, synth, timer, steps, warmup):
     return res
 
 
-def bench_chained(torch, Q, synth, timer, bits, steps, warmup):
+def bench_chained(torch, Q, synth, timer, bits, steps, warmup, packed=False):
     """10 loops of x = qmm(qmm(x, W1), W2): x [1024,1024], W1 [4096,1024],
-    W2 [1024,4096], g64 f16. One step = the 20 launches of the 10 loops."""
+    W2 [1024,4096], g64 f16. One step = the 20 launches of the 10 loops.
+    ``packed``: the weights in the affine-packed layout (qmm_t_affine_packed)."""
     gs = 64
     x = to_dev(synth.normal((1024, 1024), seed=0), "f16")
     l1 = make_layer(torch, Q, synth, "f16", 4096, 1024, gs, bits, 1)
     l2 = make_layer(torch, Q, synth, "f16", 1024, 4096, gs, bits, 2)
     h = torch.empty((1024, 4096), dtype=torch.float16, device="cuda")
     xs = [x.clone(), torch.empty_like(x)]
+    if packed:
+        l1 = Q.affine_pack(*l1, gs, bits)
+        l2 = Q.affine_pack(*l2, gs, bits)
 
-    def launch(i):
-        for loop in range(10):
-            Q.qmm_t(xs[loop % 2], *l1, gs, bits, out=h)
-            Q.qmm_t(h, *l2, gs, bits, out=xs[(loop + 1) % 2])
+        def launch(i):
+            for loop in range(10):
+                Q.qmm_t_affine_packed(xs[loop % 2], *l1, 4096, gs, bits, out=h)
+                Q.qmm_t_affine_packed(h, *l2, 1024, gs, bits, out=xs[(loop + 1) % 2])
+    else:
+        def launch(i):
+            for loop in range(10):
+                Q.qmm_t(xs[loop % 2], *l1, gs, bits, out=h)
+                Q.qmm_t(h, *l2, gs, bits, out=xs[(loop + 1) % 2])
 
     ms = timer.run(launch, steps, warmup)
     flops = 10 * 2 * (2 * 1024 * 4096 * 1024)
@@ -651,6 +660,7 @@ def main():
     K_, W_ = args.steps, args.warmup
     if args.mfma_only:
         r = {"chained_bits4": bench_chained(torch, Q, synth, timer, 4, 10, 2),
+             "chained_bits4_affine_packed": bench_chained(torch, Q, synth, timer, 4, 10, 2, True),
              "conv_groups1": bench_conv(torch, Q, synth, timer, 1, 50, 5),
              "conv_groups2": bench_conv(torch, Q, synth, timer, 2, 50, 5)}
         print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r.items()}))
@@ -731,8 +741,10 @@ def main():
         log("affine-packed rows done")
         ch = {}
         for bits in (2, 4, 8):
-            ch[f"bits{bits}"] = {k: round(v, 4) for k, v in
-                                 bench_chained(torch, Q, synth, timer, bits, 10, 2).items()}
+            for packed in (False, True):
+                ch[f"bits{bits}" + ("_affine_packed" if packed else "")] = {
+                    k: round(v, 4) for k, v in
+                    bench_chained(torch, Q, synth, timer, bits, 10, 2, packed).items()}
         rows["qmm_t_chained_M1024_f16_g64"] = ch
         log("chained done")
         rows["qconv2d_64x64x320_3x3_f16_4bit_g64"] = {

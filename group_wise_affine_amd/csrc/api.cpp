@@ -559,32 +559,82 @@ qmm_status qmm_affine_pack(const uint32_t* wq, const void* scales, const void* b
                   "qmm_affine_pack");
 }
 
+// Shared checks of the affine-packed products; gemv selects the GEMV limits.
+static qmm_status check_affine_packed(const char* tag, const void* x, const uint32_t* wq_packed,
+                                      const void* sb_packed, qmm_dtype dt, int64_t M, int64_t N,
+                                      int64_t K, int group_size, int bits, const void* y) {
+  if (!x || !wq_packed || !sb_packed || !y)
+    return fail(QMM_E_NULL, "%s: x, wq_packed, sb_packed and y must be non-NULL", tag);
+  qmm_status st = check_bits_gs(bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "%s: only float16 and bfloat16 are supported", tag);
+  st = check_k(K, group_size);
+  if (st) return st;
+  const int rp = (bits & (bits - 1)) == 0 ? 4 : 2;
+  if (M < 1 || N < rp || N % rp != 0 || M > kI32 || N > kI32)
+    return fail(QMM_E_SHAPE, "%s: M (%lld) must be >= 1 and N (%lld) a positive multiple of %d "
+                "(rows per block of the packed layout at %d bits)", tag, (long long)M,
+                (long long)N, rp, bits);
+  if (N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "%s: problem too large", tag);
+  if (!aligned(x, 16) || !aligned(wq_packed, 16) || !aligned(sb_packed, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "%s: x, wq_packed, sb_packed and y must be 16-byte aligned", tag);
+  return QMM_OK;
+}
+
+// GEMV on the packed layout: bits 2/4/8 the interleaved-row GEMV (K up to
+// kFpMaxK), bits 3/5/6 the streaming GEMV with packed scale addressing (K up
+// to its LDS-staged row).
+static qmm_status packed_gemv(const char* tag, const void* x, const uint32_t* wq_packed,
+                              const void* sb_packed, qmm_dtype dt, int64_t M, int64_t N,
+                              int64_t K, int group_size, int bits, void* y, void* stream) {
+  const bool pow2 = (bits & (bits - 1)) == 0;
+  const int64_t kmax = pow2 ? qmm::kFpMaxK : qmm::qmv_max_k(bits, (int)dt);
+  if (M > 65535 || K > kmax)
+    return fail(QMM_E_SHAPE, "%s: the GEMV takes M (%lld) up to 65535 and K (%lld) up to %lld",
+                tag, (long long)M, (long long)K, (long long)kmax);
+  if (pow2)
+    return launched(qmm::launch_affine_packed_qmv((int)dt, bits, group_size, x, wq_packed,
+                                                  sb_packed, M, N, K, y, (hipStream_t)stream),
+                    tag);
+  return launched(qmm::launch_qmv_packed_sb((int)dt, bits, group_size, x, wq_packed, sb_packed,
+                                            M, N, K, y, (hipStream_t)stream),
+                  tag);
+}
+
 qmm_status qmv_affine_packed(const void* x, const uint32_t* wq_packed, const void* sb_packed,
                              qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
                              int bits, void* y, void* stream) {
-  if (!x || !wq_packed || !sb_packed || !y)
-    return fail(QMM_E_NULL, "qmv_affine_packed: x, wq_packed, sb_packed and y must be non-NULL");
-  qmm_status st = check_bits_gs(bits, group_size);
+  qmm_status st = check_affine_packed("qmv_affine_packed", x, wq_packed, sb_packed, dt, M, N, K,
+                                      group_size, bits, y);
   if (st) return st;
-  if (bits != 2 && bits != 4 && bits != 8)
-    return fail(QMM_E_BITS, "qmv_affine_packed: the interleaved weight layout exists for bits "
-                "2, 4 and 8 only (got %d)", bits);
-  if (dt != QMM_F16 && dt != QMM_BF16)
-    return fail(QMM_E_DTYPE, "qmv_affine_packed: only float16 and bfloat16 are supported");
-  st = check_k(K, group_size);
+  return packed_gemv("qmv_affine_packed", x, wq_packed, sb_packed, dt, M, N, K, group_size, bits,
+                     y, stream);
+}
+
+// Rows of x from which the packed product takes the tile kernel: the
+// interleaved-row GEMV reads W once per row of x, the streaming GEMV once
+// per 4 rows.
+static int64_t packed_crossover_m(int bits) { return (bits & (bits - 1)) == 0 ? 3 : 5; }
+
+qmm_status qmm_t_affine_packed(const void* x, const uint32_t* wq_packed, const void* sb_packed,
+                               qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
+                               int bits, void* y, void* stream) {
+  const char* tag = "qmm_t_affine_packed";
+  qmm_status st = check_affine_packed(tag, x, wq_packed, sb_packed, dt, M, N, K, group_size, bits,
+                                      y);
   if (st) return st;
-  if (M < 1 || M > 65535 || N < 4 || N % 4 != 0 || N > kI32 || K > qmm::kFpMaxK)
-    return fail(QMM_E_SHAPE, "qmv_affine_packed: M (%lld) must be in [1, 65535], N (%lld) a "
-                "positive multiple of 4, K (%lld) at most %lld", (long long)M, (long long)N,
-                (long long)K, (long long)qmm::kFpMaxK);
-  if (N * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40))
-    return fail(QMM_E_SHAPE, "qmv_affine_packed: problem too large");
-  if (!aligned(x, 16) || !aligned(wq_packed, 16) || !aligned(sb_packed, 16) || !aligned(y, 16))
-    return fail(QMM_E_ALIGN, "qmv_affine_packed: x, wq_packed, sb_packed and y must be 16-byte "
-                "aligned");
-  return launched(qmm::launch_affine_packed_qmv((int)dt, bits, group_size, x, wq_packed,
-                                                sb_packed, M, N, K, y, (hipStream_t)stream),
-                  "qmv_affine_packed");
+  const bool pow2 = (bits & (bits - 1)) == 0;
+  const int64_t kmax = pow2 ? qmm::kFpMaxK : qmm::qmv_max_k(bits, (int)dt);
+  if (M < packed_crossover_m(bits) && K <= kmax)
+    return packed_gemv(tag, x, wq_packed, sb_packed, dt, M, N, K, group_size, bits, y, stream);
+  if (K >= qmm::kTileMaxK)
+    return fail(QMM_E_SHAPE, "%s: K (%lld) must be below %lld for the MFMA tile kernel", tag,
+                (long long)K, (long long)qmm::kTileMaxK);
+  return launched(qmm::launch_apk_mfma((int)dt, bits, group_size, x, wq_packed, sb_packed, M, N,
+                                       K, y, (hipStream_t)stream),
+                  tag);
 }
 
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,

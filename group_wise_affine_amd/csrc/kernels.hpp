@@ -138,6 +138,18 @@ hipError_t launch_affine_packed_qmv(int dt, int bits, int gs, const void* x,
                                     const uint32_t* wq_packed, const void* sb_packed, int64_t M,
                                     int64_t N, int64_t K, void* y, hipStream_t st);
 
+// GEMV on the affine-packed layout of 3/5/6-bit weights (standard words,
+// scales and biases interleaved in pairs of rows; N even): the streaming
+// GEMV with packed scale addressing.
+hipError_t launch_qmv_packed_sb(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                                const void* sbp, int64_t M, int64_t N, int64_t K, void* y,
+                                hipStream_t st);
+// Product on the affine-packed layout on the MFMA tile kernel, any M (N a
+// multiple of 4 for bits 2/4/8, of 2 otherwise; limits as launch_qmm_mfma).
+hipError_t launch_apk_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq_packed,
+                           const void* sbp, int64_t M, int64_t N, int64_t K, void* y,
+                           hipStream_t st);
+
 // Implicit-im2col conv on the MFMA tile GEMM.
 struct ConvGeom {
   int64_t B, H, W, C, O, OH, OW;

@@ -85,6 +85,25 @@ hipError_t launch_fp_qmm_mfma(int dt, int bits, int gs, const void* x, const uin
   return launch_tile_fp(dt, bits, gs, a, st);
 }
 
+hipError_t launch_apk_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq_packed,
+                           const void* sbp, int64_t M, int64_t N, int64_t K, void* y,
+                           hipStream_t st) {
+  GemmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.wq = reinterpret_cast<const uint8_t*>(wq_packed);
+  a.s = static_cast<const uint16_t*>(sbp);
+  a.b = a.s;
+  a.y = static_cast<uint16_t*>(y);
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.gs_log2 = ilog2(gs);
+  a.ldy = N;
+  a.magic = F16::kMagic;
+  a.nxb = 1; a.nwb = 1;
+  a.ws = splitk_ws();
+  if (!a.ws) return hipErrorInvalidSymbol;
+  return launch_tile_apk(dt, bits, a, st);
+}
+
 // The fp GEMV reads W once per row of x; the tile kernel once per 128 rows.
 // Measured (f16, 4096 x 4096 and 2048 x 8192, hot weights): the GEMV takes
 // 6.9-9.6 us at M = 2 and 8.1-12.4 us at M = 4, the tile kernel 8.1-11.0 us

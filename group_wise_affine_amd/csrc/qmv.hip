@@ -165,7 +165,13 @@ __device__ __forceinline__ void chunk_fence() { asm volatile("; chunk fence" :::
 // Lane work: R rows x CPL chunks; lane t of a row group handles chunks
 // c = t + TPR*i (i < CPL) of each of its R rows, so an x chunk read from LDS
 // serves R rows.
-template <class T, int BITS, int MB, int CPL, int R, bool SBL, int WW, bool GATHER>
+// PK: scales and biases in the affine-packed layout of 3/5/6-bit weights
+// ("Add the 3bit packed qmm_t", ops.cpp quantize with AffinePacked): one
+// array, rows in pairs, per pair and group the two scales then the two
+// biases (scale of row n at ((n/2)*G + g)*4 + n%2, its bias 2 further); the
+// biases argument is unused.
+template <class T, int BITS, int MB, int CPL, int R, bool SBL, int WW, bool GATHER,
+          bool PK = false>
 __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -232,8 +238,14 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
         load_chunk<BITS>(wq + (int64_t)rowc * row_bytes + (int64_t)cc * (4 * BITS), wv[r][i]);
         if constexpr (!SBL) {
           const int g = (cc << 5) >> gs_log2;
-          sw[r][i] = scales[(int64_t)rowc * G + g];
-          bw[r][i] = biases[(int64_t)rowc * G + g];
+          if constexpr (PK) {
+            const int64_t e = ((int64_t)(rowc >> 1) * G + g) * 4 + (rowc & 1);
+            sw[r][i] = scales[e];
+            bw[r][i] = scales[e + 2];
+          } else {
+            sw[r][i] = scales[(int64_t)rowc * G + g];
+            bw[r][i] = biases[(int64_t)rowc * G + g];
+          }
         }
       }
       chunk_fence();
@@ -250,8 +262,15 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
       const int g = (cc << 5) >> gs_log2;
 #pragma unroll
       for (int r = 0; r < R; r++) {
-        sw[r][i] = sbl[(lr0 + r) * G + g];
-        bw[r][i] = sbl[(rows_blk + lr0 + r) * G + g];
+        if constexpr (PK) {
+          // the staged run is the packed rows of the workgroup (rows_blk even)
+          const int lr = lr0 + r, e = ((lr >> 1) * G + g) * 4 + (lr & 1);
+          sw[r][i] = sbl[e];
+          bw[r][i] = sbl[e + 2];
+        } else {
+          sw[r][i] = sbl[(lr0 + r) * G + g];
+          bw[r][i] = sbl[(rows_blk + lr0 + r) * G + g];
+        }
       }
     }
   };
@@ -261,8 +280,13 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     const bool bias = u >= sb_units;
     const int uu = bias ? u - sb_units : u;
     const uint16_t* src = bias ? biases : scales;
-    const int64_t e0 = (int64_t)blockIdx.x * rows_blk * G + 8 * (int64_t)uu;
-    const int64_t total = (int64_t)N * G;
+    int64_t e0 = (int64_t)blockIdx.x * rows_blk * G + 8 * (int64_t)uu;
+    int64_t total = (int64_t)N * G;
+    if constexpr (PK) {   // one run of 2 * rows_blk * G values
+      src = scales;
+      e0 = (int64_t)blockIdx.x * rows_blk * 2 * G + 8 * (int64_t)u;
+      total = (int64_t)N * 2 * G;
+    }
     if (e0 + 8 <= total) return *reinterpret_cast<const uint4*>(src + e0);
     uint32_t h[4] = {0, 0, 0, 0};
     for (int e = 0; e < 8; e++)
@@ -456,6 +480,7 @@ struct QmvBatch {
   const int32_t* lidx;
   const int32_t* ridx;
   int nxb, nwb, B;
+  bool pk = false;   // scales / biases in the affine-packed layout (3/5/6 bits)
 };
 static constexpr QmvBatch kOneBatch{nullptr, nullptr, 1, 1, 1};
 static bool gathered(const QmvBatch& bt) {
@@ -505,11 +530,19 @@ static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
   const auto sp = static_cast<const uint16_t*>(s);
   const auto bp = static_cast<const uint16_t*>(b);
   const auto yp = static_cast<uint16_t*>(y);
-  auto go = [&]<bool S, bool GA>() {
-    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, S, WW, GA>), grid, block,
+  auto go = [&]<bool S, bool GA, bool PK = false>() {
+    hipLaunchKernelGGL((qmv_kernel<T, BITS, MB, CPL, R, S, WW, GA, PK>), grid, block,
                        S ? lds_sb : lds_x, st, xp, wp, sp, bp, yp, M, N, K, ilog2(gs),
                        ilog2(tpr), m2, magic, bt.lidx, bt.ridx, bt.nxb, bt.nwb);
   };
+  // affine-packed scales (3/5/6 bits only; one packed run, N even)
+  if constexpr (!Pack<BITS>::kPow2) {
+    if (bt.pk) {
+      if (sbl) go.template operator()<true, false, true>();
+      else go.template operator()<false, false, true>();
+      return hipGetLastError();
+    }
+  }
   // gathered launches come with one row of x per pass (launch_t)
   if constexpr (MB == 1) {
     if (gathered(bt)) {
@@ -609,6 +642,18 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
   if (dt == 0)
     return launch_bits<F16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st, kOneBatch);
   return launch_bits<BF16>(bits, x, wq, s, b, (int)M, (int)N, (int)K, gs, y, st, kOneBatch);
+}
+
+// GEMV on the affine-packed layout of 3/5/6-bit weights: standard packed
+// words, scales and biases interleaved in pairs of rows (N even)
+hipError_t launch_qmv_packed_sb(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                                const void* sbp, int64_t M, int64_t N, int64_t K, void* y,
+                                hipStream_t st) {
+  QmvBatch bt = kOneBatch;
+  bt.pk = true;
+  if (dt == 0)
+    return launch_bits<F16>(bits, x, wq, sbp, sbp, (int)M, (int)N, (int)K, gs, y, st, bt);
+  return launch_bits<BF16>(bits, x, wq, sbp, sbp, (int)M, (int)N, (int)K, gs, y, st, bt);
 }
 
 hipError_t launch_gather_qmv(int dt, int bits, int gs, const void* x, int64_t nxb,

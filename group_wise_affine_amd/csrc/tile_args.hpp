@@ -59,5 +59,9 @@ hipError_t launch_tile_conv_bf16(int bits, const GemmArgs& a, int groups, bool d
 // mxfp8; dt 0 f16, 1 bf16): a.s points to the scale bytes [N, K/gs], a.b is
 // unused.
 hipError_t launch_tile_fp(int dt, int bits, int gs, const GemmArgs& a, hipStream_t st);
+// Affine-packed layout (bits 2/4/8: rows interleaved in blocks of 4, words
+// and scales; bits 3/5/6: scales in blocks of 2): a.wq the packed words,
+// a.s = a.b the packed scale / bias array.
+hipError_t launch_tile_apk(int dt, int bits, const GemmArgs& a, hipStream_t st);
 
 }  // namespace qmm

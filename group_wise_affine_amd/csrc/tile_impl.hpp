@@ -498,7 +498,7 @@ __device__ __forceinline__ void keep(const uint4& v) {
 
 constexpr int kStageSteps = 8;      // K steps per scale stage (512 codes)
 
-template <int BM, int BN, int BITS, int KW, int SL>
+template <int BM, int BN, int BITS, int KW, int SL, bool WU4 = false>
 struct DmaGeo {
   // SL output slices, KW wavefronts per slice (each taking 1/KW of the codes
   // of every K step): SL*KW wavefronts
@@ -513,7 +513,9 @@ struct DmaGeo {
   static constexpr int A_ELEMS = BM * 64;          // x tile of one step
   static constexpr int A_BLOCKS = BM / 8;          // 8 rows per DMA instruction
   static constexpr int A_PER_WAVE = A_BLOCKS / NW;
-  static constexpr int WU = (BITS == 8 || (BITS == 4 && BN == 128)) ? 16 : 4;
+  // W copy unit: 4 bytes when each lane must pick its own word (WU4: rows
+  // interleaved in memory)
+  static constexpr int WU = (!WU4 && (BITS == 8 || (BITS == 4 && BN == 128))) ? 16 : 4;
   static constexpr int W_ROW = 8 * BITS;           // bytes per W row and step
   static constexpr int W_BYTES = BN * W_ROW;
   static constexpr int UPR = W_ROW / WU;           // DMA units per W row
@@ -592,9 +594,17 @@ constexpr int filler_slot(int f, int nf, int nm, int lead) {
 // scales one scaled conversion per code pair (v_cvt_scalef32_pk_*, which
 // applies a power-of-two scale exactly), for E4M3 scales the conversion at
 // scale 1 and an fp32 product rounded to T.
-template <class T, int BITS, int BM, int BN, int CONV, int KW, int SL, int FPM>
+//
+// APK != 0: the affine-packed layout ("Add the 3bit packed qmm_t", ops.cpp
+// quantize with AffinePacked): scales and biases in one array, rows in
+// blocks of APK (4 for power-of-two bits, 2 otherwise), per block and group
+// the APK scales then the APK biases; with APK = 4 the block's weight words
+// are interleaved too (word w of row 4i + r at word 4w + r of packed row i),
+// and the W copies use 4-byte units so that each lane fetches one row's word
+// and the slot gets the plain row layout.
+template <class T, int BITS, int BM, int BN, int CONV, int KW, int SL, int FPM, int APK = 0>
 __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
-  using G = DmaGeo<BM, BN, BITS, KW, SL>;
+  using G = DmaGeo<BM, BN, BITS, KW, SL, APK == 4>;
   constexpr int NW = G::NW, NT = G::NT;
   constexpr bool kFp = FPM != 0;
   constexpr bool kSplit = !kFp && __is_same(T, BF16);
@@ -774,7 +784,10 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
     const int u = WU == 16 ? (p ^ ((r >> G::SWZ) & (UPR - 1))) : p;
     const int rc = n_blk + r < a.N ? r : a.N - 1 - n_blk;
     wuo[i] = WU * u;
-    woff[i] = (uint32_t)rc * (uint32_t)row_bytes + (uint32_t)(WU * u);
+    if constexpr (APK == 4)   // word u of row rc: word 4u + rc % 4 of packed row rc / 4
+      woff[i] = (uint32_t)(rc >> 2) * (uint32_t)(4 * row_bytes) + (uint32_t)(4 * (4 * u + (rc & 3)));
+    else
+      woff[i] = (uint32_t)rc * (uint32_t)row_bytes + (uint32_t)(WU * u);
   }
 
   // ---- issue the copies of step tt into slot S. Pieces past the end of a
@@ -821,13 +834,14 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
     } else {
       constexpr int i = D - G::A_PER_WAVE;
       uint8_t* wd = wslot.template operator()<S>();
-      const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;
+      const uint32_t wsoff = (uint32_t)(8 * BITS) * tt;   // byte of the step in a row
       const int blk = NW * i + wave;
       const bool real = G::W_BLOCKS % NW == 0 || blk < G::W_BLOCKS;
       bool ok = real;
       if constexpr (CHK) ok = ok && (int)wsoff + wuo[i] < row_bytes;
+      // (interleaved rows: the step's words of a packed row start 4x further)
       dma_lds<WU>(wr, real ? (void*)(wd + blk * 64 * WU) : (void*)wjunk, ok ? woff[i] : kOob,
-                  wsoff);
+                  APK == 4 ? 4 * wsoff : wsoff);
     }
   };
   auto issue = [&]<int S>(int tt) QMM_INLINE {
@@ -854,32 +868,41 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   // loop-invariant lane offsets plus a per-stage scalar offset. Groups past
   // the end of a row read the next row (or zeros): they only meet zero x.
   constexpr int kSL = BN * kSgMax / NT;
-  const char* sbase = sp + (int64_t)n_blk * n_groups * ES;
-  const char* bbase = kFp ? sbase : bp + (int64_t)n_blk * n_groups * ES;
-  const int64_t s_bytes = (int64_t)(a.N - n_blk) * n_groups * ES;
+  // (packed: the tile's rows start at packed row n_blk / APK, whose 2 * APK
+  // values per group make the same 2 * n_groups values per row)
+  const char* sbase = sp + (int64_t)n_blk * n_groups * ES * (APK ? 2 : 1);
+  const char* bbase = (kFp || APK) ? sbase : bp + (int64_t)n_blk * n_groups * ES;
+  const int64_t s_bytes = (int64_t)(a.N - n_blk) * n_groups * ES * (APK ? 2 : 1);
   const uint32_t s_rb = (uint32_t)(s_bytes < 0x7fffffff ? s_bytes : 0x7fffffff);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(sbase, s_rb), br = make_rsrc(bbase, s_rb);
-  uint32_t soffv[kSL];
+  uint32_t soffv[kSL], soffb[kSL];
   int sdst[kSL];
 #pragma unroll
   for (int i = 0; i < kSL; i++) {
     const int e = (tid + NT * i) & (BN * SG - 1);
     const int grp = e & (SG - 1), row = e >> sg_log2;
     const int rc = n_blk + row < a.N ? row : a.N - 1 - n_blk;
-    soffv[i] = (uint32_t)((rc * n_groups + grp) * ES);
+    if constexpr (APK) {
+      const int es = ((rc / APK) * n_groups + grp) * 2 * APK + rc % APK;
+      soffv[i] = (uint32_t)(es * 2);
+      soffb[i] = (uint32_t)((es + APK) * 2);
+    } else {
+      soffv[i] = (uint32_t)((rc * n_groups + grp) * ES);
+      soffb[i] = soffv[i];
+    }
     sdst[i] = row * SGP + grp;
   }
   uint32_t sreg[kSL], breg[kSL];
   constexpr int kSGrp = kSL >= 4 ? 4 : kSL;          // loads of a group (each array)
   auto scale_load_grp = [&]<int GR>(int j) QMM_INLINE {
-    const uint32_t so = (uint32_t)(j * SG * ES);
+    const uint32_t so = (uint32_t)(j * SG * ES * (APK ? 2 * APK : 1));
 #pragma unroll
     for (int i = GR * kSGrp; i < (GR + 1) * kSGrp; i++) {
       if constexpr (kFp) {
         sreg[i] = __builtin_amdgcn_raw_buffer_load_b8(sr, soffv[i], so, 0);
       } else {
         sreg[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soffv[i], so, 0);
-        breg[i] = __builtin_amdgcn_raw_buffer_load_b16(br, soffv[i], so, 0);
+        breg[i] = __builtin_amdgcn_raw_buffer_load_b16(br, soffb[i], so, 0);
       }
     }
   };
@@ -1322,14 +1345,14 @@ constexpr int dma_sl() {
   return 4;
 }
 
-template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0>
+template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0, int APK = 0>
 static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
   constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   const dim3 grid(tiles, 1, groups);
   a.ksplit = 1;
   a.ksteps = ((a.K + 63) / 64 + kStageSteps - 1) / kStageSteps * kStageSteps;
-  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM>), grid,
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM, APK>), grid,
                      dim3(64 * SL * KW), 0, st, a);
   return hipGetLastError();
 }
@@ -1414,7 +1437,7 @@ static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm 
 
 // tile kernel over a BM x BN tiling with K split by plan (fp32 partials +
 // reduction when split)
-template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0>
+template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0, int APK = 0>
 static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   int ksteps = 0;
@@ -1422,7 +1445,7 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
                          !CONV && BM == 128 && (__is_same(T, F16) || FPM != 0), CONV ? 1 : groups);
   a.ksteps = ksteps;
   constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
-  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM>),
+  hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM, APK>),
                      dim3(tiles, a.ksplit, groups), dim3(64 * SL * KW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
@@ -1431,7 +1454,7 @@ static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   return launch_splitk_reduce<T>(a, (int)a.ldy, st);
 }
 
-template <class T, int BITS, int CONV, bool DMA, int FPM = 0>
+template <class T, int BITS, int CONV, bool DMA, int FPM = 0, int APK = 0>
 static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
   const int64_t tiles128 = (int64_t)((a.N + 127) / 128) * ((a.M + 127) / 128) * groups;
   // the plain f16 GEMM (and the fp modes, which run one MFMA per fragment in
@@ -1440,17 +1463,17 @@ static hipError_t launch_shape(GemmArgs a, int groups, hipStream_t st) {
   if constexpr (DMA) {
     // at most 32 rows: one 32-row block per tile (W is read once)
     if constexpr (!CONV) {
-      if (a.M <= 32) return launch_dma_split<T, BITS, 32, 128, CONV, FPM>(a, groups, st);
+      if (a.M <= 32) return launch_dma_split<T, BITS, 32, 128, CONV, FPM, APK>(a, groups, st);
     }
     // 128-wide tiles that would leave more than half a tile of columns idle
     // (e.g. 160-channel conv groups): 64 x 64 tiles
     if (a.N % 128 != 0 && a.N % 128 < 64)
-      return launch_dma<T, BITS, 64, 64, CONV, FPM>(a, groups, st);
-    if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV, FPM>(a, groups, st);
+      return launch_dma<T, BITS, 64, 64, CONV, FPM, APK>(a, groups, st);
+    if (tiles128 >= 192) return launch_dma<T, BITS, 128, 128, CONV, FPM, APK>(a, groups, st);
     int ks;
     if (splitk_plan(a, tiles128, &ks, kGemmPlan, CONV ? 1 : groups) > 1)
-      return launch_dma_split<T, BITS, 128, 128, CONV, FPM>(a, groups, st);
-    return launch_dma<T, BITS, 64, 64, CONV, FPM>(a, groups, st);
+      return launch_dma_split<T, BITS, 128, 128, CONV, FPM, APK>(a, groups, st);
+    return launch_dma<T, BITS, 64, 64, CONV, FPM, APK>(a, groups, st);
   } else {
     if (tiles128 >= 256) return launch_gather<T, BITS, 128, 128>(a, groups, st);
     return launch_gather<T, BITS, 64, 64>(a, groups, st);

@@ -22,7 +22,7 @@ STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
            "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
-           "qmm_affine_pack", "qmv_affine_packed",
+           "qmm_affine_pack", "qmv_affine_packed", "qmm_t_affine_packed",
            "qmm_crossover_m", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -59,6 +59,7 @@ def lib():
         L.qmm_gather_qmm.argtypes = L.qmm_gather_qmv.argtypes
         L.qmm_affine_pack.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, vp, vp, vp]
         L.qmv_affine_packed.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
+        L.qmm_t_affine_packed.argtypes = L.qmv_affine_packed.argtypes
         L.qmm_t_batched.argtypes = [vp, vp, vp, vp, i64, i64, i32, i64, i64, i64, i32, i32,
                                     vp, vp]
         L.qmm_fp_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
@@ -70,7 +71,7 @@ def lib():
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
                   "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched", "qmm_fp_quantize",
                   "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
-                  "qmm_affine_pack", "qmv_affine_packed"):
+                  "qmm_affine_pack", "qmv_affine_packed", "qmm_t_affine_packed"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32]
         L.qmm_crossover_m.restype = i32
@@ -414,8 +415,9 @@ def affine_pack(wq, scales, biases, group_size=64, bits=4, stream=None):
     return (wp if pow2 else wq), sbp
 
 
-def qmv_affine_packed(x, wq_packed, sb_packed, N, group_size=64, bits=4, out=None, stream=None):
-    """y [M,N] = x [M,K] . dequant(W)^T from the affine-packed layout."""
+def qmv_affine_packed(x, wq_packed, sb_packed, N, group_size=64, bits=4, out=None, stream=None,
+                      _fn="qmv_affine_packed"):
+    """y [M,N] = x [M,K] . dequant(W)^T from the affine-packed layout (GEMV)."""
     _check_tensor(x, "x", dims=2)
     M, K = x.shape
     if out is None:
@@ -428,9 +430,17 @@ def qmv_affine_packed(x, wq_packed, sb_packed, N, group_size=64, bits=4, out=Non
             _check_tensor(sb_packed, "sb_packed", (N // rp, K // group_size * 2 * rp), x.dtype)
     _check_tensor(out, "out", (M, N), x.dtype)
     _check_device(("x", x), ("wq_packed", wq_packed), ("sb_packed", sb_packed), ("out", out))
-    _check(lib().qmv_affine_packed(_ptr(x), _ptr(wq_packed), _ptr(sb_packed), _dt(x.dtype), M, N,
-                                   K, group_size, bits, _ptr(out), _stream(stream)))
+    _check(getattr(lib(), _fn)(_ptr(x), _ptr(wq_packed), _ptr(sb_packed), _dt(x.dtype), M, N,
+                               K, group_size, bits, _ptr(out), _stream(stream)))
     return out
+
+
+def qmm_t_affine_packed(x, wq_packed, sb_packed, N, group_size=64, bits=4, out=None,
+                        stream=None):
+    """Same as qmv_affine_packed for any M (the MFMA tile kernel beyond a few
+    rows)."""
+    return qmv_affine_packed(x, wq_packed, sb_packed, N, group_size, bits, out, stream,
+                             _fn="qmm_t_affine_packed")
 
 
 def conv_out_hw(H, W, kh, kw, stride, padding):

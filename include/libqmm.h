@@ -43,8 +43,8 @@
  *    in library-owned workspaces: static device arrays, one set per GPU,
  *    holding their last call's contents (nothing is allocated per call):
  *      * the tile-kernel workspace (64 MiB): qmm_t, qmm_t_batched,
- *        qmm_gather_qmm, qconv2d_nhwc and qmm_fp_t when they split K, and
- *        qmm_n;
+ *        qmm_gather_qmm, qconv2d_nhwc, qmm_fp_t and qmm_t_affine_packed
+ *        when they split K, and qmm_n;
  *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
  *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
  *        the MFMA GEMV on a narrow layer.
@@ -253,16 +253,35 @@ qmm_status qmm_affine_pack(const uint32_t* wq, const void* scales,
                            uint32_t* wq_packed, void* sb_packed, void* stream);
 
 /*
- * y[M,N] = x[M,K] . dequant(W)^T read from the affine-packed layout (bits 2,
- * 4 or 8; f16 / bf16; N % 4 == 0; K <= 16384; M <= 65535): the same product
- * as qmv, y[m,n] = sum over groups of s * sum x*q + b * sum x in fp32, one
- * pass over W per row of x. (Source: "Add the 3bit packed qmm_t",
- * affine_packed_qmv_fast_impl: a wide load per row block.)
+ * y[M,N] = x[M,K] . dequant(W)^T read from the affine-packed layout, on a
+ * GEMV (meant for a few rows of x): the same product as qmv, y[m,n] = sum
+ * over groups of s * sum x*q + b * sum x in fp32. Bits 2, 4, 8: wq_packed
+ * the interleaved words, N % 4 == 0, K <= 16384, one pass over W per row of
+ * x. Bits 3, 5, 6: wq_packed the plain packed rows (as qmm_quantize writes
+ * them), N % 2 == 0, K up to the streaming GEMV's limit (29120 at 4 bits
+ * f16, less for wider codes), one pass over W per 4 rows of x. f16 / bf16,
+ * M <= 65535; x, wq_packed, sb_packed and y 16-byte aligned. (Source: "Add
+ * the 3bit packed qmm_t", affine_packed_qmv_fast_impl and
+ * affine_packed_byte_qmv_fast_impl.)
  */
 qmm_status qmv_affine_packed(const void* x, const uint32_t* wq_packed,
                              const void* sb_packed, qmm_dtype dt, int64_t M,
                              int64_t N, int64_t K, int group_size, int bits,
                              void* y, void* stream);
+
+/*
+ * The same product for any M: the GEMV above for a few rows of x, the MFMA
+ * tile kernel beyond, which reads the packed layout directly (the
+ * interleaved rows are separated as they are copied to LDS). Same layout
+ * and alignment rules; K below 2^22 on the tile kernel; the tile kernel may
+ * split K and use the library's tile-kernel workspace. (Source: "Add the
+ * 3bit packed qmm_t", affine_packed_qmm_op: qmv for few rows, otherwise
+ * affine_packed_qmm_t.)
+ */
+qmm_status qmm_t_affine_packed(const void* x, const uint32_t* wq_packed,
+                               const void* sb_packed, qmm_dtype dt, int64_t M,
+                               int64_t N, int64_t K, int group_size, int bits,
+                               void* y, void* stream);
 
 /*
  * Non-transposed product: y[M,N] = x[M,K] . dequant(W)[K,N], where the

@@ -283,13 +283,22 @@ def test_affine_packed_arguments(L):
     assert pk(N=5, bits=3, wp=None) == Q.QMM_E_SHAPE   # blocks of 2 rows
     assert pk(K=48) == Q.QMM_E_SHAPE
     assert pk(wq=P2) == Q.QMM_E_ALIGN
-    assert mv(x=None) == Q.QMM_E_NULL
-    assert mv(bits=3) == Q.QMM_E_BITS           # no interleaved words for 3 bits
-    assert mv(dt=2) == Q.QMM_E_DTYPE
-    assert mv(N=6) == Q.QMM_E_SHAPE
-    assert mv(K=32768) == Q.QMM_E_SHAPE
-    assert mv(M=0) == Q.QMM_E_SHAPE
-    assert mv(sbp=P2) == Q.QMM_E_ALIGN
+    def mt(x=P, wp=P, sbp=P, dt=0, M=64, N=8, K=64, gs=64, bits=4, y=P):
+        return _st(L, "qmm_t_affine_packed", x, wp, sbp, dt, M, N, K, gs, bits, y, None)
+    for f in (mv, mt):
+        assert f(x=None) == Q.QMM_E_NULL and f(sbp=None) == Q.QMM_E_NULL
+        assert f(bits=7) == Q.QMM_E_BITS
+        assert f(gs=16) == Q.QMM_E_GROUP
+        assert f(dt=2) == Q.QMM_E_DTYPE
+        assert f(N=6) == Q.QMM_E_SHAPE              # blocks of 4 rows (bits 2, 4, 8)
+        assert f(N=5, bits=3) == Q.QMM_E_SHAPE      # blocks of 2 rows (bits 3, 5, 6)
+        assert f(K=48) == Q.QMM_E_SHAPE
+        assert f(M=0) == Q.QMM_E_SHAPE
+        assert f(sbp=P2) == Q.QMM_E_ALIGN and f(y=P2) == Q.QMM_E_ALIGN
+    assert mv(K=32768) == Q.QMM_E_SHAPE          # beyond the interleaved-row GEMV's x row
+    assert mv(K=65536, bits=3) == Q.QMM_E_SHAPE  # beyond the streaming GEMV's x row
+    assert mv(M=65536) == Q.QMM_E_SHAPE
+    assert mt(K=1 << 22) == Q.QMM_E_SHAPE        # beyond the tile kernel
 
 
 def test_batched_arguments(L):

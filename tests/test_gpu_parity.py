@@ -600,23 +600,71 @@ def test_affine_pack_bit_exact(orc, dt, bits):
     assert np.array_equal(from_dev(sbp), sbp_o)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("dt,M,N,K,gs", [
     ("f16", 1, 4096, 4096, 64),
     ("bf16", 1, 4096, 4096, 64),
     ("f16", 3, 72, 640, 32),       # 18 row blocks: a partial workgroup; few words per lane
-    ("bf16", 2, 8, 16384, 128),    # the largest K
+    ("bf16", 2, 8, 16384, 128),    # the largest K of the interleaved-row GEMV
+    ("f16", 5, 130, 1024, 64),     # 3/5/6 bits: rows of x in blocks of 4, N % 4 == 2
 ])
 def test_qmv_affine_packed(orc, dt, M, N, K, gs, bits):
+    if N % (4 if bits in (2, 4, 8) else 2):
+        pytest.skip("the packed layout takes whole row blocks")
     code = orc_code(orc, dt)
     x = synth.normal((M, K), seed=M + N, dt=dt)
     w = synth.normal((N, K), seed=N + K, dt=dt)
+    w[: min(N, 8)] = synth.structured_rows(min(N, 8), K, gs, seed=N, dt=dt)
     wq, s, b = orc.quantize(w, code, gs, bits)
     yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
     wp, sbp = Q.affine_pack(bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
     y = Q.qmv_affine_packed(to_dev(x, dt), wp, sbp, N, gs, bits)
     torch.cuda.synchronize()
     assert_parity(from_dev(y), yo, dt, f"qmv_affine_packed {dt} M{M} N{N} K{K} b{bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("dt,M,N,K,gs", [
+    ("f16", 64, 256, 512, 64),      # 32-row-free tiles, K split
+    ("bf16", 100, 200, 1024, 32),   # ragged M; N % 128 == 72
+    ("f16", 256, 384, 2080, 32),    # K % 64 == 32, split K
+    ("bf16", 1024, 256, 1024, 128),
+    ("f16", 20, 136, 4096, 64),     # 32-row tiles, K split
+    ("f16", 2, 96, 640, 64),        # the GEMV
+])
+def test_qmm_t_affine_packed(orc, dt, M, N, K, gs, bits):
+    """The product on the affine-packed layout for any M (the MFMA tile kernel
+    reading the interleaved rows and packed scales beyond a few rows) against
+    the oracle's qmm_t on the plain layout, with structured weight rows."""
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=M + K, dt=dt)
+    _, wq, s, b = _quantized(orc, dt, N, K, gs, bits, seed=N + bits, structured=True)
+    yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
+    wp, sbp = Q.affine_pack(bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    y = Q.qmm_t_affine_packed(to_dev(x, dt), wp, sbp, N, gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"qmm_t_affine_packed {dt} M{M} N{N} K{K} b{bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_chained_affine_packed_config(orc, bits):
+    """The packed half of the chained bench: x f16 [1024,1024], W1 [4096,1024],
+    W2 [1024,4096] in the affine-packed layout, first loop, sampled rows."""
+    gs = 64
+    x = synth.normal((1024, 1024), seed=0)
+    _, wq1, s1, b1 = _quantized(orc, "f16", 4096, 1024, gs, bits, seed=1)
+    _, wq2, s2, b2 = _quantized(orc, "f16", 1024, 4096, gs, bits, seed=2)
+    p1 = Q.affine_pack(bytes_to_words_dev(wq1), to_dev(s1, "f16"), to_dev(b1, "f16"), gs, bits)
+    p2 = Q.affine_pack(bytes_to_words_dev(wq2), to_dev(s2, "f16"), to_dev(b2, "f16"), gs, bits)
+    h = Q.qmm_t_affine_packed(to_dev(x, "f16"), *p1, 4096, gs, bits)
+    y = Q.qmm_t_affine_packed(h, *p2, 1024, gs, bits)
+    torch.cuda.synchronize()
+    hg, yg = from_dev(h), from_dev(y)
+    for rows in [(0, 16), (1000, 1024)]:
+        ho, _ = orc.qmm_t(x, wq1, s1, b1, orc.F16, gs, bits, nthreads=8, rows=rows)
+        assert_parity(hg[rows[0]:rows[1]], ho, "f16", f"packed chained h bits{bits}")
+        yo, _ = orc.qmm_t(hg, wq2, s2, b2, orc.F16, gs, bits, nthreads=8, rows=rows)
+        assert_parity(yg[rows[0]:rows[1]], yo, "f16", f"packed chained y bits{bits}")
 
 
 # ------------------------------------------------------------ batched weights
