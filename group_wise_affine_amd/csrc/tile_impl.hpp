@@ -1161,11 +1161,12 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
   issue.template operator()<0>(t0);
   issue.template operator()<1>(t0 + 1);
   issue.template operator()<2>(t0 + 2);
-  // the stage's scales and step 0 (steps 1 and 2 stay in flight: the first
-  // step's end waits for step 1)
-  wait_vmcnt<2 * kDma>();
+  // the stage's scales and steps 0 and 1 (step 0's body builds step 1's
+  // state from its slot); step 2 stays in flight, and the first step's end
+  // waits for it
+  wait_vmcnt<kDma>();
   scale_store(js0);
-  wait_vmcnt_barrier<2 * kDma>();
+  wait_vmcnt_barrier<kDma>();
   read_w.template operator()<0>(t0);
   [&]<int... F>(std::integer_sequence<int, F...>) QMM_INLINE {
     (filler.template operator()<F, 0>(af[0], bq[0]), ...);

@@ -343,6 +343,31 @@ def test_qmm_t_split_k_back_to_back(orc):
         assert_parity(from_dev(y), yo, "f16", f"split-K back to back {shape}")
 
 
+@pytest.mark.parametrize("M,N,K,bits", [
+    (31, 136, 3072, 5),     # 32-row tiles, K split 6 ways
+    (200, 160, 1472, 4),    # 64 x 64 tiles, two wavefronts per slice
+    (1024, 3072, 512, 4),   # 128 x 128 tiles (192 of them)
+])
+def test_tile_reads_only_landed_copies(orc, M, N, K, bits):
+    """Regression: each workgroup of the tile kernel must read a ring slot
+    only after its copies have landed (the first step builds the second
+    step's state). Launches on NaN activations leave NaN in the LDS slots of
+    the CUs; a read of a slot before its copy lands then shows as NaN or a
+    parity failure in the following launch on finite inputs."""
+    gs, dt = 64, "f16"
+    _, wq, s, b = _quantized(orc, dt, N, K, gs, bits, seed=N + K)
+    x = synth.normal((M, K), seed=M, dt=dt)
+    yo, _ = orc.qmm_t(x, wq, s, b, orc.F16, gs, bits, nthreads=8)
+    wd, sd, bd = bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt)
+    xd = to_dev(x, dt)
+    xnan = torch.full((M, K), float("nan"), dtype=torch.float16, device="cuda")
+    for it in range(8):
+        Q.qmm_t(xnan, wd, sd, bd, gs, bits)
+        y = Q.qmm_t(xd, wd, sd, bd, gs, bits)
+        torch.cuda.synchronize()
+        assert_parity(from_dev(y), yo, dt, f"tile after NaN launch {it} M{M} N{N} K{K} b{bits}")
+
+
 def test_qmm_t_routes_consistently(orc):
     """Around the crossover both kernels agree with the oracle."""
     mx = Q.crossover_m(4)
