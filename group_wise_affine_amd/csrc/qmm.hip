@@ -10,32 +10,50 @@
 
 namespace qmm {
 
-// Split-K workspace, one per device (a static device array: no allocation
-// at call time). Calls that overlap on one device share it.
+// Split-K workspace and the tile kernel's per-tile arrival counters, one of
+// each per device (static device arrays: no allocation at call time). Calls
+// that overlap on one device share them.
 __device__ float g_splitk_ws[kSplitWsFloats];
+__device__ unsigned g_tile_cnt[kTileCntMax];
 
 namespace {
 
 constexpr int kMaxDevices = 64;
 
-// address of the current device's workspace (looked up once per device)
-float* splitk_ws() {
+struct SplitScratch {
+  float* ws;
+  unsigned* cnt;
+};
+
+// addresses of the current device's workspace and counters (looked up once
+// per device)
+SplitScratch split_scratch() {
   static std::mutex mu;
-  static float* addr[kMaxDevices] = {};
+  static SplitScratch addr[kMaxDevices] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return {};
   std::lock_guard<std::mutex> lock(mu);
-  if (!addr[dev]) {
-    void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_splitk_ws)) != hipSuccess) return nullptr;
-    addr[dev] = static_cast<float*>(p);
+  if (!addr[dev].ws) {
+    void *p = nullptr, *q = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_splitk_ws)) != hipSuccess ||
+        hipGetSymbolAddress(&q, HIP_SYMBOL(g_tile_cnt)) != hipSuccess)
+      return {};
+    addr[dev] = {static_cast<float*>(p), static_cast<unsigned*>(q)};
   }
   return addr[dev];
 }
 
+// the tile kernel's scratch into a (false when the lookup failed)
+bool set_scratch(GemmArgs& a) {
+  const SplitScratch sc = split_scratch();
+  a.ws = sc.ws;
+  a.cnt = sc.cnt;
+  return sc.ws && sc.cnt;
+}
+
 }  // namespace
 
-float* splitk_workspace() { return splitk_ws(); }
+float* splitk_workspace() { return split_scratch().ws; }
 
 hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,
@@ -61,8 +79,7 @@ hipError_t launch_gather_qmm_mfma(int dt, int bits, int gs, const void* x, int64
   a.magic = F16::kMagic;
   a.lidx = lidx; a.ridx = ridx;
   a.nxb = (int)nxb; a.nwb = (int)nwb;
-  a.ws = splitk_ws();
-  if (!a.ws) return hipErrorInvalidSymbol;
+  if (!set_scratch(a)) return hipErrorInvalidSymbol;
   return dt == 0 ? launch_tile_gemm_f16(bits, a, (int)B, st)
                  : launch_tile_gemm_bf16(bits, a, (int)B, st);
 }
@@ -80,8 +97,7 @@ hipError_t launch_fp_qmm_mfma(int dt, int bits, int gs, const void* x, const uin
   a.gs_log2 = ilog2(gs);
   a.ldy = N;
   a.nxb = 1; a.nwb = 1;
-  a.ws = splitk_ws();
-  if (!a.ws) return hipErrorInvalidSymbol;
+  if (!set_scratch(a)) return hipErrorInvalidSymbol;
   return launch_tile_fp(dt, bits, gs, a, st);
 }
 
@@ -99,8 +115,7 @@ hipError_t launch_apk_mfma(int dt, int bits, int gs, const void* x, const uint32
   a.ldy = N;
   a.magic = F16::kMagic;
   a.nxb = 1; a.nwb = 1;
-  a.ws = splitk_ws();
-  if (!a.ws) return hipErrorInvalidSymbol;
+  if (!set_scratch(a)) return hipErrorInvalidSymbol;
   return launch_tile_apk(dt, bits, a, st);
 }
 
@@ -145,8 +160,7 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
   // (and x below 2^30 bytes, in range of one buffer resource)
   const bool dma = (cg.Cg % 8) == 0 && nk * 8 <= kKtabMax && cg.kh < 256 && cg.kw < 256 &&
                    cg.B * cg.H * cg.W * cg.C < ((int64_t)1 << 29);
-  a.ws = splitk_ws();
-  if (!a.ws) return hipErrorInvalidSymbol;
+  if (!set_scratch(a)) return hipErrorInvalidSymbol;
   return dt == 0 ? launch_tile_conv_f16(bits, a, cg.groups, dma, st)
                  : launch_tile_conv_bf16(bits, a, cg.groups, dma, st);
 }

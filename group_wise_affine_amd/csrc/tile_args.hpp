@@ -27,9 +27,12 @@ struct GemmArgs {
   // split K (tile kernel only): blockIdx.y takes K steps [y*ksteps,
   // (y+1)*ksteps) and, with ksplit > 1, writes fp32 partial sums to the
   // split-K workspace ws ([split][M][ldy], for a batched GEMM
-  // [split][batch][M][ldy]; kSplitWsFloats floats) instead of y
+  // [split][batch][M][ldy]; kSplitWsFloats floats); the last workgroup of a
+  // tile to arrive at its counter in cnt (kTileCntMax of them, each back at
+  // zero after every call) adds the partial sums and writes y
   int ksplit, ksteps;
   float* ws;
+  unsigned* cnt;
   // gathered GEMM (plain GEMM only): batch g multiplies x batch lidx[g] (of
   // nxb) by weight batch ridx[g] (of nwb), indices clamped into range; a
   // null array means g
@@ -41,6 +44,7 @@ struct GemmArgs {
 // Split-K workspace size: [split][M][ldy] fp32 partial sums, library-owned
 // (a static device array of the host dispatch, passed to the kernels as ws).
 constexpr int64_t kSplitWsFloats = (int64_t)16 << 20;   // 64 MiB
+constexpr int kTileCntMax = 256;    // split tiles per launch (tiles x batches), at most
 constexpr int kKtabMax = 4096;      // conv k-unit table entries (K_pad <= 32768)
 
 // Tile kernel launchers, one translation unit each (they compile in

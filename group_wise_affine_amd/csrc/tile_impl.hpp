@@ -1251,26 +1251,92 @@ __global__ __launch_bounds__(64 * SL * KW) void qmm_dma_kernel(GemmArgs a) {
 
   // ---- split K: fp32 partial sums straight from the accumulators (lane:
   // column 32j + lane%32, rows 8(r/4) + 4(lane/32) + r%4 of each 32x32 tile;
-  // each store instruction covers two 128-byte row pieces)
+  // each store instruction covers two 128-byte row pieces). The last
+  // workgroup of the tile to arrive adds the ksplit partial sums in split
+  // order (the same sum whichever workgroup arrives last) and writes y.
+  // Partial sums and the counter use device-scope atomic accesses,
+  // coherent across the per-XCD L2 caches; every store has completed before
+  // the barrier that precedes the counter update, and the last workgroup
+  // reads the partial sums only after its update has returned. The counter
+  // is a wrapping increment with limit ksplit - 1, so the last arrival
+  // leaves it at zero for the next call.
   if (a.ksplit > 1) {
-    wait_vmcnt<0>();   // no copy may still be landing in LDS when the wave ends
-    if (kh != 0) return;
+    wait_vmcnt<0>();   // no copy may still be landing in LDS
     // conv: [split][M][ldy], the groups side by side in a row; batched GEMM:
     // [split][batch][M][ldy]
-    float* ws = a.ws + (CONV ? (int64_t)sk * a.M * a.ldy + (int64_t)g * a.Og
-                             : ((int64_t)sk * gridDim.z + g) * a.M * a.ldy);
+    const int64_t plane = CONV ? (int64_t)a.M * a.ldy : (int64_t)gridDim.z * a.M * a.ldy;
+    float* ws0 = a.ws + (CONV ? (int64_t)g * a.Og : (int64_t)g * a.M * a.ldy);
+    if (kh == 0) {
+      float* ws = ws0 + sk * plane;
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+      for (int i = 0; i < FM; i++)
 #pragma unroll
-      for (int j = 0; j < FN; j++) {
-        const int n = n_blk + wn * WTN + 32 * j + rr;
+        for (int j = 0; j < FN; j++) {
+          const int n = n_blk + wn * WTN + 32 * j + rr;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int m = m_blk + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-          // m * ldy + n < kSplitWsFloats = 2^24 floats per split: 24-bit product
-          if (m < a.M && n < a.N) ws[__umul24((uint32_t)m, (uint32_t)a.ldy) + n] = acc[i][j][r];
+          for (int r = 0; r < 16; r++) {
+            const int m = m_blk + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            // m * ldy + n < kSplitWsFloats = 2^24 floats per split: 24-bit product
+            if (m < a.M && n < a.N)
+              __hip_atomic_store(ws + __umul24((uint32_t)m, (uint32_t)a.ldy) + n, acc[i][j][r],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the stores have completed
+    __syncthreads();
+    __shared__ unsigned last;
+    if (tid == 0)
+      last = __builtin_amdgcn_atomic_inc32(a.cnt + g * gridDim.x + blockIdx.x,
+                                           (unsigned)(a.ksplit - 1), __ATOMIC_RELAXED,
+                                           "agent") == (unsigned)(a.ksplit - 1);
+    __syncthreads();
+    if (!last) return;
+    // the tile's partial sums as 16-byte units (row-major, BN / 4 per row),
+    // all ksplit loads of a unit in flight together; agent-scope loads (sc1)
+    constexpr int kUnits = BM * BN / 4 / NT;
+    static_assert(BM * BN / 4 % NT == 0, "whole units per thread");
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(ws0, 0x7fffffffu);
+    uint16_t* yb = a.y + (CONV ? (int64_t)g * a.Og : (int64_t)g * a.M * a.ldy);
+    auto finish = [&]<int KS>() QMM_INLINE {
+#pragma unroll
+      for (int i = 0; i < kUnits; i++) {
+        const int u = tid + NT * i;
+        const int m = m_blk + u / (BN / 4), n = n_blk + 4 * (u % (BN / 4));
+        const bool in = m < a.M && n < a.N;
+        // (the unit's byte offset in a plane: m * ldy + n < 2^24 floats)
+        const uint32_t off = in ? 4u * (__umul24((uint32_t)m, (uint32_t)a.ldy) + n) : kOob;
+        float4_t v[KS];
+#pragma unroll
+        for (int sp = 0; sp < KS; sp++)
+          v[sp] = __builtin_bit_cast(
+              float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                            pr, off, (uint32_t)(sp * plane * 4), 16));
+        float4_t t = v[0];
+#pragma unroll
+        for (int sp = 1; sp < KS; sp++) t += v[sp];
+        if (in) {
+          uint16_t* yp = yb + (int64_t)m * a.ldy + n;
+          if (n + 4 <= a.N && (reinterpret_cast<uintptr_t>(yp) & 7) == 0) {
+            uint2 o;
+            o.x = (uint32_t)from_f32(T{}, t[0]) | ((uint32_t)from_f32(T{}, t[1]) << 16);
+            o.y = (uint32_t)from_f32(T{}, t[2]) | ((uint32_t)from_f32(T{}, t[3]) << 16);
+            *reinterpret_cast<uint2*>(yp) = o;
+          } else {
+            for (int e = 0; e < 4 && n + e < a.N; e++) yp[e] = from_f32(T{}, t[e]);
+          }
         }
       }
+    };
+    switch (a.ksplit) {
+      case 2: finish.template operator()<2>(); break;
+      case 3: finish.template operator()<3>(); break;
+      case 4: finish.template operator()<4>(); break;
+      case 5: finish.template operator()<5>(); break;
+      case 6: finish.template operator()<6>(); break;
+      case 7: finish.template operator()<7>(); break;
+      default: finish.template operator()<8>(); break;
+    }
     return;
   }
 
@@ -1358,49 +1424,6 @@ static hipError_t launch_dma(GemmArgs a, int groups, hipStream_t st) {
   return hipGetLastError();
 }
 
-// y[m][c] = T(sum over splits of the fp32 partial sums), c < ncols, four
-// columns per thread; SPLITS partial loads per thread are issued together
-template <class T, int SPLITS>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, uint16_t* y, int M,
-                                                            int ncols, int64_t ldy) {
-  const int64_t quads = (int64_t)M * (ncols / 4);
-  const int64_t plane = (int64_t)M * ldy;
-  for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < quads; q += (int64_t)gridDim.x * 256) {
-    const int m = (int)(q / (ncols / 4));
-    const int c = (int)(q - (int64_t)m * (ncols / 4)) * 4;
-    const float* p = ws + (int64_t)m * ldy + c;
-    float4 u[SPLITS];
-#pragma unroll
-    for (int sp = 0; sp < SPLITS; sp++) u[sp] = *reinterpret_cast<const float4*>(p + sp * plane);
-    float4 v = u[0];
-#pragma unroll
-    for (int sp = 1; sp < SPLITS; sp++) {
-      v.x += u[sp].x; v.y += u[sp].y; v.z += u[sp].z; v.w += u[sp].w;
-    }
-    uint2 o;
-    o.x = (uint32_t)from_f32(T{}, v.x) | ((uint32_t)from_f32(T{}, v.y) << 16);
-    o.y = (uint32_t)from_f32(T{}, v.z) | ((uint32_t)from_f32(T{}, v.w) << 16);
-    *reinterpret_cast<uint2*>(y + (int64_t)m * ldy + c) = o;
-  }
-}
-
-template <class T>
-hipError_t launch_splitk_reduce(const GemmArgs& a, int ncols, hipStream_t st) {
-  const int64_t quads = (int64_t)a.M * (ncols / 4);
-  const int blocks = (int)((quads + 255) / 256 < 2048 ? (quads + 255) / 256 : 2048);
-  const dim3 g(blocks), b(256);
-  switch (a.ksplit) {
-    case 2: hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-    case 3: hipLaunchKernelGGL((splitk_reduce_kernel<T, 3>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-    case 4: hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-    case 5: hipLaunchKernelGGL((splitk_reduce_kernel<T, 5>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-    case 6: hipLaunchKernelGGL((splitk_reduce_kernel<T, 6>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-    case 7: hipLaunchKernelGGL((splitk_reduce_kernel<T, 7>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-    default: hipLaunchKernelGGL((splitk_reduce_kernel<T, 8>), g, b, 0, st, a.ws, a.y, a.M, ncols, a.ldy); break;
-  }
-  return hipGetLastError();
-}
-
 // Split-K plan for the 128 x 128 tile kernel: as many splits as keep the
 // workgroups within one wave over the 256 CUs (a second, partial wave costs
 // more than it saves), each split a whole number of 8-step stages, and the
@@ -1436,23 +1459,23 @@ static int splitk_plan(const GemmArgs& a, int64_t tiles, int* ksteps, bool gemm 
   return (nk + per - 1) / per;
 }
 
-// tile kernel over a BM x BN tiling with K split by plan (fp32 partials +
-// reduction when split)
+// tile kernel over a BM x BN tiling with K split by plan (fp32 partial sums,
+// added by the last workgroup of each tile)
 template <class T, int BITS, int BM, int BN, int CONV, int FPM = 0, int APK = 0>
 static hipError_t launch_dma_split(GemmArgs a, int groups, hipStream_t st) {
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   int ksteps = 0;
   a.ksplit = splitk_plan(a, (int64_t)tiles * groups, &ksteps,
                          !CONV && BM == 128 && (__is_same(T, F16) || FPM != 0), CONV ? 1 : groups);
+  if (a.ksplit > 1 && (int64_t)tiles * groups > kTileCntMax) {   // one counter per tile
+    a.ksplit = 1;
+    ksteps = ((a.K + 63) / 64 + kStageSteps - 1) / kStageSteps * kStageSteps;
+  }
   a.ksteps = ksteps;
   constexpr int KW = dma_kw<BM>(), SL = dma_sl<BM, BN>();
   hipLaunchKernelGGL((qmm_dma_kernel<T, BITS, BM, BN, CONV, KW, SL, FPM, APK>),
                      dim3(tiles, a.ksplit, groups), dim3(64 * SL * KW), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ksplit == 1) return e;
-  // every column of y (all conv groups); the batches of a GEMM as consecutive rows
-  if constexpr (!CONV) a.M *= groups;
-  return launch_splitk_reduce<T>(a, (int)a.ldy, st);
+  return hipGetLastError();
 }
 
 template <class T, int BITS, int CONV, bool DMA, int FPM = 0, int APK = 0>
