@@ -486,6 +486,56 @@ def bench_conv(torch, Q, synth, timer, groups, steps, warmup):
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
 
 
+ROUTE_SHAPES = [("f16", 4096, 4096, 4), ("f16", 4096, 4096, 2), ("f16", 4096, 4096, 8),
+                ("f16", 8192, 2048, 4), ("f16", 2048, 8192, 4), ("f16", 512, 2048, 4),
+                ("bf16", 4096, 4096, 4), ("bf16", 4096, 4096, 8), ("bf16", 2048, 8192, 4), ("bf16", 8192, 2048, 4),
+                ("bf16", 2048, 2048, 4), ("bf16", 512, 2048, 4), ("bf16", 2048, 8192, 3),
+                ("bf16", 8192, 2048, 6)]
+ROUTE_MS = (1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32)
+ROUTE_LAUNCHES = 24     # eager launches per (layer, kernel, M), each on its own weight copy
+
+
+def route_table(torch, Q, synth):
+    """Each affine product kernel (streaming GEMV, MFMA GEMV, tile GEMM)
+    forced in turn on the layers above at M = 1..32 rows of x (g64; bf16
+    weights at sigma 0.02), ROUTE_LAUNCHES eager launches per point on
+    distinct copies of the weight from a >= 1 GiB pool, nothing else launched
+    in between (so a kernel trace splits into the points in the order of the
+    printed manifest). Prints the manifest, the automatic choice and the
+    eager per-launch time (HIP events) of each point as one JSON line."""
+    names = {Q.KERNEL_GEMV: "gemv", Q.KERNEL_MFMA_GEMV: "mfma_gemv", Q.KERNEL_TILE: "tile"}
+    gs, rows = 64, []
+    for dt, N, K, bits in ROUTE_SHAPES:
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        layer = make_layer(torch, Q, synth, dt, N, K, gs, bits, 1, 1.0 if dt == "f16" else 0.02)
+        wqs, ss, bs, P = pooled(torch, layer)
+        x = to_dev(synth.normal((max(ROUTE_MS), K), seed=0), dt)
+        y = torch.empty((max(ROUTE_MS), N), dtype=tdt, device="cuda")
+        torch.cuda.synchronize()
+        for kern in (Q.KERNEL_GEMV, Q.KERNEL_MFMA_GEMV, Q.KERNEL_TILE):
+            Q.force_kernel(kern)
+            for M in ROUTE_MS:
+                if Q.route(M, N, K, bits, tdt, gs) != kern:
+                    continue
+                xm, ym = x[:M], y[:M]
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                for i in range(ROUTE_LAUNCHES):
+                    Q.qmm_t(xm, wqs[i % P], ss[i % P], bs[i % P], gs, bits, out=ym)
+                ev1.record()
+                torch.cuda.synchronize()
+                Q.force_kernel(Q.KERNEL_NONE)
+                auto = names[Q.route(M, N, K, bits, tdt, gs)]
+                Q.force_kernel(kern)
+                rows.append({"dt": dt, "N": N, "K": K, "bits": bits, "M": M,
+                             "kernel": names[kern], "auto": auto, "launches": ROUTE_LAUNCHES,
+                             "eager_us": round(ev0.elapsed_time(ev1) * 1e3 / ROUTE_LAUNCHES, 3)})
+        Q.force_kernel(Q.KERNEL_NONE)
+        del wqs, ss, bs, layer
+        torch.cuda.empty_cache()
+    print(json.dumps({"route_table": rows}))
+
+
 def cpu_threads():
     """Threads the oracle runs with on all cores: OMP_NUM_THREADS when set,
     else the CPUs this process may run on."""
@@ -637,6 +687,9 @@ def main():
                     help="run the PMC calibration copy and headline launches, print nothing else")
     ap.add_argument("--mfma-only", action="store_true",
                     help="time only the MFMA tile rows (chained 4-bit layers, conv), for profiling")
+    ap.add_argument("--route-table", action="store_true",
+                    help="force each product kernel in turn at M = 1..32 on the routing layers "
+                         "(for a kernel trace and counters that the route is derived from)")
     ap.add_argument("--next-only", action="store_true",
                     help="time only the gathered, batched, non-transposed and fp-mode rows, "
                          "for profiling")
@@ -655,6 +708,9 @@ def main():
     Q.lib()
     if args.traffic_probe:
         traffic_probe(torch, Q, synth)
+        return
+    if args.route_table:
+        route_table(torch, Q, synth)
         return
     timer = Timer(torch)
     K_, W_ = args.steps, args.warmup

@@ -30,11 +30,15 @@ bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
+bool valid_bits(int bits) {
+  return bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8;
+}
+bool valid_gs(int gs) { return gs == 32 || gs == 64 || gs == 128; }
+
 qmm_status check_bits_gs(int bits, int gs) {
-  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 ||
-        bits == 8))
+  if (!valid_bits(bits))
     return fail(QMM_E_BITS, "bits must be 2, 3, 4, 5, 6 or 8 (got %d)", bits);
-  if (!(gs == 32 || gs == 64 || gs == 128))
+  if (!valid_gs(gs))
     return fail(QMM_E_GROUP, "group_size must be 32, 64 or 128 (got %d)", gs);
   return QMM_OK;
 }
@@ -94,8 +98,37 @@ extern "C" {
 
 const char* qmm_last_error(void) { return g_err; }
 
-int qmm_crossover_m(int bits, qmm_dtype dt) {
-  return qmm::crossover_m(bits, (int)dt);
+int qmm_route(qmm_dtype dt, int bits, int group_size, int64_t M, int64_t N, int64_t K) {
+  if ((dt != QMM_F16 && dt != QMM_BF16) || !valid_bits(bits) || !valid_gs(group_size) ||
+      M < 1 || N < 1 || K < 1 || K % group_size != 0)
+    return QMM_KERNEL_NONE;
+  return (int)qmm::route((int)dt, bits, group_size, M, N, K, true);
+}
+
+int64_t qmm_crossover_m(qmm_dtype dt, int bits, int group_size, int64_t N, int64_t K) {
+  // route() is a step function of M for fixed (dt, bits, group_size, N, K):
+  // the GEMVs up to some M, the tile kernel from there on
+  for (int64_t M = 1; M <= ((int64_t)1 << 20); M = M < 64 ? M + 1 : 2 * M) {
+    const int r = qmm_route(dt, bits, group_size, M, N, K);
+    if (r == QMM_KERNEL_NONE) return 0;
+    if (r == QMM_KERNEL_TILE) {
+      if (M <= 64) return M;
+      int64_t lo = M / 2, hi = M;   // route(lo) is a GEMV, route(hi) the tile kernel
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        (qmm_route(dt, bits, group_size, mid, N, K) == QMM_KERNEL_TILE ? hi : lo) = mid;
+      }
+      return hi;
+    }
+  }
+  return 0;
+}
+
+qmm_status qmm_force_kernel(int kernel) {
+  if (kernel < QMM_KERNEL_NONE || kernel > QMM_KERNEL_TILE)
+    return fail(QMM_E_ARG, "qmm_force_kernel: kernel %d is not one of QMM_KERNEL_*", kernel);
+  qmm::force_route((qmm::Route)kernel);
+  return QMM_OK;
 }
 
 qmm_status qmm_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,

@@ -47,13 +47,17 @@ inline QmvMfmaPlan qmv_mfma_plan(int64_t N, int64_t K) {
   const int64_t klen = sps * 128 < K ? sps * 128 : K;
   return {(int)ks, (int)sps, (int)klen};
 }
-size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs);
-inline bool qmv_mfma_fits(int64_t M, int64_t N, int64_t K, int gs) {
+// the MFMA GEMV multiplies the codes themselves (bf16, 4- and 8-bit codes)
+// and keeps the group sums of x in LDS
+inline bool qmv_mfma_exact(int dt, int bits) { return dt == 1 && (bits == 4 || bits == 8); }
+size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs, bool xsums);
+inline bool qmv_mfma_fits(int64_t M, int64_t N, int64_t K, int gs, int dt, int bits) {
   if (M < 1 || M > kQmvMfmaMaxM || K >= kQmvMfmaMaxK) return false;
   const QmvMfmaPlan p = qmv_mfma_plan(N, K);
   // the workgroup's 1024 threads copy x with at most 8 16-byte loads each,
   // the scales and biases with at most 2
-  return qmv_mfma_lds(M, p.klen, K, gs) <= kQmvMfmaMaxLds && M * (p.klen / 8) <= 8 * 1024 &&
+  return qmv_mfma_lds(M, p.klen, K, gs, qmv_mfma_exact(dt, bits)) <= kQmvMfmaMaxLds &&
+         M * (p.klen / 8) <= 8 * 1024 &&
          (15 + 32 * (K / gs) + 15) / 16 <= 2 * 1024;
 }
 // Non-transposed GEMV: y[M,N] = x[M,K] . dequant(W[K,N]) with W quantized
@@ -161,21 +165,19 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
                              const void* s, const void* b, void* y,
                              hipStream_t st);
 
-// Kernel choice for y = x . dequant(W)^T (measured on MI355X, 4096-wide
-// layers): the MFMA GEMV up to 16 rows when x fits in LDS, for f16 from
-// M = 3 (and M <= 2 when K > 8192 on N >= 4096: long rows make the
-// streaming GEMV's passes slow), for bf16 from M = 4 (any M for 8-bit
-// codes); the
-// streaming dot2 GEMV for a few rows otherwise; the MFMA tile kernel for the
-// rest. qmv never takes the tile kernel (kRouteNone when neither GEMV
-// accepts the shape).
+// Kernel choice for y = x . dequant(W)^T, from measured kernel times (see
+// route()): the streaming dot2 GEMV for a row or two of x (and for up to 32
+// rows of small layers), the MFMA GEMV for up to 16 rows, the MFMA tile
+// kernel for the rest. qmv never takes the tile kernel (kRouteNone when
+// neither GEMV accepts the shape).
 enum Route { kRouteNone = 0, kRouteQmv = 1, kRouteQmvMfma = 2, kRouteTile = 3 };
 Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allow_tile);
 
 // Largest K the streaming dot2 GEMV stages in LDS.
 int64_t qmv_max_k(int bits, int dt);
 
-// Smallest M routed to the MFMA tile kernel by qmm_t for K <= 4096.
-int crossover_m(int bits, int dt);
+// Measurement override: route() returns r wherever that kernel takes the
+// shape (kRouteNone: the automatic choice everywhere).
+void force_route(Route r);
 
 }  // namespace qmm

@@ -2,6 +2,7 @@
 // packing, the split-K workspace, and the routing between the GEMV kernels
 // and the tile kernels (kernels in tile_impl.hpp, instantiated by
 // tile_gemm_{f16,bf16}.hip and tile_conv_{f16,bf16}.hip).
+#include <atomic>
 #include <mutex>
 
 #include "common.hpp"
@@ -167,11 +168,11 @@ hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
 
 // The GEMV kernels' share of small M (see route()): up to 16 rows on the
 // MFMA GEMV when x fits in LDS (K <= 4096 at 16 rows).
-int crossover_m(int bits, int dt) {
-  (void)bits;
-  (void)dt;
-  return kQmvMfmaMaxM + 1;
-}
+namespace {
+std::atomic<int> g_forced{kRouteNone};   // measurement override (force_route)
+}  // namespace
+
+void force_route(Route r) { g_forced.store((int)r, std::memory_order_relaxed); }
 
 int64_t qmv_max_k(int bits, int dt) {
   const int64_t words = (bits == 8 && dt == 1) ? 34 : 18;
@@ -180,16 +181,41 @@ int64_t qmv_max_k(int bits, int dt) {
 
 Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allow_tile) {
   const bool dot2_ok = K <= qmv_max_k(bits, dt);
-  const bool mfma_ok = qmv_mfma_fits(M, N, K, gs);
-  if (dt == 0 && mfma_ok && (M >= 3 || (K > 8192 && N >= 4096) || !dot2_ok)) return kRouteQmvMfma;
-  // bf16 dequantizes in fp32 and multiplies hi and lo halves: worth it from
-  // 4 rows, and always for 8-bit codes, which the streaming GEMV handles in
-  // fp32
-  if (dt == 1 && mfma_ok && (M >= 4 || bits == 8 || !dot2_ok)) return kRouteQmvMfma;
+  const bool mfma_ok = qmv_mfma_fits(M, N, K, gs, dt, bits);
+  switch (g_forced.load(std::memory_order_relaxed)) {
+    case kRouteQmv: if (dot2_ok) return kRouteQmv; break;
+    case kRouteQmvMfma: if (mfma_ok) return kRouteQmvMfma; break;
+    case kRouteTile: if (allow_tile) return kRouteTile; break;
+    default: break;
+  }
+  // Switch points from kernel-only times of the three kernels forced at
+  // M = 1..32 (rocprofv3 kernel trace, g64, f16 and bf16 layers from
+  // [512, 2048] to [8192, 2048]; cold weights):
+  //  * the streaming GEMV reads W once per pass of up to 4 rows of x and
+  //    costs ~5 us at M = 1 on a 9.4 MB layer, ~7 at 2 and ~10 at 3-4; the
+  //    MFMA GEMV is nearly flat in M (6.9-8.0 us f16, 8.5-9.6 bf16 on
+  //    4096 x 4096) but slow at M = 1, and slower on layers of >= 512 blocks
+  //    of 16 rows, which it runs in two rounds (8.3-9.8 us on 8192 x 2048);
+  //  * bf16 with 8-bit codes: the streaming GEMV works in fp32 (33 us at
+  //    M = 1), so the MFMA GEMV takes every M it fits;
+  //  * the tile kernel costs 9-12 us at M <= 32 whatever the layer size, so
+  //    layers of at most 2^22 weights, whose streaming passes take ~1 us,
+  //    stay on the streaming GEMV up to 32 rows.
+  const bool gemv_fp32 = dt == 1 && bits == 8;
+  int64_t m0;   // first M on the MFMA GEMV
+  if (gemv_fp32 || !dot2_ok) m0 = 1;
+  else if (dt == 0 && K > 8192 && N >= 4096) m0 = 1;   // long rows: few streaming passes fit
+  else if (dt == 0) m0 = (N < 8192 && N * K >= ((int64_t)1 << 23)) ? 2 : 3;
+  else m0 = N >= 8192 ? 5 : 3;
+  if (mfma_ok && M >= m0) return kRouteQmvMfma;
   if (!allow_tile) return dot2_ok ? kRouteQmv : kRouteNone;
-  // the MFMA GEMV does not take the shape: a few rows on the streaming GEMV
-  // (one pass over W per 4 rows at K = 4096), the rest on the tile kernel
-  if (M < (dt == 0 ? 4 : 8) && dot2_ok) return kRouteQmv;
+  if (dot2_ok) {
+    if (M < m0) return kRouteQmv;
+    // the MFMA GEMV does not take the shape (more than 16 rows, or x too
+    // long for LDS): a few rows, or a small layer, on the streaming GEMV
+    if (M < (dt == 0 ? 4 : 8)) return kRouteQmv;
+    if (!gemv_fp32 && M <= 32 && N * K <= ((int64_t)1 << 22)) return kRouteQmv;
+  }
   return kRouteTile;
 }
 

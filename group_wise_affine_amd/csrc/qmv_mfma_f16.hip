@@ -44,11 +44,12 @@ hipError_t launch_qmv_mfma_bf16(int bits, const MvLaunch& L, hipStream_t st);
 
 // LDS of the GEMV kernel: rows of x over a K range of klen plus padding and
 // the 16 rows of scales and biases, or the reduction buffer if larger
-size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs) {
+size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs, bool xsums) {
   const size_t xb = (((size_t)M * (klen + 8) + 7) & ~(size_t)7) * 2;
   const size_t sb = (size_t)2 * 16 * ((15 + 32 * (K / gs) + 15) / 16);
+  const size_t gb = xsums ? (size_t)((klen + gs - 1) / gs) * 16 * 4 : 0;   // group sums of x
   const size_t rb = (size_t)kMvThreads * 4 * 4;
-  return xb + sb > rb ? xb + sb : rb;
+  return xb + sb + gb > rb ? xb + sb + gb : rb;
 }
 
 hipError_t launch_qmv_mfma(int dt, int bits, int gs, const void* x, const uint32_t* wq,

@@ -15,9 +15,21 @@
 //    v_mfma_f32_16x16x32_{f16,bf16}: MFMA i takes codes 8i..8i+7 of the four
 //    chunks, so A lane (m, g) holds the matching 8 elements of row m of x in
 //    natural order (rows m >= M stay zero). f16: magic pairs and packed f16
-//    FMAs, one rounding of s*q+b. bf16: s*q+b in fp32 split into
-//    hi = bf16(w) and lo = bf16(w - hi), both multiplied (a single bf16
-//    rounding of the weights would cost ~1e-3 relative error).
+//    FMAs, one rounding of s*q+b. bf16 with 2, 3, 5 or 6 bits: s*q+b in
+//    fp32 split into hi = bf16(w) and lo = bf16(w - hi), both multiplied (a
+//    single bf16 rounding of the weights would cost ~1e-3 relative error).
+//  * bf16 with 4- or 8-bit codes (exact codes): the MFMA multiplies the
+//    codes themselves, which bf16 holds exactly, and the affine map is
+//    applied per group to the fp32 result, sum_k x (s q + b) = s sum_k x q +
+//    b sum_k x. For that every MFMA must stay inside one group: the four
+//    lanes of a row exchange their chunks' 8-code pieces (a 4 x 4 transpose
+//    across the wavefront's 16-lane rows with v_permlane32_swap and
+//    v_permlane16_swap), so that MFMA i takes chunk i of the step. 4-bit
+//    codes become bf16 128 + q by or-ing them into the mantissa of 128 (two
+//    per instruction, codes k and k + 4 of the piece, so x is staged with
+//    each 8-element piece in that order), 8-bit codes go through fp32; the
+//    128 is taken back with b - 128 s. The group sums of x are formed once
+//    per workgroup in LDS.
 //  * The workgroup copies x[0:M] and the scales and biases of its 16 rows
 //    into LDS once, with coalesced loads issued ahead of the weight loads; A
 //    fragments, scales and biases are read from there. The number of vector
@@ -106,6 +118,7 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem4);
   float* red = reinterpret_cast<float*>(smem4);
 
+  constexpr bool kExact = __is_same(T, BF16) && (BITS == 4 || BITS == 8);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -220,7 +233,13 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < kMvMaxXu; i++) {
     const int u = tid + kMvThreads * i;
-    if (i < xu && u < xunits) *reinterpret_cast<uint4*>(xs + xlds[i]) = xl[i];
+    uint4 v = xl[i];
+    if constexpr (kExact && BITS == 4)   // piece order 0 4 1 5 2 6 3 7
+      v = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                     __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                     __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                     __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+    if (i < xu && u < xunits) *reinterpret_cast<uint4*>(xs + xlds[i]) = v;
   }
 #pragma unroll
   for (int i = 0; i < kMvMaxSb; i++) {
@@ -232,7 +251,97 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   }
   __syncthreads();
 
+  // exact codes: xg[gl][m] = sum of x[m] over group gl of the split's range
+  // (16 rows, rows >= M zero), after the scales and biases
+  float* xg = reinterpret_cast<float*>(bs4 + sbun);
+  if constexpr (kExact) {
+    const int ngl = (klen + (1 << gs_log2) - 1) >> gs_log2;
+    for (int t = tid; t < ngl * 16; t += kMvThreads) {
+      const int m = t & 15, gl = t >> 4;
+      float sum = 0.0f;
+      if (m < M) {
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + m * ldx + (gl << gs_log2));
+        for (int u = 0; u < (1 << gs_log2) / 8; u++) {
+          const uint4 v = xp[u];
+          sum += (__builtin_bit_cast(float, v.x << 16) + __builtin_bit_cast(float, v.x & 0xffff0000u)) +
+                 (__builtin_bit_cast(float, v.y << 16) + __builtin_bit_cast(float, v.y & 0xffff0000u)) +
+                 (__builtin_bit_cast(float, v.z << 16) + __builtin_bit_cast(float, v.z & 0xffff0000u)) +
+                 (__builtin_bit_cast(float, v.w << 16) + __builtin_bit_cast(float, v.w & 0xffff0000u));
+        }
+      }
+      xg[t] = sum;
+    }
+    __syncthreads();
+  }
+
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // exact codes: chunk i of the step on MFMA i (see the header), groups of
+  // gs codes applied to the fp32 sums as s * D + (b - 128 s) * sum(x)
+  auto compute_exact = [&](int j, int d) QMM_INLINE {
+    const int cs = c0 + 4 * (wave + kMvWaves * j);   // the step's first chunk
+    uint32_t t[BITS];
+#pragma unroll
+    for (int q = 0; q < BITS; q++) t[q] = wv[d][q];
+    // 4 x 4 transpose of 8-code pieces across the 16-lane rows g: row g held
+    // chunk g's pieces 0..3, it gets piece g of chunks 0..3 (per word of a
+    // piece: W = BITS / 4 words)
+    constexpr int W = BITS / 4;
+#pragma unroll
+    for (int w = 0; w < W; w++) {
+      auto r = __builtin_amdgcn_permlane32_swap(t[w], t[2 * W + w], false, false);
+      t[w] = r[0]; t[2 * W + w] = r[1];
+      r = __builtin_amdgcn_permlane32_swap(t[W + w], t[3 * W + w], false, false);
+      t[W + w] = r[0]; t[3 * W + w] = r[1];
+      r = __builtin_amdgcn_permlane16_swap(t[w], t[W + w], false, false);
+      t[w] = r[0]; t[W + w] = r[1];
+      r = __builtin_amdgcn_permlane16_swap(t[2 * W + w], t[3 * W + w], false, false);
+      t[2 * W + w] = r[0]; t[3 * W + w] = r[1];
+    }
+    const int cpg_log2 = gs_log2 - 5;                // chunks per group: 1, 2, 4
+    float4_t dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int c = cs + i;
+      const int cx = c < c1 ? c : c1 - 1;
+      uint4 a = make_uint4(0, 0, 0, 0);
+      if (n < M) a = *reinterpret_cast<const uint4*>(xs + n * ldx + (cx - c0) * 32 + 8 * g);
+      uint4 b;
+      if constexpr (BITS == 4) {
+        const uint32_t w = t[i];
+        b = make_uint4((w & 0x000f000fu) | 0x43004300u, ((w >> 4) & 0x000f000fu) | 0x43004300u,
+                       ((w >> 8) & 0x000f000fu) | 0x43004300u,
+                       ((w >> 12) & 0x000f000fu) | 0x43004300u);
+      } else {
+        uint32_t p[4];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const uint32_t w = t[2 * i + h];
+          const float f0 = (float)(w & 0xff), f1 = (float)((w >> 8) & 0xff),
+                      f2 = (float)((w >> 16) & 0xff), f3 = (float)(w >> 24);
+          p[2 * h] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                                           __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+          p[2 * h + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
+                                               __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+        }
+        b = make_uint4(p[0], p[1], p[2], p[3]);
+      }
+      dsum = mfma16(BF16{}, a, b, dsum);
+      if (((i + 1) & ((1 << cpg_log2) - 1)) == 0) {
+        // end of a group: its scale and bias (zero past the split's end)
+        const uint32_t keep = ~(uint32_t)((c1 - 1 - c) >> 31);
+        const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
+        const float sf = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(ssb + gi) & keep));
+        const float bfl = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(bsb + gi) & keep));
+        const float bq = bfl - 128.0f * sf * (BITS == 4 ? 1.0f : 0.0f);
+        const float4_t xsum = *reinterpret_cast<const float4_t*>(
+            xg + ((((cx - c0) << 5) >> gs_log2) << 4) + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc[e] += sf * dsum[e] + bq * xsum[e];
+        dsum = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+  };
+
   auto compute = [&](int j, int d) QMM_INLINE {
     // A fragments: lane (m, g) = (n, g) takes 8 elements of row m of x
     // (rows m >= M stay zero); the chunk is clamped into the row (a chunk
@@ -281,10 +390,14 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     }
   };
 
+  auto step = [&](int j, int d) QMM_INLINE {
+    if constexpr (kExact) compute_exact(j, d);
+    else compute(j, d);
+  };
   if constexpr (!RING) {
 #pragma unroll
     for (int d = 0; d < DEPTH; d++) {
-      compute(d, d);
+      step(d, d);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -295,7 +408,7 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     do {
 #pragma unroll
       for (int d = 0; d < DEPTH; d++) {
-        compute(r * DEPTH + d, d);
+        step(r * DEPTH + d, d);
         __builtin_amdgcn_sched_barrier(0);
         issue((r + 1) * DEPTH + d, d);
         load_fence();
@@ -357,7 +470,7 @@ hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st)
   const int xu = (L.M * (p.klen / 8) + kMvThreads - 1) / kMvThreads;
   const int sbu = ((15 + 32 * (L.K / L.gs) + 15) / 16 + kMvThreads - 1) / kMvThreads;
   hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING>), dim3((L.N + 15) / 16, p.ks),
-                     dim3(kMvThreads), qmv_mfma_lds(L.M, p.klen, L.K, L.gs), st,
+                     dim3(kMvThreads), qmv_mfma_lds(L.M, p.klen, L.K, L.gs, __is_same(T, BF16) && (BITS == 4 || BITS == 8)), st,
                      static_cast<const uint16_t*>(L.x), reinterpret_cast<const uint8_t*>(L.wq),
                      static_cast<const uint16_t*>(L.s), static_cast<const uint16_t*>(L.b),
                      static_cast<uint16_t*>(L.y), L.M, L.N, L.K, ilog2(L.gs), m2, xu, sbu, p.ks,

@@ -16,14 +16,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
 QMM_OK, QMM_E_NULL, QMM_E_BITS, QMM_E_GROUP, QMM_E_SHAPE, QMM_E_DTYPE, \
-    QMM_E_ALIGN, QMM_E_LAUNCH = range(8)
+    QMM_E_ALIGN, QMM_E_LAUNCH, QMM_E_ARG = range(9)
 STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
-                "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH"]
+                "QMM_E_SHAPE", "QMM_E_DTYPE", "QMM_E_ALIGN", "QMM_E_LAUNCH", "QMM_E_ARG"]
+# kernels of the affine products (qmm_route, force_kernel)
+KERNEL_NONE, KERNEL_GEMV, KERNEL_MFMA_GEMV, KERNEL_TILE = range(4)
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
            "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
            "qmm_affine_pack", "qmv_affine_packed", "qmm_t_affine_packed",
-           "qmm_crossover_m", "qmm_last_error"]
+           "qmm_crossover_m", "qmm_route", "qmm_force_kernel", "qmm_last_error"]
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
 
@@ -32,7 +34,7 @@ _lib = None
 
 class QmmError(RuntimeError):
     def __init__(self, status, msg):
-        super().__init__(f"{STATUS_NAMES[status] if 0 <= status < 8 else status}: {msg}")
+        super().__init__(f"{STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else status}: {msg}")
         self.status = status
 
 
@@ -73,8 +75,12 @@ def lib():
                   "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
                   "qmm_affine_pack", "qmv_affine_packed", "qmm_t_affine_packed"):
             getattr(L, f).restype = i32
-        L.qmm_crossover_m.argtypes = [i32, i32]
-        L.qmm_crossover_m.restype = i32
+        L.qmm_crossover_m.argtypes = [i32, i32, i32, i64, i64]
+        L.qmm_crossover_m.restype = i64
+        L.qmm_route.argtypes = [i32, i32, i32, i64, i64, i64]
+        L.qmm_route.restype = i32
+        L.qmm_force_kernel.argtypes = [i32]
+        L.qmm_force_kernel.restype = i32
         L.qmm_last_error.argtypes = []
         L.qmm_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -487,5 +493,16 @@ def quantize_conv_weight(w, group_size=64, bits=4, stream=None):
     return qmm_quantize(conv_weight_matrix(w, group_size), group_size, bits, stream=stream)
 
 
-def crossover_m(bits, dtype=torch.float16):
-    return lib().qmm_crossover_m(bits, _dt(dtype))
+def crossover_m(bits, dtype=torch.float16, N=4096, K=4096, group_size=64):
+    """Smallest M at which qmm_t runs the MFMA tile kernel for an [N, K] layer."""
+    return lib().qmm_crossover_m(_dt(dtype), bits, group_size, N, K)
+
+
+def route(M, N, K, bits=4, dtype=torch.float16, group_size=64):
+    """Kernel qmm_t runs for the shape: KERNEL_GEMV, KERNEL_MFMA_GEMV or KERNEL_TILE."""
+    return lib().qmm_route(_dt(dtype), bits, group_size, M, N, K)
+
+
+def force_kernel(kernel):
+    """Measurement: run `kernel` wherever the shape fits it (KERNEL_NONE: automatic)."""
+    _check(lib().qmm_force_kernel(kernel))

@@ -78,7 +78,8 @@ typedef enum {
   QMM_E_SHAPE = 4,  /* a size < 1, K % group_size != 0, or bad conv geometry */
   QMM_E_DTYPE = 5,  /* element type not supported by this call */
   QMM_E_ALIGN = 6,  /* a pointer violates the alignment rules above */
-  QMM_E_LAUNCH = 7  /* the kernel launch itself failed (hipGetLastError) */
+  QMM_E_LAUNCH = 7, /* the kernel launch itself failed (hipGetLastError) */
+  QMM_E_ARG = 8     /* an argument outside its documented set of values */
 } qmm_status;
 
 /*
@@ -112,8 +113,8 @@ qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
  * y[M,N] = x[M,K] . dequant(wq, scales, biases)[N,K]^T, fp32 accumulation,
  * y rounded to nearest even in dt (f16 or bf16). Routes small M to the GEMV
  * kernels of qmv (the MFMA GEMV up to 16 rows, the streaming GEMV for a
- * few rows) and larger M to the MFMA tile kernel; the crossover is returned
- * by qmm_crossover_m. (Source: mlx 1.0.0 CPU backend, _qmm_t;
+ * few rows) and larger M to the MFMA tile kernel; qmm_route names the
+ * kernel for a shape and qmm_crossover_m the first M on the tile kernel. (Source: mlx 1.0.0 CPU backend, _qmm_t;
  * the packed-quants compare, the qmv/qmm_t split in the Metal dispatch.)
  */
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
@@ -375,11 +376,39 @@ qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
                         void* y, void* stream);
 
 /*
- * Smallest M for which qmm_t uses the MFMA tile kernel instead of the GEMV
- * kernels, for layers whose rows of x fit the MFMA GEMV's LDS (K <= 4096 at
- * 16 rows); longer rows leave the GEMV kernels earlier.
+ * Kernels of the affine products (qmm_t, qmv, qmm_t_batched, the packed
+ * layout's entry points): which one runs is a function of (dt, bits,
+ * group_size, M, N, K) only. (Source: the qmv / qmm_t split of "Add the
+ * 3bit packed qmm_t", affine_packed_qmm_op, which switches at a fixed row
+ * count; here the switch points come from measured kernel times.)
  */
-int qmm_crossover_m(int bits, qmm_dtype dt);
+#define QMM_KERNEL_NONE 0       /* no kernel takes the shape */
+#define QMM_KERNEL_GEMV 1       /* streaming dot2 GEMV (x staged in LDS) */
+#define QMM_KERNEL_MFMA_GEMV 2  /* MFMA GEMV, at most 16 rows of x */
+#define QMM_KERNEL_TILE 3       /* MFMA tile GEMM */
+
+/*
+ * The kernel qmm_t runs for this shape (QMM_KERNEL_*; QMM_KERNEL_NONE for
+ * invalid bits/group sizes or non-positive sizes). Host only, no GPU call.
+ */
+int qmm_route(qmm_dtype dt, int bits, int group_size, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Smallest M (>= 1) at which qmm_t runs the MFMA tile kernel for an [N, K]
+ * layer, i.e. where it leaves the GEMV kernels (0 when it never does below
+ * 2^20 rows). Host only.
+ */
+int64_t qmm_crossover_m(qmm_dtype dt, int bits, int group_size, int64_t N, int64_t K);
+
+/*
+ * For measurement: from now on, in this process, qmm_t, qmv and
+ * qmm_t_batched run `kernel` (QMM_KERNEL_GEMV, _MFMA_GEMV or _TILE) for every
+ * shape that kernel takes (qmv never runs the tile kernel) and the automatic
+ * choice otherwise; QMM_KERNEL_NONE restores the automatic choice
+ * everywhere. Not synchronised with calls in flight on other threads.
+ * Returns QMM_E_ARG for other values.
+ */
+qmm_status qmm_force_kernel(int kernel);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char* qmm_last_error(void);

@@ -147,10 +147,50 @@ def test_conv_geometry(L):
     assert conv(B=0) == Q.QMM_E_SHAPE
 
 
-def test_crossover_is_positive(L):
-    for bits in (2, 3, 4, 5, 6, 8):
-        for dt in (0, 1):
-            assert L.qmm_crossover_m(bits, dt) >= 1
+SHAPES = [(4096, 4096), (2048, 8192), (8192, 2048), (512, 2048), (4096, 11008), (64, 16384),
+          (4096, 32768)]
+
+
+def test_route_is_a_step_function_of_m(L):
+    """Host-only routing: for a fixed layer, qmm_t runs GEMV kernels up to
+    some M and the tile kernel from there on; qmm_crossover_m reports that M."""
+    for dt in (0, 1):
+        for bits in (2, 3, 4, 5, 6, 8):
+            for gs in (32, 64, 128):
+                for (N, K) in SHAPES:
+                    rs = [L.qmm_route(dt, bits, gs, M, N, K) for M in range(1, 129)]
+                    assert all(r in (Q.KERNEL_GEMV, Q.KERNEL_MFMA_GEMV, Q.KERNEL_TILE) for r in rs)
+                    first = rs.index(Q.KERNEL_TILE) + 1 if Q.KERNEL_TILE in rs else None
+                    assert first is not None, (dt, bits, gs, N, K)
+                    assert all(r == Q.KERNEL_TILE for r in rs[first - 1:]), (dt, bits, gs, N, K)
+                    assert L.qmm_crossover_m(dt, bits, gs, N, K) == first
+                    # the MFMA GEMV never takes more than 16 rows
+                    assert all(r != Q.KERNEL_MFMA_GEMV for r in rs[16:])
+
+
+def test_route_rejects_invalid_arguments(L):
+    assert L.qmm_route(0, 7, 64, 1, 64, 64) == Q.KERNEL_NONE
+    assert L.qmm_route(0, 4, 48, 1, 64, 96) == Q.KERNEL_NONE
+    assert L.qmm_route(2, 4, 64, 1, 64, 64) == Q.KERNEL_NONE   # f32 products do not exist
+    assert L.qmm_route(0, 4, 64, 0, 64, 64) == Q.KERNEL_NONE
+    assert L.qmm_route(0, 4, 64, 1, 64, 96) == Q.KERNEL_NONE   # K % group_size
+    assert L.qmm_crossover_m(0, 7, 64, 64, 64) == 0
+
+
+def test_force_kernel(L):
+    try:
+        assert L.qmm_force_kernel(4) == Q.QMM_E_ARG
+        assert L.qmm_force_kernel(-1) == Q.QMM_E_ARG
+        assert L.qmm_force_kernel(Q.KERNEL_TILE) == Q.QMM_OK
+        assert L.qmm_route(0, 4, 64, 1, 4096, 4096) == Q.KERNEL_TILE
+        assert L.qmm_force_kernel(Q.KERNEL_MFMA_GEMV) == Q.QMM_OK
+        assert L.qmm_route(0, 4, 64, 1, 4096, 4096) == Q.KERNEL_MFMA_GEMV
+        assert L.qmm_route(0, 4, 64, 17, 4096, 4096) == Q.KERNEL_TILE   # does not fit: automatic
+        assert L.qmm_force_kernel(Q.KERNEL_GEMV) == Q.QMM_OK
+        assert L.qmm_route(0, 4, 64, 64, 4096, 4096) == Q.KERNEL_GEMV
+    finally:
+        assert L.qmm_force_kernel(Q.KERNEL_NONE) == Q.QMM_OK
+    assert L.qmm_route(0, 4, 64, 64, 4096, 4096) == Q.KERNEL_TILE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -319,9 +319,9 @@ def test_qmm_t_split_k(orc, M, N, K, gs, bits):
 def test_qmm_t_skinny(orc, M, N, K, gs, bits):
     """At most 32 rows above the crossover: 32-row tiles, K split over
     workgroups when the output has few tiles."""
-    M = max(M, Q.crossover_m(bits, torch.float16))
+    M = max(M, Q.crossover_m(bits, torch.float16, N, K, gs))
     _run_mm(Q.qmm_t, orc, "f16", M, N, K, gs, bits, seed=K + M)
-    M = max(M, Q.crossover_m(bits, torch.bfloat16))
+    M = max(M, Q.crossover_m(bits, torch.bfloat16, N, K, gs))
     _run_mm(Q.qmm_t, orc, "bf16", M, N, K, gs, bits, seed=K + M + 1)
 
 
@@ -370,7 +370,7 @@ def test_tile_reads_only_landed_copies(orc, M, N, K, bits):
 
 def test_qmm_t_routes_consistently(orc):
     """Around the crossover both kernels agree with the oracle."""
-    mx = Q.crossover_m(4)
+    mx = Q.crossover_m(4, torch.float16, 96, 512, 64)
     for M in (mx - 1, mx, mx + 1):
         if M >= 1:
             _run_mm(Q.qmm_t, orc, "f16", M, 96, 512, 64, 4, seed=M)
