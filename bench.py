@@ -408,9 +408,10 @@ def bench_batched(torch, Q, synth, timer, steps, warmup, B, M, N=4096, K=4096, b
 
 
 def bench_qmm_n(torch, Q, synth, timer, steps, warmup, M=1, K=4096, N=4096, bits=4, gs=64):
-    """Non-transposed decode product y = x . dequant(W), W [K, N] quantized
-    along N (4-bit g64, f16); every step reads a different copy of W from a
-    >= 1 GiB pool."""
+    """Non-transposed product y = x . dequant(W), x f16 [M, K], W [K, N]
+    quantized along N (4-bit g64, f16): the GEMV at M = 1, the MFMA tile
+    kernel at M = 1024; every step reads a different copy of W from a >= 1 GiB
+    pool."""
     w = to_dev(synth.normal((K, N), seed=1), "f16")
     layer = Q.qmm_quantize(w, gs, bits)
     del w
@@ -422,8 +423,11 @@ def bench_qmm_n(torch, Q, synth, timer, steps, warmup, M=1, K=4096, N=4096, bits
     nbytes = alg_bytes(M, N, K, bits, gs)
     del wqs, ss, bs
     torch.cuda.empty_cache()
+    flops = 2 * M * N * K
     return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+            "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "pool_copies": P, "workload": f"x f16 [{M},{K}], W [{K},{N}] {bits}-bit g{gs} along N"}
 
 
@@ -725,7 +729,8 @@ def main():
         r = {"gather_qmv_moe_decode": bench_gather(torch, Q, synth, timer, 200, 20),
              "gather_qmm_moe_prefill": bench_gather_prefill(torch, Q, synth, timer, 20, 5),
              "qmm_t_batched_B4_M256": bench_batched(torch, Q, synth, timer, 20, 5, 4, 256),
-             "qmm_n_decode": bench_qmm_n(torch, Q, synth, timer, 200, 20)}
+             "qmm_n_decode": bench_qmm_n(torch, Q, synth, timer, 200, 20),
+             "qmm_n_prefill_M1024": bench_qmm_n(torch, Q, synth, timer, 20, 5, M=1024)}
         for name, bits, gs in (("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)):
             r[f"fp_qmv_{name}"] = bench_fp(torch, Q, synth, timer, 200, 20, bits, gs)
         r["fp_gather_qmv_moe_decode_mxfp4"] = bench_fp_gather(torch, Q, synth, timer, 200, 20)
@@ -770,6 +775,8 @@ def main():
         rows["qmm_n_decode_4096x4096_f16_g64"] = {
             k: round(v, 4) if isinstance(v, float) else v
             for k, v in bench_qmm_n(torch, Q, synth, timer, n_small, 20).items()}
+        rows["qmm_n_prefill_1024x4096x4096_f16_g64"] = round_rows(
+            bench_qmm_n(torch, Q, synth, timer, 20, 5, M=1024))
         log("qmm_n row done")
         rows["qmm_t_batched_4096x4096_f16_g64"] = {
             f"B{B}_M{M}": {k: round(v, 4) if isinstance(v, float) else v

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libqmm.so")
 CEILING_LIB = os.path.join(HERE, "libqmm_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "quantize.hip", "qmv.hip", "qmn.hip", "fpq.hip", "apk.hip", "qmv_mfma_f16.hip", "qmv_mfma_bf16.hip", "qmm.hip",
+SOURCES = ["api.cpp", "quantize.hip", "qmv.hip", "qmn.hip", "qmn_tile.hip", "fpq.hip", "apk.hip", "qmv_mfma_f16.hip", "qmv_mfma_bf16.hip", "qmm.hip",
            "tile_gemm_f16.hip", "tile_gemm_bf16.hip", "tile_conv_f16.hip", "tile_conv_bf16.hip",
            "tile_fp.hip", "tile_apk.hip"]
 FLAGS = [

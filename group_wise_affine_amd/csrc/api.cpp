@@ -300,6 +300,11 @@ qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const vo
     return fail(QMM_E_ALIGN, "qmm_n: x, wq and y must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(biases, 2))
     return fail(QMM_E_ALIGN, "qmm_n: scales and biases must be 2-byte aligned");
+  // many rows of x: the MFMA tile kernel (one pass over W per 128 rows)
+  if (qmm::qmm_n_tile_fits((int)dt, M, N, K, bits))
+    return launched(qmm::launch_qmm_n_tile((int)dt, bits, group_size, x, wq, scales, biases, M, N,
+                                           K, y, (hipStream_t)stream),
+                    "qmm_n");
   if (M > chunk && ((chunk * K * 2) % 16 != 0 || (chunk * N * 2) % 16 != 0))
     return fail(QMM_E_ALIGN,
                 "qmm_n: with more than %lld rows of x the rows are taken %lld at a time, whose "

@@ -68,8 +68,23 @@ int64_t qmm_n_splits(int64_t K);
 hipError_t launch_qmm_n(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                         const void* s, const void* b, int64_t M, int64_t N, int64_t K, void* y,
                         hipStream_t st);
-// the current device's split-K workspace (a static device array), or null
+// the current device's split-K workspace and the tile kernels' per-tile
+// arrival counters (static device arrays), or null
 float* splitk_workspace();
+unsigned* tile_counters();
+// Non-transposed product on the MFMA tile kernel (many rows of x, K split
+// over workgroups when the output has few tiles), for K % 8 == 0 (16-byte x
+// units) and W below 2 GiB, from 5 rows of x for f16 and 7 for bf16: the GEMV
+// reads W once per row (4096 x 4096 4-bit: 9.7 / 15.5 / 19.3 us at M = 1 / 4
+// / 6), the tile kernel once per 128 rows with K split (17.0 us at M = 8,
+// 84 us at M = 1024; bf16 20.7 us at M = 8).
+inline bool qmm_n_tile_fits(int dt, int64_t M, int64_t N, int64_t K, int bits) {
+  return M >= (dt == 0 ? 5 : 7) && K % 8 == 0 && N * K * bits / 8 < ((int64_t)1 << 31) &&
+         (M + 127) / 128 <= 65535 && K * 128 * 2 < ((int64_t)1 << 31);
+}
+hipError_t launch_qmm_n_tile(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                             const void* s, const void* b, int64_t M, int64_t N, int64_t K,
+                             void* y, hipStream_t st);
 
 // Gathered streaming GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T
 // with x [nxb, M, K], W [nwb, N, K] (scales / biases [nwb, N, K/gs]) and

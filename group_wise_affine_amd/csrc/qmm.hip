@@ -55,6 +55,7 @@ bool set_scratch(GemmArgs& a) {
 }  // namespace
 
 float* splitk_workspace() { return split_scratch().ws; }
+unsigned* tile_counters() { return split_scratch().cnt; }
 
 hipError_t launch_qmm_mfma(int dt, int bits, int gs, const void* x,
                            const uint32_t* wq, const void* s, const void* b,

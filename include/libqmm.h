@@ -42,9 +42,9 @@
  *  - Several entry points split K over workgroups and keep fp32 partial sums
  *    in library-owned workspaces: static device arrays, one set per GPU,
  *    holding their last call's contents (nothing is allocated per call):
- *      * the tile-kernel workspace (64 MiB): qmm_t, qmm_t_batched,
- *        qmm_gather_qmm, qconv2d_nhwc, qmm_fp_t and qmm_t_affine_packed
- *        when they split K, and qmm_n;
+ *      * the tile-kernel workspace (64 MiB) and 256 per-tile arrival
+ *        counters: qmm_t, qmm_t_batched, qmm_gather_qmm, qconv2d_nhwc,
+ *        qmm_fp_t, qmm_t_affine_packed and qmm_n when they split K;
  *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
  *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
  *        the MFMA GEMV on a narrow layer.
@@ -290,15 +290,19 @@ qmm_status qmm_t_affine_packed(const void* x, const uint32_t* wq_packed,
  *   y[m,n] = sum_k x[m,k] * (scale[k,n/gs] * q[k,n] + bias[k,n/gs]),
  * fp32 accumulation, y rounded to nearest even in dt. wq is [K, N*bits/32]
  * uint32, scales and biases [K, N/group_size]; N must be a multiple of
- * group_size (QMM_E_SHAPE otherwise). Meant for small M (decode): one pass
- * over W per row of x, K split over workgroups; when K > 128 the fp32
- * partial sums of the ceil(K/128) K ranges go to the library's split-K
- * workspace (shared with qmm_t on the device: calls that overlap on one
- * device share it), so the rows of x are taken in blocks of at most
+ * group_size (QMM_E_SHAPE otherwise). From 5 rows of x (f16) or 7 (bf16),
+ * when K % 8 == 0 and W is below 2 GiB, an MFMA tile kernel (W read once
+ * per 128 rows; with few output tiles K is split over workgroups, whose
+ * fp32 partial tiles go to the library's split-K workspace and the tile
+ * counters, the last split of each tile adding them). Otherwise the GEMV:
+ * one pass over W per row of x, K split over workgroups; when K > 128 the
+ * fp32 partial sums of the ceil(K/128) K ranges go to the split-K
+ * workspace, so the rows of x are taken in blocks of at most
  * floor(16M / (ceil(K/128) * N)) (and 65535) rows, one launch pair each;
  * QMM_E_SHAPE when a single row does not fit, QMM_E_ALIGN when a block's x
  * or y would not start 16-byte aligned (K or N not a multiple of 8 with
- * more rows than one block).
+ * more rows than one block). Both share the workspace with qmm_t on the
+ * device: calls that overlap on one device race.
  * (Source: "mlx 1.0.0 backend/cpu/quantized.cpp", _qmm, the non-transposed
  * branch of quantized_matmul.)
  */

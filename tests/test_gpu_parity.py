@@ -753,6 +753,38 @@ def test_qmm_n(orc, dt, M, K, N, gs, bits):
     assert_parity(from_dev(y), yo, dt, f"qmm_n {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("dt,M,K,N,gs", [
+    ("f16", 8, 256, 128, 32),       # the first M on the tile kernel
+    ("bf16", 200, 1000, 160, 32),   # ragged M, K (a partial 64-row step) and N (a partial tile)
+    ("f16", 130, 4096, 384, 128),
+    ("bf16", 64, 512, 2048, 64),
+])
+def test_qmm_n_tile(orc, dt, M, K, N, gs, bits):
+    """Many rows of x on the MFMA tile kernel for the non-transposed product,
+    with structured weight rows."""
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=M + K, dt=dt)
+    w = synth.normal((K, N), seed=K + N + bits, dt=dt)
+    w[:8] = synth.structured_rows(8, N, gs, seed=bits, dt=dt)
+    wq, s, b = orc.quantize(w, code, gs, bits)
+    yo, _ = orc.qmm_n(x, wq, s, b, code, gs, bits, nthreads=8)
+    y = Q.qmm_n(to_dev(x, dt), bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"qmm_n tile {dt} {M}x{K}x{N} g{gs} b{bits}")
+
+
+def test_qmm_n_tile_large(orc):
+    """x f16 [1024, 2048] . dequant(W [2048, 2048] 4-bit g64 along N)."""
+    x = synth.normal((1024, 2048), seed=3)
+    w = synth.normal((2048, 2048), seed=4)
+    wq, s, b = orc.quantize(w, orc.F16, 64, 4)
+    yo, _ = orc.qmm_n(x, wq, s, b, orc.F16, 64, 4, nthreads=16)
+    y = Q.qmm_n(to_dev(x, "f16"), bytes_to_words_dev(wq), to_dev(s, "f16"), to_dev(b, "f16"), 64, 4)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, "f16", "qmm_n tile 1024x2048x2048")
+
+
 def test_qmm_n_repeat(orc):
     """Calls in a row reuse the split-K workspace: a larger then a smaller
     problem, both exact."""
