@@ -86,6 +86,8 @@ def _declare(L):
     L.orc_fp_dequantize.restype = i32
     L.orc_fp_qmm_t.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp, i32]
     L.orc_fp_qmm_t.restype = i32
+    L.orc_fp_qmm_n.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp, i32]
+    L.orc_fp_qmm_n.restype = i32
 
 
 class OracleError(RuntimeError):
@@ -377,6 +379,25 @@ def fp_qmm_t(x, wq, scales, dt, group_size=32, bits=4, nthreads=1):
     yo = np.zeros((M, N), storage_dtype(dt))
     _chk(lib().orc_fp_qmm_t(_p(x), _p(wq), _p(scales), dt, M, N, K, group_size, bits, _p(y32),
                             _p(yo), nthreads), "orc_fp_qmm_t")
+    return y32, yo
+
+
+def fp_qmm_n(x, wq, scales, dt, group_size=32, bits=4, nthreads=1):
+    """Non-transposed product in an fp mode ("mlx 1.0.0 backend/cpu/
+    quantized.cpp", fp_qmm): y = x . dequant(W), W [K, N] quantized along N.
+    x: [M,K] words; wq: [K, N*bits/8] bytes; scales: uint8 [K, N/gs].
+    Returns (y32, y_T)."""
+    x = _words(x, dt)
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M, K = x.shape
+    N = wq.shape[1] * 8 // bits
+    if wq.shape[0] != K:
+        raise ValueError("fp_qmm_n: W must have K rows")
+    y32 = np.zeros((M, N), np.float32)
+    yo = np.zeros((M, N), storage_dtype(dt))
+    _chk(lib().orc_fp_qmm_n(_p(x), _p(wq), _p(scales), dt, M, N, K, group_size, bits, _p(y32),
+                            _p(yo), nthreads), "orc_fp_qmm_n")
     return y32, yo
 
 

@@ -224,3 +224,53 @@ int orc_fp_qmm_t(const void* x, const uint8_t* wq, const uint8_t* scales, int dt
   free(xall);
   return 0;
 }
+
+/* Non-transposed product in an fp mode (the page's fp_qmm): the weight
+ * W [K, N] is quantized along N (row k holds N codes, one scale byte per
+ * group of N), y[m,n] = sum over k ascending of x[m,k] * w[k,n] with
+ * w[k,n] = scale_T(s[k, n/gs]) * v(code[k,n]) (exact in fp32), products and
+ * sums in fp32, no fused multiply-add. */
+int orc_fp_qmm_n(const void* x, const uint8_t* wq, const uint8_t* scales, int dtype, int64_t M,
+                 int64_t N, int64_t K, int group_size, int bits, float* y32, void* y_out,
+                 int nthreads) {
+  const int st = fp_mode_ok(bits, group_size);
+  if (st) return st;
+  if (dtype != ORC_F16 && dtype != ORC_BF16 && dtype != ORC_F32) return -4;
+  if (M < 1 || N < 1 || K < 1 || N % group_size) return -3;
+  float* w = (float*)malloc((size_t)K * N * sizeof(float));
+  float* xall = (float*)malloc((size_t)M * K * sizeof(float));
+  if (!w || !xall) {
+    free(w);
+    free(xall);
+    return -3;
+  }
+  const int rc = orc_fp_dequantize(wq, scales, dtype, K, N, group_size, bits, w, NULL);
+  if (rc) {
+    free(w);
+    free(xall);
+    return rc;
+  }
+  if (nthreads < 1) nthreads = 1;
+  for (int64_t m = 0; m < M; m++) {
+    if (dtype == ORC_F32) memcpy(xall + m * K, (const float*)x + m * K, (size_t)K * 4);
+    else orc_to_f32((const uint16_t*)x + m * K, dtype, K, xall + m * K);
+  }
+#pragma omp parallel for collapse(2) num_threads(nthreads) schedule(static)
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t n = 0; n < N; n++) {
+      float acc = 0.0f;
+      for (int64_t k = 0; k < K; k++) {
+        const float p = xall[m * K + k] * w[k * N + n];
+        acc = acc + p;
+      }
+      if (y32) y32[m * N + n] = acc;
+      if (y_out) {
+        if (dtype == ORC_F32) ((float*)y_out)[m * N + n] = acc;
+        else orc_from_f32(&acc, dtype, 1, (uint16_t*)y_out + m * N + n);
+      }
+    }
+  }
+  free(w);
+  free(xall);
+  return 0;
+}

@@ -131,6 +131,9 @@ int orc_fp_dequantize(const uint8_t* wq, const uint8_t* scales, int dtype, int64
 int orc_fp_qmm_t(const void* x, const uint8_t* wq, const uint8_t* scales, int dtype, int64_t M,
                  int64_t N, int64_t K, int group_size, int bits, float* y32, void* y_out,
                  int nthreads);
+int orc_fp_qmm_n(const void* x, const uint8_t* wq, const uint8_t* scales, int dtype, int64_t M,
+                 int64_t N, int64_t K, int group_size, int bits, float* y32, void* y_out,
+                 int nthreads);
 
 #ifdef __cplusplus
 }

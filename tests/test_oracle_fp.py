@@ -12,8 +12,9 @@ dequantize_scale, fp_quantize_dequantize, fp_qmm_t).
 * quantization: groups built on the code grid come back exactly; on random data
   each code is the grid point nearest to w / scale (float64 search) and the
   scale byte follows the rule;
-* the product against a float64 matmul of the dequantized weights within the
-  forward error bound, and pure-Python loops on a tiny case.
+* the product (transposed and non-transposed) against a float64 matmul of the
+  dequantized weights within the forward error bound, and pure-Python loops on
+  tiny cases; one-hot rows of x pick rows of the dequantized weight exactly.
 """
 import math
 
@@ -209,6 +210,65 @@ def test_fp_qmm_t_tiny_bruteforce(orc):
                 byte = int(wq[n, k // 2])
                 c = (byte >> 4) if k % 2 else (byte & 15)
                 s = orc.e4m3_value(int(sc[n, k // gs]))
+                v = GRID[c & 7] * (-1 if c & 8 else 1) * s
+                acc += float(xf[m, k]) * v
+                mag += abs(float(xf[m, k]) * v)
+            assert abs(y32[m, n] - acc) <= (K + 2) * U32 * mag * 1.01 + 1e-30
+
+
+# ---------------------------------------------------- the non-transposed product
+# "mlx 1.0.0 backend/cpu/quantized.cpp", fp_qmm: W [K, N] quantized along N
+# (one scale byte per group of N), y[m, n] = sum_k x[m, k] * scale * code value.
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fp_qmm_n_vs_float64(orc, name, bits, gs, dt):
+    """Against a float64 matmul of x and the dequantized [K, N] weight within
+    the forward error bound (K != N: a transposed weight fails)."""
+    code = _code(orc, dt)
+    M, K, N = 3, 72, 4 * gs
+    x = synth.normal((M, K), seed=15, dt=dt)
+    w = synth.normal((K, N), seed=16, dt=dt)
+    wq, sc = orc.fp_quantize(w, code, gs, bits)
+    w32, _ = orc.fp_dequantize(wq, sc, code, N, gs, bits)
+    y32, yt = orc.fp_qmm_n(x, wq, sc, code, gs, bits)
+    xf = synth.words_to_f32(x, dt).astype(np.float64)
+    wf = w32.astype(np.float64)
+    ref = xf @ wf
+    gamma = (K + 2) * U32 / (1 - (K + 2) * U32)
+    assert np.all(np.abs(y32 - ref) <= gamma * (np.abs(xf) @ np.abs(wf)))
+    assert np.array_equal(yt, synth.to_words(y32, dt))
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+def test_fp_qmm_n_one_hot_rows(orc, name, bits, gs):
+    """x = e_k picks row k of the dequantized weight exactly."""
+    K, N = 40, 2 * gs
+    w = synth.normal((K, N), seed=17)
+    wq, sc = orc.fp_quantize(w, orc.F16, gs, bits)
+    w32, _ = orc.fp_dequantize(wq, sc, orc.F16, N, gs, bits)
+    x = synth.to_words(np.eye(K, dtype=np.float32), "f16")
+    y32, _ = orc.fp_qmm_n(x, wq, sc, orc.F16, gs, bits)
+    assert np.array_equal(y32, w32)
+
+
+def test_fp_qmm_n_tiny_bruteforce(orc):
+    """mxfp4, pure-Python decoding of codes and e8m0 scales."""
+    M, K, N, gs, bits = 2, 5, 64, 32, 4
+    x = synth.normal((M, K), seed=18, dt="f16")
+    w = synth.normal((K, N), seed=19, dt="f16")
+    wq, sc = orc.fp_quantize(w, orc.F16, gs, bits)
+    y32, _ = orc.fp_qmm_n(x, wq, sc, orc.F16, gs, bits)
+    xf = synth.words_to_f32(x, "f16")
+    for m in range(M):
+        for n in range(N):
+            acc = mag = 0.0
+            for k in range(K):
+                byte = int(wq[k, n // 2])
+                c = (byte >> 4) if n % 2 else (byte & 15)
+                b = int(sc[k, n // gs])
+                s = 2.0 ** (b - 127) if b else 2.0 ** -127
+                s = float(np.float64(s).astype(np.float16))   # the scale rounded to f16
                 v = GRID[c & 7] * (-1 if c & 8 else 1) * s
                 acc += float(xf[m, k]) * v
                 mag += abs(float(xf[m, k]) * v)
