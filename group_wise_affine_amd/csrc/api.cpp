@@ -526,6 +526,37 @@ qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales, qm
                   "qmm_fp_t");
 }
 
+qmm_status qmm_fp_n(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
+                    int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
+                    void* stream) {
+  if (!x || !wq || !scales || !y)
+    return fail(QMM_E_NULL, "qmm_fp_n: x, wq, scales and y must be non-NULL");
+  qmm_status st = check_fp_mode("qmm_fp_n", bits, group_size);
+  if (st) return st;
+  if (dt != QMM_F16 && dt != QMM_BF16)
+    return fail(QMM_E_DTYPE, "qmm_fp_n: only float16 and bfloat16 are supported (got dtype %d)",
+                (int)dt);
+  if (M < 1 || K < 1 || M > kI32 || K > kI32)
+    return fail(QMM_E_SHAPE, "qmm_fp_n: M (%lld) and K (%lld) must be >= 1", (long long)M,
+                (long long)K);
+  if (N < 32 || N % 32 != 0 || N > kI32)
+    return fail(QMM_E_SHAPE,
+                "qmm_fp_n: N (%lld) must be a positive multiple of 32: the weight [K, N] is "
+                "quantized along N",
+                (long long)N);
+  if (K % 8 != 0)
+    return fail(QMM_E_SHAPE, "qmm_fp_n: K (%lld) must be a multiple of 8 (16-byte rows of x)",
+                (long long)K);
+  if (!qmm::qmm_n_tile_fits(0, 1 << 20, N, K, bits) || M * N > ((int64_t)1 << 40) ||
+      M * K > ((int64_t)1 << 40))
+    return fail(QMM_E_SHAPE, "qmm_fp_n: problem too large");
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(QMM_E_ALIGN, "qmm_fp_n: x, wq and y must be 16-byte aligned");
+  return launched(qmm::launch_fp_qmm_n_tile((int)dt, bits, group_size, x, wq, scales, M, N, K, y,
+                                            (hipStream_t)stream),
+                  "qmm_fp_n");
+}
+
 qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_indices,
                              const uint32_t* wq, const uint8_t* scales, int64_t w_batches,
                              const int32_t* rhs_indices, int64_t batches, qmm_dtype dt, int64_t M,

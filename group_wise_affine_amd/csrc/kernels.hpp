@@ -85,6 +85,10 @@ inline bool qmm_n_tile_fits(int dt, int64_t M, int64_t N, int64_t K, int bits) {
 hipError_t launch_qmm_n_tile(int dt, int bits, int gs, const void* x, const uint32_t* wq,
                              const void* s, const void* b, int64_t M, int64_t N, int64_t K,
                              void* y, hipStream_t st);
+// the same kernel in the fp modes (scales: bytes [K, N/gs], no bias)
+hipError_t launch_fp_qmm_n_tile(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                                const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
+                                hipStream_t st);
 
 // Gathered streaming GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T
 // with x [nxb, M, K], W [nwb, N, K] (scales / biases [nwb, N, K/gs]) and

@@ -22,6 +22,11 @@
 //    the W tile double-buffered).
 //  * Loads go through buffer resources: rows of W and of the scales past K
 //    read zero (so those k contribute nothing), rows of x past M read zero.
+//  * FPM != 0: the floating-point modes (the page's fp_qmm): 1 mxfp4 (E2M1
+//    codes, e8m0 scale per 32 columns), 2 nvfp4 (E2M1, E4M3 scale per 16), 3
+//    mxfp8 (E4M3, e8m0 per 32), no bias; codes are decoded by gfx950's
+//    conversions at scale 1 and multiplied by the scale rounded to T, which
+//    is exact in T within T's range, so one W tile serves f16 and bf16.
 //  * Few output tiles (the launch would leave CUs idle): K is split over up
 //    to 8 workgroups per tile; each stores its fp32 partial tile to the
 //    split-K workspace with device-scope stores and counts itself in on the
@@ -40,13 +45,32 @@ constexpr int kQtM = 128, kQtN = 128, kQtK = 64;   // tile and K step
 constexpr int kQtThreads = 256;
 constexpr int kQtLd = kQtK + 8;                     // LDS row length (elements) of xs and ws
 
-template <class T, int BITS>
+// the 8 E2M1 codes of a word (FPM 1, 2) or the 4 E4M3 codes (FPM 3) as fp32
+template <int FPM>
+__device__ __forceinline__ void fp_decode_word(uint32_t w, float* v) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (FPM == 3) {
+    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+  } else {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+  }
+}
+
+template <class T, int BITS, int FPM = 0>
 __global__ __launch_bounds__(kQtThreads) void qmn_tile_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, int ksplit, int ksteps,
     float* __restrict__ ws, unsigned* __restrict__ cnt) {
-  constexpr bool kSplit = __is_same(T, BF16);     // hi / lo W tiles
+  constexpr bool kFp = FPM != 0;
+  constexpr bool kSplit = !kFp && __is_same(T, BF16);   // hi / lo W tiles
   constexpr int NB = kSplit ? 2 : 1;
   constexpr int kRowBytes = 16 * BITS;            // raw codes of one tile row (128 codes)
   constexpr int kRawUnits = kQtK * BITS;          // 16-byte units of the raw tile
@@ -72,12 +96,13 @@ __global__ __launch_bounds__(kQtThreads) void qmn_tile_kernel(
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(x + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0 < kQtM ? M - m0 : kQtM) * K * 2));
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq, (uint32_t)((int64_t)K * row_bytes));
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (uint32_t)((int64_t)K * G * 2));
-  const __amdgpu_buffer_rsrc_t br = make_rsrc(biases, (uint32_t)((int64_t)K * G * 2));
+  constexpr int ES = kFp ? 1 : 2;                       // bytes per scale
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (uint32_t)((int64_t)K * G * ES));
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(kFp ? scales : biases, (uint32_t)((int64_t)K * G * ES));
 
   // dequantization role: rows 2p, 2p+1 of the step, columns 32c + 16h + [0, 16)
   const int p = tid & 31, c = (tid >> 5) & 3, h = tid >> 7;
-  const int grp = (n0 + 32 * c) >> gs_log2;            // the chunk's group
+  const int grp = (n0 + 32 * c + 16 * h) >> gs_log2;   // the thread's group
   const int wbyte = (4 * c + 2 * h) * BITS;            // window start in a raw row
   const int wshift = 8 * (wbyte & 3);                  // 0 or 16 (uniform per wavefront)
 
@@ -105,9 +130,14 @@ __global__ __launch_bounds__(kQtThreads) void qmn_tile_kernel(
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int k = k0 + 2 * p + j;
-      const uint32_t off = k < K ? (uint32_t)(k * G + grp) * 2 : kOob;
-      snext[2 * j] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
-      snext[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+      const uint32_t off = k < K ? (uint32_t)(k * G + grp) * ES : kOob;
+      if constexpr (kFp) {
+        snext[2 * j] = __builtin_amdgcn_raw_buffer_load_b8(sr, off, 0, 0);
+        snext[2 * j + 1] = 0;
+      } else {
+        snext[2 * j] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        snext[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+      }
     }
   };
   // ---- registers into the LDS x slot b and the raw code tile (and the
@@ -156,6 +186,25 @@ __global__ __launch_bounds__(kQtThreads) void qmn_tile_kernel(
       return __builtin_amdgcn_alignbit(win[j][wd + 1], win[j][wd], of) & mask;
     };
     uint16_t* wlo = wsl[b][0];
+    if constexpr (kFp) {
+      // w = scale_T * code value (exact in T within its range)
+      float v[2][16];
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int q = 0; q < BITS / 2; q++) fp_decode_word<FPM>(win[j][q], &v[j][q * 32 / BITS]);
+      float sc[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        sc[j] = __builtin_bit_cast(float, fp_scale_t_bits<T, FPM>(scur[2 * j]));
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const int n = 32 * c + 16 * h + e;
+        *reinterpret_cast<uint32_t*>(&wlo[n * kQtLd + 2 * p]) =
+            (uint32_t)from_f32(T{}, sc[0] * v[0][e]) | ((uint32_t)from_f32(T{}, sc[1] * v[1][e]) << 16);
+      }
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 16; e++) {
       const int n = 32 * c + 16 * h + e;
@@ -315,7 +364,7 @@ int qmn_splits(int64_t M, int64_t N, int64_t K, int* ksteps) {
   return (nk + per - 1) / per;
 }
 
-template <class T, int BITS>
+template <class T, int BITS, int FPM = 0>
 hipError_t launch_bits(const void* x, const uint32_t* wq, const void* s, const void* b,
                        int64_t M, int64_t N, int64_t K, int gs, void* y, float* ws,
                        unsigned* cnt, hipStream_t st) {
@@ -323,7 +372,7 @@ hipError_t launch_bits(const void* x, const uint32_t* wq, const void* s, const v
   const int ks = qmn_splits(M, N, K, &ksteps);
   const dim3 grid((unsigned)((N + kQtN - 1) / kQtN), (unsigned)((M + kQtM - 1) / kQtM),
                   (unsigned)ks);
-  hipLaunchKernelGGL((qmn_tile_kernel<T, BITS>), grid, dim3(kQtThreads), 0, st,
+  hipLaunchKernelGGL((qmn_tile_kernel<T, BITS, FPM>), grid, dim3(kQtThreads), 0, st,
                      static_cast<const uint16_t*>(x), reinterpret_cast<const uint8_t*>(wq),
                      static_cast<const uint16_t*>(s), static_cast<const uint16_t*>(b),
                      static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, ilog2(gs), ks, ksteps,
@@ -355,6 +404,23 @@ hipError_t launch_qmm_n_tile(int dt, int bits, int gs, const void* x, const uint
   if (!ws || !cnt) return hipErrorInvalidSymbol;
   if (dt == 0) return launch_t<F16>(bits, x, wq, s, b, M, N, K, gs, y, ws, cnt, st);
   return launch_t<BF16>(bits, x, wq, s, b, M, N, K, gs, y, ws, cnt, st);
+}
+
+hipError_t launch_fp_qmm_n_tile(int dt, int bits, int gs, const void* x, const uint32_t* wq,
+                                const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
+                                hipStream_t st) {
+  float* ws = splitk_workspace();
+  unsigned* cnt = tile_counters();
+  if (!ws || !cnt) return hipErrorInvalidSymbol;
+  const void* s = scales;
+  if (dt == 0) {
+    if (bits == 8) return launch_bits<F16, 8, 3>(x, wq, s, s, M, N, K, gs, y, ws, cnt, st);
+    if (gs == 16) return launch_bits<F16, 4, 2>(x, wq, s, s, M, N, K, gs, y, ws, cnt, st);
+    return launch_bits<F16, 4, 1>(x, wq, s, s, M, N, K, gs, y, ws, cnt, st);
+  }
+  if (bits == 8) return launch_bits<BF16, 8, 3>(x, wq, s, s, M, N, K, gs, y, ws, cnt, st);
+  if (gs == 16) return launch_bits<BF16, 4, 2>(x, wq, s, s, M, N, K, gs, y, ws, cnt, st);
+  return launch_bits<BF16, 4, 1>(x, wq, s, s, M, N, K, gs, y, ws, cnt, st);
 }
 
 }  // namespace qmm

@@ -23,7 +23,7 @@ STATUS_NAMES = ["QMM_OK", "QMM_E_NULL", "QMM_E_BITS", "QMM_E_GROUP",
 KERNEL_NONE, KERNEL_GEMV, KERNEL_MFMA_GEMV, KERNEL_TILE = range(4)
 EXPORTS = ["qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
            "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched",
-           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
+           "qmm_fp_quantize", "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_n", "qmm_fp_gather_qmv",
            "qmm_affine_pack", "qmv_affine_packed", "qmm_t_affine_packed",
            "qmm_crossover_m", "qmm_route", "qmm_force_kernel", "qmm_last_error"]
 
@@ -68,11 +68,12 @@ def lib():
         L.qmm_fp_dequantize.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp, vp]
         L.qmm_fp_qmv.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, vp, vp]
         L.qmm_fp_t.argtypes = L.qmm_fp_qmv.argtypes
+        L.qmm_fp_n.argtypes = L.qmm_fp_qmv.argtypes
         L.qmm_fp_gather_qmv.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i32, i64, i64, i64,
                                         i32, i32, vp, vp]
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_t", "qmv", "qmm_n", "qconv2d_nhwc",
                   "qmm_gather_qmv", "qmm_gather_qmm", "qmm_t_batched", "qmm_fp_quantize",
-                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_gather_qmv",
+                  "qmm_fp_dequantize", "qmm_fp_qmv", "qmm_fp_t", "qmm_fp_n", "qmm_fp_gather_qmv",
                   "qmm_affine_pack", "qmv_affine_packed", "qmm_t_affine_packed"):
             getattr(L, f).restype = i32
         L.qmm_crossover_m.argtypes = [i32, i32, i32, i64, i64]
@@ -369,6 +370,26 @@ def fp_qmm_t(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
     """Same as fp_qmv for any M: the GEMV for a few rows, the MFMA tile kernel
     beyond."""
     return fp_qmv(x, wq, scales, group_size, bits, out, stream, _fn="qmm_fp_t")
+
+
+def fp_qmm_n(x, wq, scales, group_size=32, bits=4, out=None, stream=None):
+    """y [M,N] = x [M,K] . dequant(W) for a floating-point mode, W [K, N]
+    quantized along N: wq [K, N*bits/32], scales uint8 [K, N/gs]."""
+    _check_tensor(x, "x", dims=2)
+    _check_tensor(wq, "wq", dims=2, dtype=torch.int32)
+    M, K = x.shape
+    if wq.shape[0] != K:
+        raise ValueError(f"fp_qmm_n: wq has {wq.shape[0]} rows, x has K = {K}")
+    N = wq.shape[1] * 32 // bits if bits in (4, 8) else 0
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if N >= group_size and group_size in (16, 32) and N % group_size == 0:
+        _check_tensor(scales, "scales", (K, N // group_size), torch.uint8)
+    _check_tensor(out, "out", (M, N), x.dtype)
+    _check_device(("x", x), ("wq", wq), ("scales", scales), ("out", out))
+    _check(lib().qmm_fp_n(_ptr(x), _ptr(wq), _ptr(scales), _dt(x.dtype), M, N, K, group_size,
+                          bits, _ptr(out), _stream(stream)))
+    return out
 
 
 def fp_gather_qmv(x, wq, scales, lhs_indices=None, rhs_indices=None, group_size=32, bits=4,

@@ -44,7 +44,7 @@
  *    holding their last call's contents (nothing is allocated per call):
  *      * the tile-kernel workspace (64 MiB) and 256 per-tile arrival
  *        counters: qmm_t, qmm_t_batched, qmm_gather_qmm, qconv2d_nhwc,
- *        qmm_fp_t, qmm_t_affine_packed and qmm_n when they split K;
+ *        qmm_fp_t, qmm_fp_n, qmm_t_affine_packed and qmm_n when they split K;
  *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
  *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
  *        the MFMA GEMV on a narrow layer.
@@ -217,6 +217,23 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales,
 qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales,
                     qmm_dtype dt, int64_t M, int64_t N, int64_t K,
                     int group_size, int bits, void* y, void* stream);
+
+/*
+ * Non-transposed product in an fp mode: y[M,N] = x[M,K] . dequant(W)[K,N],
+ * where W [K, N] is quantized along N by qmm_fp_quantize of its K rows:
+ *   y[m,n] = sum_k x[m,k] * scale_T(scales[k, n/gs]) * value(code[k,n]),
+ * fp32 accumulation, y rounded to nearest even in dt. wq is [K, N*bits/32]
+ * uint32 (the rows' code bytes), scales [K, N/group_size] uint8; modes as
+ * qmm_fp_quantize ((4, 32) mxfp4, (4, 16) nvfp4, (8, 32) mxfp8). N must be a
+ * multiple of 32 and K of 8 (QMM_E_SHAPE), x, wq and y 16-byte aligned. Runs
+ * the non-transposed MFMA tile kernel for any M (K split over workgroups
+ * when the output has few tiles: the tile-kernel workspace and counters,
+ * shared as described above). (Source: "mlx 1.0.0 backend/cpu/quantized.cpp",
+ * fp_qmm.)
+ */
+qmm_status qmm_fp_n(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
+                    int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
+                    void* stream);
 
 /*
  * Gathered product in a floating-point mode (e.g. mixture-of-experts decode

@@ -289,6 +289,20 @@ def test_fp_t_arguments(L):
     assert t(y=P2) == Q.QMM_E_ALIGN and t(wq=P2) == Q.QMM_E_ALIGN
 
 
+def test_fp_n_arguments(L):
+    def t(x=P, wq=P, sc=P, dt=0, M=64, N=64, K=64, gs=32, bits=4, y=P):
+        return _st(L, "qmm_fp_n", x, wq, sc, dt, M, N, K, gs, bits, y, None)
+    assert t(bits=3) == Q.QMM_E_BITS
+    assert t(gs=64) == Q.QMM_E_GROUP
+    assert t(x=None) == Q.QMM_E_NULL and t(sc=None) == Q.QMM_E_NULL
+    assert t(dt=2) == Q.QMM_E_DTYPE
+    assert t(N=48) == Q.QMM_E_SHAPE             # the quantized dimension: a multiple of 32
+    assert t(K=12) == Q.QMM_E_SHAPE             # rows of x: a multiple of 8
+    assert t(M=0) == Q.QMM_E_SHAPE and t(K=0) == Q.QMM_E_SHAPE
+    assert t(N=1 << 16, K=1 << 16) == Q.QMM_E_SHAPE   # weight beyond 2 GiB
+    assert t(y=P2) == Q.QMM_E_ALIGN and t(x=P2) == Q.QMM_E_ALIGN
+
+
 def test_fp_gather_arguments(L):
     def g(x=P, nxb=2, li=None, wq=P, sc=P, nwb=3, ri=None, B=2, dt=0, M=1, N=8, K=64, gs=32,
           bits=4, y=P):

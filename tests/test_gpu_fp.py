@@ -1,8 +1,8 @@
 """GPU parity of the floating-point modes (mxfp4, nvfp4, mxfp8) against the
 oracle ("mlx 1.0.0 backend/cpu/quantized.cpp": to_fp4_e2m1, to_fp8_e8m0,
-dequantize_scale, fp_quantize_dequantize, fp_qmm_t): quantize and dequantize
-bit-exact, the GEMV and the any-M product (MFMA tile kernel) within the
-floating-point gate."""
+dequantize_scale, fp_quantize_dequantize, fp_qmm_t, fp_qmm): quantize and
+dequantize bit-exact, the GEMV, the any-M product (MFMA tile kernel) and the
+non-transposed product within the floating-point gate."""
 import numpy as np
 import pytest
 import torch
@@ -130,6 +130,28 @@ def test_fp_qmm_t(orc, name, bits, gs, dt, M, N, K):
     y = Q.fp_qmm_t(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs, bits)
     torch.cuda.synchronize()
     assert_parity(from_dev(y), yo, dt, f"fp_qmm_t {name} {dt} M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("name,bits,gs", MODES)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 64),         # one row of x, one tile
+    (37, 1000, 160),     # ragged M, K (a partial 64-row step) and N (a partial tile), K split
+    (256, 4096, 384),    # K split 8 ways
+    (300, 512, 2048),    # 48 tiles over 3 row blocks
+])
+def test_fp_qmm_n(orc, name, bits, gs, dt, M, K, N):
+    """The non-transposed fp-mode product (W [K, N] quantized along N) on the
+    tile kernel against the oracle's fp_qmm_n, with structured groups and rows
+    of small (2^-12) and large (x16) scales."""
+    code = orc_code(orc, dt)
+    x = synth.normal((M, K), seed=M + K + 2, dt=dt)
+    w = _weights(K, N, gs, dt, seed=N + K + bits + 1, big=16.0)
+    wq, sc = orc.fp_quantize(w, code, gs, bits)
+    yo, _ = orc.fp_qmm_n(x, wq, sc, code, gs, bits, nthreads=8)
+    y = Q.fp_qmm_n(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs, bits)
+    torch.cuda.synchronize()
+    assert_parity(from_dev(y), yo, dt, f"fp_qmm_n {name} {dt} M{M} K{K} N{N}")
 
 
 @pytest.mark.parametrize("name,bits,gs", MODES)
