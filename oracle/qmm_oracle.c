@@ -127,24 +127,63 @@ static int check_args(int dtype, int64_t K, int gs, int bits) {
 
 int64_t orc_row_bytes(int64_t K, int bits) { return K * bits / 8; }
 
-/* Values per pack and bytes per pack ([P4] get_pack_factor with a 32-bit
- * word, get_bytes_per_pack): power-of-two widths fill a 4-byte word;
- * 3 bits = 8 values in 3 bytes, 5 bits = 8 values in 5 bytes,
- * 6 bits = 4 values in 3 bytes. */
-static int pack_values(int bits) {
-  if (bits == 3 || bits == 5) return 8;
-  if (bits == 6) return 4;
-  return 32 / bits;
+/* ------------------------------------------------------------------ */
+/* Quantizer ([P3] item 1 a-c; the rounding and fp32 arithmetic of [P4]  */
+/* quantize). Per group of gs weights:                                   */
+/*  1. the anchor is the extreme of larger magnitude (the maximum when    */
+/*     |min| == |max|), the step spans from it to the other extreme over  */
+/*     2^bits - 1 levels, at least 1e-7 in magnitude, negative when the   */
+/*     anchor is the maximum (codes then count down from it);             */
+/*  2. zero point: the anchor is k = rint(anchor / step) steps from 0;    */
+/*     for k != 0 the step becomes anchor / k and the offset (bias) is    */
+/*     the anchor, so 0 lies on the grid; for k == 0 the offset is 0;     */
+/*  3. each weight's code is rint((w - offset) / step), clamped to the    */
+/*     levels, written into the row's little-endian bit stream at bit     */
+/*     k*bits. [P4] packs power-of-two widths into 4-byte words, 3 and 5  */
+/*     bits as 8 values in 3 / 5 bytes and 6 bits as 4 values in 3 bytes */
+/*     (get_pack_factor, get_bytes_per_pack), each pack little-endian:    */
+/*     the same bytes as this stream.                                     */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+  float step, offset;
+} qparams;
+
+static void group_range(const void* w, int dtype, int64_t first, int n, float* lo, float* hi) {
+  float a = INFINITY, b = -INFINITY;
+  for (int j = 0; j < n; j++) {
+    const float v = load_t(w, dtype, first + j);
+    if (v < a) a = v;
+    if (b < v) b = v;
+  }
+  *lo = a;
+  *hi = b;
 }
 
-static int pack_bytes(int bits) {
-  if ((bits & (bits - 1)) == 0) return 4;
-  return bits == 5 ? 5 : 3;
+static qparams group_params(float lo, float hi, int bits) {
+  const float levels = (float)((1 << bits) - 1);
+  const int anchor_is_lo = fabsf(lo) > fabsf(hi);
+  const float anchor = anchor_is_lo ? lo : hi;
+  float step = (hi - lo) / levels;
+  if (step < 1e-7f) step = 1e-7f;
+  if (!anchor_is_lo) step = -step;
+  qparams p = {step, 0.0f};
+  const float k = rintf(anchor / step);
+  if (k != 0.0f) {
+    p.step = anchor / k;
+    p.offset = anchor;
+  }
+  return p;
 }
 
-/* ------------------------------------------------------------------ */
-/* Quantizer: [P3] item 1 a-c, steps as in [P4] quantize.               */
-/* ------------------------------------------------------------------ */
+/* code of v, clamped to [0, 2^bits - 1] */
+static uint32_t encode(float v, qparams p, int bits) {
+  float q = rintf((v - p.offset) / p.step);
+  const float top = (float)((1 << bits) - 1);
+  if (q < 0.0f) q = 0.0f;
+  if (q > top) q = top;
+  return (uint32_t)q;
+}
 
 int orc_quantize(const void* w, int dtype, int64_t rows, int64_t K,
                  int group_size, int bits, uint8_t* wq, void* scales,
@@ -152,60 +191,27 @@ int orc_quantize(const void* w, int dtype, int64_t rows, int64_t K,
   int rc = check_args(dtype, K, group_size, bits);
   if (rc) return rc;
   if (rows < 1) return -3;
-  const float n_bins = (float)((1 << bits) - 1);
-  const float eps = 1e-7f;
-  const int vpp = pack_values(bits);
-  const int bpp = pack_bytes(bits);
-  const int64_t n_groups = rows * (K / group_size);
-  const int64_t group_bytes = (int64_t)group_size * bits / 8;
-
-  for (int64_t i = 0; i < n_groups; i++) {
-    const int64_t w0 = i * group_size;
-    /* group minimum and maximum, in fp32 */
-    float w_min = INFINITY, w_max = -INFINITY;
-    for (int j = 0; j < group_size; j++) {
-      float v = load_t(w, dtype, w0 + j);
-      w_max = (w_max < v) ? v : w_max;
-      w_min = (v < w_min) ? v : w_min;
-    }
-    /* (a) the bias is the extreme with the larger magnitude (strictly
-       larger |min| picks the minimum, so a tie picks the maximum);
-       (b) the scale spans from that extreme to the other one, so it is
-       negative when the bias is the maximum. */
-    int bias_is_min = fabsf(w_min) > fabsf(w_max);
-    float scale = (w_max - w_min) / n_bins;
-    if (scale < eps) scale = eps;
-    if (!bias_is_min) scale = -scale;
-    /* (c) adjust the scale so that the chosen extreme sits exactly q0
-       steps from zero, which puts 0 on the grid. If the extreme is less
-       than half a step from zero, the bias stays 0. */
-    float edge = bias_is_min ? w_min : w_max;
-    float q0 = rintf(edge / scale);
-    float bias = 0.0f;
-    if (q0 != 0.0f) {
-      scale = edge / q0;
-      bias = edge;
-    }
-    /* codes: nearest grid step from the bias, clamped to [0, n_bins],
-       packed little-endian, value j of a pack at bit j*bits */
-    uint8_t* out = wq + i * group_bytes;
-    const int n_packs = group_size / vpp;
-    for (int p = 0; p < n_packs; p++) {
-      uint64_t word = 0;
-      for (int j = 0; j < vpp; j++) {
-        float v = load_t(w, dtype, w0 + (int64_t)p * vpp + j);
-        float q = rintf((v - bias) / scale);
-        if (q < 0.0f) q = 0.0f;
-        if (q > n_bins) q = n_bins;
-        word |= (uint64_t)q << (j * bits);
+  const int64_t groups_per_row = K / group_size;
+  const int64_t row_bytes = K * bits / 8;
+  for (int64_t r = 0; r < rows; r++) {
+    uint8_t* stream = wq + r * row_bytes;
+    memset(stream, 0, (size_t)row_bytes);
+    for (int64_t g = 0; g < groups_per_row; g++) {
+      const int64_t first = r * K + g * group_size, gi = r * groups_per_row + g;
+      float lo, hi;
+      group_range(w, dtype, first, group_size, &lo, &hi);
+      const qparams p = group_params(lo, hi, bits);
+      for (int j = 0; j < group_size; j++) {
+        const uint32_t c = encode(load_t(w, dtype, first + j), p, bits);
+        const int64_t bit = (g * group_size + j) * bits;   /* position in the row */
+        for (int t = 0; t < bits; t++)
+          if ((c >> t) & 1u) stream[(bit + t) >> 3] |= (uint8_t)(1u << ((bit + t) & 7));
       }
-      for (int b = 0; b < bpp; b++)
-        out[(int64_t)p * bpp + b] = (uint8_t)((word >> (8 * b)) & 0xffu);
+      store_t(scales, dtype, gi, p.step);
+      store_t(biases, dtype, gi, p.offset);
+      if (s32) s32[gi] = p.step;
+      if (b32) b32[gi] = p.offset;
     }
-    store_t(scales, dtype, i, scale);
-    store_t(biases, dtype, i, bias);
-    if (s32) s32[i] = scale;
-    if (b32) b32[i] = bias;
   }
   return 0;
 }
