@@ -9,6 +9,7 @@
 #include <stdio.h>
 
 #include <limits>
+#include <mutex>
 
 #include "../../include/libqmm.h"
 #include "kernels.hpp"
@@ -63,6 +64,50 @@ qmm_status launched(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kI32 = std::numeric_limits<int32_t>::max();
+
+// Calls whose kernels may use the device's static scratch (the split-K
+// workspace, the tile counters, the MFMA GEMV's partial tiles and counters)
+// are ordered across streams: a call queued on another stream than the
+// previous such call on the device first waits for that call's work (one
+// event per device, recorded after each call's launches), so calls from
+// different streams or host threads do not race on the scratch. During
+// stream capture nothing is waited for or recorded: a capturing caller
+// orders its own work.
+constexpr int kMaxDev = 64;
+std::recursive_mutex g_ord_mu;
+hipEvent_t g_ord_ev[kMaxDev] = {};
+hipStream_t g_ord_st[kMaxDev] = {};
+bool g_ord_used[kMaxDev] = {};
+
+class ScratchOrder {
+ public:
+  explicit ScratchOrder(void* stream) : st_(static_cast<hipStream_t>(stream)) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st_, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return;
+    g_ord_mu.lock();   // held until the launches are queued
+    dev_ = dev;
+    if (!g_ord_ev[dev] && hipEventCreateWithFlags(&g_ord_ev[dev], hipEventDisableTiming) != hipSuccess)
+      g_ord_ev[dev] = nullptr;
+    if (g_ord_ev[dev] && g_ord_used[dev] && g_ord_st[dev] != st_)
+      (void)hipStreamWaitEvent(st_, g_ord_ev[dev], 0);
+  }
+  ~ScratchOrder() {
+    if (dev_ < 0) return;
+    if (g_ord_ev[dev_] && hipEventRecord(g_ord_ev[dev_], st_) == hipSuccess) {
+      g_ord_st[dev_] = st_;
+      g_ord_used[dev_] = true;
+    }
+    g_ord_mu.unlock();
+  }
+  ScratchOrder(const ScratchOrder&) = delete;
+  ScratchOrder& operator=(const ScratchOrder&) = delete;
+
+ private:
+  hipStream_t st_;
+  int dev_ = -1;
+};
 
 qmm_status check_matmul(const char* tag, const void* x, const uint32_t* wq,
                         const void* s, const void* b, qmm_dtype dt, int64_t M,
@@ -190,6 +235,7 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                 "bits/dtype; M <= %d rows of x within %zu bytes of LDS for f16); use qmm_t",
                 (long long)K, (long long)qmm::qmv_max_k(bits, (int)dt), qmm::kQmvMfmaMaxM,
                 qmm::kQmvMfmaMaxLds);
+  ScratchOrder ord(stream);
   return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                   biases, M, N, K, y, (hipStream_t)stream),
                   "qmv");
@@ -213,6 +259,7 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
   if (batches * M > kI32 || batches * M * K > ((int64_t)1 << 40) ||
       batches * M * N > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40))
     return fail(QMM_E_SHAPE, "qmm_t_batched: problem too large");
+  ScratchOrder ord(stream);
   // one weight for every batch: the batches are the rows of one product
   if (w_batches == 1)
     return qmm_t(x, wq, scales, biases, dt, batches * M, N, K, group_size, bits, y, stream);
@@ -300,6 +347,7 @@ qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const vo
     return fail(QMM_E_ALIGN, "qmm_n: x, wq and y must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(biases, 2))
     return fail(QMM_E_ALIGN, "qmm_n: scales and biases must be 2-byte aligned");
+  ScratchOrder ord(stream);
   // many rows of x: the MFMA tile kernel (one pass over W per 128 rows)
   if (qmm::qmm_n_tile_fits((int)dt, M, N, K, bits))
     return launched(qmm::launch_qmm_n_tile((int)dt, bits, group_size, x, wq, scales, biases, M, N,
@@ -384,6 +432,7 @@ qmm_status qmm_gather_qmm(const void* x, int64_t x_batches, const int32_t* lhs_i
                 "qmm_gather_qmm: per-batch sizes of x (%lld B), y (%lld B) and wq (%lld B) must be "
                 "multiples of 16 bytes",
                 (long long)xs, (long long)ys, (long long)ws);
+  ScratchOrder ord(stream);
   return launched(qmm::launch_gather_qmm_mfma((int)dt, bits, group_size, x, x_batches,
                                               lhs_indices, wq, scales, biases, w_batches,
                                               rhs_indices, batches, M, N, K, y, hs),
@@ -512,6 +561,7 @@ qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales, qm
     return fail(QMM_E_SHAPE, "qmm_fp_t: problem too large");
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
     return fail(QMM_E_ALIGN, "qmm_fp_t: x, wq and y must be 16-byte aligned");
+  ScratchOrder ord(stream);
   const bool gemv = M < qmm::fp_crossover_m(bits, group_size, (int)dt) && M <= 65535 &&
                     K <= qmm::kFpMaxK;
   if (gemv)
@@ -552,6 +602,7 @@ qmm_status qmm_fp_n(const void* x, const uint32_t* wq, const uint8_t* scales, qm
     return fail(QMM_E_SHAPE, "qmm_fp_n: problem too large");
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
     return fail(QMM_E_ALIGN, "qmm_fp_n: x, wq and y must be 16-byte aligned");
+  ScratchOrder ord(stream);
   return launched(qmm::launch_fp_qmm_n_tile((int)dt, bits, group_size, x, wq, scales, M, N, K, y,
                                             (hipStream_t)stream),
                   "qmm_fp_n");
@@ -701,6 +752,7 @@ qmm_status qmm_t_affine_packed(const void* x, const uint32_t* wq_packed, const v
   if (K >= qmm::kTileMaxK)
     return fail(QMM_E_SHAPE, "%s: K (%lld) must be below %lld for the MFMA tile kernel", tag,
                 (long long)K, (long long)qmm::kTileMaxK);
+  ScratchOrder ord(stream);
   return launched(qmm::launch_apk_mfma((int)dt, bits, group_size, x, wq_packed, sb_packed, M, N,
                                        K, y, (hipStream_t)stream),
                   tag);
@@ -712,6 +764,7 @@ qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
   qmm_status st = check_matmul("qmm_t", x, wq, scales, biases, dt, M, N, K,
                                group_size, bits, y);
   if (st) return st;
+  ScratchOrder ord(stream);
   const qmm::Route r = qmm::route((int)dt, bits, group_size, M, N, K, true);
   if (r == qmm::kRouteQmv || r == qmm::kRouteQmvMfma)
     return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
@@ -763,6 +816,7 @@ qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
     return fail(QMM_E_ALIGN, "qconv2d_nhwc: x, wq and y must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(biases, 2))
     return fail(QMM_E_ALIGN, "qconv2d_nhwc: scales and biases must be 2-byte aligned");
+  ScratchOrder ord(stream);
   return launched(qmm::launch_qconv_mfma((int)dt, bits, group_size, x, g, wq,
                                          scales, biases, y, (hipStream_t)stream),
                   "qconv2d_nhwc");

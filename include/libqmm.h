@@ -48,12 +48,17 @@
  *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
  *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
  *        the MFMA GEMV on a narrow layer.
- *    Calls queued on one stream are ordered and safe. Calls that run
- *    concurrently on one GPU (different streams, or host threads without
- *    ordering) race on these arrays: serialise them. An overlap makes the
- *    overlapping calls' outputs undefined; the GEMV's counters wrap back to
- *    zero on each call's last arrival, so once overlapping calls of the same
- *    shape have finished, later calls are exact again.
+ *    Calls queued on one stream are ordered by the stream. Calls of these
+ *    entry points (and qmm_fp_t) queued on different streams of one GPU, from
+ *    one host thread or several, are ordered by the library: each waits (on
+ *    the device, hipStreamWaitEvent) for the previous such call's work when
+ *    that call was queued on another stream, through one event per GPU
+ *    recorded after each call's launches. Calls made while their stream is
+ *    being captured into a graph wait for and record nothing: the capturing
+ *    caller must order the graph's launches against concurrent calls on other
+ *    streams (an overlap makes the overlapping calls' outputs undefined; the
+ *    counters wrap back to zero on each call's last arrival, so later calls
+ *    are exact again).
  */
 #ifndef LIBQMM_H
 #define LIBQMM_H

@@ -368,6 +368,34 @@ def test_tile_reads_only_landed_copies(orc, M, N, K, bits):
         assert_parity(from_dev(y), yo, dt, f"tile after NaN launch {it} M{M} N{N} K{K} b{bits}")
 
 
+def test_scratch_calls_on_two_streams(orc):
+    """Calls that use the shared split-K scratch, queued alternately on two
+    streams without any ordering by the caller: the library orders them (an
+    event per device), so every result stays exact."""
+    code = orc_code(orc, "f16")
+    cases = []
+    for (M, N, K, seed) in [(96, 256, 4096, 21), (40, 64, 2048, 22), (8, 512, 8192, 23),
+                            (64, 256, 4096, 24)]:
+        x = synth.normal((M, K), seed=seed, dt="f16")
+        w = synth.normal((N, K), seed=seed + 1, dt="f16")
+        wq, s, b = orc.quantize(w, code, 64, 4)
+        yo, _ = orc.qmm_t(x, wq, s, b, code, 64, 4, nthreads=8)
+        dev = (to_dev(x, "f16"), bytes_to_words_dev(wq), to_dev(s, "f16"), to_dev(b, "f16"))
+        cases.append((dev, yo, (M, N, K)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for i, (dev, yo, shape) in enumerate(cases):
+            st = streams[(i + rep) % 2]
+            with torch.cuda.stream(st):
+                y = torch.empty((shape[0], shape[1]), dtype=torch.float16, device="cuda")
+                outs.append((Q.qmm_t(*dev, 64, 4, out=y), yo, shape))
+    torch.cuda.synchronize()
+    for y, yo, shape in outs:
+        assert_parity(from_dev(y), yo, "f16", f"two streams {shape}")
+
+
 def test_qmm_t_routes_consistently(orc):
     """Around the crossover both kernels agree with the oracle."""
     mx = Q.crossover_m(4, torch.float16, 96, 512, 64)
