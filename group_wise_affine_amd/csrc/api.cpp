@@ -81,7 +81,11 @@ bool g_ord_used[kMaxDev] = {};
 
 class ScratchOrder {
  public:
-  explicit ScratchOrder(void* stream) : st_(static_cast<hipStream_t>(stream)) {
+  // uses_scratch false: the call's kernels touch no scratch (the streaming
+  // GEMV), so it neither waits nor records
+  explicit ScratchOrder(void* stream, bool uses_scratch = true)
+      : st_(static_cast<hipStream_t>(stream)) {
+    if (!uses_scratch) return;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st_, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
     int dev = 0;
@@ -235,7 +239,8 @@ qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                 "bits/dtype; M <= %d rows of x within %zu bytes of LDS for f16); use qmm_t",
                 (long long)K, (long long)qmm::qmv_max_k(bits, (int)dt), qmm::kQmvMfmaMaxM,
                 qmm::kQmvMfmaMaxLds);
-  ScratchOrder ord(stream);
+  ScratchOrder ord(stream, qmm::route((int)dt, bits, group_size, M, N, K, false) !=
+                              qmm::kRouteQmv);
   return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                   biases, M, N, K, y, (hipStream_t)stream),
                   "qmv");
@@ -259,7 +264,6 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
   if (batches * M > kI32 || batches * M * K > ((int64_t)1 << 40) ||
       batches * M * N > ((int64_t)1 << 40) || w_batches * N * K > ((int64_t)1 << 40))
     return fail(QMM_E_SHAPE, "qmm_t_batched: problem too large");
-  ScratchOrder ord(stream);
   // one weight for every batch: the batches are the rows of one product
   if (w_batches == 1)
     return qmm_t(x, wq, scales, biases, dt, batches * M, N, K, group_size, bits, y, stream);
@@ -268,6 +272,7 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
   const int64_t xs = M * K * es, ys = M * N * es, ws = N * (K * bits / 8),
                 ss = N * (K / group_size) * es;
   const qmm::Route r = qmm::route((int)dt, bits, group_size, M, N, K, true);
+  ScratchOrder ord(stream, r != qmm::kRouteQmv);
   // the streaming GEMV's rows: one gathered launch (batch b with weight b)
   if (r == qmm::kRouteQmv)
     return launched(qmm::launch_gather_qmv((int)dt, bits, group_size, x, batches, nullptr, wq,
@@ -764,8 +769,8 @@ qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
   qmm_status st = check_matmul("qmm_t", x, wq, scales, biases, dt, M, N, K,
                                group_size, bits, y);
   if (st) return st;
-  ScratchOrder ord(stream);
   const qmm::Route r = qmm::route((int)dt, bits, group_size, M, N, K, true);
+  ScratchOrder ord(stream, r != qmm::kRouteQmv);
   if (r == qmm::kRouteQmv || r == qmm::kRouteQmvMfma)
     return launched(qmm::launch_qmv((int)dt, bits, group_size, x, wq, scales,
                                     biases, M, N, K, y, (hipStream_t)stream),

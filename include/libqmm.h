@@ -49,8 +49,9 @@
  *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
  *        the MFMA GEMV on a narrow layer.
  *    Calls queued on one stream are ordered by the stream. Calls of these
- *    entry points (and qmm_fp_t) queued on different streams of one GPU, from
- *    one host thread or several, are ordered by the library: each waits (on
+ *    entry points queued on different streams of one GPU, from one host
+ *    thread or several, are ordered by the library (except calls that run on
+ *    the streaming GEMV, which uses no scratch): each waits (on
  *    the device, hipStreamWaitEvent) for the previous such call's work when
  *    that call was queued on another stream, through one event per GPU
  *    recorded after each call's launches. Calls made while their stream is
