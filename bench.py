@@ -331,6 +331,25 @@ def bench_fp_qmm(torch, Q, synth, timer, steps, warmup, bits, gs, M=1024, N=4096
             "workload": f"x f16 [{M},{K}] x W [{N},{K}], fp mode bits {bits} g{gs}"}
 
 
+def bench_qmm_t_prefill(torch, Q, synth, timer, steps, warmup, dt="f16", M=1024, N=4096, K=4096,
+                        bits=4, gs=64):
+    """Affine qmm_t at large M on the MFMA tile kernel: x [M, K] times W [N, K]
+    quantized affine; every step reads a different copy of W from a >= 1 GiB
+    pool."""
+    layer = make_layer(torch, Q, synth, dt, N, K, gs, bits, 1, 1.0 if dt == "f16" else 0.02)
+    wqs, ss, bs, P = pooled(torch, layer)
+    x = to_dev(synth.normal((M, K), seed=0, dt=dt), dt)
+    y = torch.empty((M, N), dtype=x.dtype, device="cuda")
+    ms = timer.run(lambda i: Q.qmm_t(x, wqs[i % P], ss[i % P], bs[i % P], gs, bits, out=y),
+                   steps, warmup)
+    fl = 2 * M * N * K
+    del wqs, ss, bs
+    torch.cuda.empty_cache()
+    return {"us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, "pool_copies": P,
+            "workload": f"x {dt} [{M},{K}] x W [{N},{K}], affine {bits}-bit g{gs}"}
+
+
 def bench_fp_gather(torch, Q, synth, timer, steps, warmup, E=8, T=4, topk=2, N=4096, K=4096):
     """Mixture-of-experts decode with mxfp4 experts: T tokens x [1, K] f16,
     each routed to topk of E experts W_e [N, K] (a seeded permutation, every
@@ -722,8 +741,14 @@ def main():
         r = {"chained_bits4": bench_chained(torch, Q, synth, timer, 4, 10, 2),
              "chained_bits4_affine_packed": bench_chained(torch, Q, synth, timer, 4, 10, 2, True),
              "conv_groups1": bench_conv(torch, Q, synth, timer, 1, 50, 5),
-             "conv_groups2": bench_conv(torch, Q, synth, timer, 2, 50, 5)}
-        print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in r.items()}))
+             "conv_groups2": bench_conv(torch, Q, synth, timer, 2, 50, 5),
+             "prefill_f16_1024x4096x4096": bench_qmm_t_prefill(torch, Q, synth, timer, 20, 5),
+             "prefill_bf16_1024x4096x4096": bench_qmm_t_prefill(torch, Q, synth, timer, 20, 5,
+                                                                "bf16"),
+             "prefill_f16_4096x4096x4096": bench_qmm_t_prefill(torch, Q, synth, timer, 20, 5,
+                                                               M=4096)}
+        print(json.dumps({k: {kk: round(vv, 4) for kk, vv in v.items() if isinstance(vv, float)}
+                          for k, v in r.items()}))
         return
     if args.next_only:
         r = {"gather_qmv_moe_decode": bench_gather(torch, Q, synth, timer, 200, 20),
@@ -810,6 +835,12 @@ def main():
                     bench_chained(torch, Q, synth, timer, bits, 10, 2, packed).items()}
         rows["qmm_t_chained_M1024_f16_g64"] = ch
         log("chained done")
+        rows["qmm_t_prefill_4bit_g64"] = {
+            f"{dt}_{M}x{N}x{K}": round_rows(bench_qmm_t_prefill(torch, Q, synth, timer, 20, 5,
+                                                                dt, M, N, K))
+            for dt, M, N, K in (("f16", 1024, 4096, 4096), ("bf16", 1024, 4096, 4096),
+                                ("f16", 4096, 4096, 4096))}
+        log("prefill rows done")
         rows["qconv2d_64x64x320_3x3_f16_4bit_g64"] = {
             f"groups{g}": {k: round(v, 4) for k, v in
                            bench_conv(torch, Q, synth, timer, g, 50, 5).items()}
