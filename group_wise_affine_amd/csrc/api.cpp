@@ -55,6 +55,22 @@ qmm_status check_k(int64_t K, int gs) {
 
 size_t elem_bytes(qmm_dtype dt) { return dt == QMM_F32 ? 4 : 2; }
 
+// the stream (NULL: the current device's default stream) belongs to the
+// current device, whose memory and static scratch the launch will use
+qmm_status check_stream(const char* tag, void* stream) {
+  if (!stream) return QMM_OK;
+  int cur = -1;
+  hipDevice_t sd = -1;
+  if (hipGetDevice(&cur) != hipSuccess)
+    return fail(QMM_E_LAUNCH, "%s: no current HIP device", tag);
+  if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd) != hipSuccess)
+    return fail(QMM_E_ARG, "%s: stream is not a valid HIP stream", tag);
+  if ((int)sd != cur)
+    return fail(QMM_E_ARG, "%s: stream belongs to device %d, the current device is %d", tag,
+                (int)sd, cur);
+  return QMM_OK;
+}
+
 qmm_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(QMM_E_LAUNCH, "%s: launch failed: %s", what,
@@ -183,6 +199,7 @@ qmm_status qmm_force_kernel(int kernel) {
 qmm_status qmm_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
                         int group_size, int bits, uint32_t* wq, void* scales,
                         void* biases, void* stream) {
+  if (qmm_status ss = check_stream("qmm_quantize", stream)) return ss;
   if (!w || !wq || !scales || !biases)
     return fail(QMM_E_NULL, "qmm_quantize: w, wq, scales and biases must be non-NULL");
   qmm_status st = check_bits_gs(bits, group_size);
@@ -207,6 +224,7 @@ qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
                           const void* biases, qmm_dtype dt, int64_t rows,
                           int64_t K, int group_size, int bits, void* w_out,
                           void* stream) {
+  if (qmm_status ss = check_stream("qmm_dequantize", stream)) return ss;
   if (!wq || !scales || !biases || !w_out)
     return fail(QMM_E_NULL, "qmm_dequantize: wq, scales, biases and w_out must be non-NULL");
   qmm_status st = check_bits_gs(bits, group_size);
@@ -231,6 +249,7 @@ qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
 qmm_status qmv(const void* x, const uint32_t* wq, const void* scales,
                const void* biases, qmm_dtype dt, int64_t M, int64_t N,
                int64_t K, int group_size, int bits, void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmv", stream)) return ss;
   qmm_status st = check_matmul("qmv", x, wq, scales, biases, dt, M, N, K,
                                group_size, bits, y);
   if (st) return st;
@@ -250,6 +269,7 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
                          const void* biases, int64_t batches, int64_t w_batches, qmm_dtype dt,
                          int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
                          void* stream) {
+  if (qmm_status ss = check_stream("qmm_t_batched", stream)) return ss;
   qmm_status st = check_matmul("qmm_t_batched", x, wq, scales, biases, dt, M, N, K, group_size,
                                bits, y);
   if (st) return st;
@@ -317,6 +337,7 @@ qmm_status qmm_t_batched(const void* x, const uint32_t* wq, const void* scales,
 qmm_status qmm_n(const void* x, const uint32_t* wq, const void* scales, const void* biases,
                  qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size, int bits,
                  void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmm_n", stream)) return ss;
   if (!x || !wq || !scales || !biases || !y)
     return fail(QMM_E_NULL, "qmm_n: x, wq, scales, biases and y must be non-NULL");
   qmm_status st = check_bits_gs(bits, group_size);
@@ -416,6 +437,7 @@ qmm_status qmm_gather_qmm(const void* x, int64_t x_batches, const int32_t* lhs_i
                           int64_t w_batches, const int32_t* rhs_indices, int64_t batches,
                           qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
                           int bits, void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmm_gather_qmm", stream)) return ss;
   qmm_status st = check_gather("qmm_gather_qmm", x, x_batches, lhs_indices, wq, scales, biases,
                                w_batches, rhs_indices, batches, dt, M, N, K, group_size, bits,
                                y);
@@ -449,6 +471,7 @@ qmm_status qmm_gather_qmv(const void* x, int64_t x_batches, const int32_t* lhs_i
                           int64_t w_batches, const int32_t* rhs_indices, int64_t batches,
                           qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
                           int bits, void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmm_gather_qmv", stream)) return ss;
   qmm_status st = check_gather("qmm_gather_qmv", x, x_batches, lhs_indices, wq, scales, biases,
                                w_batches, rhs_indices, batches, dt, M, N, K, group_size, bits,
                                y);
@@ -483,6 +506,7 @@ extern "C" {
 qmm_status qmm_fp_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
                            int group_size, int bits, uint32_t* wq, uint8_t* scales,
                            void* stream) {
+  if (qmm_status ss = check_stream("qmm_fp_quantize", stream)) return ss;
   if (!w || !wq || !scales)
     return fail(QMM_E_NULL, "qmm_fp_quantize: w, wq and scales must be non-NULL");
   qmm_status st = check_fp_mode("qmm_fp_quantize", bits, group_size);
@@ -504,6 +528,7 @@ qmm_status qmm_fp_quantize(const void* w, qmm_dtype dt, int64_t rows, int64_t K,
 qmm_status qmm_fp_dequantize(const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
                              int64_t rows, int64_t K, int group_size, int bits, void* w_out,
                              void* stream) {
+  if (qmm_status ss = check_stream("qmm_fp_dequantize", stream)) return ss;
   if (!wq || !scales || !w_out)
     return fail(QMM_E_NULL, "qmm_fp_dequantize: wq, scales and w_out must be non-NULL");
   qmm_status st = check_fp_mode("qmm_fp_dequantize", bits, group_size);
@@ -525,6 +550,7 @@ qmm_status qmm_fp_dequantize(const uint32_t* wq, const uint8_t* scales, qmm_dtyp
 qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
                       int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
                       void* stream) {
+  if (qmm_status ss = check_stream("qmm_fp_qmv", stream)) return ss;
   if (!x || !wq || !scales || !y)
     return fail(QMM_E_NULL, "qmm_fp_qmv: x, wq, scales and y must be non-NULL");
   qmm_status st = check_fp_mode("qmm_fp_qmv", bits, group_size);
@@ -550,6 +576,7 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales, 
 qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
                     int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
                     void* stream) {
+  if (qmm_status ss = check_stream("qmm_fp_t", stream)) return ss;
   if (!x || !wq || !scales || !y)
     return fail(QMM_E_NULL, "qmm_fp_t: x, wq, scales and y must be non-NULL");
   qmm_status st = check_fp_mode("qmm_fp_t", bits, group_size);
@@ -584,6 +611,7 @@ qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales, qm
 qmm_status qmm_fp_n(const void* x, const uint32_t* wq, const uint8_t* scales, qmm_dtype dt,
                     int64_t M, int64_t N, int64_t K, int group_size, int bits, void* y,
                     void* stream) {
+  if (qmm_status ss = check_stream("qmm_fp_n", stream)) return ss;
   if (!x || !wq || !scales || !y)
     return fail(QMM_E_NULL, "qmm_fp_n: x, wq, scales and y must be non-NULL");
   qmm_status st = check_fp_mode("qmm_fp_n", bits, group_size);
@@ -618,6 +646,7 @@ qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches, const int32_t* lh
                              const int32_t* rhs_indices, int64_t batches, qmm_dtype dt, int64_t M,
                              int64_t N, int64_t K, int group_size, int bits, void* y,
                              void* stream) {
+  if (qmm_status ss = check_stream("qmm_fp_gather_qmv", stream)) return ss;
   if (!x || !wq || !scales || !y)
     return fail(QMM_E_NULL, "qmm_fp_gather_qmv: x, wq, scales and y must be non-NULL");
   qmm_status st = check_fp_mode("qmm_fp_gather_qmv", bits, group_size);
@@ -658,6 +687,7 @@ qmm_status qmm_fp_gather_qmv(const void* x, int64_t x_batches, const int32_t* lh
 qmm_status qmm_affine_pack(const uint32_t* wq, const void* scales, const void* biases,
                            qmm_dtype dt, int64_t N, int64_t K, int group_size, int bits,
                            uint32_t* wq_packed, void* sb_packed, void* stream) {
+  if (qmm_status ss = check_stream("qmm_affine_pack", stream)) return ss;
   const bool pow2 = (bits & (bits - 1)) == 0;
   if (!wq || !scales || !biases || !sb_packed || (pow2 && !wq_packed))
     return fail(QMM_E_NULL, "qmm_affine_pack: wq, scales, biases, sb_packed (and wq_packed for "
@@ -731,6 +761,7 @@ static qmm_status packed_gemv(const char* tag, const void* x, const uint32_t* wq
 qmm_status qmv_affine_packed(const void* x, const uint32_t* wq_packed, const void* sb_packed,
                              qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
                              int bits, void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmv_affine_packed", stream)) return ss;
   qmm_status st = check_affine_packed("qmv_affine_packed", x, wq_packed, sb_packed, dt, M, N, K,
                                       group_size, bits, y);
   if (st) return st;
@@ -746,6 +777,7 @@ static int64_t packed_crossover_m(int bits) { return (bits & (bits - 1)) == 0 ? 
 qmm_status qmm_t_affine_packed(const void* x, const uint32_t* wq_packed, const void* sb_packed,
                                qmm_dtype dt, int64_t M, int64_t N, int64_t K, int group_size,
                                int bits, void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmm_t_affine_packed", stream)) return ss;
   const char* tag = "qmm_t_affine_packed";
   qmm_status st = check_affine_packed(tag, x, wq_packed, sb_packed, dt, M, N, K, group_size, bits,
                                       y);
@@ -766,6 +798,7 @@ qmm_status qmm_t_affine_packed(const void* x, const uint32_t* wq_packed, const v
 qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
                  const void* biases, qmm_dtype dt, int64_t M, int64_t N,
                  int64_t K, int group_size, int bits, void* y, void* stream) {
+  if (qmm_status ss = check_stream("qmm_t", stream)) return ss;
   qmm_status st = check_matmul("qmm_t", x, wq, scales, biases, dt, M, N, K,
                                group_size, bits, y);
   if (st) return st;
@@ -789,6 +822,7 @@ qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
                         int stride_h, int stride_w, int pad_h, int pad_w,
                         int groups, qmm_dtype dt, int group_size, int bits,
                         void* y, void* stream) {
+  if (qmm_status ss = check_stream("qconv2d_nhwc", stream)) return ss;
   if (!x || !wq || !scales || !biases || !y)
     return fail(QMM_E_NULL, "qconv2d_nhwc: x, wq, scales, biases and y must be non-NULL");
   qmm_status st = check_bits_gs(bits, group_size);

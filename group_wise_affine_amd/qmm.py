@@ -104,6 +104,9 @@ def _ptr(t):
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {stream.device} but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -161,6 +164,11 @@ def _check_device(*named):
             dev = t.device
         elif t.device != dev:
             raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    # the library launches on the current device (its memory, its static
+    # scratch, its streams)
+    if dev is not None and dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"the tensors are on {dev} but the current device is "
+                         f"cuda:{torch.cuda.current_device()}; call under torch.cuda.device({dev})")
 
 
 def _check_indices(t, name, B):

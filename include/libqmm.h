@@ -35,7 +35,8 @@
  *    returns a status; on error nothing is launched or written and
  *    qmm_last_error() describes the problem. On success the work is queued
  *    asynchronously on `stream` (a hipStream_t passed as void*; NULL is the
- *    default stream). No call synchronizes the host. Device faults surface at
+ *    default stream), which must belong to the current HIP device (QMM_E_ARG
+ *    otherwise); every pointer is memory of that device. No call synchronizes the host. Device faults surface at
  *    the caller's next synchronization.
  *  - Supported: bits in {2,3,4,5,6,8}; group_size in {32,64,128};
  *    K a positive multiple of group_size.
