@@ -105,12 +105,24 @@ __device__ __forceinline__ void load_wchunk_buf(__amdgpu_buffer_rsrc_t r, uint32
 // RING = false the kernel runs one round (every wavefront has at most DEPTH
 // steps); with RING = true slot d is refilled with the step one round later
 // right after it is consumed.
-template <class T, int BITS, int DEPTH, bool RING>
+// vector-memory instructions of one W chunk load (load_wchunk_buf)
+template <int BITS>
+constexpr int wchunk_loads() {
+  return (BITS == 4 || BITS == 8) ? BITS / 4 : (BITS == 2 || BITS == 6) ? BITS / 2 : BITS;
+}
+
+typedef __attribute__((address_space(3))) void mv_lds_t;
+
+// XDMA: x is copied into LDS by buffer loads that write LDS directly (no
+// register round trip, no LDS store instructions), in blocks of 512 elements
+// of one row: the split's range is a power-of-two number of whole blocks
+// (xb_log2 = log2 of blocks per row).
+template <class T, int BITS, int DEPTH, bool RING, bool XDMA>
 __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     uint16_t* __restrict__ y, int M, int N, int K, int gs_log2, uint32_t m2, int xu, int sbu,
-    int ks, int sps, float* __restrict__ ws, unsigned* __restrict__ cnt) {
+    int ks, int sps, float* __restrict__ ws, unsigned* __restrict__ cnt, int xb_log2) {
   // x rows [M][klen + 8] (8 elements of padding per row spread the rows over
   // the LDS banks), then scales [16][G] and biases [16][G]; afterwards the
   // cross-wavefront reduction buffer
@@ -167,9 +179,24 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   // (row m and unit kk of unit u stepped from one division: u grows by 1024)
   const int xrow_units = klen >> 3, xunits = M * xrow_units;
   const int dq = kMvThreads / xrow_units, dr = kMvThreads - dq * xrow_units;
-  uint4 xl[kMvMaxXu];
-  uint32_t xoff[kMvMaxXu], xlds[kMvMaxXu];
-  {
+  uint4 xl[XDMA ? 1 : kMvMaxXu];
+  uint32_t xoff[XDMA ? 1 : kMvMaxXu], xlds[XDMA ? 1 : kMvMaxXu];
+  if constexpr (XDMA) {
+    // block b = wave + 16 i: part b % bpr of row b / bpr (uniform per
+    // wavefront), 64 lanes x 16 bytes
+    const int nxb = M << xb_log2;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int i = 0; i < kMvMaxXu; i++) {
+      const int b = wu + kMvWaves * i;
+      if (b < nxb) {
+        const int m = b >> xb_log2, p = b & ((1 << xb_log2) - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (mv_lds_t*)(xs + m * ldx + p * 512), 16, lane * 16,
+            (int)(((uint32_t)m * K + c0 * 32 + p * 512) * 2), 0, 0);
+      }
+    }
+  } else {
     int m = tid / xrow_units, kk = tid - m * xrow_units;
 #pragma unroll
     for (int i = 0; i < kMvMaxXu; i++) {
@@ -180,13 +207,13 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       kk += dr;
       if (kk >= xrow_units) { kk -= xrow_units; m++; }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < kMvMaxXu; i++) {
-    if (i < xu) {
-      const u32x4_t v =
-          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], 0, 0));
-      xl[i] = make_uint4(v.x, v.y, v.z, v.w);
+    for (int i = 0; i < kMvMaxXu; i++) {
+      if (i < xu) {
+        const u32x4_t v = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], 0, 0));
+        xl[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
     }
   }
   // scale and bias units (rows past N read zero), sbu per thread
@@ -230,16 +257,18 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 
   // ---- x, scales and biases into LDS (waits for those loads only: they
   // were issued first)
+  if constexpr (!XDMA) {
 #pragma unroll
-  for (int i = 0; i < kMvMaxXu; i++) {
-    const int u = tid + kMvThreads * i;
-    uint4 v = xl[i];
-    if constexpr (kExact && BITS == 4)   // piece order 0 4 1 5 2 6 3 7
-      v = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
-                     __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
-                     __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
-                     __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
-    if (i < xu && u < xunits) *reinterpret_cast<uint4*>(xs + xlds[i]) = v;
+    for (int i = 0; i < kMvMaxXu; i++) {
+      const int u = tid + kMvThreads * i;
+      uint4 v = xl[i];
+      if constexpr (kExact && BITS == 4)   // piece order 0 4 1 5 2 6 3 7
+        v = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                       __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                       __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                       __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+      if (i < xu && u < xunits) *reinterpret_cast<uint4*>(xs + xlds[i]) = v;
+    }
   }
 #pragma unroll
   for (int i = 0; i < kMvMaxSb; i++) {
@@ -249,7 +278,20 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       bs4[u] = bl[i];
     }
   }
-  __syncthreads();
+  if constexpr (XDMA) {
+    // every copy and load older than the weight loads (the youngest
+    // DEPTH * wchunk_loads of this wavefront) has landed, the LDS stores
+    // have completed, then the barrier; no fence, which would also wait for
+    // the weight loads
+    constexpr int kW = DEPTH * wchunk_loads<BITS>();
+    static_assert(kW < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((kW & 15) | ((kW >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  } else {
+    __syncthreads();
+  }
 
   // exact codes: xg[gl][m] = sum of x[m] over group gl of the split's range
   // (16 rows, rows >= M zero), after the scales and biases
@@ -466,15 +508,33 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
 
 template <class T, int BITS, int DEPTH, bool RING>
 hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st) {
+  constexpr bool kExact = __is_same(T, BF16) && (BITS == 4 || BITS == 8);
   const uint32_t m2 = Pack<BITS>::kMask | (Pack<BITS>::kMask << 16);
   const int xu = (L.M * (p.klen / 8) + kMvThreads - 1) / kMvThreads;
   const int sbu = ((15 + 32 * (L.K / L.gs) + 15) / 16 + kMvThreads - 1) / kMvThreads;
-  hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING>), dim3((L.N + 15) / 16, p.ks),
-                     dim3(kMvThreads), qmv_mfma_lds(L.M, p.klen, L.K, L.gs, __is_same(T, BF16) && (BITS == 4 || BITS == 8)), st,
-                     static_cast<const uint16_t*>(L.x), reinterpret_cast<const uint8_t*>(L.wq),
-                     static_cast<const uint16_t*>(L.s), static_cast<const uint16_t*>(L.b),
-                     static_cast<uint16_t*>(L.y), L.M, L.N, L.K, ilog2(L.gs), m2, xu, sbu, p.ks,
-                     p.sps, L.ws, L.cnt);
+  const size_t lds = qmv_mfma_lds(L.M, p.klen, L.K, L.gs, kExact);
+  // direct x copies: every split's range (all of the same length) is whole
+  // 512-element blocks, a power of two of them per row, at most 8 per
+  // wavefront (the exact-code path permutes x and sums its groups on the
+  // way, through registers)
+  const int bpr = p.klen / 512;
+  const bool xdma = !kExact && p.klen % 512 == 0 && (int64_t)p.ks * p.klen == L.K &&
+                    (bpr & (bpr - 1)) == 0 && L.M * bpr <= kMvWaves * kMvMaxXu;
+  auto go = [&]<bool XD>() {
+    hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING, XD>), dim3((L.N + 15) / 16, p.ks),
+                       dim3(kMvThreads), lds, st, static_cast<const uint16_t*>(L.x),
+                       reinterpret_cast<const uint8_t*>(L.wq), static_cast<const uint16_t*>(L.s),
+                       static_cast<const uint16_t*>(L.b), static_cast<uint16_t*>(L.y), L.M, L.N,
+                       L.K, ilog2(L.gs), m2, xu, sbu, p.ks, p.sps, L.ws, L.cnt,
+                       xdma ? ilog2(bpr) : 0);
+  };
+  if constexpr (!kExact) {
+    if (xdma) {
+      go.template operator()<true>();
+      return hipGetLastError();
+    }
+  }
+  go.template operator()<false>();
   return hipGetLastError();
 }
 
