@@ -116,7 +116,8 @@ typedef __attribute__((address_space(3))) void mv_lds_t;
 // XDMA: x is copied into LDS by buffer loads that write LDS directly (no
 // register round trip, no LDS store instructions), in blocks of 512 elements
 // of one row: the split's range is a power-of-two number of whole blocks
-// (xb_log2 = log2 of blocks per row).
+// (xb_log2 = log2 of blocks per row). x then stays in natural order, and the
+// exact 4-bit path permutes each A fragment in registers instead.
 template <class T, int BITS, int DEPTH, bool RING, bool XDMA>
 __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
@@ -347,6 +348,11 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       const int cx = c < c1 ? c : c1 - 1;
       uint4 a = make_uint4(0, 0, 0, 0);
       if (n < M) a = *reinterpret_cast<const uint4*>(xs + n * ldx + (cx - c0) * 32 + 8 * g);
+      if constexpr (XDMA && BITS == 4)   // copied in natural order: piece order 0 4 1 5 2 6 3 7
+        a = make_uint4(__builtin_amdgcn_perm(a.z, a.x, 0x05040100u),
+                       __builtin_amdgcn_perm(a.z, a.x, 0x07060302u),
+                       __builtin_amdgcn_perm(a.w, a.y, 0x05040100u),
+                       __builtin_amdgcn_perm(a.w, a.y, 0x07060302u));
       uint4 b;
       if constexpr (BITS == 4) {
         const uint32_t w = t[i];
@@ -515,10 +521,9 @@ hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st)
   const size_t lds = qmv_mfma_lds(L.M, p.klen, L.K, L.gs, kExact);
   // direct x copies: every split's range (all of the same length) is whole
   // 512-element blocks, a power of two of them per row, at most 8 per
-  // wavefront (the exact-code path permutes x and sums its groups on the
-  // way, through registers)
+  // wavefront
   const int bpr = p.klen / 512;
-  const bool xdma = !kExact && p.klen % 512 == 0 && (int64_t)p.ks * p.klen == L.K &&
+  const bool xdma = p.klen % 512 == 0 && (int64_t)p.ks * p.klen == L.K &&
                     (bpr & (bpr - 1)) == 0 && L.M * bpr <= kMvWaves * kMvMaxXu;
   auto go = [&]<bool XD>() {
     hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING, XD>), dim3((L.N + 15) / 16, p.ks),
@@ -528,11 +533,9 @@ hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st)
                        L.K, ilog2(L.gs), m2, xu, sbu, p.ks, p.sps, L.ws, L.cnt,
                        xdma ? ilog2(bpr) : 0);
   };
-  if constexpr (!kExact) {
-    if (xdma) {
-      go.template operator()<true>();
-      return hipGetLastError();
-    }
+  if (xdma) {
+    go.template operator()<true>();
+    return hipGetLastError();
   }
   go.template operator()<false>();
   return hipGetLastError();
