@@ -196,25 +196,20 @@ Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allo
   //    costs ~5 us at M = 1 on a 9.4 MB layer, ~7 at 2 and ~10 at 3-4; the
   //    MFMA GEMV is nearly flat in M (6.2-7.0 us f16 on 4096 x 4096, 5.5-6.4
   //    on 8192 x 2048) but slower at M = 1;
-  //  * bf16 with 4-bit codes (the MFMA GEMV multiplies the codes and copies
-  //    x through registers) costs 8.3-9.7 us there, and on layers of >= 512
-  //    blocks of 16 rows (two rounds of workgroups) 9.3-10.6 us, where the
-  //    streaming GEMV wins up to 4 rows; other bf16 widths (hi/lo MFMAs, x
-  //    copied straight into LDS) take the MFMA GEMV from 3 rows;
-  //  * bf16 with 8-bit codes: the streaming GEMV works in fp32 (33 us at
+  //  * bf16: the MFMA GEMV (7.9-8.8 us on 4096 x 4096 4-bit, 6.9-7.8 on
+  //    8192 x 2048) wins from 3 rows on every layer, the streaming GEMV up to
+  //    2; with 8-bit codes the streaming GEMV works in fp32 (33 us at
   //    M = 1), so the MFMA GEMV takes every M it fits;
-  //  * layers of at most 2^22 weights: the two GEMVs are within a few % of
-  //    each other at 2-4 rows; the tile kernel costs 8-17 us at M <= 32
-  //    whatever the layer size, so these layers, whose streaming passes take
-  //    ~1 us, stay on the streaming GEMV up to 32 rows.
+  //  * the tile kernel costs 8-18 us at M <= 32 whatever the layer size, so
+  //    layers of at most 2^22 weights, whose streaming passes take ~1 us,
+  //    stay on the streaming GEMV up to 32 rows.
   const bool gemv_fp32 = dt == 1 && bits == 8;
   const bool small = N * K <= ((int64_t)1 << 22);
   int64_t m0;   // first M on the MFMA GEMV
   if (gemv_fp32 || !dot2_ok) m0 = 1;
   else if (dt == 0 && K > 8192 && N >= 4096) m0 = 1;   // long rows: few streaming passes fit
   else if (dt == 0) m0 = N * K >= ((int64_t)1 << 23) ? 2 : 3;
-  else if (small) m0 = 5;
-  else m0 = (bits == 4 && N >= 8192) ? 5 : 3;
+  else m0 = 3;
   if (mfma_ok && M >= m0) return kRouteQmvMfma;
   if (!allow_tile) return dot2_ok ? kRouteQmv : kRouteNone;
   if (dot2_ok) {
