@@ -171,6 +171,33 @@ __device__ __forceinline__ void decode_word(uint32_t word, float* v) {
   }
 }
 
+// One 32-bit word of codes (8 E2M1 or 4 E4M3) -> T pairs (k, k + 1), by the
+// scale-1 conversions (exact: every code value is a T value)
+template <class T, int BITS>
+__device__ __forceinline__ void decode_pairs(uint32_t word, uint32_t* p) {
+  if constexpr (BITS == 4) {
+    if constexpr (__is_same(T, F16)) {
+      p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0));
+      p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1));
+      p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2));
+      p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3));
+    } else {
+      p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 0));
+      p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 1));
+      p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 2));
+      p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 3));
+    }
+  } else {
+    if constexpr (__is_same(T, F16)) {
+      p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false));
+      p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true));
+    } else {
+      p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+      p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
+    }
+  }
+}
+
 // T(s * v) for s >= 0 and an exact product: the word of the product with the
 // sign of v restored (the compiler fuses a product converted to f16 into
 // v_fma_mixlo_f16 with a +0 addend, which turns a -0 product into +0).
@@ -227,9 +254,11 @@ __global__ __launch_bounds__(256) void fp_dequantize_kernel(const uint8_t* __res
 // ---------------------------------------------------------------- GEMV
 // y[m, n] = T(sum over groups g of scale_T[n, g] * sum_{k in g} x[m, k] *
 // value[n, k]) with fp32 accumulation. Workgroup = WV wavefronts x R rows of
-// W for one row m of x (blockIdx.y); x[m] is staged in LDS as fp32. Each
-// lane takes 16-byte units of a row (32 E2M1 or 16 E4M3 codes), unit u at
-// lane u % 64, for R rows at once so that their loads overlap.
+// W for one row m of x (blockIdx.y); x[m] is staged in LDS as T. Each lane
+// takes 16-byte units of a row (32 E2M1 or 16 E4M3 codes), unit u at lane
+// u % 64, for R rows at once so that their loads overlap; the codes are
+// decoded into T pairs and multiplied with the activation pairs by
+// v_dot2_f32_{f16,bf16} (exact products, fp32 sums).
 // Wavefronts per workgroup (WV): 8 for E4M3 codes; for E2M1, 8 when that
 // still gives 512 workgroups at 4 rows per wavefront (several rows of x or
 // gathered products), else 4. Measured on 4096 x 4096: M = 1 mxfp8 6.44 /
@@ -251,7 +280,7 @@ __global__ __launch_bounds__(64 * WV) void fp_qmv_kernel(const typename T::word*
                                                      const uint8_t* __restrict__ sc,
                                                      typename T::word* __restrict__ y, int N,
                                                      int K, FpBatch bt) {
-  extern __shared__ float xs[];
+  extern __shared__ uint4 xs4[];   // x[m] as T words, natural order
   const int m = blockIdx.y;
   if constexpr (GA) {
     const int z = blockIdx.z;
@@ -269,8 +298,11 @@ __global__ __launch_bounds__(64 * WV) void fp_qmv_kernel(const typename T::word*
     sc += (int64_t)zw * N * (K / GS);
     y += (int64_t)z * bt.M * N;
   }
-  const typename T::word* xr = x + (int64_t)m * K;
-  for (int k = threadIdx.x; k < K; k += 64 * WV) xs[k] = to_f32(T{}, xr[k]);
+  {
+    // rows of x are 16-byte aligned (x is, and K % 32 == 0)
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)m * K);
+    for (int u = threadIdx.x; u < K / 8; u += 64 * WV) xs4[u] = xr[u];
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -289,20 +321,23 @@ __global__ __launch_bounds__(64 * WV) void fp_qmv_kernel(const typename T::word*
       const int n = n0 + r < N ? n0 + r : N - 1;
       q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wq + n * rb) + u);
     }
-    const float4* xv = reinterpret_cast<const float4*>(xs + u * kCodes);
-    float xf[kCodes];
+    // the unit's activations as T pairs (k, k + 1)
+    const uint4* xv = xs4 + u * (kCodes / 8);
+    uint32_t xw[kCodes / 2];
 #pragma unroll
-    for (int i = 0; i < kCodes / 4; i++) {
-      const float4 t = xv[i];
-      xf[4 * i] = t.x; xf[4 * i + 1] = t.y; xf[4 * i + 2] = t.z; xf[4 * i + 3] = t.w;
+    for (int i = 0; i < kCodes / 8; i++) {
+      const uint4 t = xv[i];
+      xw[4 * i] = t.x; xw[4 * i + 1] = t.y; xw[4 * i + 2] = t.z; xw[4 * i + 3] = t.w;
     }
 #pragma unroll
     for (int r = 0; r < kFpRows; r++) {
       const int n = n0 + r < N ? n0 + r : N - 1;
       const uint32_t words[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
-      float v[kCodes];
+      // codes decoded into T pairs (k, k + 1), exactly: every E2M1 and E4M3
+      // value is a T value
+      uint32_t vp[kCodes / 2];
 #pragma unroll
-      for (int i = 0; i < 4; i++) decode_word<BITS>(words[i], v + i * (kCodes / 4));
+      for (int i = 0; i < 4; i++) decode_pairs<T, BITS>(words[i], vp + i * (kCodes / 8));
       // groups within the unit: BITS 4 -> 32 codes = 1 (GS 32) or 2 (GS 16)
       // groups; BITS 8 -> 16 codes = half of a group of 32
       constexpr int kGroups = kCodes >= GS ? kCodes / GS : 1;
@@ -310,9 +345,12 @@ __global__ __launch_bounds__(64 * WV) void fp_qmv_kernel(const typename T::word*
       const int64_t g0 = (int64_t)u * kCodes / GS;
 #pragma unroll
       for (int g = 0; g < kGroups; g++) {
+        // sum of x * value over the group's codes in fp32 (products of two
+        // T values are exact in fp32)
         float gsum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kLen; j++) gsum = fmaf(xf[g * kLen + j], v[g * kLen + j], gsum);
+        for (int j = 0; j < kLen / 2; j++)
+          gsum = dot2(T{}, xw[g * kLen / 2 + j], vp[g * kLen / 2 + j], gsum);
         acc[r] = fmaf(scale_t<T, GS>(sc[n * G + g0 + g]), gsum, acc[r]);
       }
     }
@@ -354,7 +392,7 @@ hipError_t fp_qmv_r(const void* x, const uint32_t* wq, const uint8_t* sc, int64_
   const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)M,
                   bt ? (unsigned)bt->B : 1u);
   auto go = [&](auto kern, const FpBatch& b) {
-    hipLaunchKernelGGL(kern, grid, dim3(64 * WV), (size_t)K * 4, st,
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WV), (size_t)K * 2, st,
                        static_cast<const typename T::word*>(x),
                        reinterpret_cast<const uint8_t*>(wq), sc,
                        static_cast<typename T::word*>(y), (int)N, (int)K, b);
