@@ -593,9 +593,13 @@ qmm_status qmm_fp_t(const void* x, const uint32_t* wq, const uint8_t* scales, qm
     return fail(QMM_E_SHAPE, "qmm_fp_t: problem too large");
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
     return fail(QMM_E_ALIGN, "qmm_fp_t: x, wq and y must be 16-byte aligned");
-  ScratchOrder ord(stream);
-  const bool gemv = M < qmm::fp_crossover_m(bits, group_size, (int)dt) && M <= 65535 &&
-                    K <= qmm::kFpMaxK;
+  // (qmm_force_kernel: the GEMV or the tile kernel where it takes the shape)
+  const qmm::Route f = qmm::forced_route();
+  const bool gemv = (f == qmm::kRouteTile   ? false
+                     : f == qmm::kRouteQmv ? true
+                                           : M < qmm::fp_crossover_m(bits, group_size, (int)dt, N, K)) &&
+                    M <= 65535 && K <= qmm::kFpMaxK;
+  ScratchOrder ord(stream, !gemv);
   if (gemv)
     return launched(qmm::launch_fp_qmv((int)dt, bits, group_size, x, wq, scales, M, N, K, y,
                                        (hipStream_t)stream),

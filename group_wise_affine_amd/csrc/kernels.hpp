@@ -142,7 +142,7 @@ hipError_t launch_fp_qmm_mfma(int dt, int bits, int gs, const void* x, const uin
                               const uint8_t* scales, int64_t M, int64_t N, int64_t K, void* y,
                               hipStream_t st);
 // Rows of x from which qmm_fp_t takes the tile kernel instead of the fp GEMV.
-int fp_crossover_m(int bits, int gs, int dt);
+int fp_crossover_m(int bits, int gs, int dt, int64_t N, int64_t K);
 // Gathered fp GEMV: for z < B, y[z] = x[lidx[z]] . dequant(W[ridx[z]])^T with
 // x [nxb, M, K], W [nwb, N, K] (codes and scale bytes), y [B, M, N]; a null
 // index array means z, indices are clamped into range. B <= 65535.
@@ -198,5 +198,6 @@ int64_t qmv_max_k(int bits, int dt);
 // Measurement override: route() returns r wherever that kernel takes the
 // shape (kRouteNone: the automatic choice everywhere).
 void force_route(Route r);
+Route forced_route();   // the current override (kRouteNone: automatic)
 
 }  // namespace qmm

@@ -121,13 +121,19 @@ hipError_t launch_apk_mfma(int dt, int bits, int gs, const void* x, const uint32
   return launch_tile_apk(dt, bits, a, st);
 }
 
-// The fp GEMV reads W once per row of x; the tile kernel once per 128 rows.
-// Measured (f16, 4096 x 4096 and 2048 x 8192, hot weights): the GEMV takes
-// 6.9-9.6 us at M = 2 and 8.1-12.4 us at M = 4, the tile kernel 8.1-11.0 us
-// at M = 8 and about the same below; E4M3 codes cost the GEMV more per row.
-int fp_crossover_m(int bits, int gs, int dt) {
-  (void)gs; (void)dt;
-  return bits == 8 ? 3 : 4;
+// The fp GEMV reads W once per row of x (from L2 after the first); the tile
+// kernel once per 128 rows, at a nearly constant 8.4-12 us for M <= 8.
+// Graph-timed with each kernel forced (f16, cold weights, 4096 x 4096,
+// 2048 x 8192 and 8192 x 2048): the GEMV wins up to M = 4 (mxfp4), 6 (nvfp4)
+// and 2 (mxfp8) on 4096 x 4096, to M = 6-8 / 8 / 4 on the long rows of
+// 2048 x 8192, and to M = 3 / 4 / 2 on 8192 x 2048, whose 8192 rows per row
+// of x cost the GEMV most. Returns the first M on the tile kernel.
+int fp_crossover_m(int bits, int gs, int dt, int64_t N, int64_t K) {
+  (void)dt;
+  const bool wide = N >= 8192, deep = K >= 8192;
+  if (bits == 8) return wide ? 3 : deep ? 5 : 3;   // mxfp8
+  if (gs == 16) return wide ? 5 : deep ? 9 : 7;    // nvfp4
+  return wide ? 4 : deep ? 8 : 5;                  // mxfp4
 }
 
 hipError_t launch_qconv_mfma(int dt, int bits, int gs, const void* x,
@@ -174,6 +180,7 @@ std::atomic<int> g_forced{kRouteNone};   // measurement override (force_route)
 }  // namespace
 
 void force_route(Route r) { g_forced.store((int)r, std::memory_order_relaxed); }
+Route forced_route() { return (Route)g_forced.load(std::memory_order_relaxed); }
 
 int64_t qmv_max_k(int bits, int dt) {
   const int64_t words = (bits == 8 && dt == 1) ? 34 : 18;

@@ -211,8 +211,9 @@ qmm_status qmm_fp_qmv(const void* x, const uint32_t* wq, const uint8_t* scales,
                       int group_size, int bits, void* y, void* stream);
 
 /*
- * The same product for any M: the qmm_fp_qmv GEMV for a few rows of x, the
- * MFMA tile kernel beyond (W dequantized on chip to dt: scale_T * value is
+ * The same product for any M: the qmm_fp_qmv GEMV for a few rows of x (up
+ * to 2-8 by mode and shape, from timings of both kernels), the MFMA tile
+ * kernel beyond (W dequantized on chip to dt: scale_T * value is
  * exact in dt whenever it lies in dt's range, which always holds for bf16
  * and for f16 scales from 2^-14 to 2^14; fp32 accumulation). K a positive
  * multiple of 32 (below 2^22 on the tile kernel, up to 16384 on the GEMV);
@@ -431,8 +432,9 @@ int64_t qmm_crossover_m(qmm_dtype dt, int bits, int group_size, int64_t N, int64
 /*
  * For measurement: from now on, in this process, qmm_t, qmv and
  * qmm_t_batched run `kernel` (QMM_KERNEL_GEMV, _MFMA_GEMV or _TILE) for every
- * shape that kernel takes (qmv never runs the tile kernel) and the automatic
- * choice otherwise; QMM_KERNEL_NONE restores the automatic choice
+ * shape that kernel takes (qmv never runs the tile kernel), and qmm_fp_t its
+ * GEMV for QMM_KERNEL_GEMV and its tile kernel for QMM_KERNEL_TILE; the
+ * automatic choice otherwise. QMM_KERNEL_NONE restores the automatic choice
  * everywhere. Not synchronised with calls in flight on other threads.
  * Returns QMM_E_ARG for other values.
  */

@@ -170,18 +170,25 @@ def test_fp_qmm_t_full_size(orc, name, bits, gs):
         assert_parity(yg[r0:r1], yo, "f16", f"fp_qmm_t {name} 1024x4096x4096 rows {r0}..{r1}")
 
 
-def test_fp_qmm_t_routes_consistently(orc):
-    """Around the GEMV / tile crossover both kernels agree with the oracle."""
-    dt, N, K, gs, bits = "f16", 96, 512, 32, 4
+@pytest.mark.parametrize("name,bits,gs", MODES)
+def test_fp_qmm_t_routes_consistently(orc, name, bits, gs):
+    """Around the GEMV / tile crossover both kernels (each forced, then the
+    automatic choice) agree with the oracle."""
+    dt, N, K = "f16", 96, 512
     w = _weights(N, K, gs, dt, seed=5, big=16.0)
     wq, sc = orc.fp_quantize(w, orc.F16, gs, bits)
-    for M in (2, 3, 4, 5, 9, 33):
-        x = synth.normal((M, K), seed=M, dt=dt)
-        yo, _ = orc.fp_qmm_t(x, wq, sc, orc.F16, gs, bits, nthreads=8)
-        y = Q.fp_qmm_t(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(), gs,
-                       bits)
-        torch.cuda.synchronize()
-        assert_parity(from_dev(y), yo, dt, f"fp_qmm_t crossover M{M}")
+    try:
+        for M in (2, 3, 4, 5, 9, 33):
+            x = synth.normal((M, K), seed=M, dt=dt)
+            yo, _ = orc.fp_qmm_t(x, wq, sc, orc.F16, gs, bits, nthreads=8)
+            for kern in (Q.KERNEL_GEMV, Q.KERNEL_TILE, Q.KERNEL_NONE):
+                Q.force_kernel(kern)
+                y = Q.fp_qmm_t(to_dev(x, dt), bytes_to_words_dev(wq), torch.from_numpy(sc).cuda(),
+                               gs, bits)
+                torch.cuda.synchronize()
+                assert_parity(from_dev(y), yo, dt, f"fp_qmm_t {name} M{M} kernel {kern}")
+    finally:
+        Q.force_kernel(Q.KERNEL_NONE)
 
 
 def _idx(v):
