@@ -20,20 +20,26 @@ hipError_t launch_qmv(int dt, int bits, int gs, const void* x,
                       int64_t M, int64_t N, int64_t K, void* y,
                       hipStream_t st);
 
-// GEMV on the matrix cores, f16 / bf16, 1 <= M <= kQmvMfmaMaxM, K < kQmvMfmaMaxK
-// (byte offsets of its buffer loads stay below 2^31), x[0:M] small enough
-// for LDS (qmv_mfma_fits).
-constexpr int kQmvMfmaMaxM = 16;
+// GEMV on the matrix cores, f16 / bf16, 1 <= M <= kQmvMfmaMaxM (one 16-row
+// tile of x, two above 16 rows), K < kQmvMfmaMaxK (byte offsets of its
+// buffer loads stay below 2^31), x[0:M] small enough for LDS
+// (qmv_mfma_fits).
+constexpr int kQmvMfmaMaxM = 32;
 constexpr int64_t kQmvMfmaMaxK = (int64_t)1 << 25;
 constexpr size_t kQmvMfmaMaxLds = 160 * 1024 - 256;   // LDS per CU, less static LDS
+// split-K partial tiles of the MFMA GEMV (floats) and its arrival counters
+// (one per row block of a split launch)
+constexpr int64_t kQmvMfmaWsFloats = 256 * 8 * 256;
+constexpr int kQmvMfmaCounters = 256;
 // K split of the MFMA GEMV: layers with fewer than 256 blocks of 16 rows
 // split K into ks ranges of sps steps (128 codes each) so that the launch
-// fills the CUs, as long as each range keeps all 16 wavefronts busy;
-// klen = codes of the longest range.
+// fills the CUs, as long as each range keeps all 16 wavefronts busy; with
+// more than 16 rows of x, ranges of at most 16 steps, so that 32 rows of x
+// fit in LDS; klen = codes of the longest range.
 struct QmvMfmaPlan {
   int ks, sps, klen;
 };
-inline QmvMfmaPlan qmv_mfma_plan(int64_t N, int64_t K) {
+inline QmvMfmaPlan qmv_mfma_plan(int64_t N, int64_t K, int64_t M) {
   const int64_t nsteps = (K / 32 + 3) / 4, rb = (N + 15) / 16;
   int64_t ks = 1;
   if (rb < 256) {
@@ -42,6 +48,7 @@ inline QmvMfmaPlan qmv_mfma_plan(int64_t N, int64_t K) {
     if (ks > nsteps / 16) ks = nsteps / 16;   // every wavefront keeps a step
     if (ks < 1) ks = 1;
   }
+  if (M > 16 && ks < (nsteps + 15) / 16) ks = (nsteps + 15) / 16;
   const int64_t sps = (nsteps + ks - 1) / ks;
   ks = (nsteps + sps - 1) / sps;          // no empty range
   const int64_t klen = sps * 128 < K ? sps * 128 : K;
@@ -53,7 +60,13 @@ inline bool qmv_mfma_exact(int dt, int bits) { return dt == 1 && (bits == 4 || b
 size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs, bool xsums);
 inline bool qmv_mfma_fits(int64_t M, int64_t N, int64_t K, int gs, int dt, int bits) {
   if (M < 1 || M > kQmvMfmaMaxM || K >= kQmvMfmaMaxK) return false;
-  const QmvMfmaPlan p = qmv_mfma_plan(N, K);
+  const QmvMfmaPlan p = qmv_mfma_plan(N, K, M);
+  // a split launch: at most 8 ranges, one counter per row block, the
+  // partial tiles within the workspace
+  const int64_t rb = (N + 15) / 16;
+  if (p.ks > 8 || (p.ks > 1 && (rb > kQmvMfmaCounters ||
+                                rb * p.ks * 256 * (M > 16 ? 2 : 1) > kQmvMfmaWsFloats)))
+    return false;
   // the workgroup's 1024 threads copy x with at most 8 16-byte loads each,
   // the scales and biases with at most 2
   return qmv_mfma_lds(M, p.klen, K, gs, qmv_mfma_exact(dt, bits)) <= kQmvMfmaMaxLds &&

@@ -5,13 +5,13 @@
 
 namespace qmm {
 
-// Split-K workspace of the MFMA GEMV: 16 x 16 fp32 partial tiles of at most
-// 256 row blocks x 8 splits, and one arrival counter per row block (zero at
-// load; a wrapping increment brings it back to zero on the last arrival of
-// each call). Calls that overlap on one device share them.
-constexpr int kMvWsFloats = 256 * 8 * 256;
-__device__ float g_mv_ws[kMvWsFloats];
-__device__ unsigned g_mv_cnt[256];
+// Split-K workspace of the MFMA GEMV: fp32 partial tiles (16 x 16, or two of
+// them above 16 rows of x) of every row block and split of a launch, and one
+// arrival counter per row block (zero at load; a wrapping increment brings
+// it back to zero on the last arrival of each call). Calls that overlap on
+// one device share them.
+__device__ float g_mv_ws[kQmvMfmaWsFloats];
+__device__ unsigned g_mv_cnt[kQmvMfmaCounters];
 
 namespace {
 
@@ -45,10 +45,11 @@ hipError_t launch_qmv_mfma_bf16(int bits, const MvLaunch& L, hipStream_t st);
 // LDS of the GEMV kernel: rows of x over a K range of klen plus padding and
 // the 16 rows of scales and biases, or the reduction buffer if larger
 size_t qmv_mfma_lds(int64_t M, int64_t klen, int64_t K, int gs, bool xsums) {
+  const size_t mt = M > 16 ? 2 : 1;   // 16-row tiles of x
   const size_t xb = (((size_t)M * (klen + 8) + 7) & ~(size_t)7) * 2;
   const size_t sb = (size_t)2 * 16 * ((15 + 32 * (K / gs) + 15) / 16);
-  const size_t gb = xsums ? (size_t)((klen + gs - 1) / gs) * 16 * 4 : 0;   // group sums of x
-  const size_t rb = (size_t)kMvThreads * 4 * 4;
+  const size_t gb = xsums ? (size_t)((klen + gs - 1) / gs) * 16 * mt * 4 : 0;   // group sums of x
+  const size_t rb = (size_t)kMvThreads * 4 * 4 * mt;
   return xb + sb + gb > rb ? xb + sb + gb : rb;
 }
 

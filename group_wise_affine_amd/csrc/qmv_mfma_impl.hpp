@@ -113,12 +113,14 @@ constexpr int wchunk_loads() {
 
 typedef __attribute__((address_space(3))) void mv_lds_t;
 
+// MT: 16-row tiles of x (1 or 2): with 2, rows 16..31 of x take a second A
+// fragment and accumulator per MFMA, sharing the dequantized W fragment.
 // XDMA: x is copied into LDS by buffer loads that write LDS directly (no
 // register round trip, no LDS store instructions), in blocks of 512 elements
 // of one row: the split's range is a power-of-two number of whole blocks
 // (xb_log2 = log2 of blocks per row). x then stays in natural order, and the
 // exact 4-bit path permutes each A fragment in registers instead.
-template <class T, int BITS, int DEPTH, bool RING, bool XDMA>
+template <class T, int BITS, int DEPTH, bool RING, bool XDMA, int MT>
 __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -295,12 +297,13 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   }
 
   // exact codes: xg[gl][m] = sum of x[m] over group gl of the split's range
-  // (16 rows, rows >= M zero), after the scales and biases
+  // (16 MT rows, rows >= M zero), after the scales and biases
+  constexpr int XR = 16 * MT;
   float* xg = reinterpret_cast<float*>(bs4 + sbun);
   if constexpr (kExact) {
     const int ngl = (klen + (1 << gs_log2) - 1) >> gs_log2;
-    for (int t = tid; t < ngl * 16; t += kMvThreads) {
-      const int m = t & 15, gl = t >> 4;
+    for (int t = tid; t < ngl * XR; t += kMvThreads) {
+      const int m = t & (XR - 1), gl = t / XR;
       float sum = 0.0f;
       if (m < M) {
         const uint4* xp = reinterpret_cast<const uint4*>(xs + m * ldx + (gl << gs_log2));
@@ -317,7 +320,9 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     __syncthreads();
   }
 
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t acc[MT];
+#pragma unroll
+  for (int h = 0; h < MT; h++) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // exact codes: chunk i of the step on MFMA i (see the header), groups of
   // gs codes applied to the fp32 sums as s * D + (b - 128 s) * sum(x)
   auto compute_exact = [&](int j, int d) QMM_INLINE {
@@ -341,18 +346,25 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       t[2 * W + w] = r[0]; t[3 * W + w] = r[1];
     }
     const int cpg_log2 = gs_log2 - 5;                // chunks per group: 1, 2, 4
-    float4_t dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t dsum[MT];
+#pragma unroll
+    for (int h = 0; h < MT; h++) dsum[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int c = cs + i;
       const int cx = c < c1 ? c : c1 - 1;
-      uint4 a = make_uint4(0, 0, 0, 0);
-      if (n < M) a = *reinterpret_cast<const uint4*>(xs + n * ldx + (cx - c0) * 32 + 8 * g);
-      if constexpr (XDMA && BITS == 4)   // copied in natural order: piece order 0 4 1 5 2 6 3 7
-        a = make_uint4(__builtin_amdgcn_perm(a.z, a.x, 0x05040100u),
-                       __builtin_amdgcn_perm(a.z, a.x, 0x07060302u),
-                       __builtin_amdgcn_perm(a.w, a.y, 0x05040100u),
-                       __builtin_amdgcn_perm(a.w, a.y, 0x07060302u));
+      uint4 a[MT];
+#pragma unroll
+      for (int h = 0; h < MT; h++) {
+        a[h] = make_uint4(0, 0, 0, 0);
+        if (n + 16 * h < M)
+          a[h] = *reinterpret_cast<const uint4*>(xs + (n + 16 * h) * ldx + (cx - c0) * 32 + 8 * g);
+        if constexpr (XDMA && BITS == 4)   // copied in natural order: piece order 0 4 1 5 2 6 3 7
+          a[h] = make_uint4(__builtin_amdgcn_perm(a[h].z, a[h].x, 0x05040100u),
+                            __builtin_amdgcn_perm(a[h].z, a[h].x, 0x07060302u),
+                            __builtin_amdgcn_perm(a[h].w, a[h].y, 0x05040100u),
+                            __builtin_amdgcn_perm(a[h].w, a[h].y, 0x07060302u));
+      }
       uint4 b;
       if constexpr (BITS == 4) {
         const uint32_t w = t[i];
@@ -373,7 +385,8 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
         }
         b = make_uint4(p[0], p[1], p[2], p[3]);
       }
-      dsum = mfma16(BF16{}, a, b, dsum);
+#pragma unroll
+      for (int h = 0; h < MT; h++) dsum[h] = mfma16(BF16{}, a[h], b, dsum[h]);
       if (((i + 1) & ((1 << cpg_log2) - 1)) == 0) {
         // end of a group: its scale and bias (zero past the split's end)
         const uint32_t keep = ~(uint32_t)((c1 - 1 - c) >> 31);
@@ -381,11 +394,14 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
         const float sf = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(ssb + gi) & keep));
         const float bfl = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(bsb + gi) & keep));
         const float bq = bfl - 128.0f * sf * (BITS == 4 ? 1.0f : 0.0f);
-        const float4_t xsum = *reinterpret_cast<const float4_t*>(
-            xg + ((((cx - c0) << 5) >> gs_log2) << 4) + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; e++) acc[e] += sf * dsum[e] + bq * xsum[e];
-        dsum = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int h = 0; h < MT; h++) {
+          const float4_t xsum = *reinterpret_cast<const float4_t*>(
+              xg + (((cx - c0) << 5) >> gs_log2) * XR + 16 * h + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[h][e] += sf * dsum[h][e] + bq * xsum[e];
+          dsum[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
       }
     }
   };
@@ -402,13 +418,16 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
     const uint32_t sh = *reinterpret_cast<const uint16_t*>(ssb + gi) & keep;
     const uint32_t bh = *reinterpret_cast<const uint16_t*>(bsb + gi) & keep;
-    uint4 a[4];
+    uint4 a[MT][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) a[i] = make_uint4(0, 0, 0, 0);
-    if (n < M) {
-      const uint4* xp = reinterpret_cast<const uint4*>(xs + n * ldx + (cx - c0) * 32);
+    for (int h = 0; h < MT; h++) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) a[i] = xp[i];
+      for (int i = 0; i < 4; i++) a[h][i] = make_uint4(0, 0, 0, 0);
+      if (n + 16 * h < M) {
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + (n + 16 * h) * ldx + (cx - c0) * 32);
+#pragma unroll
+        for (int i = 0; i < 4; i++) a[h][i] = xp[i];
+      }
     }
     if constexpr (__is_same(T, F16)) {
       uint32_t bf[16];
@@ -418,9 +437,11 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
          ...);
       }(std::make_integer_sequence<int, 32 / piece_codes<BITS>()>{});
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        acc = mfma16(F16{}, a[i],
-                     make_uint4(bf[4 * i], bf[4 * i + 1], bf[4 * i + 2], bf[4 * i + 3]), acc);
+      for (int i = 0; i < 4; i++) {
+        const uint4 b = make_uint4(bf[4 * i], bf[4 * i + 1], bf[4 * i + 2], bf[4 * i + 3]);
+#pragma unroll
+        for (int h = 0; h < MT; h++) acc[h] = mfma16(F16{}, a[h][i], b, acc[h]);
+      }
     } else {
       const float sf = to_f32(BF16{}, (uint16_t)sh), bfl = to_f32(BF16{}, (uint16_t)bh);
       uint32_t hi[16], lo[16];
@@ -430,10 +451,13 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       dequant_piece_bf16<BITS, 24>(wv[d], sf, bfl, hi, lo);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        acc = mfma16(BF16{}, a[i],
-                     make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]), acc);
-        acc = mfma16(BF16{}, a[i],
-                     make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]), acc);
+        const uint4 bh = make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]);
+        const uint4 bl = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
+#pragma unroll
+        for (int h = 0; h < MT; h++) {
+          acc[h] = mfma16(BF16{}, a[h][i], bh, acc[h]);
+          acc[h] = mfma16(BF16{}, a[h][i], bl, acc[h]);
+        }
       }
     }
   };
@@ -466,20 +490,25 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   }
 
   // ---- sum the 16 wavefront tiles (the buffer overlays x: barrier first);
-  // D[m][n] with m = 4*(lane/16) + e
+  // tile h holds D[m][n] with m = 16 h + 4*(lane/16) + e; thread t < 256 MT
+  // sums element t % 256 of tile t / 256
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 4; e++) red[(wave * 64 + lane) * 4 + e] = acc[e];
+  for (int h = 0; h < MT; h++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) red[h * kMvThreads * 4 + (wave * 64 + lane) * 4 + e] = acc[h][e];
   __syncthreads();
-  const int ln = tid >> 2, e = tid & 3;
-  const int m = 4 * (ln >> 4) + e, col = n0 + (ln & 15);
+  constexpr int kOut = 256 * MT;   // outputs of the workgroup's tiles
+  const int th = tid >> 8, tl = tid & 255;
+  const int ln = tl >> 2, e = tl & 3;
+  const int m = 16 * th + 4 * (ln >> 4) + e, col = n0 + (ln & 15);
   float v = 0.0f;
-  if (tid < 256) {
+  if (tid < kOut) {
 #pragma unroll
-    for (int w = 0; w < kMvWaves; w++) v += red[w * 256 + tid];
+    for (int w = 0; w < kMvWaves; w++) v += red[th * kMvThreads * 4 + w * 256 + tl];
   }
   if (ks == 1) {
-    if (tid < 256 && m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, v);
+    if (tid < kOut && m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, v);
     return;
   }
   // ---- K split over ks workgroups: each writes its 16 x 16 partial tile to
@@ -494,9 +523,9 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   // precedes the counter update, and the last workgroup reads the tiles only
   // after its update has returned.
   __shared__ unsigned last;
-  float* wsb = ws + (int64_t)blockIdx.x * ks * 256;
-  if (tid < 256) __hip_atomic_store(wsb + split * 256 + tid, v, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+  float* wsb = ws + (int64_t)blockIdx.x * ks * kOut;
+  if (tid < kOut) __hip_atomic_store(wsb + split * kOut + tid, v, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): the stores have completed
   __syncthreads();
   if (tid == 0)
@@ -504,10 +533,10 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
                                          "agent") == (unsigned)(ks - 1);
   __syncthreads();
   if (!last) return;
-  if (tid < 256) {
+  if (tid < kOut) {
     float t = 0.0f;
     for (int sp = 0; sp < ks; sp++)
-      t += __hip_atomic_load(wsb + sp * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t += __hip_atomic_load(wsb + sp * kOut + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (m < M && col < N) y[(int64_t)m * N + col] = from_f32(T{}, t);
   }
 }
@@ -525,19 +554,21 @@ hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st)
   const int bpr = p.klen / 512;
   const bool xdma = p.klen % 512 == 0 && (int64_t)p.ks * p.klen == L.K &&
                     (bpr & (bpr - 1)) == 0 && L.M * bpr <= kMvWaves * kMvMaxXu;
-  auto go = [&]<bool XD>() {
-    hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING, XD>), dim3((L.N + 15) / 16, p.ks),
+  auto go = [&]<bool XD, int MT>() {
+    hipLaunchKernelGGL((qmv_mfma_kernel<T, BITS, DEPTH, RING, XD, MT>), dim3((L.N + 15) / 16, p.ks),
                        dim3(kMvThreads), lds, st, static_cast<const uint16_t*>(L.x),
                        reinterpret_cast<const uint8_t*>(L.wq), static_cast<const uint16_t*>(L.s),
                        static_cast<const uint16_t*>(L.b), static_cast<uint16_t*>(L.y), L.M, L.N,
                        L.K, ilog2(L.gs), m2, xu, sbu, p.ks, p.sps, L.ws, L.cnt,
                        xdma ? ilog2(bpr) : 0);
   };
-  if (xdma) {
-    go.template operator()<true>();
-    return hipGetLastError();
+  if (L.M > 16) {
+    if (xdma) go.template operator()<true, 2>();
+    else go.template operator()<false, 2>();
+  } else {
+    if (xdma) go.template operator()<true, 1>();
+    else go.template operator()<false, 1>();
   }
-  go.template operator()<false>();
   return hipGetLastError();
 }
 
@@ -545,7 +576,7 @@ hipError_t launch_depth(const MvLaunch& L, const QmvMfmaPlan& p, hipStream_t st)
 // ring of 3 steps
 template <class T, int BITS>
 hipError_t launch_bits(const MvLaunch& L, hipStream_t st) {
-  const QmvMfmaPlan p = qmv_mfma_plan(L.N, L.K);
+  const QmvMfmaPlan p = qmv_mfma_plan(L.N, L.K, L.M);
   const int nsw = (p.sps + kMvWaves - 1) / kMvWaves;
   if (nsw <= 1) return launch_depth<T, BITS, 1, false>(L, p, st);
   if (nsw <= 2) return launch_depth<T, BITS, 2, false>(L, p, st);

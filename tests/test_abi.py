@@ -164,8 +164,8 @@ def test_route_is_a_step_function_of_m(L):
                     assert first is not None, (dt, bits, gs, N, K)
                     assert all(r == Q.KERNEL_TILE for r in rs[first - 1:]), (dt, bits, gs, N, K)
                     assert L.qmm_crossover_m(dt, bits, gs, N, K) == first
-                    # the MFMA GEMV never takes more than 16 rows
-                    assert all(r != Q.KERNEL_MFMA_GEMV for r in rs[16:])
+                    # the MFMA GEMV never takes more than 32 rows
+                    assert all(r != Q.KERNEL_MFMA_GEMV for r in rs[32:])
 
 
 def test_route_rejects_invalid_arguments(L):
@@ -185,7 +185,7 @@ def test_force_kernel(L):
         assert L.qmm_route(0, 4, 64, 1, 4096, 4096) == Q.KERNEL_TILE
         assert L.qmm_force_kernel(Q.KERNEL_MFMA_GEMV) == Q.QMM_OK
         assert L.qmm_route(0, 4, 64, 1, 4096, 4096) == Q.KERNEL_MFMA_GEMV
-        assert L.qmm_route(0, 4, 64, 17, 4096, 4096) == Q.KERNEL_TILE   # does not fit: automatic
+        assert L.qmm_route(0, 4, 64, 33, 4096, 4096) == Q.KERNEL_TILE   # does not fit: automatic
         assert L.qmm_force_kernel(Q.KERNEL_GEMV) == Q.QMM_OK
         assert L.qmm_route(0, 4, 64, 64, 4096, 4096) == Q.KERNEL_GEMV
     finally:

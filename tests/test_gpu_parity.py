@@ -147,6 +147,27 @@ def test_qmv_mfma(orc, dt, M, N, K, gs, bits):
     _run_mm(Q.qmm_t, orc, dt, M, N, K, gs, bits, seed=K + M + 1)
 
 
+@pytest.mark.parametrize("M,N,K,gs,bits", [
+    (17, 200, 4160, 64, 4),     # two row tiles, 3 K ranges of 11 steps (x through registers)
+    (24, 4096, 4096, 64, 4),    # 256 row blocks, 2 K ranges of 2048 (direct x copy)
+    (32, 96, 2048, 128, 6),     # one range, 128 x blocks of 512 (the direct copy's limit)
+    (20, 40, 8704, 32, 8),      # 5 ranges of 14 steps
+    (32, 130, 4096, 32, 5),     # ragged row block
+    (29, 72, 2048, 64, 3),
+    (25, 64, 2048, 32, 2),
+])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_qmv_mfma_two_row_tiles(orc, dt, M, N, K, gs, bits):
+    """The MFMA GEMV with 17..32 rows of x (two 16-row tiles sharing each
+    dequantized W fragment), forced through qmm_t and qmv."""
+    try:
+        Q.force_kernel(Q.KERNEL_MFMA_GEMV)
+        _run_mm(Q.qmm_t, orc, dt, M, N, K, gs, bits, seed=K + M)
+        _run_mm(Q.qmv, orc, dt, M, N, K, gs, bits, seed=K + M + 1)
+    finally:
+        Q.force_kernel(Q.KERNEL_NONE)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_qmv_mfma_split_k_repeat(orc, dt):
     """Narrow layers split K over workgroups; the last one to finish adds the
