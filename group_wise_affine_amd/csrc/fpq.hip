@@ -259,11 +259,7 @@ __global__ __launch_bounds__(256) void fp_dequantize_kernel(const uint8_t* __res
 // u % 64, for R rows at once so that their loads overlap; the codes are
 // decoded into T pairs and multiplied with the activation pairs by
 // v_dot2_f32_{f16,bf16} (exact products, fp32 sums).
-// Wavefronts per workgroup (WV): 8 for E4M3 codes; for E2M1, 8 when that
-// still gives 512 workgroups at 4 rows per wavefront (several rows of x or
-// gathered products), else 4. Measured on 4096 x 4096: M = 1 mxfp8 6.44 /
-// 7.21 us and mxfp4 6.76 / 6.19 us with 8 / 4; mxfp4 M = 4 8.57 / 9.57 us;
-// 2 wavefronts 9.2 - 9.3 us.
+// Wavefronts per workgroup (WV) and rows per wavefront: see fp_qmv_t.
 
 // Gathered products (GA): output batch z = blockIdx.z multiplies x batch
 // lidx[z] (of nxb, M rows each) by weight batch ridx[z] (of nwb), indices
@@ -402,25 +398,27 @@ hipError_t fp_qmv_r(const void* x, const uint32_t* wq, const uint8_t* sc, int64_
   return hipGetLastError();
 }
 
-// Rows per wavefront: the most (of 4, 2, 1) that still give 512 workgroups
-// (1024 for 8-bit codes, whose rows are twice as long) over the rows of W
-// and x. Measured on 4096 x 4096 at M = 1: 4-bit 7.4 / 6.2 / 7.6 us and
-// 8-bit 10.1 / 7.6 / 7.3 us for 4 / 2 / 1 rows; M = 4 (4-bit) 9.7 / 12.7 /
-// 21.4 us.
+// Rows per wavefront and wavefronts per workgroup, measured on 4096 x 4096
+// (f16, cold weights, every combination of 1/2/4 rows and 4/8 wavefronts):
+// E2M1 codes run best with 8 wavefronts and the most rows per wavefront that
+// still give 512 workgroups (mxfp4 M = 1 / 2 / 4: 4.24 / 5.03 / 7.34 us with
+// 1 / 2 / 4 rows; nvfp4 4.22 / 5.34 / 7.25), E4M3 codes with 4 wavefronts of
+// 2 rows once that gives 1024 workgroups (mxfp8 M = 2 / 4: 6.52 / 10.45 us,
+// against 6.98 / 11.9 with 8 wavefronts of 1 row), else 8 wavefronts of 1
+// row (M = 1: 5.79 us).
 template <class T, int BITS, int GS>
 hipError_t fp_qmv_t(const void* x, const uint32_t* wq, const uint8_t* sc, int64_t M, int64_t N,
                     int64_t K, void* y, hipStream_t st, const FpBatch* bt) {
   const int64_t want = BITS == 8 ? 1024 : 512, nb = bt ? bt->B : 1;
   auto blocks = [&](int64_t w, int64_t r) { return (N + w * r - 1) / (w * r) * M * nb; };
   if constexpr (BITS == 8) {
-    if (blocks(8, 4) >= want) return fp_qmv_r<T, BITS, GS, 4, 8>(x, wq, sc, M, N, K, y, st, bt);
-    if (blocks(8, 2) >= want) return fp_qmv_r<T, BITS, GS, 2, 8>(x, wq, sc, M, N, K, y, st, bt);
+    if (blocks(4, 2) >= want) return fp_qmv_r<T, BITS, GS, 2, 4>(x, wq, sc, M, N, K, y, st, bt);
     return fp_qmv_r<T, BITS, GS, 1, 8>(x, wq, sc, M, N, K, y, st, bt);
   } else {
     if (blocks(8, 4) >= want) return fp_qmv_r<T, BITS, GS, 4, 8>(x, wq, sc, M, N, K, y, st, bt);
-    if (blocks(4, 4) >= want) return fp_qmv_r<T, BITS, GS, 4, 4>(x, wq, sc, M, N, K, y, st, bt);
-    if (blocks(4, 2) >= want) return fp_qmv_r<T, BITS, GS, 2, 4>(x, wq, sc, M, N, K, y, st, bt);
-    return fp_qmv_r<T, BITS, GS, 1, 4>(x, wq, sc, M, N, K, y, st, bt);
+    if (blocks(8, 2) >= want) return fp_qmv_r<T, BITS, GS, 2, 8>(x, wq, sc, M, N, K, y, st, bt);
+    if (blocks(8, 1) >= want) return fp_qmv_r<T, BITS, GS, 1, 8>(x, wq, sc, M, N, K, y, st, bt);
+    return fp_qmv_r<T, BITS, GS, 1, 4>(x, wq, sc, M, N, K, y, st, bt);   // the most workgroups
   }
 }
 
