@@ -144,6 +144,38 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t m2,
   }
 }
 
+// x staging helpers. T pair (1, 1).
+template <class T>
+__host__ __device__ constexpr uint32_t unit_pair() {
+  return __is_same(T, F16) ? 0x3C003C00u : 0x3F803F80u;
+}
+// T bits of 2^-o (o at most 7: a normal value in both types)
+template <class T>
+__host__ __device__ constexpr uint32_t inv_pow2_bits(int o) {
+  return __is_same(T, F16) ? (uint32_t)(15 - o) << 10 : (uint32_t)(127 - o) << 7;
+}
+// T pair (2^-o(2j), 2^-o(2j+1)) for the activations of loaded word j
+// (elements 2j and 2j+1 of a chunk)
+template <class T, int BITS>
+__host__ __device__ constexpr uint32_t inv_off_pair(int j) {
+  return inv_pow2_bits<T>(pair_off<T, BITS>(2 * j)) |
+         (inv_pow2_bits<T>(pair_off<T, BITS>(2 * j + 1)) << 16);
+}
+// code of the high half of pair p
+template <int BITS>
+__host__ __device__ constexpr int pair_partner(int p) {
+  int r = 0;
+  for (int k = 0; k < 32; k++)
+    if (pair_index<BITS>(k) == p && pair_half<BITS>(k) == 1) r = k;
+  return r;
+}
+// v_perm_b32 selector: low half = half lo of the second source word, high
+// half = half hi of the first
+__host__ __device__ constexpr uint32_t pair_perm_sel(int lo, int hi) {
+  return (uint32_t)(2 * lo) | (uint32_t)(2 * lo + 1) << 8 | (uint32_t)(4 + 2 * hi) << 16 |
+         (uint32_t)(5 + 2 * hi) << 24;
+}
+
 constexpr int kXWaves = 2;                        // wavefronts staging x
 
 // One workgroup = WW W wavefronts (4 or 8) + 2 x wavefronts.
@@ -323,19 +355,28 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
         sum += f;
       }
     } else {
+      // activations keep their own bits (permuted into pair order, one byte
+      // permute per pair); the chunk's sum and the magic offset
+      // sum(x * MAGIC * 2^-o) come from dot2 of the pairs as loaded with
+      // (1, 1) and with (2^-o, 2^-o') (exact products, fp32 sums, two
+      // chains each)
+      if (!live) {
 #pragma unroll
-      for (int p = 0; p < 16; p++) px[p] = 0;
-      // activations keep their own bits (permuted into pair order); the
-      // magic offset sum(x * MAGIC * 2^-o) is formed in fp32 (exact scaling)
-#pragma unroll
-      for (int k = 0; k < 32; k++) {
-        const uint16_t h = live ? (uint16_t)(raw[k / 2] >> (16 * (k % 2))) : (uint16_t)0;
-        const float f = to_f32(T{}, h);
-        px[pair_index<BITS>(k)] |= (uint32_t)h << (16 * pair_half<BITS>(k));
-        sum += f;
-        d0 += f * __builtin_bit_cast(float, (uint32_t)(127 - pair_off<T, BITS>(k)) << 23);
+        for (int q = 0; q < 16; q++) raw[q] = 0;
       }
-      d0 *= T::kMagicF;
+      float s2[2] = {0.0f, 0.0f}, d2[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        s2[j & 1] = dot2(T{}, raw[j], unit_pair<T>(), s2[j & 1]);
+        d2[j & 1] = dot2(T{}, raw[j], inv_off_pair<T, BITS>(j), d2[j & 1]);
+      }
+      sum = s2[0] + s2[1];
+      d0 = (d2[0] + d2[1]) * T::kMagicF;
+#pragma unroll
+      for (int p = 0; p < 16; p++) {
+        const int klo = pair_code<BITS>(p), khi = pair_partner<BITS>(p);
+        px[p] = __builtin_amdgcn_perm(raw[khi / 2], raw[klo / 2], pair_perm_sel(klo & 1, khi & 1));
+      }
     }
     uint4* dst = reinterpret_cast<uint4*>(xs + (int64_t)task * XW);
 #pragma unroll
