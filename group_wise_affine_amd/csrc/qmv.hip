@@ -42,6 +42,9 @@ struct QmvCfg {
   // bf16 cannot hold 128 + q exactly for 8-bit codes: that case runs in fp32
   static constexpr bool kF32 = (BITS == 8) && __is_same(T, BF16);
   static constexpr int kXWords = kF32 ? 32 : 16;  // LDS words per x chunk
+  // LDS record of a chunk: its activations, then the chunk sum and the magic
+  // offset (padded to 16 bytes), so that one address serves all of them
+  static constexpr int kXRec = kXWords + 4;
 };
 
 // Weight chunks are read exactly once per call: nontemporal loads stream
@@ -211,7 +214,7 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     uint32_t m2, uint32_t magic, const int32_t* __restrict__ lidx,
     const int32_t* __restrict__ ridx, int nxb, int nwb) {
   using Cfg = QmvCfg<T, BITS>;
-  constexpr int XW = Cfg::kXWords;
+  constexpr int XW = Cfg::kXWords, XR = Cfg::kXRec;
   extern __shared__ uint32_t smem[];
   const int nch = K >> 5;
   // Batch z (gathered products): x batch lidx[z] and weight batch ridx[z]
@@ -231,9 +234,7 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
     y += (int64_t)z * M * N;
   }
   const int ntask = MB * nch;
-  uint32_t* xs = smem;                                            // [MB*nch][XW]
-  float* xsum = reinterpret_cast<float*>(smem + ntask * XW);       // [MB*nch]
-  float* xd0 = xsum + ntask;                                       // [MB*nch]
+  uint32_t* xs = smem;                                            // [MB*nch][XR]
   const int m0 = blockIdx.y * MB;
 
   const int tpr = 1 << tpr_log2;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
   const int G = K >> gs_log2;
   // staged scales then biases of the workgroup's rows, [2][rows_blk][G]
   // (16-byte aligned after the x region)
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(smem + ((ntask * (XW + 2) + 3) & ~3));
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(smem + ntask * XR);
   const int sb_units = SBL ? rows_blk * G / 8 : 0;  // 16-byte units per array
   const int batch = tpr * CPL;  // chunks of a row covered by one batch
   uint32_t wv[R][CPL][BITS];
@@ -378,12 +379,12 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
         px[p] = __builtin_amdgcn_perm(raw[khi / 2], raw[klo / 2], pair_perm_sel(klo & 1, khi & 1));
       }
     }
-    uint4* dst = reinterpret_cast<uint4*>(xs + (int64_t)task * XW);
+    uint4* dst = reinterpret_cast<uint4*>(xs + (int64_t)task * XR);
 #pragma unroll
     for (int q = 0; q < XW / 4; q++)
       dst[q] = make_uint4(px[4 * q], px[4 * q + 1], px[4 * q + 2], px[4 * q + 3]);
-    xsum[task] = sum;
-    xd0[task] = d0;
+    dst[XW / 4] = make_uint4(__builtin_bit_cast(uint32_t, sum), __builtin_bit_cast(uint32_t, d0),
+                             0u, 0u);
   };
 
   if (w_wave) {
@@ -447,11 +448,11 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
         if constexpr (Cfg::kF32) {
 #pragma unroll
           for (int m = 0; m < MB; m++) {
-            const float* xp = reinterpret_cast<const float*>(xs + (int64_t)(m * nch + c) * XW);
+            const float* xp = reinterpret_cast<const float*>(xs + (int64_t)(m * nch + c) * XR);
             float xv[32];
 #pragma unroll
             for (int k = 0; k < 32; k++) xv[k] = xp[k];
-            const float xsm = xsum[m * nch + c];
+            const float xsm = xp[XW];
 #pragma unroll
             for (int r = 0; r < R; r++) {
               float d = 0.0f;
@@ -469,15 +470,16 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
           for (int r = 0; r < R; r++) unpack_pairs<T, BITS>(wv[r][i], m2, magic_v, pr[r]);
 #pragma unroll
           for (int m = 0; m < MB; m++) {
-            const uint4* xp4 = reinterpret_cast<const uint4*>(xs + (int64_t)(m * nch + c) * XW);
+            const uint4* xp4 = reinterpret_cast<const uint4*>(xs + (int64_t)(m * nch + c) * XR);
             uint32_t xp[16];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
               const uint4 u = xp4[q];
               xp[4 * q] = u.x; xp[4 * q + 1] = u.y; xp[4 * q + 2] = u.z; xp[4 * q + 3] = u.w;
             }
-            const float xsm = xsum[m * nch + c];
-            const float d0 = xd0[m * nch + c];
+            const uint2 sd = *reinterpret_cast<const uint2*>(xp4 + 4);
+            const float xsm = __builtin_bit_cast(float, sd.x);
+            const float d0 = __builtin_bit_cast(float, sd.y);
             // partial sums per row: rows x partials >= 4 (rows of x give
             // independent chains as well)
             constexpr int NP = R * MB >= 4 ? 1 : 4 / (R * MB);
@@ -553,7 +555,7 @@ static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
   const int rows_per_block = WW * (64 / tpr) * R;
   const dim3 block((WW + kXWaves) * 64);
   const dim3 grid((N + rows_per_block - 1) / rows_per_block, (M + MB - 1) / MB, bt.B);
-  const size_t lds_x = (size_t)MB * nch * (Cfg::kXWords + 2) * 4;
+  const size_t lds_x = (size_t)MB * nch * Cfg::kXRec * 4;
   // staged scales / biases: one batch covers a row, the block's run of each
   // array is whole 16-byte units at 16-byte aligned addresses, the x lanes
   // copy it with kSbUnits loads each and it fits in LDS
@@ -647,7 +649,7 @@ static hipError_t launch_t(const void* x, const uint32_t* wq, const void* s,
                            const void* b, int M, int N, int K, int gs, void* y,
                            hipStream_t st, const QmvBatch& bt) {
   using Cfg = QmvCfg<T, BITS>;
-  const int64_t per_row = (int64_t)(K / 32) * (Cfg::kXWords + 2) * 4;
+  const int64_t per_row = (int64_t)(K / 32) * Cfg::kXRec * 4;
   int mb_max = (int)(kMaxLds / per_row);
   int want = 1;  // smallest of 1, 2, 4 covering M (4 at most)
   while (want < M && want < 4) want *= 2;
