@@ -254,9 +254,9 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
   const int batch = tpr * CPL;  // chunks of a row covered by one batch
   uint32_t wv[R][CPL][BITS];
   uint16_t sw[R][CPL], bw[R][CPL];  // raw scale / bias words
-  bool ok[R][CPL];
-  // Branch-free: out-of-range chunks read a clamped valid address and are
-  // zeroed through their scale and bias, so all loads issue back to back.
+  // Branch-free: out-of-range chunks read a clamped valid address, so all
+  // loads issue back to back; chunks past the row end are skipped when
+  // multiplying, and rows past N only feed sums that are never stored.
   // Chunk-major, so that chunk i of every row is in before chunk i + 1.
   auto load_batch = [&](int cb) {
 #pragma unroll
@@ -267,7 +267,6 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
         const int rowc = row < N ? row : N - 1;
         const int c = cb + t + i * tpr;
         const int cc = c < nch ? c : nch - 1;
-        ok[r][i] = (row < N) && (c < nch);
         load_chunk<BITS>(wq + (int64_t)rowc * row_bytes + (int64_t)cc * (4 * BITS), wv[r][i]);
         if constexpr (!SBL) {
           const int g = (cc << 5) >> gs_log2;
@@ -442,8 +441,8 @@ __global__ __launch_bounds__((WW + kXWaves) * 64) void qmv_kernel(
         float sf[R], bf[R];
 #pragma unroll
         for (int r = 0; r < R; r++) {
-          sf[r] = ok[r][i] ? to_f32(T{}, sw[r][i]) : 0.0f;
-          bf[r] = ok[r][i] ? to_f32(T{}, bw[r][i]) : 0.0f;
+          sf[r] = to_f32(T{}, sw[r][i]);
+          bf[r] = to_f32(T{}, bw[r][i]);
         }
         if constexpr (Cfg::kF32) {
 #pragma unroll
