@@ -14,7 +14,8 @@
 //    and dequantizes it into four 8-code B fragments of
 //    v_mfma_f32_16x16x32_{f16,bf16}: MFMA i takes codes 8i..8i+7 of the four
 //    chunks, so A lane (m, g) holds the matching 8 elements of row m of x in
-//    natural order (rows m >= M stay zero). f16: magic pairs and packed f16
+//    natural order (rows m >= M repeat row M - 1 and feed only output rows
+//    that are never stored). f16: magic pairs and packed f16
 //    FMAs, one rounding of s*q+b. bf16 with 2, 3, 5 or 6 bits: s*q+b in
 //    fp32 split into hi = bf16(w) and lo = bf16(w - hi), both multiplied (a
 //    single bf16 rounding of the weights would cost ~1e-3 relative error).
@@ -356,9 +357,10 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       uint4 a[MT];
 #pragma unroll
       for (int h = 0; h < MT; h++) {
-        a[h] = make_uint4(0, 0, 0, 0);
-        if (n + 16 * h < M)
-          a[h] = *reinterpret_cast<const uint4*>(xs + (n + 16 * h) * ldx + (cx - c0) * 32 + 8 * g);
+        // (rows m >= M repeat row M - 1: they only feed output rows that are
+        // never stored)
+        const int mr = n + 16 * h < M ? n + 16 * h : M - 1;
+        a[h] = *reinterpret_cast<const uint4*>(xs + mr * ldx + (cx - c0) * 32 + 8 * g);
         if constexpr (XDMA && BITS == 4)   // copied in natural order: piece order 0 4 1 5 2 6 3 7
           a[h] = make_uint4(__builtin_amdgcn_perm(a[h].z, a[h].x, 0x05040100u),
                             __builtin_amdgcn_perm(a[h].z, a[h].x, 0x07060302u),
@@ -406,6 +408,11 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     }
   };
 
+  // The magic pattern lives in a VGPR so that each magic pair is one
+  // v_and_or_b32 (with the mask in an SGPR; a VOP3 reads one SGPR at most
+  // and no literal on gfx9, so a literal pattern costs an and and an or).
+  uint32_t magic_v = F16::kMagic;
+  if constexpr (__is_same(T, F16)) asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "i"(F16::kMagic));
   auto compute = [&](int j, int d) QMM_INLINE {
     // A fragments: lane (m, g) = (n, g) takes 8 elements of row m of x
     // (rows m >= M stay zero); the chunk is clamped into the row (a chunk
@@ -418,22 +425,21 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
     const uint32_t sh = *reinterpret_cast<const uint16_t*>(ssb + gi) & keep;
     const uint32_t bh = *reinterpret_cast<const uint16_t*>(bsb + gi) & keep;
+    // (rows m >= M of the A fragment repeat row M - 1: they only feed
+    // output rows that are never stored)
     uint4 a[MT][4];
 #pragma unroll
     for (int h = 0; h < MT; h++) {
+      const int mr = n + 16 * h < M ? n + 16 * h : M - 1;
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + mr * ldx + (cx - c0) * 32);
 #pragma unroll
-      for (int i = 0; i < 4; i++) a[h][i] = make_uint4(0, 0, 0, 0);
-      if (n + 16 * h < M) {
-        const uint4* xp = reinterpret_cast<const uint4*>(xs + (n + 16 * h) * ldx + (cx - c0) * 32);
-#pragma unroll
-        for (int i = 0; i < 4; i++) a[h][i] = xp[i];
-      }
+      for (int i = 0; i < 4; i++) a[h][i] = xp[i];
     }
     if constexpr (__is_same(T, F16)) {
       uint32_t bf[16];
       [&]<int... C>(std::integer_sequence<int, C...>) QMM_INLINE {
         (dequant_piece_f16_pk<BITS, C * piece_codes<BITS>(), piece_codes<BITS>()>(
-             wv[d], sh * 0x10001u, bh * 0x10001u, m2, F16::kMagic, bf),
+             wv[d], sh * 0x10001u, bh * 0x10001u, m2, magic_v, bf),
          ...);
       }(std::make_integer_sequence<int, 32 / piece_codes<BITS>()>{});
 #pragma unroll
