@@ -96,9 +96,14 @@ __device__ __forceinline__ void load_wchunk_buf(__amdgpu_buffer_rsrc_t r, uint32
           u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + 8 * h, 0, 0));
       w[2 * h] = u.x; w[2 * h + 1] = u.y;
     }
-  } else {  // 3 and 5 bits: 4-byte aligned chunks
-#pragma unroll
-    for (int i = 0; i < BITS; i++) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+  } else if constexpr (BITS == 3) {   // 12-byte chunks, 4-byte aligned: one 12-byte load
+    typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+    const u32x3_t u = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
+    w[0] = u.x; w[1] = u.y; w[2] = u.z;
+  } else {   // 5 bits: 20-byte chunks, 4-byte aligned: a 16-byte and a 4-byte load
+    const u32x4_t u = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 16, 0, 0);
   }
 }
 
@@ -106,10 +111,14 @@ __device__ __forceinline__ void load_wchunk_buf(__amdgpu_buffer_rsrc_t r, uint32
 // RING = false the kernel runs one round (every wavefront has at most DEPTH
 // steps); with RING = true slot d is refilled with the step one round later
 // right after it is consumed.
-// vector-memory instructions of one W chunk load (load_wchunk_buf)
+// vector-memory instructions of one W chunk load (load_wchunk_buf). Each is
+// already the widest load of its bytes, so the compiler cannot merge them
+// into fewer instructions: the x copy's vmcnt wait below counts on that (a
+// count above the real one would let older x copies still be landing when
+// the barrier passes).
 template <int BITS>
 constexpr int wchunk_loads() {
-  return (BITS == 4 || BITS == 8) ? BITS / 4 : (BITS == 2 || BITS == 6) ? BITS / 2 : BITS;
+  return (BITS == 4 || BITS == 8) ? BITS / 4 : (BITS == 2 || BITS == 6) ? BITS / 2 : BITS == 3 ? 1 : 2;
 }
 
 typedef __attribute__((address_space(3))) void mv_lds_t;
@@ -326,6 +335,8 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
   for (int h = 0; h < MT; h++) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // exact codes: chunk i of the step on MFMA i (see the header), groups of
   // gs codes applied to the fp32 sums as s * D + (b - 128 s) * sum(x)
+  uint32_t magic_x = 0x43004300u;   // bf16 (128, 128)
+  if constexpr (__is_same(T, BF16)) asm volatile("v_mov_b32 %0, %1" : "=v"(magic_x) : "i"(0x43004300));
   auto compute_exact = [&](int j, int d) QMM_INLINE {
     const int cs = c0 + 4 * (wave + kMvWaves * j);   // the step's first chunk
     uint32_t t[BITS];
@@ -346,66 +357,71 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
       r = __builtin_amdgcn_permlane16_swap(t[2 * W + w], t[3 * W + w], false, false);
       t[2 * W + w] = r[0]; t[3 * W + w] = r[1];
     }
-    const int cpg_log2 = gs_log2 - 5;                // chunks per group: 1, 2, 4
-    float4_t dsum[MT];
+    // chunks per group (1, 2 or 4) as a compile-time count, so that the
+    // group ends are fixed places in the unrolled chunk loop
+    auto chunks = [&]<int CPG>() QMM_INLINE {
+      float4_t dsum[MT];
 #pragma unroll
-    for (int h = 0; h < MT; h++) dsum[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int c = cs + i;
-      const int cx = c < c1 ? c : c1 - 1;
-      uint4 a[MT];
-#pragma unroll
-      for (int h = 0; h < MT; h++) {
-        // (rows m >= M repeat row M - 1: they only feed output rows that are
-        // never stored)
-        const int mr = n + 16 * h < M ? n + 16 * h : M - 1;
-        a[h] = *reinterpret_cast<const uint4*>(xs + mr * ldx + (cx - c0) * 32 + 8 * g);
-        if constexpr (XDMA && BITS == 4)   // copied in natural order: piece order 0 4 1 5 2 6 3 7
-          a[h] = make_uint4(__builtin_amdgcn_perm(a[h].z, a[h].x, 0x05040100u),
-                            __builtin_amdgcn_perm(a[h].z, a[h].x, 0x07060302u),
-                            __builtin_amdgcn_perm(a[h].w, a[h].y, 0x05040100u),
-                            __builtin_amdgcn_perm(a[h].w, a[h].y, 0x07060302u));
-      }
-      uint4 b;
-      if constexpr (BITS == 4) {
-        const uint32_t w = t[i];
-        b = make_uint4((w & 0x000f000fu) | 0x43004300u, ((w >> 4) & 0x000f000fu) | 0x43004300u,
-                       ((w >> 8) & 0x000f000fu) | 0x43004300u,
-                       ((w >> 12) & 0x000f000fu) | 0x43004300u);
-      } else {
-        uint32_t p[4];
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-          const uint32_t w = t[2 * i + h];
-          const float f0 = (float)(w & 0xff), f1 = (float)((w >> 8) & 0xff),
-                      f2 = (float)((w >> 16) & 0xff), f3 = (float)(w >> 24);
-          p[2 * h] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
-                                           __builtin_bit_cast(uint32_t, f0), 0x07060302u);
-          p[2 * h + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
-                                               __builtin_bit_cast(uint32_t, f2), 0x07060302u);
-        }
-        b = make_uint4(p[0], p[1], p[2], p[3]);
-      }
-#pragma unroll
-      for (int h = 0; h < MT; h++) dsum[h] = mfma16(BF16{}, a[h], b, dsum[h]);
-      if (((i + 1) & ((1 << cpg_log2) - 1)) == 0) {
-        // end of a group: its scale and bias (zero past the split's end)
-        const uint32_t keep = ~(uint32_t)((c1 - 1 - c) >> 31);
-        const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
-        const float sf = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(ssb + gi) & keep));
-        const float bfl = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(bsb + gi) & keep));
-        const float bq = bfl - 128.0f * sf * (BITS == 4 ? 1.0f : 0.0f);
+      for (int i = 0; i < 4; i++) {
+        const int c = cs + i;
+        const int cx = c < c1 ? c : c1 - 1;
+        uint4 a[MT];
 #pragma unroll
         for (int h = 0; h < MT; h++) {
-          const float4_t xsum = *reinterpret_cast<const float4_t*>(
-              xg + (((cx - c0) << 5) >> gs_log2) * XR + 16 * h + 4 * g);
+          // (rows m >= M repeat row M - 1: they only feed output rows that
+          // are never stored)
+          const int mr = n + 16 * h < M ? n + 16 * h : M - 1;
+          a[h] = *reinterpret_cast<const uint4*>(xs + mr * ldx + (cx - c0) * 32 + 8 * g);
+          if constexpr (XDMA && BITS == 4)   // copied in natural order: piece order 0 4 1 5 2 6 3 7
+            a[h] = make_uint4(__builtin_amdgcn_perm(a[h].z, a[h].x, 0x05040100u),
+                              __builtin_amdgcn_perm(a[h].z, a[h].x, 0x07060302u),
+                              __builtin_amdgcn_perm(a[h].w, a[h].y, 0x05040100u),
+                              __builtin_amdgcn_perm(a[h].w, a[h].y, 0x07060302u));
+        }
+        uint4 b;
+        if constexpr (BITS == 4) {
+          // 128 + q: each code pair or-ed into the mantissas of bf16 (128, 128)
+          // (mask in an SGPR, pattern in a VGPR: one v_and_or_b32 per pair)
+          const uint32_t w = t[i];
+          b = make_uint4((w & m2) | magic_x, ((w >> 4) & m2) | magic_x,
+                         ((w >> 8) & m2) | magic_x, ((w >> 12) & m2) | magic_x);
+        } else {
+          uint32_t p[4];
 #pragma unroll
-          for (int e = 0; e < 4; e++) acc[h][e] += sf * dsum[h][e] + bq * xsum[e];
-          dsum[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int h = 0; h < 2; h++) {
+            const uint32_t w = t[2 * i + h];
+            const float f0 = (float)(w & 0xff), f1 = (float)((w >> 8) & 0xff),
+                        f2 = (float)((w >> 16) & 0xff), f3 = (float)(w >> 24);
+            p[2 * h] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                                             __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+            p[2 * h + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
+                                                 __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+          }
+          b = make_uint4(p[0], p[1], p[2], p[3]);
+        }
+#pragma unroll
+        for (int h = 0; h < MT; h++)
+          dsum[h] = mfma16(BF16{}, a[h], b, i % CPG == 0 ? float4_t{0.0f, 0.0f, 0.0f, 0.0f} : dsum[h]);
+        if ((i + 1) % CPG == 0) {
+          // end of a group: its scale and bias (zero past the split's end)
+          const uint32_t keep = ~(uint32_t)((c1 - 1 - c) >> 31);
+          const int gi = 2 * (n * G + ((cx << 5) >> gs_log2));
+          const float sf = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(ssb + gi) & keep));
+          const float bfl = to_f32(BF16{}, (uint16_t)(*reinterpret_cast<const uint16_t*>(bsb + gi) & keep));
+          const float bq = bfl - 128.0f * sf * (BITS == 4 ? 1.0f : 0.0f);
+#pragma unroll
+          for (int h = 0; h < MT; h++) {
+            const float4_t xsum = *reinterpret_cast<const float4_t*>(
+                xg + (((cx - c0) << 5) >> gs_log2) * XR + 16 * h + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[h][e] = fmaf(bq, xsum[e], fmaf(sf, dsum[h][e], acc[h][e]));
+          }
         }
       }
-    }
+    };
+    if (gs_log2 == 5) chunks.template operator()<1>();
+    else if (gs_log2 == 6) chunks.template operator()<2>();
+    else chunks.template operator()<4>();
   };
 
   // The magic pattern lives in a VGPR so that each magic pair is one
