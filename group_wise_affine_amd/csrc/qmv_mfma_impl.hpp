@@ -314,18 +314,20 @@ __global__ __launch_bounds__(kMvThreads) void qmv_mfma_kernel(
     const int ngl = (klen + (1 << gs_log2) - 1) >> gs_log2;
     for (int t = tid; t < ngl * XR; t += kMvThreads) {
       const int m = t & (XR - 1), gl = t / XR;
-      float sum = 0.0f;
+      // (pairs of x times bf16 (1, 1) by v_dot2: exact products, fp32 sums
+      // in four chains)
+      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (m < M) {
         const uint4* xp = reinterpret_cast<const uint4*>(xs + m * ldx + (gl << gs_log2));
         for (int u = 0; u < (1 << gs_log2) / 8; u++) {
           const uint4 v = xp[u];
-          sum += (__builtin_bit_cast(float, v.x << 16) + __builtin_bit_cast(float, v.x & 0xffff0000u)) +
-                 (__builtin_bit_cast(float, v.y << 16) + __builtin_bit_cast(float, v.y & 0xffff0000u)) +
-                 (__builtin_bit_cast(float, v.z << 16) + __builtin_bit_cast(float, v.z & 0xffff0000u)) +
-                 (__builtin_bit_cast(float, v.w << 16) + __builtin_bit_cast(float, v.w & 0xffff0000u));
+          s4[0] = dot2(BF16{}, v.x, 0x3F803F80u, s4[0]);
+          s4[1] = dot2(BF16{}, v.y, 0x3F803F80u, s4[1]);
+          s4[2] = dot2(BF16{}, v.z, 0x3F803F80u, s4[2]);
+          s4[3] = dot2(BF16{}, v.w, 0x3F803F80u, s4[3]);
         }
       }
-      xg[t] = sum;
+      xg[t] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     __syncthreads();
   }

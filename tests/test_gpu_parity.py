@@ -389,6 +389,39 @@ def test_tile_reads_only_landed_copies(orc, M, N, K, bits):
         assert_parity(from_dev(y), yo, dt, f"tile after NaN launch {it} M{M} N{N} K{K} b{bits}")
 
 
+@pytest.mark.parametrize("M,N,K,gs,bits", [
+    (12, 64, 6144, 64, 5),      # K split, one step per wavefront: 16 + 4 byte chunk loads
+    (6, 96, 4096, 64, 3),       # 12-byte chunk loads
+    (16, 4096, 4096, 64, 5),    # 256 row blocks, two steps per wavefront
+    (8, 512, 8192, 32, 3),
+    (4, 256, 4096, 64, 4),
+])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_mfma_gemv_reads_only_landed_x(orc, dt, M, N, K, gs, bits):
+    """Regression: the MFMA GEMV's direct x copy into LDS ends with a wait
+    that must leave only the weight loads in flight. When the compiler merged
+    the 3- and 5-bit chunk loads into fewer instructions than the wait
+    counted, the barrier could pass with x copies still landing. Launches on
+    NaN activations leave NaN in the x region of LDS; a read before the copy
+    lands then shows as NaN or a parity failure in the next launch."""
+    code = orc_code(orc, dt)
+    _, wq, s, b = _quantized(orc, dt, N, K, gs, bits, seed=N + K + bits)
+    x = synth.normal((M, K), seed=M + bits, dt=dt)
+    yo, _ = orc.qmm_t(x, wq, s, b, code, gs, bits, nthreads=8)
+    wd, sd, bd = bytes_to_words_dev(wq), to_dev(s, dt), to_dev(b, dt)
+    xd = to_dev(x, dt)
+    xnan = torch.full((M, K), float("nan"), dtype=xd.dtype, device="cuda")
+    try:
+        Q.force_kernel(Q.KERNEL_MFMA_GEMV)
+        for it in range(8):
+            Q.qmm_t(xnan, wd, sd, bd, gs, bits)
+            y = Q.qmm_t(xd, wd, sd, bd, gs, bits)
+            torch.cuda.synchronize()
+            assert_parity(from_dev(y), yo, dt, f"MFMA GEMV after NaN launch {it} {dt} M{M} N{N} K{K} b{bits}")
+    finally:
+        Q.force_kernel(Q.KERNEL_NONE)
+
+
 def test_scratch_calls_on_two_streams(orc):
     """Calls that use the shared split-K scratch, queued alternately on two
     streams without any ordering by the caller: the library orders them (an
