@@ -208,6 +208,12 @@ Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allo
 // Largest K the streaming dot2 GEMV stages in LDS.
 int64_t qmv_max_k(int bits, int dt);
 
+// Whether the streaming GEMV runs one row of x of a single product in its
+// 2-chunk, 8-wavefront lane shape (5-, 6- and 8-bit codes on layers that make
+// one round of 256 to 320 workgroups with 4 chunks per lane, rows of at most
+// 4096 codes): the launcher's own choice for M = 1.
+bool qmv_two_chunk_shape(int64_t N, int64_t K, int bits);
+
 // Measurement override: route() returns r wherever that kernel takes the
 // shape (kRouteNone: the automatic choice everywhere).
 void force_route(Route r);

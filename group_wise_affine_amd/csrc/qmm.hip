@@ -203,17 +203,21 @@ Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allo
   //    costs ~5 us at M = 1 on a 9.4 MB layer, ~7 at 2 and ~10 at 3-4; the
   //    MFMA GEMV is nearly flat in M (6.2-7.0 us f16 on 4096 x 4096, 5.5-6.4
   //    on 8192 x 2048) but slower at M = 1;
-  //  * bf16: the MFMA GEMV (7.9-8.8 us on 4096 x 4096 4-bit, 6.9-7.8 on
-  //    8192 x 2048) wins from 3 rows on every layer, the streaming GEMV up to
-  //    2; with 8-bit codes the streaming GEMV works in fp32 (33 us at
-  //    M = 1), so the MFMA GEMV takes every M it fits;
+  //  * bf16: the MFMA GEMV (8.3-9.7 us on 2048 x 8192 4-bit, 6.6-7.6 on
+  //    8192 x 2048) wins from 3 rows on most layers, the streaming GEMV up
+  //    to 2; with 8-bit codes the streaming GEMV works in fp32 and keeps
+  //    only M = 1, and only where it runs its 2-chunk lane shape (4096 x
+  //    4096: 7.7 against 10.3 us; 12.0 against 8.8 at M = 2); on layers of
+  //    at most 2^20 weights it matches the MFMA GEMV at 8 rows and is
+  //    5-9% faster from 12 to 32 rows (512 x 2048);
   //  * the tile kernel costs 8-18 us at M <= 32 whatever the layer size, so
   //    layers of at most 2^22 weights, whose streaming passes take ~1 us,
   //    stay on the streaming GEMV up to 32 rows.
   const bool gemv_fp32 = dt == 1 && bits == 8;
   const bool small = N * K <= ((int64_t)1 << 22);
   int64_t m0;   // first M on the MFMA GEMV
-  if (gemv_fp32 || !dot2_ok) m0 = 1;
+  if (!dot2_ok) m0 = 1;
+  else if (gemv_fp32) m0 = qmv_two_chunk_shape(N, K, bits) ? 2 : 1;
   else if (dt == 0 && K > 8192 && N >= 4096) m0 = 1;   // long rows: few streaming passes fit
   else if (dt == 0) m0 = N * K >= ((int64_t)1 << 23) ? 2 : 3;
   else m0 = 3;
@@ -222,7 +226,8 @@ Route route(int dt, int bits, int gs, int64_t M, int64_t N, int64_t K, bool allo
   // layer of >= 256 row blocks, doubling its workgroups (4096 x 4096: 11.7
   // against 10.9 us at M = 24)
   const bool rows_ok = M <= 16 || (N + 15) / 16 < 256 || K <= 2048;
-  if (mfma_ok && M >= m0 && rows_ok) return kRouteQmvMfma;
+  const bool tiny_bf16 = dt == 1 && !gemv_fp32 && dot2_ok && N * K <= ((int64_t)1 << 20) && M > 8;
+  if (mfma_ok && M >= m0 && rows_ok && !tiny_bf16) return kRouteQmvMfma;
   if (!allow_tile) return dot2_ok ? kRouteQmv : kRouteNone;
   if (dot2_ok) {
     if (M < m0) return kRouteQmv;

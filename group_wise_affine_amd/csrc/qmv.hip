@@ -598,6 +598,20 @@ static hipError_t launch_shape(const void* x, const uint32_t* wq, const void* s,
   return hipGetLastError();
 }
 
+// One row of x, one product: does the layer take the 8-wavefront lane shape
+// (4 chunks of one row per lane making one round of 256 to 320 workgroups),
+// and, for 5-, 6- and 8-bit codes, its 2-chunk form (2 chunks per lane in
+// twice the workgroups, while one batch covers the row)?
+static bool one_round_8w(int64_t N, int64_t K) {
+  const int nch = (int)(K / 32);
+  const int64_t rows = 8 * (64 / tpr_for(nch, 4));
+  const int64_t b8 = (N + rows - 1) / rows;
+  return b8 >= 256 && b8 <= 320;
+}
+bool qmv_two_chunk_shape(int64_t N, int64_t K, int bits) {
+  return bits >= 5 && one_round_8w(N, K) && K / 32 <= 2 * 64;
+}
+
 template <class T, int BITS, int MB>
 static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
                             const void* b, int M, int N, int K, int gs,
