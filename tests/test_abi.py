@@ -193,6 +193,23 @@ def test_force_kernel(L):
     assert L.qmm_route(0, 4, 64, 64, 4096, 4096) == Q.KERNEL_TILE
 
 
+def test_route_measured_switch_points(L):
+    """Host-only: switch points that the committed route table (kernel-only
+    times of the three kernels forced at M = 1..32) fixes."""
+    G, M_, T = Q.KERNEL_GEMV, Q.KERNEL_MFMA_GEMV, Q.KERNEL_TILE
+    # f16 4096 x 4096 4-bit: streaming GEMV at M = 1, MFMA GEMV 2..16, tile from 24
+    assert [L.qmm_route(0, 4, 64, M, 4096, 4096) for M in (1, 2, 16, 24)] == [G, M_, M_, T]
+    # bf16 with 8-bit codes: the streaming GEMV keeps M = 1 where it runs its
+    # 2-chunk lane shape (4096 x 4096), not where it does not (rows of 8192
+    # codes need two batches of 2 chunks per lane)
+    assert L.qmm_route(1, 8, 64, 1, 4096, 4096) == G
+    assert L.qmm_route(1, 8, 64, 2, 4096, 4096) == M_
+    assert L.qmm_route(1, 8, 64, 1, 2048, 8192) == M_
+    # bf16 layers of at most 2^20 weights: streaming GEMV above 8 rows
+    assert [L.qmm_route(1, 4, 64, M, 512, 2048) for M in (1, 4, 8, 12, 32)] == [G, M_, M_, G, G]
+    assert [L.qmm_route(1, 4, 64, M, 2048, 2048) for M in (2, 3, 12, 32)] == [G, M_, M_, M_]
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(Q, "_lib", None)
     monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "missing.so"))
