@@ -47,7 +47,7 @@
  *        counters: qmm_t, qmm_t_batched, qmm_gather_qmm, qconv2d_nhwc,
  *        qmm_fp_t, qmm_fp_n, qmm_t_affine_packed and qmm_n when they split K;
  *      * the MFMA GEMV's partial tiles (2 MiB) and its 256 arrival counters:
- *        qmm_t, qmv and qmm_t_batched when they route up to 16 rows of x to
+ *        qmm_t, qmv and qmm_t_batched when they route up to 32 rows of x to
  *        the MFMA GEMV on a narrow layer.
  *    Calls queued on one stream are ordered by the stream. Calls of these
  *    entry points queued on different streams of one GPU, from one host
@@ -119,7 +119,7 @@ qmm_status qmm_dequantize(const uint32_t* wq, const void* scales,
 /*
  * y[M,N] = x[M,K] . dequant(wq, scales, biases)[N,K]^T, fp32 accumulation,
  * y rounded to nearest even in dt (f16 or bf16). Routes small M to the GEMV
- * kernels of qmv (the MFMA GEMV up to 16 rows, the streaming GEMV for a
+ * kernels of qmv (the MFMA GEMV up to 32 rows, the streaming GEMV for a
  * few rows) and larger M to the MFMA tile kernel; qmm_route names the
  * kernel for a shape and qmm_crossover_m the first M on the tile kernel. (Source: mlx 1.0.0 CPU backend, _qmm_t;
  * the packed-quants compare, the qmv/qmm_t split in the Metal dispatch.)
@@ -130,7 +130,7 @@ qmm_status qmm_t(const void* x, const uint32_t* wq, const void* scales,
 
 /*
  * Same operation and arguments as qmm_t, always on the GEMV kernels: the
- * MFMA GEMV (up to 16 rows of x that fit in LDS; every packed weight read
+ * MFMA GEMV (up to 32 rows of x that fit in LDS; every packed weight read
  * once) or the streaming GEMV (one pass over W per up to 4 rows of x).
  * Meant for M <= 16 (decode); correct for any M. QMM_E_SHAPE when K exceeds
  * both kernels' limits.
@@ -413,7 +413,7 @@ qmm_status qconv2d_nhwc(const void* x, int64_t B, int64_t H, int64_t W,
  */
 #define QMM_KERNEL_NONE 0       /* no kernel takes the shape */
 #define QMM_KERNEL_GEMV 1       /* streaming dot2 GEMV (x staged in LDS) */
-#define QMM_KERNEL_MFMA_GEMV 2  /* MFMA GEMV, at most 16 rows of x */
+#define QMM_KERNEL_MFMA_GEMV 2  /* MFMA GEMV, at most 32 rows of x */
 #define QMM_KERNEL_TILE 3       /* MFMA tile GEMM */
 
 /*
