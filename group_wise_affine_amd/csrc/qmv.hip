@@ -625,6 +625,17 @@ static hipError_t launch_mb(const void* x, const uint32_t* wq, const void* s,
   // two wavefronts per SIMD share the arithmetic that follows the weight
   // data, when that makes one round of 256 to 320 workgroups (such a
   // workgroup fills a CU's registers: more would run in a second round).
+  // Two rows of x on the same layers: 2 chunks per lane in 8 W wavefronts
+  // (same-box timings of the forced streaming GEMV at M = 2: f16 4096 x 4096
+  // 4-bit 6.18 -> 5.69 us, 2-bit 5.70 -> 5.27, 8-bit 8.85 -> 6.80; bf16
+  // 8192 x 2048 6-bit 6.19 -> 5.45; 4-bit rows of 2048 codes measured 4.80 ->
+  // 4.90 us, so rows that short keep this only for 5- to 8-bit codes)
+  if constexpr (MB == 2) {
+    const int64_t b8 = blocks_of(kShapes[4]);
+    if (b8 >= 256 && b8 <= 320 && nch <= 2 * 64 && (nch > 64 || BITS >= 5))
+      return launch_shape<T, BITS, MB, 2, 1, 8>(x, wq, s, b, M, N, K, gs, tpr_for(nch, 2), y,
+                                                st, bt);
+  }
   if (MB == 1) {
     const int64_t b8 = blocks_of(kShapes[4]);
     if (b8 >= 256 && b8 <= 320) {
